@@ -1,0 +1,161 @@
+"""CPU oracle for the DSA hot path (indexer scores -> top-k -> sparse GQA attention).
+
+TEST INFRASTRUCTURE.  Only the test suite, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg may import this package.  The product library
+(``long_context_sparse_score_amd``) never imports, links or calls it, and this
+package never imports the product library: the two share no code.
+
+The arithmetic lives in ``dsa_oracle.c`` (IEEE double loops, OpenMP over
+query rows); this module only marshals numpy arrays into it.  Each function
+cites the passage of the pages it follows ("Kwai Keye-VL-2.0 technical report"
+summary, page 5, section 1: Lightning Indexer with one shared MQA key per
+position, top-2048 selection, attention only over the selected positions,
+one index set serving all GQA heads; section 8: deterministic top-k).
+
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
+against brute force, closed forms, library routines and invariants.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile dsa_oracle.c with gcc into liboracle.so (always recompiles)."""
+    from . import build as _b
+
+    return _b.build(verbose=verbose)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        build()
+    lib = ctypes.CDLL(LIB_PATH)
+    p = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    lib.oracle_visible_counts.argtypes = [ctypes.c_int, p, p, i64, p, p]
+    lib.oracle_index_scores.argtypes = [ctypes.c_int, p, p, p, p, p, ctypes.c_int,
+                                        ctypes.c_int, i64, p, p, i64]
+    lib.oracle_topk.argtypes = [i64, p, p, i64, ctypes.c_int, p]
+    lib.oracle_sparse_attn.argtypes = [ctypes.c_int, p, p, p, p, p, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                       i64, p, p, ctypes.c_int, p, p]
+    for f in (lib.oracle_visible_counts, lib.oracle_index_scores, lib.oracle_topk,
+              lib.oracle_sparse_attn):
+        f.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray) -> ctypes.c_void_p:
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _c(a, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _bf16_bits(a) -> np.ndarray:
+    a = np.asarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("bf16 tensors are passed as their uint16 bit patterns")
+    return np.ascontiguousarray(a)
+
+
+def visible_counts(cu_q, cu_k, rows) -> np.ndarray:
+    """p + 1 for each packed query row (the causal prefix it may attend to)."""
+    lib = _load()
+    cu_q, cu_k = _c(cu_q, np.int32), _c(cu_k, np.int32)
+    rows = _c(rows, np.int64)
+    out = np.empty(rows.shape[0], np.int64)
+    if lib.oracle_visible_counts(len(cu_q) - 1, _ptr(cu_q), _ptr(cu_k), rows.shape[0],
+                                 _ptr(rows), _ptr(out)):
+        raise ValueError("a row lies outside every sequence or before its keys")
+    return out
+
+
+def index_scores(cu_q, cu_k, q_idx, k_idx, w, rows, ld=None) -> np.ndarray:
+    """Lightning-Indexer scores I[t, s] = sum_h w[t,h] * max(0, qI[t,h] . kI[s]).
+
+    Page 5 section 1 (the scout scores every position with one shared MQA key);
+    the weighted-ReLU form is the reading stated in the module header of
+    dsa_oracle.c.  Returns float64 [len(rows), ld]; columns beyond the row's
+    causal position are NaN.
+    """
+    lib = _load()
+    cu_q, cu_k = _c(cu_q, np.int32), _c(cu_k, np.int32)
+    q_idx, k_idx = _bf16_bits(q_idx), _bf16_bits(k_idx)
+    w = _c(w, np.float32)
+    rows = _c(rows, np.int64)
+    n_heads, d = q_idx.shape[1], q_idx.shape[2]
+    if k_idx.shape[1] != d or w.shape[1] != n_heads:
+        raise ValueError("indexer shapes disagree")
+    if ld is None:
+        ld = int(np.max(np.diff(cu_k)))
+    out = np.empty((rows.shape[0], ld), np.float64)
+    if lib.oracle_index_scores(len(cu_q) - 1, _ptr(cu_q), _ptr(cu_k), _ptr(q_idx),
+                               _ptr(k_idx), _ptr(w), n_heads, d, rows.shape[0], _ptr(rows),
+                               _ptr(out), ld):
+        raise ValueError("invalid row for the varlen layout")
+    return out
+
+
+def topk(scores, counts, k: int) -> np.ndarray:
+    """Deterministic top-k (page 5 section 1: k best positions per query;
+    section 8: deterministic selection).  Order (score desc, position asc),
+    output ascending positions padded with -1.  ``scores`` may be float32 or
+    float64; float32 values convert to double exactly, so the order is the
+    one float32 comparison gives."""
+    lib = _load()
+    scores = _c(scores, np.float64)
+    counts = _c(counts, np.int64)
+    out = np.empty((scores.shape[0], k), np.int32)
+    if lib.oracle_topk(scores.shape[0], _ptr(counts), _ptr(scores), scores.shape[1], k,
+                       _ptr(out)):
+        raise ValueError("a row count is outside 1..ld")
+    return out
+
+
+def sparse_attn(cu_q, cu_k, q, k, v, idx, rows, scale: float):
+    """Softmax attention of each query head restricted to the row's selected
+    positions (page 5 section 1: attention only among the chosen positions;
+    GQA head h reads KV head h // (Hq // Hkv), one index set for all heads).
+    Returns (out float64 [n, Hq, d], lse float64 [n, Hq])."""
+    lib = _load()
+    cu_q, cu_k = _c(cu_q, np.int32), _c(cu_k, np.int32)
+    q, k, v = _bf16_bits(q), _bf16_bits(k), _bf16_bits(v)
+    idx = _c(idx, np.int32)
+    rows = _c(rows, np.int64)
+    hq, d = q.shape[1], q.shape[2]
+    hkv = k.shape[1]
+    if hq % hkv or k.shape != v.shape or k.shape[2] != d:
+        raise ValueError("attention shapes disagree")
+    n = rows.shape[0]
+    out = np.empty((n, hq, d), np.float64)
+    lse = np.empty((n, hq), np.float64)
+    if lib.oracle_sparse_attn(len(cu_q) - 1, _ptr(cu_q), _ptr(cu_k), _ptr(q), _ptr(k),
+                              _ptr(v), hq, hkv, d, float(scale), n, _ptr(rows), _ptr(idx),
+                              idx.shape[1], _ptr(out), _ptr(lse)):
+        raise ValueError("invalid row or index outside the causal prefix")
+    return out, lse
+
+
+def dsa_rows(cu_q, cu_k, q_idx, k_idx, w, q, k, v, rows, topk_k: int, scale: float,
+             ld=None):
+    """The whole path for the given rows: scores -> top-k -> sparse attention.
+    Returns dict(scores, counts, idx, out, lse)."""
+    counts = visible_counts(cu_q, cu_k, rows)
+    s = index_scores(cu_q, cu_k, q_idx, k_idx, w, rows, ld=ld)
+    sel = topk(s, counts, topk_k)
+    o, l = sparse_attn(cu_q, cu_k, q, k, v, sel, rows, scale)
+    return {"scores": s, "counts": counts, "idx": sel, "out": o, "lse": l}

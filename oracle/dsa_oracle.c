@@ -1,0 +1,235 @@
+/*
+ * dsa_oracle.c -- plain, slow CPU reference for the DeepSeek Sparse Attention
+ * (DSA) hot path: Lightning-Indexer scores, top-k selection, and sparse GQA
+ * attention over the selected positions.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library may link, load
+ * or call this file; only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header, table or helper with
+ * the HIP library.
+ *
+ * What it follows (page 5, "Kwai Keye-VL-2.0 technical report" summary,
+ * section 1 on long-video cost):
+ *   - a lightweight scout module (the Lightning Indexer) scores every
+ *     position of the context for the current query token;
+ *   - the scout keeps ONE shared key per position (an MQA design: "one set
+ *     of eyes"), used by all of its heads;
+ *   - for each query token the k = 2048 most relevant positions are kept,
+ *     and attention runs only over them, turning O(L^2) into O(L k);
+ *   - the base model is GQA (the same section, paragraph on the GQA/DSA
+ *     adaptation): one index set per token serves every query head.
+ * The indexer score itself is not printed on the pages; this file uses the
+ * plain weighted-ReLU form  I[t,s] = sum_h w[t,h] * max(0, qI[t,h] . kI[s]).
+ * Page 5 section 8 (training-side engineering) asks for a deterministic
+ * top-k; ties are broken towards the lower position here.
+ *
+ * Every floating-point step is done in IEEE double, on the exact values of
+ * the bf16 / fp32 inputs, in the textbook order of the definition.
+ *
+ * Varlen convention: sequence b owns packed query rows [cu_q[b], cu_q[b+1])
+ * and packed key rows [cu_k[b], cu_k[b+1]).  Local query i of sequence b sits
+ * at position p = Lk_b - Lq_b + i and may see local keys 0..p (self
+ * included).  Indices are sequence-local positions.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* bf16 is the upper half of an IEEE binary32; the conversion is exact. */
+static double bf16_to_double(uint16_t h) {
+  uint32_t u = ((uint32_t)h) << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* Locate the sequence that owns packed query row r; returns its index or -1. */
+static int find_seq(int batch, const int32_t* cu_q, int64_t r) {
+  for (int b = 0; b < batch; ++b)
+    if (r >= cu_q[b] && r < cu_q[b + 1]) return b;
+  return -1;
+}
+
+/* Causal position of packed query row r inside its sequence. */
+static int64_t row_position(const int32_t* cu_q, const int32_t* cu_k, int b, int64_t r) {
+  int64_t lq = cu_q[b + 1] - cu_q[b];
+  int64_t lk = cu_k[b + 1] - cu_k[b];
+  return lk - lq + (r - cu_q[b]);
+}
+
+/*
+ * Number of visible keys (p + 1) for each requested row; -1 for a row that
+ * belongs to no sequence or whose position is negative (Lq > Lk).
+ */
+int oracle_visible_counts(int batch, const int32_t* cu_q, const int32_t* cu_k,
+                          int64_t n_rows, const int64_t* rows, int64_t* counts) {
+  int bad = 0;
+  for (int64_t i = 0; i < n_rows; ++i) {
+    int b = find_seq(batch, cu_q, rows[i]);
+    if (b < 0) { counts[i] = -1; bad = 1; continue; }
+    int64_t p = row_position(cu_q, cu_k, b, rows[i]);
+    if (p < 0) { counts[i] = -1; bad = 1; continue; }
+    counts[i] = p + 1;
+  }
+  return bad;
+}
+
+/*
+ * Indexer scores for the requested packed query rows.
+ *   qI : bf16 [total_q, n_heads, d]      w : fp32 [total_q, n_heads]
+ *   kI : bf16 [total_k, d]  (one key per position, shared by every head)
+ *   scores : double [n_rows, ld]; column s <= p receives I[row, s], columns
+ *            beyond p are set to NaN so that any use of them shows.
+ * Returns 0, or 1 if a row is outside every sequence.
+ */
+int oracle_index_scores(int batch, const int32_t* cu_q, const int32_t* cu_k,
+                        const uint16_t* qI, const uint16_t* kI, const float* w,
+                        int n_heads, int d, int64_t n_rows, const int64_t* rows,
+                        double* scores, int64_t ld) {
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int64_t i = 0; i < n_rows; ++i) {
+    int64_t r = rows[i];
+    double* out = scores + i * ld;
+    for (int64_t s = 0; s < ld; ++s) out[s] = NAN;
+    int b = find_seq(batch, cu_q, r);
+    if (b < 0) { bad = 1; continue; }
+    int64_t p = row_position(cu_q, cu_k, b, r);
+    if (p < 0 || p >= ld) { bad = 1; continue; }
+    double* q = (double*)malloc(sizeof(double) * (size_t)n_heads * (size_t)d);
+    double* wr = (double*)malloc(sizeof(double) * (size_t)n_heads);
+    for (int h = 0; h < n_heads; ++h) {
+      wr[h] = (double)w[r * n_heads + h];
+      for (int j = 0; j < d; ++j)
+        q[h * d + j] = bf16_to_double(qI[(r * n_heads + h) * d + j]);
+    }
+    for (int64_t s = 0; s <= p; ++s) {
+      const uint16_t* key = kI + (cu_k[b] + s) * d;
+      double total = 0.0;
+      for (int h = 0; h < n_heads; ++h) {
+        double dot = 0.0;
+        for (int j = 0; j < d; ++j) dot += q[h * d + j] * bf16_to_double(key[j]);
+        double relu = dot > 0.0 ? dot : 0.0;
+        total += wr[h] * relu;
+      }
+      out[s] = total + 0.0; /* -0.0 becomes +0.0 */
+    }
+    free(q);
+    free(wr);
+  }
+  return bad;
+}
+
+typedef struct {
+  double score;
+  int32_t pos;
+} scored_pos;
+
+/* Larger score first; on equal scores the lower position first. */
+static int by_score_then_pos(const void* a, const void* b) {
+  const scored_pos* x = (const scored_pos*)a;
+  const scored_pos* y = (const scored_pos*)b;
+  if (x->score > y->score) return -1;
+  if (x->score < y->score) return 1;
+  return (x->pos > y->pos) - (x->pos < y->pos);
+}
+
+static int ascending_i32(const void* a, const void* b) {
+  int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+  return (x > y) - (x < y);
+}
+
+/*
+ * Top-k per row.  counts[i] = p + 1 visible positions of row i; scores row i
+ * holds valid values in columns 0..counts[i]-1 (any finite double; -0.0 and
+ * +0.0 compare equal, as IEEE comparison makes them).  The n = min(k,
+ * counts[i]) best positions by (score descending, position ascending) are
+ * written to idx[i, 0..n-1] in ascending position order; idx[i, n..k-1] = -1.
+ */
+int oracle_topk(int64_t n_rows, const int64_t* counts, const double* scores, int64_t ld,
+                int k, int32_t* idx) {
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int64_t i = 0; i < n_rows; ++i) {
+    int32_t* out = idx + i * (int64_t)k;
+    for (int j = 0; j < k; ++j) out[j] = -1;
+    int64_t cnt = counts[i];
+    if (cnt <= 0 || cnt > ld) { bad = 1; continue; }
+    scored_pos* all = (scored_pos*)malloc(sizeof(scored_pos) * (size_t)cnt);
+    for (int64_t s = 0; s < cnt; ++s) {
+      all[s].score = scores[i * ld + s];
+      all[s].pos = (int32_t)s;
+    }
+    qsort(all, (size_t)cnt, sizeof(scored_pos), by_score_then_pos);
+    int64_t n = cnt < k ? cnt : k;
+    for (int64_t j = 0; j < n; ++j) out[j] = all[j].pos;
+    qsort(out, (size_t)n, sizeof(int32_t), ascending_i32);
+    free(all);
+  }
+  return bad;
+}
+
+/*
+ * Sparse GQA attention for the requested rows over their selected positions.
+ *   Q : bf16 [total_q, n_heads_q, d]   K, V : bf16 [total_k, n_heads_kv, d]
+ *   idx : int32 [n_rows, topk] sequence-local positions, -1 = unused slot
+ *   out : double [n_rows, n_heads_q, d]    lse : double [n_rows, n_heads_q]
+ * Query head h reads KV head g = h / (n_heads_q / n_heads_kv).
+ *   z_s = scale * Q[h] . K[s, g],  O = sum_s e^{z_s - m} V[s, g] / sum_s e^{z_s - m},
+ *   lse = m + ln sum_s e^{z_s - m},  m = max_s z_s.
+ * A row with no valid index gets O = 0 and lse = -inf.
+ * Returns 0, or 1 on an invalid row or an index outside 0..p.
+ */
+int oracle_sparse_attn(int batch, const int32_t* cu_q, const int32_t* cu_k,
+                       const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                       int n_heads_q, int n_heads_kv, int d, double scale,
+                       int64_t n_rows, const int64_t* rows, const int32_t* idx, int topk,
+                       double* out, double* lse) {
+  int bad = 0;
+  int group = n_heads_q / n_heads_kv;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int64_t i = 0; i < n_rows; ++i) {
+    int64_t r = rows[i];
+    int b = find_seq(batch, cu_q, r);
+    double* o = out + i * (int64_t)n_heads_q * d;
+    for (int64_t e = 0; e < (int64_t)n_heads_q * d; ++e) o[e] = 0.0;
+    for (int h = 0; h < n_heads_q; ++h) lse[i * n_heads_q + h] = -INFINITY;
+    if (b < 0) { bad = 1; continue; }
+    int64_t p = row_position(cu_q, cu_k, b, r);
+    const int32_t* sel = idx + i * (int64_t)topk;
+    int n = 0;
+    for (int j = 0; j < topk; ++j) {
+      if (sel[j] < 0) continue;
+      if (sel[j] > p) bad = 1;
+      ++n;
+    }
+    if (n == 0) continue;
+    double* z = (double*)malloc(sizeof(double) * (size_t)topk);
+    for (int h = 0; h < n_heads_q; ++h) {
+      int g = h / group;
+      const uint16_t* q = Q + (r * n_heads_q + h) * (int64_t)d;
+      double m = -INFINITY;
+      for (int j = 0; j < topk; ++j) {
+        if (sel[j] < 0 || sel[j] > p) { z[j] = -INFINITY; continue; }
+        const uint16_t* key = K + ((cu_k[b] + sel[j]) * (int64_t)n_heads_kv + g) * d;
+        double dot = 0.0;
+        for (int c = 0; c < d; ++c) dot += bf16_to_double(q[c]) * bf16_to_double(key[c]);
+        z[j] = scale * dot;
+        if (z[j] > m) m = z[j];
+      }
+      double denom = 0.0;
+      for (int j = 0; j < topk; ++j) {
+        if (z[j] == -INFINITY) continue;
+        double e = exp(z[j] - m);
+        denom += e;
+        const uint16_t* val = V + ((cu_k[b] + sel[j]) * (int64_t)n_heads_kv + g) * d;
+        for (int c = 0; c < d; ++c) o[h * d + c] += e * bf16_to_double(val[c]);
+      }
+      for (int c = 0; c < d; ++c) o[h * d + c] /= denom;
+      lse[i * n_heads_q + h] = m + log(denom);
+    }
+    free(z);
+  }
+  return bad;
+}
