@@ -1,0 +1,189 @@
+/*
+ * dsa.h -- C ABI of libdsa.so: the DeepSeek Sparse Attention (DSA) hot path
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Method (Kwai Keye-VL-2.0 technical-report summary, page 5, section 1, the
+ * paragraphs on the Lightning Indexer and on the GQA adaptation):
+ *   1. a lightweight indexer scores every visible position of the context for
+ *      the current query token, using ONE key per position shared by all of
+ *      its heads (an MQA design);
+ *   2. the k best positions (k = 2048 on the pages) are kept for that token;
+ *   3. attention runs only over the kept positions, so its cost is O(L k)
+ *      instead of O(L^2); one index set serves every GQA query head.
+ * Page 5 section 8 requires the top-k to be deterministic, so training and
+ * inference select the same positions.  Page 1 (the launch article) states
+ * the DSA kernels run in variable-length (packed) mode; every call here takes
+ * a packed batch.
+ *
+ * Indexer score used here (the pages print no formula):
+ *   I[t, s] = sum_h w[t, h] * max(0, qI[t, h, :] . kI[s, :]).
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers into caller-owned, contiguous,
+ *     row-major buffers.  The library never allocates, frees, copies or
+ *     synchronises; it only enqueues kernels on `stream`.
+ *   - bf16 tensors are IEEE binary32 values truncated to their upper 16 bits
+ *     (torch.bfloat16), passed as `const void*`, 16-byte aligned.
+ *   - Calls are stateless and may be made from any host thread.
+ *   - Return value: DSA_OK when all work was enqueued; otherwise an error
+ *     code and nothing was enqueued.  dsa_last_error() gives a message for
+ *     the calling thread's most recent failure.  Faults during execution
+ *     surface as HIP errors on the caller's next synchronisation.
+ *   - Validation is host-side (pointers, sizes, shapes).  Device-resident
+ *     metadata (cu_seqlens, index values) is a precondition, not checked:
+ *     cu_seqlens must be non-decreasing with Lq_b <= Lk_b; indices outside
+ *     0..p are treated as empty slots by the attention kernels.
+ *
+ * Varlen layout (dsa_varlen)
+ *   Sequence b owns packed query rows [cu_seqlens_q[b], cu_seqlens_q[b+1])
+ *   and packed key rows [cu_seqlens_k[b], cu_seqlens_k[b+1]).  Local query
+ *   i of sequence b sits at position p = Lk_b - Lq_b + i and sees local keys
+ *   0..p (itself included).  Prefill has Lq_b = Lk_b; decode has Lq_b = 1 and
+ *   p = Lk_b - 1 (the new token's key is already in the caches).  Indices are
+ *   int32 sequence-local positions.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size or window */
+  DSA_ERR_UNSUPPORTED = 2,      /* a shape outside the supported set below   */
+  DSA_ERR_WORKSPACE = 3,        /* workspace missing or too small             */
+  DSA_ERR_HIP = 4               /* a HIP launch call failed                   */
+} dsa_status;
+
+/* Static text for a status code. */
+const char* dsa_status_string(int status);
+/* Message describing the calling thread's most recent failed call ("" if none). */
+const char* dsa_last_error(void);
+
+/* Packed (varlen) batch description.  The two cu_seqlens arrays live on the
+   device; the scalar fields are host copies the caller keeps consistent. */
+typedef struct {
+  int32_t batch;                /* number of sequences B >= 1                 */
+  const int32_t* cu_seqlens_q;  /* device int32 [B+1], cu_seqlens_q[0] == 0   */
+  const int32_t* cu_seqlens_k;  /* device int32 [B+1], cu_seqlens_k[0] == 0   */
+  int64_t total_q;              /* == cu_seqlens_q[B]                         */
+  int64_t total_k;              /* == cu_seqlens_k[B]                         */
+  int32_t max_seqlen_q;         /* max_b Lq_b                                 */
+  int32_t max_seqlen_k;         /* max_b Lk_b                                 */
+} dsa_varlen;
+
+/*
+ * dsa_index_scores -- Lightning-Indexer scores for a window of query rows
+ * (page 5 section 1: the scout scores every position; one MQA key per
+ * position serves all indexer heads).
+ *
+ *   q_idx  bf16 [total_q, n_heads_idx, d_idx]   indexer queries
+ *   k_idx  bf16 [total_k, d_idx]                one indexer key per position
+ *   w      fp32 [total_q, n_heads_idx]          per-head weights (any sign)
+ *   rows   packed query rows row_begin .. row_begin + row_count - 1
+ *   scores fp32 [row_count, ld_scores]: scores[i, s] = I[row_begin + i, s] for
+ *          s = 0..p of that row; columns beyond p are left untouched.
+ *
+ * Arithmetic: bf16 x bf16 products accumulated in fp32 (MFMA), the ReLU,
+ * weighting and head sum in fp32.  Integer-valued inputs whose partial sums
+ * stay below 2^24 give exact scores.
+ * Supported: d_idx in {64, 128}; 1 <= n_heads_idx <= 64.
+ * Invalid: null pointers, misaligned bf16 pointers, scores not 16-byte
+ * aligned, ld_scores < max_seqlen_k or not a multiple of 4, a window outside
+ * [0, total_q).  row_count == 0 is a no-op.
+ */
+int dsa_index_scores(const dsa_varlen* vl, const void* q_idx, const void* k_idx, const float* w,
+                     int32_t n_heads_idx, int32_t d_idx, int64_t row_begin, int64_t row_count,
+                     float* scores, int64_t ld_scores, hipStream_t stream);
+
+/* Workspace bytes dsa_topk needs for this call shape (0 today). */
+int dsa_topk_workspace_size(const dsa_varlen* vl, int64_t row_count, int32_t k, size_t* bytes);
+
+/*
+ * dsa_topk -- deterministic per-row top-k of indexer scores (page 5 section 1:
+ * the k most relevant positions per query token; section 8: deterministic).
+ *
+ *   scores  fp32 [row_count, ld_scores] as written by dsa_index_scores; only
+ *           columns 0..p of each row are read.  Values must be finite;
+ *           -0.0 and +0.0 are equal.
+ *   indices int32 [row_count, k]: the n = min(k, p + 1) positions with the
+ *           largest score, ties broken towards the LOWER position, written in
+ *           ascending position order; slots n..k-1 are -1.
+ *
+ * The result is a pure function of the inputs (bitwise repeatable).
+ * Supported: 1 <= k <= 2048.
+ * Invalid: null pointers, scores not 16-byte aligned, ld_scores <
+ * max_seqlen_k or not a multiple of 4, a window outside [0, total_q).
+ * workspace may be NULL when dsa_topk_workspace_size reports 0.
+ */
+int dsa_topk(const dsa_varlen* vl, const float* scores, int64_t ld_scores, int64_t row_begin,
+             int64_t row_count, int32_t k, int32_t* indices, void* workspace,
+             size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dsa_sparse_attn_prefill -- GQA softmax attention of each query row over its
+ * selected positions only (page 5 section 1: attention among the chosen
+ * positions, O(L k); GQA adaptation: one index set per token for all heads).
+ *
+ *   q       bf16 [total_q, n_heads_q, head_dim]
+ *   k, v    bf16 [total_k, n_heads_kv, head_dim]
+ *   indices int32 [row_count, topk]: row i belongs to packed query row
+ *           row_begin + i; entries outside 0..p are empty slots.
+ *   out     bf16 [total_q, n_heads_q, head_dim]; rows of the window written.
+ *   lse     fp32 [total_q, n_heads_q] natural-log log-sum-exp of the scaled
+ *           logits, or NULL.  A row with no valid index gets out = 0 and
+ *           lse = -inf.
+ * Query head h reads KV head h / (n_heads_q / n_heads_kv).
+ *   O[h] = sum_s softmax_s(softmax_scale * q[h] . k[s, g]) v[s, g].
+ * Arithmetic: bf16 MFMA with fp32 accumulation, fp32 softmax, probabilities
+ * rounded to bf16 for the value product, bf16 output (round to nearest even).
+ * Supported: head_dim in {64, 128}; n_heads_q / n_heads_kv in 1..16;
+ * n_heads_kv in 1..8; 1 <= topk <= 4096.
+ * Invalid: null pointers, misaligned bf16 pointers, n_heads_q % n_heads_kv,
+ * a window outside [0, total_q), non-finite softmax_scale.
+ */
+int dsa_sparse_attn_prefill(const dsa_varlen* vl, const void* q, const void* k, const void* v,
+                            const int32_t* indices, int32_t topk, int64_t row_begin,
+                            int64_t row_count, int32_t n_heads_q, int32_t n_heads_kv,
+                            int32_t head_dim, float softmax_scale, void* out, float* lse,
+                            hipStream_t stream);
+
+/* Workspace bytes dsa_sparse_attn_decode needs (partial results of the
+   split over the index list). */
+int dsa_sparse_attn_decode_workspace_size(const dsa_varlen* vl, int32_t n_heads_q,
+                                          int32_t head_dim, int32_t topk, size_t* bytes);
+
+/*
+ * dsa_sparse_attn_decode -- the same attention for one new token per
+ * sequence (Lq_b == 1, p = Lk_b - 1) reading bf16 KV caches (page 5 section 8
+ * names a DSA-specific decode optimisation without describing it; here the
+ * index list of each query is split across workgroups and the partial results
+ * are merged in a fixed order, so the output is bitwise repeatable).
+ *
+ *   q        bf16 [batch, n_heads_q, head_dim]
+ *   k_cache, v_cache  bf16 [total_k, n_heads_kv, head_dim]
+ *   indices  int32 [batch, topk]
+ *   out      bf16 [batch, n_heads_q, head_dim];  lse fp32 [batch, n_heads_q] or NULL
+ *   workspace  device buffer of at least dsa_sparse_attn_decode_workspace_size
+ *              bytes, 256-byte aligned; its contents need not be initialised
+ *              and are clobbered.  Calls sharing one workspace must be ordered.
+ * Supported / invalid: as dsa_sparse_attn_prefill, plus total_q == batch.
+ */
+int dsa_sparse_attn_decode(const dsa_varlen* vl, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* indices, int32_t topk,
+                           int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
+                           float softmax_scale, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

@@ -1,0 +1,246 @@
+"""Python binding of libdsa.so, the MI355X (gfx950) DSA hot path.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libdsa.so (see include/dsa.h for the contract of each entry point).  torch
+supplies device memory and the stream; nothing here computes.  There is no
+fallback: if libdsa.so is missing or fails to load, importing the entry
+points raises.
+
+Entry points (same names as the C ABI):
+    dsa_index_scores, dsa_topk, dsa_topk_workspace_size,
+    dsa_sparse_attn_prefill, dsa_sparse_attn_decode,
+    dsa_sparse_attn_decode_workspace_size
+plus ``Varlen`` (the packed-batch descriptor) and ``DSAError``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+EXPORTED = (
+    "dsa_status_string", "dsa_last_error", "dsa_index_scores", "dsa_topk_workspace_size",
+    "dsa_topk", "dsa_sparse_attn_prefill", "dsa_sparse_attn_decode_workspace_size",
+    "dsa_sparse_attn_decode",
+)
+
+DSA_OK = 0
+DSA_ERR_INVALID_ARGUMENT = 1
+DSA_ERR_UNSUPPORTED = 2
+DSA_ERR_WORKSPACE = 3
+DSA_ERR_HIP = 4
+
+
+class DSAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+class dsa_varlen(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("cu_seqlens_q", ctypes.c_void_p),
+        ("cu_seqlens_k", ctypes.c_void_p),
+        ("total_q", ctypes.c_int64),
+        ("total_k", ctypes.c_int64),
+        ("max_seqlen_q", ctypes.c_int32),
+        ("max_seqlen_k", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libdsa.so (raises if it is not built: there is no other path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libdsa.so not built at {path}; run "
+                          "`python -m long_context_sparse_score_amd.build_lib`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    vl = ctypes.POINTER(dsa_varlen)
+    sz = ctypes.POINTER(ctypes.c_size_t)
+    lib.dsa_status_string.argtypes = [ctypes.c_int]
+    lib.dsa_status_string.restype = ctypes.c_char_p
+    lib.dsa_last_error.argtypes = []
+    lib.dsa_last_error.restype = ctypes.c_char_p
+    lib.dsa_index_scores.argtypes = [vl, vp, vp, vp, i32, i32, i64, i64, vp, i64, vp]
+    lib.dsa_topk_workspace_size.argtypes = [vl, i64, i32, sz]
+    lib.dsa_topk.argtypes = [vl, vp, i64, i64, i64, i32, vp, vp, ctypes.c_size_t, vp]
+    lib.dsa_sparse_attn_prefill.argtypes = [vl, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, f32,
+                                            vp, vp, vp]
+    lib.dsa_sparse_attn_decode_workspace_size.argtypes = [vl, i32, i32, i32, sz]
+    lib.dsa_sparse_attn_decode.argtypes = [vl, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, vp, vp,
+                                           ctypes.c_size_t, vp]
+    for name in EXPORTED[2:]:
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _status_name(status: int) -> str:
+    try:
+        return load_library().dsa_status_string(status).decode()
+    except ImportError:
+        return str(status)
+
+
+def _check(status: int):
+    if status != DSA_OK:
+        raise DSAError(status, load_library().dsa_last_error().decode())
+
+
+# ---- marshalling helpers -----------------------------------------------------
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, name, dtype, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise TypeError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise TypeError(f"{name} must have {ndim} dimensions, got {t.dim()}")
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+class Varlen:
+    """Packed batch: cumulative query / key lengths on the device plus the host
+    scalars the C ABI wants."""
+
+    def __init__(self, cu_seqlens_q, cu_seqlens_k, device="cuda"):
+        torch = _torch()
+        cq = [int(x) for x in cu_seqlens_q]
+        ck = [int(x) for x in cu_seqlens_k]
+        if len(cq) != len(ck) or len(cq) < 2:
+            raise ValueError("cu_seqlens_q and cu_seqlens_k need the same length >= 2")
+        self.cu_q_host = cq
+        self.cu_k_host = ck
+        self.cu_q = torch.tensor(cq, dtype=torch.int32, device=device)
+        self.cu_k = torch.tensor(ck, dtype=torch.int32, device=device)
+        self.batch = len(cq) - 1
+        self.total_q = cq[-1]
+        self.total_k = ck[-1]
+        self.max_seqlen_q = max(b - a for a, b in zip(cq, cq[1:]))
+        self.max_seqlen_k = max(b - a for a, b in zip(ck, ck[1:]))
+        self._struct = dsa_varlen(self.batch, self.cu_q.data_ptr(), self.cu_k.data_ptr(),
+                                  self.total_q, self.total_k, self.max_seqlen_q, self.max_seqlen_k)
+
+    @property
+    def struct(self):
+        return ctypes.byref(self._struct)
+
+
+# ---- entry points ----------------------------------------------------------------
+
+def dsa_index_scores(vl: Varlen, q_idx, k_idx, w, scores, row_begin: int = 0,
+                     row_count: int | None = None, stream=None):
+    """Indexer scores of rows [row_begin, row_begin + row_count) into scores
+    (fp32 [row_count, ld]).  Columns beyond each row's position are untouched."""
+    torch = _torch()
+    _need(q_idx, "q_idx", torch.bfloat16, 3)
+    _need(k_idx, "k_idx", torch.bfloat16, 2)
+    _need(w, "w", torch.float32, 2)
+    _need(scores, "scores", torch.float32, 2)
+    row_count = scores.shape[0] if row_count is None else row_count
+    _check(load_library().dsa_index_scores(
+        vl.struct, _ptr(q_idx), _ptr(k_idx), _ptr(w), q_idx.shape[1], q_idx.shape[2], row_begin,
+        row_count, _ptr(scores), scores.shape[1], _stream(stream)))
+
+
+def dsa_topk_workspace_size(vl: Varlen, row_count: int, k: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().dsa_topk_workspace_size(vl.struct, row_count, k, ctypes.byref(n)))
+    return n.value
+
+
+def dsa_topk(vl: Varlen, scores, indices, row_begin: int = 0, row_count: int | None = None,
+             workspace=None, stream=None):
+    """Per-row top-k (k = indices.shape[1]) into indices (int32 [row_count, k])."""
+    torch = _torch()
+    _need(scores, "scores", torch.float32, 2)
+    _need(indices, "indices", torch.int32, 2)
+    row_count = indices.shape[0] if row_count is None else row_count
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().dsa_topk(
+        vl.struct, _ptr(scores), scores.shape[1], row_begin, row_count, indices.shape[1],
+        _ptr(indices), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dsa_sparse_attn_prefill(vl: Varlen, q, k, v, indices, out, lse=None, softmax_scale=None,
+                            row_begin: int = 0, row_count: int | None = None, stream=None):
+    """Sparse GQA attention of rows [row_begin, row_begin + row_count) over
+    indices (int32 [row_count, topk]) into out (bf16 [total_q, Hq, d])."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k, "k", torch.bfloat16, 3)
+    _need(v, "v", torch.bfloat16, 3)
+    _need(indices, "indices", torch.int32, 2)
+    _need(out, "out", torch.bfloat16, 3)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2)
+    d = q.shape[2]
+    scale = d ** -0.5 if softmax_scale is None else softmax_scale
+    row_count = indices.shape[0] if row_count is None else row_count
+    _check(load_library().dsa_sparse_attn_prefill(
+        vl.struct, _ptr(q), _ptr(k), _ptr(v), _ptr(indices), indices.shape[1], row_begin,
+        row_count, q.shape[1], k.shape[1], d, scale, _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def dsa_sparse_attn_decode_workspace_size(vl: Varlen, n_heads_q: int, head_dim: int,
+                                          topk: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().dsa_sparse_attn_decode_workspace_size(vl.struct, n_heads_q, head_dim,
+                                                                 topk, ctypes.byref(n)))
+    return n.value
+
+
+def dsa_sparse_attn_decode(vl: Varlen, q, k_cache, v_cache, indices, out, workspace, lse=None,
+                           softmax_scale=None, stream=None):
+    """Sparse GQA attention of one new token per sequence over its indices."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 3)
+    _need(v_cache, "v_cache", torch.bfloat16, 3)
+    _need(indices, "indices", torch.int32, 2)
+    _need(out, "out", torch.bfloat16, 3)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2)
+    d = q.shape[2]
+    scale = d ** -0.5 if softmax_scale is None else softmax_scale
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().dsa_sparse_attn_decode(
+        vl.struct, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(indices), indices.shape[1],
+        q.shape[1], k_cache.shape[1], d, scale, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
+def build(verbose: bool = False) -> str:
+    from . import build_lib as _b
+
+    return _b.build(verbose=verbose)

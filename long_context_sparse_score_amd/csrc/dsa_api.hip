@@ -1,0 +1,224 @@
+// dsa_api.hip -- the C ABI of libdsa.so: host-side validation and launches.
+// Behaviour of every entry point is specified in include/dsa.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "dsa.h"
+#include "dsa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return DSA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_varlen(const dsa_varlen* vl) {
+  if (vl == nullptr) return fail(DSA_ERR_INVALID_ARGUMENT, "varlen descriptor is NULL");
+  if (vl->batch < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", vl->batch);
+  if (vl->cu_seqlens_q == nullptr || vl->cu_seqlens_k == nullptr)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "cu_seqlens pointer is NULL");
+  if (!aligned(vl->cu_seqlens_q, 4) || !aligned(vl->cu_seqlens_k, 4))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "cu_seqlens pointers must be 4-byte aligned");
+  if (vl->total_q < 0 || vl->total_k < 1)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "total_q must be >= 0 and total_k >= 1");
+  if (vl->max_seqlen_q < 0 || vl->max_seqlen_k < 1)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "max_seqlen_k must be >= 1");
+  if (vl->max_seqlen_k > vl->total_k || vl->max_seqlen_q > vl->total_q)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "max_seqlen exceeds the packed total");
+  if (vl->total_q > INT32_MAX || vl->total_k > INT32_MAX)
+    return fail(DSA_ERR_UNSUPPORTED, "packed totals must fit int32");
+  return DSA_OK;
+}
+
+int check_window(const dsa_varlen* vl, int64_t row_begin, int64_t row_count) {
+  if (row_begin < 0 || row_count < 0 || row_begin + row_count > vl->total_q)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "row window [%lld, %lld) outside [0, %lld)",
+                (long long)row_begin, (long long)(row_begin + row_count), (long long)vl->total_q);
+  if (row_count > INT32_MAX) return fail(DSA_ERR_UNSUPPORTED, "row_count must fit int32");
+  return DSA_OK;
+}
+
+int check_scores(const dsa_varlen* vl, const float* scores, int64_t ld) {
+  if (scores == nullptr) return fail(DSA_ERR_INVALID_ARGUMENT, "scores pointer is NULL");
+  if (!aligned(scores, 16)) return fail(DSA_ERR_INVALID_ARGUMENT, "scores must be 16-byte aligned");
+  if (ld < vl->max_seqlen_k)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "ld_scores (%lld) < max_seqlen_k (%d)", (long long)ld,
+                vl->max_seqlen_k);
+  if (ld % 4 != 0) return fail(DSA_ERR_INVALID_ARGUMENT, "ld_scores must be a multiple of 4");
+  return DSA_OK;
+}
+
+int check_bf16(const void* p, const char* name) {
+  if (p == nullptr) return fail(DSA_ERR_INVALID_ARGUMENT, "%s pointer is NULL", name);
+  if (!aligned(p, 16)) return fail(DSA_ERR_INVALID_ARGUMENT, "%s must be 16-byte aligned", name);
+  return DSA_OK;
+}
+
+int check_attn_shape(int32_t hq, int32_t hkv, int32_t d, int32_t topk, float scale) {
+  if (hq < 1 || hkv < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "head counts must be >= 1");
+  if (hq % hkv != 0)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "n_heads_q (%d) is not a multiple of n_heads_kv (%d)",
+                hq, hkv);
+  if (d != 64 && d != 128) return fail(DSA_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", d);
+  if (hkv > 8) return fail(DSA_ERR_UNSUPPORTED, "n_heads_kv %d > 8", hkv);
+  if (hq / hkv > 16) return fail(DSA_ERR_UNSUPPORTED, "group size %d > 16", hq / hkv);
+  if (topk < 1 || topk > 4096) return fail(DSA_ERR_UNSUPPORTED, "topk %d not in 1..4096", topk);
+  if (!std::isfinite(scale)) return fail(DSA_ERR_INVALID_ARGUMENT, "softmax_scale is not finite");
+  return DSA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(int status) {
+  switch (status) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_INVALID_ARGUMENT: return "DSA_ERR_INVALID_ARGUMENT";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP";
+    default: return "DSA_ERR_UNKNOWN";
+  }
+}
+
+const char* dsa_last_error(void) { return g_last_error; }
+
+int dsa_index_scores(const dsa_varlen* vl, const void* q_idx, const void* k_idx, const float* w,
+                     int32_t n_heads_idx, int32_t d_idx, int64_t row_begin, int64_t row_count,
+                     float* scores, int64_t ld_scores, hipStream_t stream) {
+  int st;
+  if ((st = check_varlen(vl))) return st;
+  if ((st = check_window(vl, row_begin, row_count))) return st;
+  if ((st = check_bf16(q_idx, "q_idx"))) return st;
+  if ((st = check_bf16(k_idx, "k_idx"))) return st;
+  if (w == nullptr || !aligned(w, 4)) return fail(DSA_ERR_INVALID_ARGUMENT, "w is NULL or misaligned");
+  if ((st = check_scores(vl, scores, ld_scores))) return st;
+  if (d_idx != 64 && d_idx != 128) return fail(DSA_ERR_UNSUPPORTED, "d_idx %d not in {64, 128}", d_idx);
+  if (n_heads_idx < 1 || n_heads_idx > 64)
+    return fail(DSA_ERR_UNSUPPORTED, "n_heads_idx %d not in 1..64", n_heads_idx);
+  if (row_count == 0) return ok();
+  return hip_status(dsa::launch_index_scores(*vl, static_cast<const uint16_t*>(q_idx),
+                                             static_cast<const uint16_t*>(k_idx), w, n_heads_idx,
+                                             d_idx, row_begin, row_count, scores, ld_scores, stream),
+                    "index_scores launch");
+}
+
+int dsa_topk_workspace_size(const dsa_varlen* vl, int64_t row_count, int32_t k, size_t* bytes) {
+  int st;
+  if ((st = check_varlen(vl))) return st;
+  if (bytes == nullptr) return fail(DSA_ERR_INVALID_ARGUMENT, "bytes pointer is NULL");
+  if (row_count < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "row_count < 0");
+  if (k < 1 || k > 2048) return fail(DSA_ERR_UNSUPPORTED, "k %d not in 1..2048", k);
+  *bytes = 0;
+  return ok();
+}
+
+int dsa_topk(const dsa_varlen* vl, const float* scores, int64_t ld_scores, int64_t row_begin,
+             int64_t row_count, int32_t k, int32_t* indices, void* workspace,
+             size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  int st;
+  if ((st = check_varlen(vl))) return st;
+  if ((st = check_window(vl, row_begin, row_count))) return st;
+  if ((st = check_scores(vl, scores, ld_scores))) return st;
+  if (indices == nullptr || !aligned(indices, 4))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "indices is NULL or misaligned");
+  if (k < 1 || k > 2048) return fail(DSA_ERR_UNSUPPORTED, "k %d not in 1..2048", k);
+  if (row_count == 0) return ok();
+  return hip_status(dsa::launch_topk(*vl, scores, ld_scores, row_begin, row_count, k, indices, stream),
+                    "topk launch");
+}
+
+int dsa_sparse_attn_prefill(const dsa_varlen* vl, const void* q, const void* k, const void* v,
+                            const int32_t* indices, int32_t topk, int64_t row_begin,
+                            int64_t row_count, int32_t n_heads_q, int32_t n_heads_kv,
+                            int32_t head_dim, float softmax_scale, void* out, float* lse,
+                            hipStream_t stream) {
+  int st;
+  if ((st = check_varlen(vl))) return st;
+  if ((st = check_window(vl, row_begin, row_count))) return st;
+  if ((st = check_bf16(q, "q"))) return st;
+  if ((st = check_bf16(k, "k"))) return st;
+  if ((st = check_bf16(v, "v"))) return st;
+  if ((st = check_bf16(out, "out"))) return st;
+  if (indices == nullptr || !aligned(indices, 4))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "indices is NULL or misaligned");
+  if (lse != nullptr && !aligned(lse, 4)) return fail(DSA_ERR_INVALID_ARGUMENT, "lse misaligned");
+  if ((st = check_attn_shape(n_heads_q, n_heads_kv, head_dim, topk, softmax_scale))) return st;
+  if (row_count == 0) return ok();
+  return hip_status(
+      dsa::launch_sparse_attn(*vl, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                              static_cast<const uint16_t*>(v), indices, topk, row_begin, row_count,
+                              n_heads_q, n_heads_kv, head_dim, softmax_scale,
+                              static_cast<uint16_t*>(out), lse, 1, nullptr, stream),
+      "sparse_attn_prefill launch");
+}
+
+int dsa_sparse_attn_decode_workspace_size(const dsa_varlen* vl, int32_t n_heads_q,
+                                          int32_t head_dim, int32_t topk, size_t* bytes) {
+  int st;
+  if ((st = check_varlen(vl))) return st;
+  if (bytes == nullptr) return fail(DSA_ERR_INVALID_ARGUMENT, "bytes pointer is NULL");
+  if (n_heads_q < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "n_heads_q must be >= 1");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", head_dim);
+  if (topk < 1 || topk > 4096) return fail(DSA_ERR_UNSUPPORTED, "topk %d not in 1..4096", topk);
+  const int splits = dsa::attn_decode_splits(vl->batch, 1, topk);
+  *bytes = dsa::attn_workspace_bytes(vl->batch, n_heads_q, head_dim, splits);
+  return ok();
+}
+
+int dsa_sparse_attn_decode(const dsa_varlen* vl, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* indices, int32_t topk,
+                           int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
+                           float softmax_scale, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  int st;
+  if ((st = check_varlen(vl))) return st;
+  if (vl->total_q != vl->batch || vl->max_seqlen_q != 1)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "decode needs exactly one query per sequence");
+  if ((st = check_bf16(q, "q"))) return st;
+  if ((st = check_bf16(k_cache, "k_cache"))) return st;
+  if ((st = check_bf16(v_cache, "v_cache"))) return st;
+  if ((st = check_bf16(out, "out"))) return st;
+  if (indices == nullptr || !aligned(indices, 4))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "indices is NULL or misaligned");
+  if (lse != nullptr && !aligned(lse, 4)) return fail(DSA_ERR_INVALID_ARGUMENT, "lse misaligned");
+  if ((st = check_attn_shape(n_heads_q, n_heads_kv, head_dim, topk, softmax_scale))) return st;
+  const int splits = dsa::attn_decode_splits(vl->batch, n_heads_kv, topk);
+  const size_t need = dsa::attn_workspace_bytes(vl->batch, n_heads_q, head_dim, splits);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)))
+    return fail(DSA_ERR_WORKSPACE, "decode workspace needs %zu bytes (256-byte aligned), got %zu",
+                need, workspace_bytes);
+  return hip_status(
+      dsa::launch_sparse_attn(*vl, static_cast<const uint16_t*>(q),
+                              static_cast<const uint16_t*>(k_cache),
+                              static_cast<const uint16_t*>(v_cache), indices, topk, 0, vl->batch,
+                              n_heads_q, n_heads_kv, head_dim, softmax_scale,
+                              static_cast<uint16_t*>(out), lse, splits,
+                              static_cast<float*>(workspace), stream),
+      "sparse_attn_decode launch");
+}
+
+}  // extern "C"

@@ -29,7 +29,7 @@ _lib = None
 
 def build(verbose: bool = False) -> str:
     """Compile dsa_oracle.c with gcc into liboracle.so (always recompiles)."""
-    from . import build as _b
+    from . import build_lib as _b
 
     return _b.build(verbose=verbose)
 

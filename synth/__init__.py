@@ -46,7 +46,7 @@ S_QIDX, S_KIDX, S_W, S_Q, S_K, S_V, S_KIDX_MEAN, S_K_MEAN, S_LENGTHS = range(1, 
 
 
 def build(verbose: bool = False) -> str:
-    from . import build as _b
+    from . import build_lib as _b
 
     return _b.build(verbose=verbose)
 

