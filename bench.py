@@ -1,0 +1,367 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  * prefill of one causal 131072-token sequence (k = 2048, attention 32 query
+    / 4 KV heads x 128, indexer 64 heads x 128): for each window of query rows
+    dsa_index_scores -> dsa_topk -> dsa_sparse_attn_prefill;
+  * decode of one new token for each of 64 sequences with 131072 cached
+    tokens: dsa_index_scores -> dsa_topk -> dsa_sparse_attn_decode.
+Inputs are resident in HBM before the timed region starts.
+
+Printed: ONE JSON line.  `value` is prefill tokens/s; decode queries/s, the
+per-kernel times, the rooflines, a same-shape dense causal attention run (torch
+SDPA, flash backend) and the CPU oracle on a bounded sample of the same
+prefill are reported beside it.
+
+    python bench.py [--steps K] [--warmup W] [--window ROWS] [--no-dense]
+                    [--no-cpu-baseline] [--cpu-rows N] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--window", type=int, default=8192, help="prefill query rows per score window")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=256)
+    return ap.parse_args()
+
+
+def upload_bf16(torch, bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.bfloat16)
+
+
+def upload(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def gen_upload(torch, wl, parts, keep_host=False):
+    dev, host = {}, {}
+    for p in parts:
+        t0 = time.time()
+        a = getattr(wl, p)()
+        dev[p] = upload(torch, a) if p == "w" else upload_bf16(torch, a)
+        if keep_host:
+            host[p] = a
+        del a
+        log(f"  {wl.name}.{p}: {tuple(dev[p].shape)} in {time.time() - t0:.1f}s")
+    return dev, host
+
+
+# ---------------------------------------------------------------- algorithmic counts
+
+def prefill_counts(wl):
+    """Work the method itself must do (causal pairs for the indexer, selected
+    pairs for the attention)."""
+    pairs = 0
+    sel = 0
+    for L in wl.seqlens_q:
+        pairs += L * (L + 1) // 2
+        # rows p = 0..L-1 select min(k, p + 1) positions
+        k = wl.topk
+        m = min(L, k)
+        sel += m * (m + 1) // 2 + (L - m) * k
+    f_idx = pairs * 2 * wl.n_heads_idx * wl.d_idx
+    f_attn = sel * 4 * wl.n_heads_q * wl.head_dim
+    b_gather = sel * 2 * wl.n_heads_kv * wl.head_dim * 2
+    b_scores = pairs * 4 * 2  # fp32 write by the indexer + read by top-k
+    return dict(pairs=pairs, selected=sel, f_idx=f_idx, f_attn=f_attn, b_gather=b_gather,
+                b_scores=b_scores)
+
+
+def window_flops(wl, r0, n):
+    """Indexer flops of packed rows [r0, r0 + n) of a single-sequence prefill."""
+    pairs = sum(p + 1 for p in range(r0, r0 + n))
+    return pairs * 2 * wl.n_heads_idx * wl.d_idx
+
+
+def decode_bytes(wd):
+    N = wd.seqlens_k[0]
+    k = min(wd.topk, N)
+    per = (N * wd.d_idx * 2                                # indexer keys
+           + k * 2 * wd.n_heads_kv * wd.head_dim * 2       # gathered K and V rows
+           + N * 4 * 2                                     # score write + read
+           + wd.topk * 4 * 2                               # indices write + read
+           + wd.n_heads_idx * wd.d_idx * 2 + wd.n_heads_idx * 4   # qI, w
+           + 2 * wd.n_heads_q * wd.head_dim * 2)           # q, out
+    return per * wd.batch, per
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(wl, host, n_rows):
+    """The oracle, untuned, on query rows evenly spaced over the prefill."""
+    import oracle
+
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    L = wl.seqlens_q[0]
+    rows = np.unique(np.linspace(0, L - 1, n_rows).round().astype(np.int64))
+    t0 = time.time()
+    oracle.dsa_rows(wl.cu_q, wl.cu_k, host["q_idx"], host["k_idx"], host["w"], host["q"],
+                    host["k"], host["v"], rows, wl.topk, wl.softmax_scale)
+    dt = time.time() - t0
+    work = int((rows + 1).sum())
+    full_work = L * (L + 1) // 2
+    return {
+        "value": round(len(rows) / dt, 3),
+        "unit": "tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"{len(rows)} query rows evenly spaced over positions 0..{L - 1} of the "
+                   f"131072-token prefill, whole path (scores, top-k, attention) in fp64, "
+                   f"{dt:.1f} s; the full prefill extrapolates to "
+                   f"{dt * full_work / work / 3600:.1f} h"),
+        "seconds": round(dt, 2),
+    }
+
+
+# ---------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import long_context_sparse_score_amd as dsa
+    from long_context_sparse_score_amd import pipeline
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dsa.load_library()
+    stream = torch.cuda.current_stream()
+
+    # ---- prefill workload: one causal 131072-token sequence
+    wl = synth.prefill_128k()
+    log(f"generating {wl.name}")
+    P, P_host = gen_upload(torch, wl, ("q_idx", "k_idx", "w", "q", "k", "v"),
+                           keep_host=not args.no_cpu_baseline)
+    vl = dsa.Varlen(wl.cu_q.tolist(), wl.cu_k.tolist())
+    bufs = pipeline.alloc_prefill(vl, wl.topk, args.window)
+    out = torch.empty((wl.total_q, wl.n_heads_q, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((wl.total_q, wl.n_heads_q), dtype=torch.float32, device="cuda")
+    window = bufs.scores.shape[0]
+    windows = [(r0, min(window, wl.total_q - r0)) for r0 in range(0, wl.total_q, window)]
+
+    # ---- decode workload: 64 sequences x 131072 cached tokens
+    wd = synth.decode_b64_128k()
+    if not args.no_decode:
+        log(f"generating {wd.name}")
+        D, _ = gen_upload(torch, wd, ("q_idx", "k_idx", "w", "q", "k", "v"))
+        vd = dsa.Varlen(wd.cu_q.tolist(), wd.cu_k.tolist())
+        dbufs = pipeline.alloc_decode(vd, wd.n_heads_q, wd.head_dim, wd.topk)
+        dout = torch.empty((wd.batch, wd.n_heads_q, wd.head_dim), dtype=torch.bfloat16,
+                           device="cuda")
+        dlse = torch.empty((wd.batch, wd.n_heads_q), dtype=torch.float32, device="cuda")
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def run_prefill(rec):
+        for r0, n in windows:
+            e = [ev() for _ in range(4)] if rec is not None else None
+            if e: e[0].record(stream)
+            dsa.dsa_index_scores(vl, P["q_idx"], P["k_idx"], P["w"], bufs.scores, row_begin=r0,
+                                 row_count=n)
+            if e: e[1].record(stream)
+            dsa.dsa_topk(vl, bufs.scores, bufs.indices, row_begin=r0, row_count=n)
+            if e: e[2].record(stream)
+            dsa.dsa_sparse_attn_prefill(vl, P["q"], P["k"], P["v"], bufs.indices, out, lse=lse,
+                                        row_begin=r0, row_count=n)
+            if e:
+                e[3].record(stream)
+                rec.append((r0, n, e))
+
+    def run_decode(rec):
+        e = [ev() for _ in range(4)] if rec is not None else None
+        if e: e[0].record(stream)
+        dsa.dsa_index_scores(vd, D["q_idx"], D["k_idx"], D["w"], dbufs.scores)
+        if e: e[1].record(stream)
+        dsa.dsa_topk(vd, dbufs.scores, dbufs.indices)
+        if e: e[2].record(stream)
+        dsa.dsa_sparse_attn_decode(vd, D["q"], D["k"], D["v"], dbufs.indices, dout,
+                                   dbufs.workspace, lse=dlse)
+        if e:
+            e[3].record(stream)
+            rec.append(e)
+
+    log(f"warmup {args.warmup} step(s)")
+    for _ in range(args.warmup):
+        run_prefill(None)
+        if not args.no_decode:
+            run_decode(None)
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} step(s)")
+    prec, drec, marks = [], [], []
+    t_wall = time.time()
+    for _ in range(args.steps):
+        m = [ev(), ev(), ev()]
+        m[0].record(stream)
+        run_prefill(prec)
+        m[1].record(stream)
+        if not args.no_decode:
+            run_decode(drec)
+        m[2].record(stream)
+        marks.append(m)
+    torch.cuda.synchronize()
+    t_wall = time.time() - t_wall
+
+    pre_ms = sum(m[0].elapsed_time(m[1]) for m in marks)
+    dec_ms = sum(m[1].elapsed_time(m[2]) for m in marks) if not args.no_decode else 0.0
+    step_ms = (pre_ms + dec_ms) / args.steps
+    idx_ms = sum(e[0].elapsed_time(e[1]) for _, _, e in prec)
+    topk_ms = sum(e[1].elapsed_time(e[2]) for _, _, e in prec)
+    attn_ms = sum(e[2].elapsed_time(e[3]) for _, _, e in prec)
+    n_idx_launches = len(prec)
+
+    pc = prefill_counts(wl)
+    tokens_per_s = wl.total_q * args.steps / (pre_ms / 1e3)
+    f_idx_total = pc["f_idx"] * args.steps
+    idx_tflops = f_idx_total / (idx_ms / 1e3) / 1e12
+    t_mfma = (pc["f_idx"] + pc["f_attn"]) / (PEAK_BF16_TFLOPS * 1e12)
+    t_comb = (pc["f_idx"] / (PEAK_BF16_TFLOPS * 1e12) + pc["b_scores"] / (PEAK_HBM_GBS * 1e9)
+              + max(pc["f_attn"] / (PEAK_BF16_TFLOPS * 1e12), pc["b_gather"] / (PEAK_HBM_GBS * 1e9)))
+    pre_s_per_step = pre_ms / 1e3 / args.steps
+
+    result = {
+        "metric": "DSA prefill tokens/s & decode queries/s at 128K ctx, k=2048; % of roofline",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; block-clustered keys for prefill, N(0,1) caches for decode)",
+        "config": {
+            "workload": "prefill_128k (1 x 131072 tokens) + decode_b64_128k (64 x 131072 cached)",
+            "seq_len": wl.seqlens_q[0], "topk": wl.topk, "n_heads_q": wl.n_heads_q,
+            "n_heads_kv": wl.n_heads_kv, "head_dim": wl.head_dim,
+            "n_heads_idx": wl.n_heads_idx, "d_idx": wl.d_idx, "decode_batch": wd.batch,
+            "window_rows": window,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "index_scores (prefill)",
+            "achieved": round(idx_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(idx_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "launches_per_step": n_idx_launches // args.steps,
+            "avg_launch_ms": round(idx_ms / n_idx_launches, 3),
+            "flops_per_causal_pair": 2 * wl.n_heads_idx * wl.d_idx,
+        },
+        "prefill": {
+            "ms": round(pre_ms / args.steps, 3),
+            "tokens_per_s": round(tokens_per_s, 1),
+            "index_scores_ms": round(idx_ms / args.steps, 3),
+            "topk_ms": round(topk_ms / args.steps, 3),
+            "topk_score_read_GBps": round(pc["b_scores"] / 2 * args.steps / (topk_ms / 1e3) / 1e9, 1),
+            "sparse_attn_ms": round(attn_ms / args.steps, 3),
+            "sparse_attn_gather_GBps": round(pc["b_gather"] * args.steps / (attn_ms / 1e3) / 1e9, 1),
+            "sparse_attn_tflops": round(pc["f_attn"] * args.steps / (attn_ms / 1e3) / 1e12, 2),
+            "mfma_roofline_ms": round(t_mfma * 1e3, 3),
+            "mfma_roofline_frac": round(t_mfma / pre_s_per_step, 4),
+            "combined_roofline_ms": round(t_comb * 1e3, 3),
+            "combined_roofline_frac": round(t_comb / pre_s_per_step, 4),
+            "algorithmic": {k: int(v) for k, v in pc.items()},
+        },
+        "wall_s_timed": round(t_wall, 3),
+    }
+
+    if not args.no_decode:
+        b_dec, per_q = decode_bytes(wd)
+        d_idx_ms = sum(e[0].elapsed_time(e[1]) for e in drec)
+        d_topk_ms = sum(e[1].elapsed_time(e[2]) for e in drec)
+        d_attn_ms = sum(e[2].elapsed_time(e[3]) for e in drec)
+        q_per_s = wd.batch * args.steps / (dec_ms / 1e3)
+        achieved = b_dec * args.steps / (dec_ms / 1e3) / 1e9
+        result["decode"] = {
+            "value": round(q_per_s, 1),
+            "unit": "queries/s",
+            "ms": round(dec_ms / args.steps, 4),
+            "index_scores_ms": round(d_idx_ms / args.steps, 4),
+            "topk_ms": round(d_topk_ms / args.steps, 4),
+            "sparse_attn_ms": round(d_attn_ms / args.steps, 4),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                         "bytes_per_query": per_q},
+            "index_scores_GBps": round(wd.batch * wd.seqlens_k[0] * wd.d_idx * 2 * args.steps
+                                       / (d_idx_ms / 1e3) / 1e9, 1),
+        }
+
+    if not args.no_dense:
+        result["dense"] = dense_comparator(torch, P, wl, args, pre_ms / args.steps)
+
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_rows} sampled rows")
+        result["cpu_baseline"] = cpu_baseline(wl, P_host, args.cpu_rows)
+
+    print(json.dumps(result), flush=True)
+
+
+def dense_comparator(torch, P, wl, args, sparse_ms):
+    """Same-shape dense causal attention (torch SDPA, flash backend only)."""
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+
+        q = P["q"].view(1, wl.total_q, wl.n_heads_q, wl.head_dim).transpose(1, 2)
+        k = P["k"].view(1, wl.total_k, wl.n_heads_kv, wl.head_dim).transpose(1, 2)
+        v = P["v"].view(1, wl.total_k, wl.n_heads_kv, wl.head_dim).transpose(1, 2)
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        f = torch.nn.functional.scaled_dot_product_attention
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            for _ in range(max(1, args.warmup)):
+                f(q, k, v, is_causal=True, enable_gqa=True)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                f(q, k, v, is_causal=True, enable_gqa=True)
+            e1.record()
+            torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        flops = wl.total_q * (wl.total_q + 1) / 2 * 4 * wl.n_heads_q * wl.head_dim
+        return {"kind": "torch SDPA flash backend, causal, GQA", "ms": round(ms, 3),
+                "tflops": round(flops / (ms / 1e3) / 1e12, 1),
+                "sparse_over_dense_time": round(sparse_ms / ms, 3)}
+    except Exception as exc:  # the comparator is context, not the product
+        return {"kind": "torch SDPA flash backend", "error": repr(exc)[:300]}
+
+
+if __name__ == "__main__":
+    main()

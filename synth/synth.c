@@ -11,9 +11,10 @@
  * and element i of the stream is mix(key + (i + 1) * 0x9E3779B97F4A7C15).
  * Any slice of any stream can therefore be produced on its own.
  *
- * Normals: Box-Muller (Box & Muller, 1958) in IEEE double.  Elements 2j and
- * 2j+1 share one pair (u1, u2) built from draws 2j and 2j+1:
- *   u1 = (top 53 bits + 1) * 2^-53 in (0, 1],  u2 = top 53 bits * 2^-53,
+ * Normals: Box-Muller (Box & Muller, 1958) in IEEE single precision (the
+ * values are rounded to bf16 afterwards).  Elements 2j and 2j+1 share one
+ * pair (u1, u2) built from draws 2j and 2j+1:
+ *   u1 = (top 24 bits + 1) * 2^-24 in (0, 1],  u2 = top 24 bits * 2^-24,
  *   x_{2j} = sqrt(-2 ln u1) cos(2 pi u2),  x_{2j+1} = sqrt(-2 ln u1) sin(2 pi u2).
  * Uniform reals use the top 24 bits: lo + (hi - lo) * (bits * 2^-24).
  * Uniform integers in [lo, hi] use (top 32 bits * (hi - lo + 1)) >> 32.
@@ -39,13 +40,19 @@ uint64_t synth_stream_key(uint64_t seed, uint64_t stream) {
 
 uint64_t synth_draw(uint64_t key, uint64_t i) { return mix64(key + (i + 1) * GOLDEN_GAMMA); }
 
+static void box_muller(uint64_t key, uint64_t pair, float* c, float* sn) {
+  float u1 = (float)((synth_draw(key, 2 * pair) >> 40) + 1) * 0x1p-24f;
+  float u2 = (float)(synth_draw(key, 2 * pair + 1) >> 40) * 0x1p-24f;
+  float r = sqrtf(-2.0f * logf(u1));
+  float a = 6.28318530717958647692f * u2;
+  *c = r * cosf(a);
+  *sn = r * sinf(a);
+}
+
 static double normal_at(uint64_t key, uint64_t i) {
-  uint64_t j = i >> 1;
-  double u1 = (double)((synth_draw(key, 2 * j) >> 11) + 1) * 0x1p-53;
-  double u2 = (double)(synth_draw(key, 2 * j + 1) >> 11) * 0x1p-53;
-  double r = sqrt(-2.0 * log(u1));
-  double a = 6.283185307179586476925286766559 * u2;
-  return (i & 1) ? r * sin(a) : r * cos(a);
+  float c, sn;
+  box_muller(key, i >> 1, &c, &sn);
+  return (i & 1) ? (double)sn : (double)c;
 }
 
 static double uniform_at(uint64_t key, uint64_t i, double lo, double hi) {
@@ -80,13 +87,10 @@ void synth_normal_bf16(uint64_t seed, uint64_t stream, uint64_t start, int64_t c
   uint64_t pair0 = (start + (uint64_t)head) >> 1;
 #pragma omp parallel for schedule(static)
   for (int64_t j = 0; j < npairs; ++j) {
-    uint64_t pj = pair0 + (uint64_t)j;
-    double u1 = (double)((synth_draw(key, 2 * pj) >> 11) + 1) * 0x1p-53;
-    double u2 = (double)(synth_draw(key, 2 * pj + 1) >> 11) * 0x1p-53;
-    double r = sqrt(-2.0 * log(u1));
-    double a = 6.283185307179586476925286766559 * u2;
-    out[head + 2 * j] = float_to_bf16_rne((float)(scale * (r * cos(a))));
-    out[head + 2 * j + 1] = float_to_bf16_rne((float)(scale * (r * sin(a))));
+    float c, sn;
+    box_muller(key, pair0 + (uint64_t)j, &c, &sn);
+    out[head + 2 * j] = float_to_bf16_rne((float)(scale * (double)c));
+    out[head + 2 * j + 1] = float_to_bf16_rne((float)(scale * (double)sn));
   }
   int64_t done = head + 2 * npairs;
   if (done < count) out[done] = float_to_bf16_rne((float)(scale * normal_at(key, start + (uint64_t)done)));
