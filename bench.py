@@ -217,14 +217,17 @@ def main():
     log(f"warmup {args.warmup} step(s)")
     for _ in range(args.warmup):
         run_prefill(None)
+        torch.cuda.synchronize()
+        log("  warmup prefill done")
         if not args.no_decode:
             run_decode(None)
-    torch.cuda.synchronize()
+            torch.cuda.synchronize()
+            log("  warmup decode done")
 
     log(f"timing {args.steps} step(s)")
     prec, drec, marks = [], [], []
     t_wall = time.time()
-    for _ in range(args.steps):
+    for step in range(args.steps):
         m = [ev(), ev(), ev()]
         m[0].record(stream)
         run_prefill(prec)
@@ -233,7 +236,9 @@ def main():
             run_decode(drec)
         m[2].record(stream)
         marks.append(m)
-    torch.cuda.synchronize()
+        # Waiting between steps leaves the event-timed regions unchanged.
+        torch.cuda.synchronize()
+        log(f"  step {step}: {m[0].elapsed_time(m[2]):.2f} ms")
     t_wall = time.time() - t_wall
 
     pre_ms = sum(m[0].elapsed_time(m[1]) for m in marks)

@@ -28,6 +28,14 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-file device flags.  The indexer's inputs are finite by contract, so its
+# ReLU may skip the NaN-quieting pass fmaxf otherwise needs (one VALU op per
+# head x key).
+FILE_FLAGS = {
+    "index_scores.hip": ["-fno-honor-nans"],
+}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
@@ -38,7 +46,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
     def compile_one(src):
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
-        cmd = [HIPCC, *COMMON_FLAGS, "-c", src, "-o", obj]
+        cmd = [HIPCC, *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src,
+               "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

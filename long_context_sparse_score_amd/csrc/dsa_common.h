@@ -10,6 +10,9 @@ namespace dsa {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+// Native 16-byte vector (HIP's uint4 is a union-based struct that register
+// promotion of local arrays does not always see through).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 

@@ -4,20 +4,30 @@
 // (Keye-VL-2.0 report summary, page 5 section 1: a lightweight scout scores
 // every position with one MQA key shared by all of its heads.)
 //
-// Mapping.  For one query row the head-by-key product is a small GEMM with
-// M = indexer heads (up to 64), N = keys, K = d_idx.  Heads sit on the MFMA
-// rows so that after v_mfma_f32_32x32x16_bf16 every lane holds one key column
-// and 16 heads of it: the ReLU, the weight and the head sum happen in
-// registers, and one exchange between the two half-waves finishes the sum.
-// The contraction over d_idx is ordered so that each half-wave reads one
-// contiguous half of every qI / kI row (64 B or 128 B per lane), which keeps
-// every global load a full 16-byte vector.
+// For one query row the head-by-key product is a small GEMM with M = indexer
+// heads (up to 64), N = keys, K = d_idx.  Heads sit on the MFMA rows so that
+// after v_mfma_f32_32x32x16_bf16 every lane holds one key column and 16 heads
+// of it: the ReLU, the weight and the head sum happen in registers, and one
+// exchange between the two half-waves finishes the sum.  The contraction over
+// d_idx is ordered so that each half-wave covers one contiguous half of every
+// qI / kI row, which keeps every load a full 16-byte vector.
 //
-// One wave owns one query row; a workgroup's four waves own four consecutive
-// rows and walk the same key tiles, so the shared kI tile is served from the
-// CU's L1 after the first wave touches it.  The grid's second dimension splits
-// long rows into key chunks so that a handful of rows (decode) still spreads
-// over the whole chip.
+// Two kernels share that core:
+//  * index_scores_block (prefill): a 512-thread workgroup owns 8 consecutive
+//    query rows of one sequence, one wave per row.  Key tiles of 64 rows
+//    (16 KB) are staged once per workgroup in LDS (double-buffered, 16-byte
+//    chunks XOR-swizzled by key so the B-fragment reads are bank-conflict
+//    free) and feed all 8 waves, so L2 traffic is 1/8 of a per-wave scheme.
+//    Two waves per SIMD let one wave's MFMAs overlap the other's epilogue.
+//    A workgroup whose rows straddle a sequence boundary falls back to the
+//    per-wave path below.
+//  * index_scores_stream (decode / few rows): each wave streams its own key
+//    range of one row straight from HBM with two tiles in flight; long rows
+//    are split over the grid's second dimension so a handful of rows still
+//    covers the whole chip.
+// Every global load is issued unconditionally (addresses are clamped into
+// the sequence instead): a load under a branch makes the compiler wait for
+// it on the spot, which would serialise the prefetch.
 #include "dsa_common.h"
 #include "dsa_internal.h"
 
@@ -25,77 +35,291 @@ namespace dsa {
 
 namespace {
 
-constexpr int kRowsPerBlock = 4;
+constexpr int kBlockRows = 8;        // query rows (waves) per prefill workgroup
+constexpr int kStageKeys = 64;       // keys per LDS stage
+constexpr int kStreamRows = 4;       // waves per stream workgroup
 
-template <int D>
-__global__ __launch_bounds__(256) void index_scores_kernel(
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
-    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
-    const float* __restrict__ w, int n_heads, int64_t row_begin, int64_t row_count,
-    float* __restrict__ scores, int64_t ld, int key_chunk) {
-  constexpr int KS = D / 16;   // MFMA k-steps over d_idx
-  constexpr int HALF = D / 2;  // d range of one half-wave
-  const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
-  // Later rows have longer causal prefixes: hand them out first.
-  const int64_t blk = static_cast<int64_t>(gridDim.x) - 1 - blockIdx.x;
-  const int64_t local = blk * kRowsPerBlock + wave;
-  if (local >= row_count) return;
-  const int64_t row = row_begin + local;
-  const RowInfo ri = row_info(cu_q, cu_k, batch, row);
-  const int32_t c0 = blockIdx.y * key_chunk;
-  const int32_t c1 = min(c0 + key_chunk, ri.pos + 1);
-  if (c0 >= c1) return;
+// Per-wave stationary state: this row's indexer queries (A operand, heads on
+// MFMA rows, MT tiles of 32 heads) and its head weights laid out like the
+// accumulator rows.
+template <int D, int MT>
+struct RowState {
+  static constexpr int KS = D / 16;
+  bf16x8 a[MT][KS];
+  float wv[MT][16];
+};
 
-  const int col = lane & 31;   // MFMA row (A) / column (B) owned by this lane
-  const int half = lane >> 5;  // which half of d_idx this lane feeds
-  const int m_tiles = (n_heads + 31) / 32;
-
-  // Stationary operand: this row's indexer queries, heads on MFMA rows.
-  bf16x8 a[2][KS];
-  float wv[2][16];
+template <int D, int MT>
+__device__ __forceinline__ void load_row_state(RowState<D, MT>& st,
+                                               const uint16_t* __restrict__ q_idx,
+                                               const float* __restrict__ w, int64_t row,
+                                               int n_heads, int col, int half) {
+  constexpr int KS = D / 16, HALF = D / 2;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+  for (int mt = 0; mt < MT; ++mt) {
     const int h = mt * 32 + col;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      a[mt][ks] = (mt < m_tiles && h < n_heads)
-                      ? load_bf16x8(q_idx + (row * n_heads + h) * D + half * HALF + ks * 8)
-                      : zero_bf16x8();
-    }
+    for (int ks = 0; ks < KS; ++ks)
+      st.a[mt][ks] = h < n_heads ? load_bf16x8(q_idx + (row * n_heads + h) * D + half * HALF + ks * 8)
+                                 : zero_bf16x8();
     // Accumulator element v of this lane is MFMA row 8*(v/4) + 4*half + v%4.
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int hr = mt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-      wv[mt][v] = (mt < m_tiles && hr < n_heads) ? w[row * n_heads + hr] : 0.0f;
+      st.wv[mt][v] = hr < n_heads ? w[row * n_heads + hr] : 0.0f;
     }
   }
+}
 
-  float* out_row = scores + local * ld;
-  const uint16_t* kbase = k_idx + ri.key_base * D + half * HALF;
-  for (int32_t t0 = c0; t0 < c1; t0 += 32) {
-    const int32_t key = t0 + col;
-    const int32_t key_ld = min(key, ri.pos);  // stay inside the sequence
-    bf16x8 b[KS];
+// Head products of one 32-key tile.
+template <int D, int MT>
+__device__ __forceinline__ void tile_mfma(const RowState<D, MT>& st, const bf16x8 (&b)[D / 16],
+                                          f32x16 (&acc)[MT]) {
+  constexpr int KS = D / 16;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) b[ks] = load_bf16x8(kbase + static_cast<int64_t>(key_ld) * D + ks * 8);
-    f32x16 acc0 = {}, acc1 = {};
+  for (int mt = 0; mt < MT; ++mt) {
+    acc[mt] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][ks], b[ks], acc0, 0, 0, 0);
-    float s = 0.0f;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) s += wv[0][v] * fmaxf(acc0[v], 0.0f);
-    if (m_tiles > 1) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][ks], b[ks], acc1, 0, 0, 0);
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s += wv[1][v] * fmaxf(acc1[v], 0.0f);
-    }
-    s += __shfl_xor(s, 32);
-    if (half == 0 && key < c1) out_row[key] = s;
+      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(st.a[mt][ks], b[ks], acc[mt], 0, 0, 0);
   }
+}
+
+// Sum over heads of w * relu(acc); lanes 0..31 end up with the score of key
+// (lane & 31).
+template <int D, int MT>
+__device__ __forceinline__ float tile_epilogue(const RowState<D, MT>& st,
+                                               const f32x16 (&acc)[MT]) {
+  float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) {
+      s0 += st.wv[mt][v] * fmaxf(acc[mt][v], 0.0f);
+      s1 += st.wv[mt][v + 1] * fmaxf(acc[mt][v + 1], 0.0f);
+    }
+  }
+  const float s = s0 + s1;
+  return s + __shfl_xor(s, 32);
+}
+
+// One wave, one row, keys [c0, c1) read straight from global memory.  Two
+// register buffers alternate roles (the loop is unrolled by two tiles), so
+// the next tile's load is always in flight while one is multiplied.
+template <int D, int MT>
+__device__ void row_direct(const RowState<D, MT>& st, const uint16_t* __restrict__ k_idx,
+                           const RowInfo& ri, int32_t c0, int32_t c1,
+                           float* __restrict__ out_row, int col, int half) {
+  constexpr int KS = D / 16, HALF = D / 2;
+  const uint16_t* kbase = k_idx + ri.key_base * D + half * HALF;
+  auto fetch = [&](bf16x8 (&dst)[KS], int32_t t0) {
+    const int32_t key_ld = min(t0 + col, ri.pos);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) dst[ks] = load_bf16x8(kbase + static_cast<int64_t>(key_ld) * D + ks * 8);
+  };
+  bf16x8 x[KS], y[KS];
+  fetch(x, c0);
+  fetch(y, c0 + 32);
+  for (int32_t t0 = c0; t0 < c1; t0 += 64) {
+    f32x16 acc[MT];
+    tile_mfma<D, MT>(st, x, acc);
+    fetch(x, t0 + 64);
+    float s = tile_epilogue<D, MT>(st, acc);
+    if (half == 0 && t0 + col < c1) out_row[t0 + col] = s;
+    tile_mfma<D, MT>(st, y, acc);
+    fetch(y, t0 + 96);
+    s = tile_epilogue<D, MT>(st, acc);
+    if (half == 0 && t0 + 32 + col < c1) out_row[t0 + 32 + col] = s;
+  }
+}
+
+// ---------------------------------------------------------------- prefill kernel
+
+template <int D, int MT>
+// k_idx is deliberately not restrict-qualified: as a restrict read-only
+// pointer its loads would count as invariant and the compiler would sink the
+// stage prefetch down to its LDS store, exposing the full load latency.
+__global__ __launch_bounds__(kBlockRows * kWave, 2) void index_scores_block(
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
+    const uint16_t* __restrict__ q_idx, const uint16_t* k_idx,
+    const float* __restrict__ w, int n_heads, int64_t row_begin, int64_t row_count,
+    float* __restrict__ scores, int64_t ld, int key_chunk) {
+  constexpr int KS = D / 16;
+  constexpr int CHUNKS = D / 8;                   // 16-byte chunks per key row
+  constexpr int STAGE_BYTES = kStageKeys * D * 2;
+  constexpr int LOADS = STAGE_BYTES / 16 / (kBlockRows * kWave);  // per thread per stage
+  __shared__ __attribute__((aligned(16))) uint16_t tile[2][kStageKeys * D];
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  // Later rows have longer causal prefixes: hand them out first.
+  const int64_t blk = static_cast<int64_t>(gridDim.x) - 1 - blockIdx.x;
+  const int64_t first = blk * kBlockRows;
+  const int64_t last = min(first + kBlockRows, row_count) - 1;
+  const int64_t local = first + wave;
+  const bool active = local < row_count;
+  const int64_t row = row_begin + (active ? local : last);
+
+  const RowInfo ri = row_info(cu_q, cu_k, batch, row);
+  const RowInfo r_first = row_info(cu_q, cu_k, batch, row_begin + first);
+  const RowInfo r_last = row_info(cu_q, cu_k, batch, row_begin + last);
+  const int32_t c0 = blockIdx.y * key_chunk;
+
+  RowState<D, MT> st;
+  load_row_state<D, MT>(st, q_idx, w, row, n_heads, col, half);
+  float* out_row = scores + local * ld;
+
+  if (r_first.key_base != r_last.key_base) {
+    // Rows of several sequences: every wave walks its own keys.
+    const int32_t c1 = min(c0 + key_chunk, ri.pos + 1);
+    if (active && c0 < c1) row_direct<D, MT>(st, k_idx, ri, c0, c1, out_row, col, half);
+    return;
+  }
+
+  // All rows share one sequence; positions grow with the row.
+  const int32_t c_end = min(c0 + key_chunk, r_last.pos + 1);
+  if (c0 >= c_end) return;
+  const int32_t my_end = active ? min(c0 + key_chunk, ri.pos + 1) : c0;
+  const uint16_t* kseq = k_idx + r_first.key_base * D;
+
+  // Stage loader: thread -> (key, 16-byte chunk), chunk XOR-swizzled by key.
+  // The global side of each entry and its LDS slot are fixed per thread.
+  const uint16_t* gsrc[LOADS];
+  int lds_off[LOADS], key_of[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int e = tid + i * kBlockRows * kWave;
+    const int key = e / CHUNKS, chunk = e % CHUNKS;
+    key_of[i] = key;
+    gsrc[i] = kseq + chunk * 8;
+    lds_off[i] = key * D + (chunk ^ (key & (CHUNKS - 1))) * 8;
+  }
+  u32x4 stage_regs[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i)
+    stage_regs[i] = *reinterpret_cast<const u32x4*>(
+        gsrc[i] + static_cast<int64_t>(min(c0 + key_of[i], r_last.pos)) * D);
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i)
+    *reinterpret_cast<u32x4*>(&tile[0][lds_off[i]]) = stage_regs[i];
+  __syncthreads();
+  int buf = 0;
+  for (int32_t t0 = c0; t0 < c_end; t0 += kStageKeys) {
+    // Next stage in flight while this one is multiplied (past the end the
+    // clamped addresses re-read the last key; that copy is never used).
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      stage_regs[i] = *reinterpret_cast<const u32x4*>(
+          gsrc[i] + static_cast<int64_t>(min(t0 + kStageKeys + key_of[i], r_last.pos)) * D);
+    // Keep the loads here, ahead of the multiply (the scheduler would
+    // otherwise sink them next to their LDS store and expose their latency).
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      // Waves whose row ends earlier still multiply (no branch here, so the
+      // loads above stay in flight); their stores are masked.
+      f32x16 acc0[MT], acc1[MT];
+      bf16x8 b[KS];
+      const uint16_t* tb = tile[buf];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int slot = (half * KS + ks) ^ (col & (CHUNKS - 1));  // d = half*D/2 + ks*8
+        b[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&tb[col * D + slot * 8]));
+      }
+      tile_mfma<D, MT>(st, b, acc0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int key = 32 + col;
+        const int slot = (half * KS + ks) ^ (key & (CHUNKS - 1));
+        b[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&tb[key * D + slot * 8]));
+      }
+      tile_mfma<D, MT>(st, b, acc1);
+      const float s0 = tile_epilogue<D, MT>(st, acc0);
+      const float s1 = tile_epilogue<D, MT>(st, acc1);
+      if (half == 0) {
+        if (t0 + col < my_end) out_row[t0 + col] = s0;
+        if (t0 + 32 + col < my_end) out_row[t0 + 32 + col] = s1;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      *reinterpret_cast<u32x4*>(&tile[buf ^ 1][lds_off[i]]) = stage_regs[i];
+    __syncthreads();
+    buf ^= 1;
+  }
+}
+
+// ---------------------------------------------------------------- decode kernel
+
+template <int D, int MT>
+__global__ __launch_bounds__(kStreamRows * kWave) void index_scores_stream(
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
+    const float* __restrict__ w, int n_heads, int64_t row_begin, int64_t row_count,
+    float* __restrict__ scores, int64_t ld, int key_chunk) {
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  // Workgroup = one row and four consecutive key chunks (one per wave).
+  const int64_t local = static_cast<int64_t>(gridDim.x) - 1 - blockIdx.x;
+  if (local >= row_count) return;
+  const int64_t row = row_begin + local;
+  const RowInfo ri = row_info(cu_q, cu_k, batch, row);
+  const int32_t c0 = (blockIdx.y * kStreamRows + wave) * key_chunk;
+  const int32_t c1 = min(c0 + key_chunk, ri.pos + 1);
+  if (c0 >= c1) return;
+  RowState<D, MT> st;
+  load_row_state<D, MT>(st, q_idx, w, row, n_heads, col, half);
+  row_direct<D, MT>(st, k_idx, ri, c0, c1, scores + local * ld, col, half);
+}
+
+template <int D, int MT>
+hipError_t launch_dm(const dsa_varlen& vl, const uint16_t* q_idx, const uint16_t* k_idx,
+                     const float* w, int n_heads, int64_t row_begin, int64_t row_count,
+                     float* scores, int64_t ld, hipStream_t stream) {
+  if (vl.max_seqlen_q >= kBlockRows) {
+    // Prefill-like: whole rows per workgroup unless there are too few
+    // workgroups to fill the chip, then split the keys.
+    const int64_t blocks = (row_count + kBlockRows - 1) / kBlockRows;
+    int64_t chunk = vl.max_seqlen_k;
+    if (blocks < 1024) {
+      const int64_t parts = (1024 + blocks - 1) / blocks;
+      chunk = (vl.max_seqlen_k + parts - 1) / parts;
+    }
+    chunk = ((chunk + kStageKeys - 1) / kStageKeys) * kStageKeys;
+    if (chunk < 512) chunk = 512;
+    const int64_t chunks = (vl.max_seqlen_k + chunk - 1) / chunk;
+    hipLaunchKernelGGL((index_scores_block<D, MT>), dim3(static_cast<unsigned>(blocks),
+                       static_cast<unsigned>(chunks)), dim3(kBlockRows * kWave), 0, stream,
+                       vl.cu_seqlens_q, vl.cu_seqlens_k, vl.batch, q_idx, k_idx, w, n_heads,
+                       row_begin, row_count, scores, ld, static_cast<int>(chunk));
+  } else {
+    // Decode-like: each wave streams one key chunk (a multiple of 64 keys)
+    // of one row.
+    int64_t parts = (8192 + row_count - 1) / row_count;  // waves per row wanted
+    int64_t chunk = (vl.max_seqlen_k + parts - 1) / parts;
+    chunk = ((chunk + 63) / 64) * 64;
+    if (chunk < 256) chunk = 256;
+    const int64_t waves = (vl.max_seqlen_k + chunk - 1) / chunk;
+    const int64_t groups = (waves + kStreamRows - 1) / kStreamRows;
+    hipLaunchKernelGGL((index_scores_stream<D, MT>), dim3(static_cast<unsigned>(row_count),
+                       static_cast<unsigned>(groups)), dim3(kStreamRows * kWave), 0, stream,
+                       vl.cu_seqlens_q, vl.cu_seqlens_k, vl.batch, q_idx, k_idx, w, n_heads,
+                       row_begin, row_count, scores, ld, static_cast<int>(chunk));
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const dsa_varlen& vl, const uint16_t* q_idx, const uint16_t* k_idx,
+                    const float* w, int n_heads, int64_t row_begin, int64_t row_count,
+                    float* scores, int64_t ld, hipStream_t stream) {
+  if (n_heads > 32)
+    return launch_dm<D, 2>(vl, q_idx, k_idx, w, n_heads, row_begin, row_count, scores, ld, stream);
+  return launch_dm<D, 1>(vl, q_idx, k_idx, w, n_heads, row_begin, row_count, scores, ld, stream);
 }
 
 }  // namespace
@@ -103,30 +327,9 @@ __global__ __launch_bounds__(256) void index_scores_kernel(
 hipError_t launch_index_scores(const dsa_varlen& vl, const uint16_t* q_idx, const uint16_t* k_idx,
                                const float* w, int n_heads, int d, int64_t row_begin,
                                int64_t row_count, float* scores, int64_t ld, hipStream_t stream) {
-  // A long row is split into chunks when there are too few rows to fill the
-  // chip (decode); prefill windows keep whole rows per wave.
-  const int64_t blocks_x = (row_count + kRowsPerBlock - 1) / kRowsPerBlock;
-  int key_chunk = vl.max_seqlen_k;
-  if (blocks_x < 2048) {
-    const int64_t want_chunks = (4096 + blocks_x - 1) / blocks_x;
-    int64_t c = (vl.max_seqlen_k + want_chunks - 1) / want_chunks;
-    c = ((c + 31) / 32) * 32;
-    key_chunk = static_cast<int>(c < 256 ? 256 : c);
-  }
-  key_chunk = ((key_chunk + 31) / 32) * 32;
-  const int chunks = (vl.max_seqlen_k + key_chunk - 1) / key_chunk;
-  dim3 grid(static_cast<unsigned>(blocks_x), static_cast<unsigned>(chunks));
-  dim3 block(256);
-  if (d == 128) {
-    hipLaunchKernelGGL(index_scores_kernel<128>, grid, block, 0, stream, vl.cu_seqlens_q,
-                       vl.cu_seqlens_k, vl.batch, q_idx, k_idx, w, n_heads, row_begin, row_count,
-                       scores, ld, key_chunk);
-  } else {
-    hipLaunchKernelGGL(index_scores_kernel<64>, grid, block, 0, stream, vl.cu_seqlens_q,
-                       vl.cu_seqlens_k, vl.batch, q_idx, k_idx, w, n_heads, row_begin, row_count,
-                       scores, ld, key_chunk);
-  }
-  return hipGetLastError();
+  if (d == 128)
+    return launch_d<128>(vl, q_idx, k_idx, w, n_heads, row_begin, row_count, scores, ld, stream);
+  return launch_d<64>(vl, q_idx, k_idx, w, n_heads, row_begin, row_count, scores, ld, stream);
 }
 
 }  // namespace dsa

@@ -6,19 +6,32 @@
 // 1 keeps the k = 2048 best positions per query token; section 8 needs the
 // selection to be deterministic so training and inference agree).
 //
-// One workgroup of 1024 threads owns one row and reads it from HBM exactly
-// once, in position order, 4096 scores per step.  A score survives only if
-// its order-preserving key beats the running threshold; survivors are
-// appended to a candidate buffer in LDS (one LDS atomic per wave per step,
-// slots assigned by ballot prefix counts).  When the buffer could overflow
-// on the next step it is compacted to exactly k entries by a three-level
-// radix select over the buffer (11 + 11 + 10 bits of the key), ties at the
-// threshold resolved by a second radix select on the position.  The new
-// threshold is the k-th key: later scores equal to it sit at higher positions
-// and can never displace the kept ties, so the test is a strict "greater
-// than".  At the end the k kept positions are sorted by a bitonic network in
-// LDS.  Every decision depends only on key and position values, never on the
-// order in which lanes appended, so the output is bitwise repeatable.
+// One workgroup of 256 threads owns one row and reads it from HBM exactly
+// once, in position order, 1024 scores per step with four steps in flight.
+// The workgroup needs ~37 KB of LDS, so four rows run per CU and hide each
+// other's latencies; its barriers span only four waves.
+//
+// A score survives only if its order-preserving key beats the running
+// threshold; survivors are appended to a candidate buffer in LDS (one LDS
+// atomic per wave per step, slots assigned by ballot prefix counts).  Long
+// rows start from a threshold read off a 1024-score sample of the row (256
+// spread 16-byte pieces) at the rank where about 2.5 k scores of the whole
+// row are expected above it, so the buffer is cut once or twice per row
+// instead of a dozen times.  The estimate only decides speed: if fewer than
+// k scores beat it, the row is streamed again from threshold zero, so the
+// result is exact for any input.  When
+// the buffer could overflow on the next step it is cut to exactly k entries
+// by a radix select whose digits are taken relative to the range of the
+// candidates' keys (min..max, 1024 bins): the bins spread over the values
+// actually present, so atomics rarely collide and each level shrinks the
+// range 1024-fold.  Ties at the k-th key are cut by a second select on the
+// position.  The new threshold is the k-th key: later scores equal to it sit
+// at higher positions and can never displace the kept ties, so the test
+// stays a strict "greater than".  At the end the kept positions are marked
+// in an LDS bitmask and written in ascending order by a prefix count over
+// its words (a bitonic sort serves rows too long for the bitmask).  Every
+// decision depends only on key and position values, never on the order in
+// which lanes appended, so the output is bitwise repeatable.
 #include "dsa_common.h"
 #include "dsa_internal.h"
 
@@ -26,23 +39,48 @@ namespace dsa {
 
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
 constexpr int kChunk = 4 * kThreads;  // scores per step (one float4 per thread)
-constexpr int kCap = 8192;            // candidate buffer entries (>= k + kChunk)
+constexpr int kWaveStep = 4 * kWave;  // most entries one wave appends per step
+constexpr int kDepth = 4;             // steps in flight
+constexpr int kCap = 4096;            // candidate buffer entries
+constexpr int kSeg = kCap / kWaves;   // one buffer segment per wave
 constexpr int kPerThread = kCap / kThreads;
-constexpr int kBins = 2048;
+constexpr int kBins = 1024;
+constexpr int kBinsPerThread = kBins / kThreads;
 constexpr int kMaxK = 2048;
+constexpr int kMaskBits = kCap * 32;  // longest row emitted through the bitmask
+constexpr int kSampleMinRow = 8192;   // shorter rows start from threshold zero
+
+static_assert(kSeg == kThreads * (kPerThread / kWaves), "entry j of a thread lies in segment j / 4");
 
 struct TopkShared {
-  uint32_t key[kCap];
+  uint32_t key[kCap];  // reused as the position bitmask when emitting
   uint32_t pos[kCap];
   uint32_t hist[kBins];
+  uint32_t red[2 * kWaves];
+  uint32_t fill[2][kWaves];  // per-wave segment fill, double-buffered by step parity
   uint32_t count;
-  uint32_t prefix;
-  uint32_t remaining;
-  uint32_t above;
-  uint32_t equal;
+  uint32_t lo, hi, above, remaining, equal;
 };
+
+// Fill levels of the four segments, held in registers (uniform).
+struct Fill {
+  uint32_t f[kWaves];
+  __device__ uint32_t total() const {
+    uint32_t t = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) t += f[w];
+    return t;
+  }
+};
+
+// Entry j (0..15) of thread t is buffer slot t + 256 j, i.e. segment j / 4 at
+// offset t + 256 (j % 4).
+__device__ __forceinline__ bool slot_valid(const Fill& fl, int tid, int j) {
+  return static_cast<uint32_t>(tid + kThreads * (j & 3)) < fl.f[j >> 2];
+}
 
 // Monotone map float -> uint32 (larger float, larger key); -0 maps like +0.
 __device__ __forceinline__ uint32_t order_key(float x) {
@@ -51,177 +89,229 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// m-th largest of keyf(e) over buffer entries e < cnt with pred(e) (needs
-// 1 <= m <= number of such entries).  Returns tau, the count strictly above
-// it and the count equal to it.  Block-wide; all threads must call.
-template <class KeyF, class Pred>
-__device__ void select_kth(TopkShared& sh, uint32_t cnt, uint32_t m, KeyF keyf, Pred pred,
-                           uint32_t& tau, uint32_t& above, uint32_t& equal) {
-  const int tid = threadIdx.x;
-  uint32_t prefix = 0, mask = 0, remaining = m, gt = 0;
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
 #pragma unroll
-  for (int level = 0; level < 3; ++level) {
-    const int shift = level == 0 ? 21 : (level == 1 ? 10 : 0);
-    const int bins = level == 2 ? 1024 : 2048;
-    for (int b = tid; b < bins; b += kThreads) sh.hist[b] = 0u;
-    __syncthreads();
-    for (uint32_t e = tid; e < cnt; e += kThreads) {
-      if (pred(e)) {
-        const uint32_t kv = keyf(e);
-        if ((kv & mask) == prefix) atomicAdd(&sh.hist[(kv >> shift) & (bins - 1)], 1u);
-      }
-    }
-    __syncthreads();
-    if (tid < kWave) {
-      const int lane = tid;
-      const int per = bins / kWave;
-      uint32_t local = 0;
-      for (int b = 0; b < per; ++b) local += sh.hist[lane * per + b];
-      uint32_t suffix = local;  // inclusive suffix sum over lanes
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t t = __shfl_down(suffix, off);
-        if (lane + off < kWave) suffix += t;
-      }
-      const unsigned long long ok = __ballot(suffix >= remaining);
-      const int last = ok ? 63 - __builtin_clzll(ok) : 0;
-      if (lane == last) {
-        uint32_t run = suffix - local;  // entries in higher lanes' bins
-        int digit = lane * per;
-        for (int b = lane * per + per - 1; b >= lane * per; --b) {
-          const uint32_t c = sh.hist[b];
-          if (run + c >= remaining) { digit = b; break; }
-          run += c;
-        }
-        sh.prefix = prefix | (static_cast<uint32_t>(digit) << shift);
-        sh.above = gt + run;
-        sh.remaining = remaining - run;
-        sh.equal = sh.hist[digit];
-      }
-    }
-    __syncthreads();
-    prefix = sh.prefix;
-    gt = sh.above;
-    remaining = sh.remaining;
-    mask |= static_cast<uint32_t>(bins - 1) << shift;
-  }
-  tau = prefix;
-  above = gt;
-  equal = sh.equal;
-  __syncthreads();
+  for (int off = 32; off > 0; off >>= 1) v = min(v, static_cast<uint32_t>(__shfl_xor(v, off)));
+  return v;
 }
 
-// Keep exactly the m best entries (key desc, position asc).  Returns the
-// m-th key, the new acceptance threshold.
-__device__ uint32_t compact_to(TopkShared& sh, uint32_t m) {
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(v, off)));
+  return v;
+}
+
+// m-th largest value of keyf(j) over this thread's entries j = 0..kPerThread-1
+// (slot tid + 256 j) for which pred(j) holds, across the workgroup (needs
+// 1 <= m <= number of such entries).  Returns tau, the count of entries
+// strictly above it and the count equal to it.  Block-wide: every thread
+// calls it with the same m.
+template <class KeyF, class Pred>
+__device__ void select_kth(TopkShared& sh, uint32_t m, KeyF keyf, Pred pred, uint32_t& tau,
+                           uint32_t& above, uint32_t& equal) {
   const int tid = threadIdx.x;
-  const uint32_t cnt = sh.count;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  uint32_t kv[kPerThread];
+  bool in[kPerThread];
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    in[j] = pred(j);
+    kv[j] = in[j] ? keyf(j) : 0u;
+    if (in[j]) {
+      lo = min(lo, kv[j]);
+      hi = max(hi, kv[j]);
+    }
+  }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  if (lane == 0) {
+    sh.red[wave] = lo;
+    sh.red[kWaves + wave] = hi;
+  }
+  for (int b = tid; b < kBins; b += kThreads) sh.hist[b] = 0u;
+  __syncthreads();
+  lo = sh.red[0];
+  hi = sh.red[kWaves];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) {
+    lo = min(lo, sh.red[i]);
+    hi = max(hi, sh.red[kWaves + i]);
+  }
+  __syncthreads();  // sh.red is reused below
+  uint32_t gt = 0, remaining = m;
+  while (true) {
+    // Histogram of (key - lo) >> shift over [lo, hi]; a single value is one bin.
+    const uint32_t span = hi - lo;
+    const int bits = span == 0u ? 0 : 32 - __builtin_clz(span);  // span < 2^bits
+    const int shift = bits > 10 ? bits - 10 : 0;                  // digit < 1024
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j)
+      if (in[j] && kv[j] >= lo && kv[j] <= hi) atomicAdd(&sh.hist[(kv[j] - lo) >> shift], 1u);
+    __syncthreads();
+    // Suffix counts: thread t owns bins [t*4, t*4 + 4).
+    uint32_t hb[kBinsPerThread];
+    uint32_t local = 0;
+#pragma unroll
+    for (int i = 0; i < kBinsPerThread; ++i) {
+      hb[i] = sh.hist[tid * kBinsPerThread + i];
+      local += hb[i];
+    }
+    uint32_t suffix = local;  // inclusive suffix sum within the wave
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const uint32_t t = __shfl_down(suffix, off);
+      if (lane + off < kWave) suffix += t;
+    }
+    if (lane == 0) sh.red[wave] = suffix;  // wave total
+    __syncthreads();
+    for (int wv = wave + 1; wv < kWaves; ++wv) suffix += sh.red[wv];
+    // The owner of the crossing bin: suffix >= remaining > suffix - local.
+    if (suffix >= remaining && suffix - local < remaining) {
+      uint32_t run = suffix - local;  // entries in higher bins
+      int digit = tid * kBinsPerThread;
+#pragma unroll
+      for (int i = kBinsPerThread - 1; i >= 0; --i) {
+        if (run + hb[i] >= remaining) { digit = tid * kBinsPerThread + i; break; }
+        run += hb[i];
+      }
+      const uint32_t nlo = lo + (static_cast<uint32_t>(digit) << shift);
+      const uint32_t width_m1 = shift == 0 ? 0u : ((1u << shift) - 1u);
+      sh.lo = nlo;
+      sh.hi = (hi - nlo <= width_m1) ? hi : nlo + width_m1;  // no wrap-around
+      sh.above = gt + run;
+      sh.remaining = remaining - run;
+      sh.equal = hb[digit - tid * kBinsPerThread];
+    }
+    __syncthreads();
+    lo = sh.lo;
+    hi = sh.hi;
+    gt = sh.above;
+    remaining = sh.remaining;
+    equal = sh.equal;
+    // Every thread has read the level's results and its bins: clear them.
+    for (int b = tid; b < kBins; b += kThreads) sh.hist[b] = 0u;
+    __syncthreads();
+    if (shift == 0) break;
+  }
+  tau = lo;
+  above = gt;
+}
+
+// Keep exactly the m best valid entries (key desc, position asc) and spread
+// them round-robin over the four segments (m/4 each).  Returns the m-th key,
+// the new acceptance threshold, and the new fill levels.
+__device__ uint32_t compact_to(TopkShared& sh, uint32_t m, Fill& fl) {
+  const int tid = threadIdx.x;
   uint32_t tau, above, equal;
   select_kth(
-      sh, cnt, m, [&](uint32_t e) { return sh.key[e]; }, [](uint32_t) { return true; }, tau,
-      above, equal);
+      sh, m, [&](int j) { return sh.key[tid + kThreads * j]; },
+      [&](int j) { return slot_valid(fl, tid, j); }, tau, above, equal);
   const uint32_t need = m - above;
   uint32_t pos_cut = 0xFFFFFFFFu;
   if (equal > need) {
     uint32_t t2, a2, e2;
     select_kth(
-        sh, cnt, need, [&](uint32_t e) { return ~sh.pos[e]; },
-        [&](uint32_t e) { return sh.key[e] == tau; }, t2, a2, e2);
+        sh, need, [&](int j) { return ~sh.pos[tid + kThreads * j]; },
+        [&](int j) { return slot_valid(fl, tid, j) && sh.key[tid + kThreads * j] == tau; }, t2,
+        a2, e2);
     pos_cut = ~t2;
   }
   uint32_t kk[kPerThread], pp[kPerThread];
-  bool keep[kPerThread];
   uint32_t nk = 0;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
-    const uint32_t e = tid + j * kThreads;
-    keep[j] = false;
-    if (e < cnt) {
-      kk[j] = sh.key[e];
-      pp[j] = sh.pos[e];
-      keep[j] = kk[j] > tau || (kk[j] == tau && pp[j] <= pos_cut);
+    kk[j] = 0u;
+    pp[j] = 0u;
+    if (slot_valid(fl, tid, j)) {
+      const uint32_t kv = sh.key[tid + kThreads * j], pv = sh.pos[tid + kThreads * j];
+      if (kv > tau || (kv == tau && pv <= pos_cut)) {
+        kk[j] = kv;
+        pp[j] = pv | 0x80000000u;  // mark as kept (positions < 2^31)
+        ++nk;
+      }
     }
-    nk += keep[j] ? 1u : 0u;
   }
-  __syncthreads();
   if (tid == 0) sh.count = 0u;
   __syncthreads();
-  uint32_t slot = nk ? atomicAdd(&sh.count, nk) : 0u;
+  uint32_t s = nk ? atomicAdd(&sh.count, nk) : 0u;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
-    if (keep[j]) {
-      sh.key[slot] = kk[j];
-      sh.pos[slot] = pp[j];
-      ++slot;
+    if (pp[j] & 0x80000000u) {
+      const int e = (s & (kWaves - 1)) * kSeg + (s >> 2);  // round-robin over segments
+      sh.key[e] = kk[j];
+      sh.pos[e] = pp[j] & 0x7FFFFFFFu;
+      ++s;
     }
   }
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) fl.f[w] = (m + kWaves - 1 - w) / kWaves;
   __syncthreads();
   return tau;
 }
 
-__global__ __launch_bounds__(kThreads) void topk_kernel(
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
-    const float* __restrict__ scores, int64_t ld, int64_t row_begin, int64_t row_count, int k,
-    int32_t* __restrict__ indices) {
-  __shared__ TopkShared sh;
+// Write the kept positions (valid entries, k of them) in ascending order.
+__device__ void emit_sorted(TopkShared& sh, const Fill& fl, int k, int32_t n,
+                            int32_t* __restrict__ orow) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  // Later rows are longer: hand them out first.
-  const int64_t local = row_count - 1 - static_cast<int64_t>(blockIdx.x);
-  const RowInfo ri = row_info(cu_q, cu_k, batch, row_begin + local);
-  const int32_t n = ri.pos + 1;
-  int32_t* orow = indices + local * k;
-  if (n <= k) {
-    for (int j = tid; j < k; j += kThreads) orow[j] = j < n ? j : -1;
-    return;
-  }
-  const float* srow = scores + local * ld;
-  if (tid == 0) sh.count = 0u;
-  __syncthreads();
-
-  uint32_t thr = 0u;  // accept key > thr; 0 admits every finite score
-  float4 cur = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (4 * tid < n) cur = *reinterpret_cast<const float4*>(srow + 4 * tid);
-  for (int32_t base = 0; base < n; base += kChunk) {
-    const int32_t j = base + 4 * tid;
-    float4 nxt = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (j + kChunk < n) nxt = *reinterpret_cast<const float4*>(srow + j + kChunk);
-    const float xs[4] = {cur.x, cur.y, cur.z, cur.w};
-    uint32_t kv[4];
-    unsigned long long mk[4];
-    uint32_t total = 0;
+  const int wave = tid / kWave;
+  uint32_t pv[kPerThread];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      kv[e] = order_key(xs[e]);
-      const bool acc = (j + e < n) && kv[e] > thr;
-      mk[e] = __ballot(acc);
-      total += __popcll(mk[e]);
+  for (int j = 0; j < kPerThread; ++j)
+    pv[j] = slot_valid(fl, tid, j) ? sh.pos[tid + kThreads * j] : 0xFFFFFFFFu;
+  __syncthreads();  // the key array becomes the bitmask / the pos array is rewritten
+  if (n <= kMaskBits) {
+    // Bitmask over positions 0..n-1 in the (now free) key array.
+    uint32_t* mask = sh.key;
+    const int words = (n + 31) / 32;
+    for (int i = tid; i < words; i += kThreads) mask[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j)
+      if (pv[j] != 0xFFFFFFFFu) atomicOr(&mask[pv[j] >> 5], 1u << (pv[j] & 31));
+    __syncthreads();
+    // Thread t owns words [t*per, t*per + per).
+    const int per = (words + kThreads - 1) / kThreads;
+    const int w0 = tid * per;
+    uint32_t cnt = 0;
+    for (int i = 0; i < per; ++i)
+      if (w0 + i < words) cnt += __popc(mask[w0 + i]);
+    uint32_t incl = cnt;  // inclusive prefix within the wave
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const uint32_t t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
     }
-    if (total) {
-      uint32_t wbase = 0;
-      if (lane == 0) wbase = atomicAdd(&sh.count, total);
-      wbase = __shfl(wbase, 0);
-      const unsigned long long below = (1ull << lane) - 1ull;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if ((mk[e] >> lane) & 1ull) {
-          const uint32_t s = wbase + __popcll(mk[e] & below);
-          sh.key[s] = kv[e];
-          sh.pos[s] = static_cast<uint32_t>(j + e);
-        }
-        wbase += __popcll(mk[e]);
+    if (lane == kWave - 1) sh.red[wave] = incl;
+    __syncthreads();
+    uint32_t base = incl - cnt;
+    for (int i = 0; i < wave; ++i) base += sh.red[i];
+    for (int i = 0; i < per; ++i) {
+      if (w0 + i >= words) break;
+      uint32_t bitsw = mask[w0 + i];
+      while (bitsw) {
+        const int b = __builtin_ctz(bitsw);
+        orow[base++] = (w0 + i) * 32 + b;
+        bitsw &= bitsw - 1u;
       }
     }
-    __syncthreads();
-    if (sh.count > static_cast<uint32_t>(kCap - kChunk) && base + kChunk < n)
-      thr = compact_to(sh, k);
-    cur = nxt;
+    return;
   }
-  if (sh.count > static_cast<uint32_t>(k)) compact_to(sh, k);
-
-  // Sort the k kept positions ascending (bitonic network over a power of two).
+  // Very long rows: gather the k positions densely, then a bitonic sort.
+  if (tid == 0) sh.count = 0u;
+  __syncthreads();
+  uint32_t nv = 0;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) nv += pv[j] != 0xFFFFFFFFu ? 1u : 0u;
+  uint32_t s = nv ? atomicAdd(&sh.count, nv) : 0u;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j)
+    if (pv[j] != 0xFFFFFFFFu) sh.pos[s++] = pv[j];
   int k2 = 1;
   while (k2 < k) k2 <<= 1;
+  __syncthreads();
   for (int e = k + tid; e < k2; e += kThreads) sh.pos[e] = 0xFFFFFFFFu;
   __syncthreads();
   for (int size = 2; size <= k2; size <<= 1) {
@@ -242,11 +332,121 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
   for (int e = tid; e < k; e += kThreads) orow[e] = static_cast<int32_t>(sh.pos[e]);
 }
 
+// Branch-free load of scores j..j+3 (the address is clamped into the row, the
+// caller masks positions >= n): a load under a branch would make the
+// compiler wait for it right away and defeat the prefetch ring.
+__device__ __forceinline__ float4 load_step(const float* __restrict__ srow, int32_t j, int32_t n) {
+  const int32_t last = (n - 1) & ~3;
+  return *reinterpret_cast<const float4*>(srow + min(j, last));
+}
+
+__global__ __launch_bounds__(kThreads) void topk_kernel(
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
+    const float* __restrict__ scores, int64_t ld, int64_t row_begin, int64_t row_count, int k,
+    int32_t* __restrict__ indices) {
+  __shared__ TopkShared sh;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  // Later rows are longer: hand them out first.
+  const int64_t local = row_count - 1 - static_cast<int64_t>(blockIdx.x);
+  const RowInfo ri = row_info(cu_q, cu_k, batch, row_begin + local);
+  const int32_t n = ri.pos + 1;
+  int32_t* orow = indices + local * k;
+  if (n <= k) {
+    for (int j = tid; j < k; j += kThreads) orow[j] = j < n ? j : -1;
+    return;
+  }
+  const float* srow = scores + local * ld;
+  for (int b = tid; b < kBins; b += kThreads) sh.hist[b] = 0u;
+  uint32_t thr0 = 0u;  // accept key > thr; 0 admits every finite score
+  if (n > kSampleMinRow) {
+    // Start threshold: the m-th largest of a spread sample (thread t reads 4
+    // scores at t/256 of the row), m chosen so that about 2.5 k scores of the
+    // row are expected above it.
+    const int32_t at = (static_cast<int32_t>((static_cast<int64_t>(tid) * n) / kThreads)) & ~3;
+    const float4 v = *reinterpret_cast<const float4*>(srow + at);
+    const uint32_t sk[4] = {order_key(v.x), order_key(v.y), order_key(v.z), order_key(v.w)};
+    const int64_t want = (static_cast<int64_t>(5 * k) * kChunk + 2 * static_cast<int64_t>(n) - 1) /
+                         (2 * static_cast<int64_t>(n));
+    const uint32_t m = static_cast<uint32_t>(want < 1 ? 1 : (want > kChunk ? kChunk : want));
+    uint32_t tau, above, equal;
+    select_kth(
+        sh, m, [&](int j) { return sk[j & 3]; }, [](int j) { return j < 4; }, tau, above, equal);
+    // Keys equal to tau are not admitted; lower it by one so they are.
+    thr0 = tau > 0u ? tau - 1u : 0u;
+  }
+  uint32_t thr = thr0;
+  Fill fl;
+  uint32_t mine;  // this wave's segment fill (uniform within the wave)
+  uint32_t* seg_key = sh.key + wave * kSeg;
+  uint32_t* seg_pos = sh.pos + wave * kSeg;
+  int parity;
+restart:
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) fl.f[w] = 0u;
+  mine = 0u;
+  parity = 0;
+  float4 ring[kDepth];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) ring[d] = load_step(srow, d * kChunk + 4 * tid, n);
+  for (int32_t base = 0; base < n; base += kChunk) {
+    const int32_t j = base + 4 * tid;
+    const float4 cur = ring[0];
+#pragma unroll
+    for (int d = 0; d + 1 < kDepth; ++d) ring[d] = ring[d + 1];
+    ring[kDepth - 1] = load_step(srow, j + kDepth * kChunk, n);
+    const float xs[4] = {cur.x, cur.y, cur.z, cur.w};
+    // Append this wave's survivors to its own segment: slots by ballot
+    // prefix counts, no shared counter.
+    const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t kv = order_key(xs[e]);
+      const bool acc = (j + e < n) && kv > thr;
+      const unsigned long long mk = __ballot(acc);
+      if (acc) {
+        const uint32_t s = mine + __popcll(mk & below);
+        seg_key[s] = kv;
+        seg_pos[s] = static_cast<uint32_t>(j + e);
+      }
+      mine += __popcll(mk);
+    }
+    // Publish the fill level under this step's parity; the slots of the other
+    // parity are only rewritten after the next barrier, when every wave has
+    // read them.
+    if (lane == 0) sh.fill[parity][wave] = mine;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) fl.f[w] = sh.fill[parity][w];
+    parity ^= 1;
+    bool full = false;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) full |= fl.f[w] > static_cast<uint32_t>(kSeg - kWaveStep);
+    if (full && base + kChunk < n) {
+      thr = compact_to(sh, k, fl);
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w)
+        if (w == wave) mine = fl.f[w];  // no dynamic register indexing
+    }
+  }
+  if (fl.total() < static_cast<uint32_t>(k)) {
+    // The sampled threshold was too high for this row (fewer than k scores
+    // beat it and no cut happened): stream the row again from zero.
+    thr = 0u;
+    __syncthreads();
+    goto restart;
+  }
+  if (fl.total() > static_cast<uint32_t>(k)) compact_to(sh, k, fl);
+  emit_sorted(sh, fl, k, n, orow);
+}
+
 }  // namespace
 
 hipError_t launch_topk(const dsa_varlen& vl, const float* scores, int64_t ld, int64_t row_begin,
                        int64_t row_count, int k, int32_t* indices, hipStream_t stream) {
-  static_assert(kCap >= kMaxK + kChunk, "candidate buffer too small");
+  static_assert(kSeg - kWaveStep >= (kMaxK + kWaves - 1) / kWaves, "segments too small");
+  static_assert(kBins % kThreads == 0, "bins split evenly over threads");
   hipLaunchKernelGGL(topk_kernel, dim3(static_cast<unsigned>(row_count)), dim3(kThreads), 0,
                      stream, vl.cu_seqlens_q, vl.cu_seqlens_k, vl.batch, scores, ld, row_begin,
                      row_count, k, indices);
