@@ -199,25 +199,11 @@ __device__ void select_kth(TopkShared& sh, uint32_t m, KeyF keyf, Pred pred, uin
   above = gt;
 }
 
-// Keep exactly the m best valid entries (key desc, position asc) and spread
-// them round-robin over the four segments (m/4 each).  Returns the m-th key,
-// the new acceptance threshold, and the new fill levels.
-__device__ uint32_t compact_to(TopkShared& sh, uint32_t m, Fill& fl) {
+// Keep the valid entries with key > tau, or key == tau and position <=
+// pos_cut, and lay them out round-robin over the four segments (kept/4 each).
+// Updates the fill levels.  Block-wide.
+__device__ void regroup(TopkShared& sh, Fill& fl, uint32_t tau, uint32_t pos_cut) {
   const int tid = threadIdx.x;
-  uint32_t tau, above, equal;
-  select_kth(
-      sh, m, [&](int j) { return sh.key[tid + kThreads * j]; },
-      [&](int j) { return slot_valid(fl, tid, j); }, tau, above, equal);
-  const uint32_t need = m - above;
-  uint32_t pos_cut = 0xFFFFFFFFu;
-  if (equal > need) {
-    uint32_t t2, a2, e2;
-    select_kth(
-        sh, need, [&](int j) { return ~sh.pos[tid + kThreads * j]; },
-        [&](int j) { return slot_valid(fl, tid, j) && sh.key[tid + kThreads * j] == tau; }, t2,
-        a2, e2);
-    pos_cut = ~t2;
-  }
   uint32_t kk[kPerThread], pp[kPerThread];
   uint32_t nk = 0;
 #pragma unroll
@@ -245,9 +231,32 @@ __device__ uint32_t compact_to(TopkShared& sh, uint32_t m, Fill& fl) {
       ++s;
     }
   }
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) fl.f[w] = (m + kWaves - 1 - w) / kWaves;
   __syncthreads();
+  const uint32_t kept = sh.count;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) fl.f[w] = (kept + kWaves - 1 - w) / kWaves;
+  __syncthreads();  // everyone has read sh.count before it is reused
+}
+
+// Keep exactly the m best valid entries (key desc, position asc), needs more
+// than m valid entries.  Returns the m-th key, the new acceptance threshold.
+__device__ uint32_t compact_to(TopkShared& sh, uint32_t m, Fill& fl) {
+  const int tid = threadIdx.x;
+  uint32_t tau, above, equal;
+  select_kth(
+      sh, m, [&](int j) { return sh.key[tid + kThreads * j]; },
+      [&](int j) { return slot_valid(fl, tid, j); }, tau, above, equal);
+  const uint32_t need = m - above;
+  uint32_t pos_cut = 0xFFFFFFFFu;
+  if (equal > need) {
+    uint32_t t2, a2, e2;
+    select_kth(
+        sh, need, [&](int j) { return ~sh.pos[tid + kThreads * j]; },
+        [&](int j) { return slot_valid(fl, tid, j) && sh.key[tid + kThreads * j] == tau; }, t2,
+        a2, e2);
+    pos_cut = ~t2;
+  }
+  regroup(sh, fl, tau, pos_cut);
   return tau;
 }
 
@@ -424,7 +433,13 @@ restart:
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) full |= fl.f[w] > static_cast<uint32_t>(kSeg - kWaveStep);
     if (full && base + kChunk < n) {
-      thr = compact_to(sh, k, fl);
+      // One segment is nearly full.  With more than k entries held, cut to
+      // the k best and raise the threshold; otherwise (survivors crowd one
+      // wave's segment) keep them all and spread them evenly.
+      if (fl.total() > static_cast<uint32_t>(k))
+        thr = compact_to(sh, k, fl);
+      else
+        regroup(sh, fl, 0u, 0xFFFFFFFFu);
 #pragma unroll
       for (int w = 0; w < kWaves; ++w)
         if (w == wave) mine = fl.f[w];  // no dynamic register indexing

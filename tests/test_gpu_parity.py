@@ -92,6 +92,24 @@ def test_topk_k2048_long_rows_and_boundaries():
     _topk_case(s, cu_q, cu_k, k, ld)
 
 
+def test_topk_survivors_crowd_one_segment():
+    """Regression: survivors concentrated in one quarter of every 1024-score
+    step (block-structured scores) fill one wave's candidate segment while the
+    total is still below k; the selection must stay exact."""
+    rng = np.random.default_rng(11)
+    k = 2048
+    lens = [9000, 12106, 20000, 40000, 131072]
+    ld = 131072
+    s = rng.standard_normal((len(lens), ld)).astype(np.float32)
+    hot = (np.arange(ld) % 1024) < 256
+    s[:, hot] += 6.0
+    s[1, (np.arange(ld) % 1024) >= 768] += 3.0  # two crowded quarters
+    cu_q = list(range(len(lens) + 1))
+    cu_k = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    log("topk crowded segments")
+    _topk_case(s, cu_q, cu_k, k, ld)
+
+
 @pytest.mark.parametrize("k", [1, 7, 64, 1000, 2048])
 def test_topk_various_k_varlen(k):
     rng = np.random.default_rng(k)
