@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
 
 
@@ -91,8 +93,11 @@ def prefill_counts(wl):
     f_attn = sel * 4 * wl.n_heads_q * wl.head_dim
     b_gather = sel * 2 * wl.n_heads_kv * wl.head_dim * 2
     b_scores = pairs * 4 * 2  # fp32 write by the indexer + read by top-k
+    T = sum(wl.seqlens_q)
+    # indexer: qI and w read once, each key read once, every causal score written once
+    b_idx = T * wl.n_heads_idx * (wl.d_idx * 2 + 4) + T * wl.d_idx * 2 + pairs * 4
     return dict(pairs=pairs, selected=sel, f_idx=f_idx, f_attn=f_attn, b_gather=b_gather,
-                b_scores=b_scores)
+                b_scores=b_scores, b_idx=b_idx)
 
 
 def window_flops(wl, r0, n):
@@ -114,6 +119,23 @@ def decode_bytes(wd):
 
 
 # ---------------------------------------------------------------- CPU baseline
+
+def counter_traffic(kernel_source, record):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE counter
+    record, or None once the kernel source differs from the one measured."""
+    import hashlib
+
+    try:
+        with open(os.path.join(ROOT, record)) as f:
+            rec = json.load(f)
+        with open(os.path.join(ROOT, kernel_source), "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if rec.get("source_sha256") != digest:
+        return None
+    return int(rec["fetch_bytes_per_dispatch"] + rec["write_bytes_per_dispatch"])
+
 
 def cpu_baseline(wl, host, n_rows):
     """The oracle, untuned, on query rows evenly spaced over the prefill."""
@@ -285,7 +307,10 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(idx_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": counter_traffic("long_context_sparse_score_amd/csrc/index_scores.hip",
+                                       "profiles/index_scores_traffic.json"),
+            "traffic_unit": "HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
+            "algorithmic_bytes_per_launch": int(pc["b_idx"] / max(1, n_idx_launches // args.steps)),
             "launches_per_step": n_idx_launches // args.steps,
             "avg_launch_ms": round(idx_ms / n_idx_launches, 3),
             "flops_per_causal_pair": 2 * wl.n_heads_idx * wl.d_idx,
@@ -328,6 +353,17 @@ def main():
             "index_scores_GBps": round(wd.batch * wd.seqlens_k[0] * wd.d_idx * 2 * args.steps
                                        / (d_idx_ms / 1e3) / 1e9, 1),
         }
+
+    if args.calib_copy:
+        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counter readings
+        # calibrate the same counters taken on the DSA kernels.
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     if not args.no_dense:
         result["dense"] = dense_comparator(torch, P, wl, args, pre_ms / args.steps)

@@ -83,6 +83,54 @@ def test_prefill_128k_repeatable():
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
 
 
+def test_prefill_128k_topk_property_all_rows():
+    """Every row of the 128K prefill, at the bench's window size: the selection
+    is causal, ascending, unique, min(k, p + 1) long, and exact for the GPU's own
+    fp32 scores -- each selected score beats each unselected visible score, and
+    on an equal score the selected position is the lower one.  (A property of
+    the top-k that holds at any size; the fp32 scores are the kernel's.)"""
+    wl = synth.prefill_128k()
+    _, dev = device_workload(wl, ("q_idx", "k_idx", "w"))
+    vl = dsa.Varlen(wl.cu_q.tolist(), wl.cu_k.tolist())
+    bufs = pipeline.alloc_prefill(vl, wl.topk, BENCH_WINDOW)
+    ld = bufs.scores.shape[1]
+    cols = torch.arange(ld, device="cuda")
+    bad_rows = 0
+    for r0 in range(0, wl.total_q, BENCH_WINDOW):
+        n = min(BENCH_WINDOW, wl.total_q - r0)
+        dsa.dsa_index_scores(vl, dev["q_idx"], dev["k_idx"], dev["w"], bufs.scores,
+                             row_begin=r0, row_count=n)
+        dsa.dsa_topk(vl, bufs.scores, bufs.indices, row_begin=r0, row_count=n)
+        for c0 in range(0, n, 1024):
+            c1 = min(n, c0 + 1024)
+            sc = bufs.scores[c0:c1]
+            idx = bufs.indices[c0:c1].long()
+            pos = torch.arange(r0 + c0, r0 + c1, device="cuda")[:, None]
+            vis = cols[None, :] <= pos
+            cnt = torch.clamp(pos[:, 0] + 1, max=wl.topk)
+            slot = torch.arange(wl.topk, device="cuda")[None, :]
+            valid = slot < cnt[:, None]
+            ok = torch.where(valid, (idx >= 0) & (idx <= pos), idx == -1).all(dim=1)
+            d = idx[:, 1:] - idx[:, :-1]
+            ok &= torch.where(valid[:, 1:], d > 0, torch.ones_like(d, dtype=torch.bool)).all(dim=1)
+            # mark selected columns; empty slots go to a spare last column
+            sel = torch.zeros((c1 - c0, ld + 1), dtype=torch.bool, device="cuda")
+            sel.scatter_(1, torch.where(valid, idx.clamp(min=0), ld), True)
+            sel = sel[:, :ld]
+            neg = torch.tensor(float("-inf"), device="cuda")
+            tau = torch.where(sel, sc, torch.tensor(float("inf"), device="cuda")).min(dim=1).values
+            rest = vis & ~sel
+            top_rest = torch.where(rest, sc, neg).max(dim=1).values
+            ok &= top_rest <= tau
+            # on a tie with tau, every selected tied position is below every unselected one
+            last_tied_sel = torch.where(sel & (sc == tau[:, None]), cols[None, :], -1).max(dim=1).values
+            first_tied_rest = torch.where(rest & (sc == tau[:, None]), cols[None, :], ld).min(dim=1).values
+            ok &= last_tied_sel < first_tied_rest
+            bad_rows += int((~ok).sum())
+    torch.cuda.synchronize()
+    assert bad_rows == 0, f"{bad_rows} rows violate the top-k property"
+
+
 def test_decode_b64_128k_all_queries():
     wl = synth.decode_b64_128k()
     log("decode_b64_128k: generate")
