@@ -14,11 +14,13 @@
 //
 // Two kernels share that core:
 //  * index_scores_block (prefill): a 512-thread workgroup owns 8 consecutive
-//    query rows of one sequence, one wave per row.  Key tiles of 64 rows
-//    (16 KB) are staged once per workgroup in LDS (double-buffered, 16-byte
-//    chunks XOR-swizzled by key so the B-fragment reads are bank-conflict
-//    free) and feed all 8 waves, so L2 traffic is 1/8 of a per-wave scheme.
-//    Two waves per SIMD let one wave's MFMAs overlap the other's epilogue.
+//    query rows of one sequence, one wave per row.  Key stages of 256 rows
+//    (64 KB at d_idx = 128) are copied by buffer->LDS DMA into one of two LDS
+//    buffers (16-byte chunks XOR-swizzled by key so the B-fragment reads are
+//    bank-conflict free) and feed all 8 waves, so L2 traffic is 1/8 of a
+//    per-wave scheme.  Inside a stage the MFMAs of one 32-key tile overlap
+//    the previous tile's epilogue, and scores leave through range-checked
+//    buffer stores, so a stage waits only for the next stage's DMA.
 //    A workgroup whose rows straddle a sequence boundary falls back to the
 //    per-wave path below.
 //  * index_scores_stream (decode / few rows): each wave streams its own key
@@ -36,7 +38,7 @@ namespace dsa {
 namespace {
 
 constexpr int kBlockRows = 8;        // query rows (waves) per prefill workgroup
-constexpr int kStageKeys = 64;       // keys per LDS stage
+constexpr int kStageKeys = 256;      // keys per LDS stage (2 stages: 128 KB at d_idx = 128)
 constexpr int kStreamRows = 4;       // waves per stream workgroup
 
 // Per-wave stationary state: this row's indexer queries (A operand, heads on
@@ -135,24 +137,43 @@ __device__ void row_direct(const RowState<D, MT>& st, const uint16_t* __restrict
 
 // ---------------------------------------------------------------- prefill kernel
 
+// Raw buffer resources (gfx9 family word 3): loads past num_records return
+// zero and stores past it are dropped by the hardware.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes,
+                                           kRawBufferWord3);
+}
+
+// s_waitcnt immediate: vmcnt(n), expcnt and lgkmcnt left unconstrained.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+
+// Workgroup barrier for LDS hand-off.  The waits it needs are explicit
+// (s_waitcnt before it); the wavefront-scope fences only keep the compiler
+// from moving LDS accesses across it, without the vmcnt(0) a workgroup
+// fence would add (that would also wait for this stage's score stores).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int D, int MT>
-// k_idx is deliberately not restrict-qualified: as a restrict read-only
-// pointer its loads would count as invariant and the compiler would sink the
-// stage prefetch down to its LDS store, exposing the full load latency.
 __global__ __launch_bounds__(kBlockRows * kWave, 2) void index_scores_block(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
     const uint16_t* __restrict__ q_idx, const uint16_t* k_idx,
     const float* __restrict__ w, int n_heads, int64_t row_begin, int64_t row_count,
     float* __restrict__ scores, int64_t ld, int key_chunk) {
   constexpr int KS = D / 16;
-  constexpr int CHUNKS = D / 8;                   // 16-byte chunks per key row
-  constexpr int STAGE_BYTES = kStageKeys * D * 2;
-  constexpr int LOADS = STAGE_BYTES / 16 / (kBlockRows * kWave);  // per thread per stage
+  constexpr int CHUNKS = D / 8;                                     // 16-byte chunks per key row
+  constexpr int DMA_PER_WAVE = kStageKeys * CHUNKS / (kBlockRows * kWave);
+  constexpr int TILES = kStageKeys / 32;                            // 32-key MFMA tiles per stage
+  static_assert(TILES % 2 == 0 && DMA_PER_WAVE * kBlockRows * kWave == kStageKeys * CHUNKS, "stage shape");
   __shared__ __attribute__((aligned(16))) uint16_t tile[2][kStageKeys * D];
 
-  const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   const int col = lane & 31;
   const int half = lane >> 5;
   // Later rows have longer causal prefixes: hand them out first.
@@ -182,73 +203,76 @@ __global__ __launch_bounds__(kBlockRows * kWave, 2) void index_scores_block(
   // All rows share one sequence; positions grow with the row.
   const int32_t c_end = min(c0 + key_chunk, r_last.pos + 1);
   if (c0 >= c_end) return;
+  // Scores of keys my_end and beyond (and every score of an inactive wave)
+  // fall outside the store resource and are dropped.
   const int32_t my_end = active ? min(c0 + key_chunk, ri.pos + 1) : c0;
   const uint16_t* kseq = k_idx + r_first.key_base * D;
+  const __amdgpu_buffer_rsrc_t keys = raw_buffer(kseq, (r_last.pos + 1) * D * 2);
+  const __amdgpu_buffer_rsrc_t outs = raw_buffer(out_row, my_end * 4);
 
-  // Stage loader: thread -> (key, 16-byte chunk), chunk XOR-swizzled by key.
-  // The global side of each entry and its LDS slot are fixed per thread.
-  const uint16_t* gsrc[LOADS];
-  int lds_off[LOADS], key_of[LOADS];
+  // Stage fill by buffer->LDS DMA: DMA instruction i of a wave writes 64
+  // consecutive 16-byte LDS chunks; LDS chunk (key, s) receives global chunk
+  // s ^ (key & (CHUNKS - 1)), so the B-fragment reads below are conflict free.
+  auto fill_stage = [&](int b, int32_t t) {
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int e = tid + i * kBlockRows * kWave;
-    const int key = e / CHUNKS, chunk = e % CHUNKS;
-    key_of[i] = key;
-    gsrc[i] = kseq + chunk * 8;
-    lds_off[i] = key * D + (chunk ^ (key & (CHUNKS - 1))) * 8;
-  }
-  u32x4 stage_regs[LOADS];
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      const int e = (i * kBlockRows + wave) * kWave + lane;
+      const int key = e / CHUNKS, s = e % CHUNKS;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          keys, (__attribute__((address_space(3))) void*)(&tile[b][(i * kBlockRows + wave) * kWave * 8]),
+          16, key * D * 2 + (s ^ (key & (CHUNKS - 1))) * 16, t * D * 2, 0, 0);
+    }
+  };
+  // One score per lane of the lower half-wave (the upper half holds copies).
+  auto store = [&](float v, int32_t pos) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), outs, half == 0 ? pos * 4 : 0x7FFFFFF0, 0, 0);
+  };
+
+  fill_stage(0, c0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  lds_barrier();
+  // Tile j's MFMAs run while tile j-1's epilogue executes on the VALU; each
+  // B fragment register is refilled from LDS for tile j+1 as soon as tile
+  // j's MFMAs have consumed it.
+  f32x16 acc_even[MT], acc_odd[MT];
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i)
-    stage_regs[i] = *reinterpret_cast<const u32x4*>(
-        gsrc[i] + static_cast<int64_t>(min(c0 + key_of[i], r_last.pos)) * D);
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i)
-    *reinterpret_cast<u32x4*>(&tile[0][lds_off[i]]) = stage_regs[i];
-  __syncthreads();
+  for (int mt = 0; mt < MT; ++mt) acc_odd[mt] = f32x16{};
+  int32_t prev_pos = 1 << 28;  // the first epilogue has nothing to store
   int buf = 0;
   for (int32_t t0 = c0; t0 < c_end; t0 += kStageKeys) {
-    // Next stage in flight while this one is multiplied (past the end the
-    // clamped addresses re-read the last key; that copy is never used).
+    if (t0 + kStageKeys < c_end) fill_stage(buf ^ 1, t0 + kStageKeys);
+    const uint16_t* tb = tile[buf];
+    bf16x8 b[KS];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i)
-      stage_regs[i] = *reinterpret_cast<const u32x4*>(
-          gsrc[i] + static_cast<int64_t>(min(t0 + kStageKeys + key_of[i], r_last.pos)) * D);
-    // Keep the loads here, ahead of the multiply (the scheduler would
-    // otherwise sink them next to their LDS store and expose their latency).
-    __builtin_amdgcn_sched_barrier(0);
-    {
-      // Waves whose row ends earlier still multiply (no branch here, so the
-      // loads above stay in flight); their stores are masked.
-      f32x16 acc0[MT], acc1[MT];
-      bf16x8 b[KS];
-      const uint16_t* tb = tile[buf];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int slot = (half * KS + ks) ^ (col & (CHUNKS - 1));  // d = half*D/2 + ks*8
-        b[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&tb[col * D + slot * 8]));
-      }
-      tile_mfma<D, MT>(st, b, acc0);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int key = 32 + col;
-        const int slot = (half * KS + ks) ^ (key & (CHUNKS - 1));
-        b[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&tb[key * D + slot * 8]));
-      }
-      tile_mfma<D, MT>(st, b, acc1);
-      const float s0 = tile_epilogue<D, MT>(st, acc0);
-      const float s1 = tile_epilogue<D, MT>(st, acc1);
-      if (half == 0) {
-        if (t0 + col < my_end) out_row[t0 + col] = s0;
-        if (t0 + 32 + col < my_end) out_row[t0 + 32 + col] = s1;
-      }
+    for (int ks = 0; ks < KS; ++ks) {
+      const int slot = (half * KS + ks) ^ (col & (CHUNKS - 1));
+      b[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&tb[col * D + slot * 8]));
     }
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i)
-      *reinterpret_cast<u32x4*>(&tile[buf ^ 1][lds_off[i]]) = stage_regs[i];
-    __syncthreads();
+    for (int tj = 0; tj < TILES; ++tj) {
+      f32x16 (&acc)[MT] = (tj & 1) ? acc_odd : acc_even;
+      f32x16 (&prev)[MT] = (tj & 1) ? acc_even : acc_odd;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(st.a[mt][ks], b[ks],
+                                                            ks == 0 ? f32x16{} : acc[mt], 0, 0, 0);
+        if (tj + 1 < TILES) {
+          const int slot = (half * KS + ks) ^ (col & (CHUNKS - 1));  // (32 (tj+1) + col) & 15 == col & 15
+          b[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&tb[((tj + 1) * 32 + col) * D + slot * 8]));
+        }
+      }
+      store(tile_epilogue<D, MT>(st, prev), prev_pos);
+      prev_pos = t0 + tj * 32 + col;
+    }
+    // Wait for the next stage's DMA only: the TILES score stores issued after
+    // it may stay in flight.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(TILES));
+    lds_barrier();
     buf ^= 1;
   }
+  store(tile_epilogue<D, MT>(st, acc_odd), prev_pos);
 }
 
 // ---------------------------------------------------------------- decode kernel
