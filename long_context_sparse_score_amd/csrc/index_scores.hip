@@ -24,9 +24,9 @@
 //    A workgroup whose rows straddle a sequence boundary falls back to the
 //    per-wave path below.
 //  * index_scores_stream (decode / few rows): each wave streams its own key
-//    range of one row straight from HBM with two tiles in flight; long rows
-//    are split over the grid's second dimension so a handful of rows still
-//    covers the whole chip.
+//    range of one row through a private LDS ring filled by coalesced
+//    buffer->LDS DMA, three 32-key tiles in flight; long rows are split into
+//    chunks so that a handful of rows still covers the whole chip.
 // Every global load is issued unconditionally (addresses are clamped into
 // the sequence instead): a load under a branch makes the compiler wait for
 // it on the spot, which would serialise the prefetch.
@@ -277,27 +277,99 @@ __global__ __launch_bounds__(kBlockRows * kWave, 2) void index_scores_block(
 
 // ---------------------------------------------------------------- decode kernel
 
+// Each wave owns one (row, key chunk) work item and a private LDS ring of
+// kRing 32-key tiles.  Tiles arrive by buffer->LDS DMA: every DMA
+// instruction reads 1 KB of whole key rows (coalesced, unlike loading the
+// MFMA operand layout straight from memory, which touches 32 rows per
+// instruction and caps the scan well below HBM speed), and the XOR swizzle
+// is applied on the global side so the B-fragment reads from LDS are
+// conflict free.  kRing - 1 tiles are in flight while one is multiplied; the
+// ring is private to the wave, so no workgroup barrier is needed.
+constexpr int kRing = 4;
+
 template <int D, int MT>
 __global__ __launch_bounds__(kStreamRows * kWave) void index_scores_stream(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
     const float* __restrict__ w, int n_heads, int64_t row_begin, int64_t row_count,
-    float* __restrict__ scores, int64_t ld, int key_chunk) {
+    float* __restrict__ scores, int64_t ld, int key_chunk, int chunks_per_row) {
+  constexpr int KS = D / 16;
+  constexpr int CHUNKS = D / 8;
+  constexpr int DMA_PER_TILE = 32 * CHUNKS / kWave;   // 16-byte DMA instructions per tile
+  static_assert(DMA_PER_TILE * kWave == 32 * CHUNKS, "tile shape");
+  __shared__ __attribute__((aligned(16))) uint16_t ring[kStreamRows][kRing][32 * D];
+
   const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   const int col = lane & 31;
   const int half = lane >> 5;
-  // Workgroup = one row and four consecutive key chunks (one per wave).
-  const int64_t local = static_cast<int64_t>(gridDim.x) - 1 - blockIdx.x;
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * kStreamRows + wave;
+  const int64_t local = item / chunks_per_row;
   if (local >= row_count) return;
   const int64_t row = row_begin + local;
   const RowInfo ri = row_info(cu_q, cu_k, batch, row);
-  const int32_t c0 = (blockIdx.y * kStreamRows + wave) * key_chunk;
+  const int32_t c0 = static_cast<int32_t>(item % chunks_per_row) * key_chunk;
   const int32_t c1 = min(c0 + key_chunk, ri.pos + 1);
   if (c0 >= c1) return;
   RowState<D, MT> st;
   load_row_state<D, MT>(st, q_idx, w, row, n_heads, col, half);
-  row_direct<D, MT>(st, k_idx, ri, c0, c1, scores + local * ld, col, half);
+
+  // Keys [c0, c1) only (DMA past c1 reads zeros without touching memory);
+  // scores past c1 are dropped.
+  const __amdgpu_buffer_rsrc_t keys = raw_buffer(k_idx + (ri.key_base + c0) * D, (c1 - c0) * D * 2);
+  const __amdgpu_buffer_rsrc_t outs = raw_buffer(scores + local * ld, c1 * 4);
+  auto fill = [&](int slot, int32_t t) {  // tile of keys c0 + t .. c0 + t + 31
+#pragma unroll
+    for (int i = 0; i < DMA_PER_TILE; ++i) {
+      const int e = i * kWave + lane;
+      const int key = e / CHUNKS, s = e % CHUNKS;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          keys, (__attribute__((address_space(3))) void*)(&ring[wave][slot][i * kWave * 8]), 16,
+          (key * D + (s ^ (key & (CHUNKS - 1))) * 8) * 2, t * D * 2, 0, 0);
+    }
+  };
+  auto store = [&](float v, int32_t pos) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), outs, half == 0 ? pos * 4 : 0x7FFFFFF0, 0, 0);
+  };
+
+  // Prologue: tiles 0 .. kRing-2, each followed by a dropped store so that
+  // every tile's DMA is trailed by the same count of memory operations as in
+  // the loop (one store, then the next tile's DMA).
+#pragma unroll
+  for (int p = 0; p < kRing - 1; ++p) {
+    fill(p, p * 32);
+    store(0.0f, 1 << 28);
+  }
+  f32x16 acc[MT], prev[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) prev[mt] = f32x16{};
+  int32_t prev_pos = 1 << 28;
+  const int ntiles = (c1 - c0 + 31) / 32;
+  for (int j = 0; j < ntiles; ++j) {
+    fill((j + kRing - 1) % kRing, (j + kRing - 1) * 32);
+    // Tile j has landed once at most the kRing - 1 younger tiles' DMAs and
+    // their trailing stores are outstanding.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kRing - 1) * (DMA_PER_TILE + 1)));
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint16_t* tb = ring[wave][j % kRing];
+    bf16x8 b[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int slot = (half * KS + ks) ^ (col & (CHUNKS - 1));
+      b[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&tb[col * D + slot * 8]));
+    }
+    tile_mfma<D, MT>(st, b, acc);
+    store(tile_epilogue<D, MT>(st, prev), prev_pos);
+    prev_pos = c0 + j * 32 + col;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) prev[mt] = acc[mt];
+    // The slot refilled next iteration was read above: those reads must be
+    // done before its DMA is issued.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  }
+  store(tile_epilogue<D, MT>(st, prev), prev_pos);
+  // No DMA may still be writing this wave's ring when the wave ends.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
 template <int D, int MT>
@@ -321,18 +393,19 @@ hipError_t launch_dm(const dsa_varlen& vl, const uint16_t* q_idx, const uint16_t
                        vl.cu_seqlens_q, vl.cu_seqlens_k, vl.batch, q_idx, k_idx, w, n_heads,
                        row_begin, row_count, scores, ld, static_cast<int>(chunk));
   } else {
-    // Decode-like: each wave streams one key chunk (a multiple of 64 keys)
-    // of one row.
-    int64_t parts = (8192 + row_count - 1) / row_count;  // waves per row wanted
-    int64_t chunk = (vl.max_seqlen_k + parts - 1) / parts;
-    chunk = ((chunk + 63) / 64) * 64;
-    if (chunk < 256) chunk = 256;
-    const int64_t waves = (vl.max_seqlen_k + chunk - 1) / chunk;
-    const int64_t groups = (waves + kStreamRows - 1) / kStreamRows;
-    hipLaunchKernelGGL((index_scores_stream<D, MT>), dim3(static_cast<unsigned>(row_count),
-                       static_cast<unsigned>(groups)), dim3(kStreamRows * kWave), 0, stream,
-                       vl.cu_seqlens_q, vl.cu_seqlens_k, vl.batch, q_idx, k_idx, w, n_heads,
-                       row_begin, row_count, scores, ld, static_cast<int>(chunk));
+    // Decode-like: one wave per (row, key chunk), about 2048 work items (two
+    // rounds of one 4-wave workgroup per CU; measured best among 2048-8192).
+    const int64_t per_row = (2048 + row_count - 1) / row_count;
+    int64_t chunk = (vl.max_seqlen_k + per_row - 1) / per_row;
+    chunk = ((chunk + 31) / 32) * 32;
+    if (chunk < 512) chunk = 512;
+    const int64_t chunks_per_row = (vl.max_seqlen_k + chunk - 1) / chunk;
+    const int64_t items = row_count * chunks_per_row;
+    hipLaunchKernelGGL((index_scores_stream<D, MT>),
+                       dim3(static_cast<unsigned>((items + kStreamRows - 1) / kStreamRows)),
+                       dim3(kStreamRows * kWave), 0, stream, vl.cu_seqlens_q, vl.cu_seqlens_k,
+                       vl.batch, q_idx, k_idx, w, n_heads, row_begin, row_count, scores, ld,
+                       static_cast<int>(chunk), static_cast<int>(chunks_per_row));
   }
   return hipGetLastError();
 }
