@@ -228,7 +228,7 @@ def main():
         if e: e[0].record(stream)
         dsa.dsa_index_scores(vd, D["q_idx"], D["k_idx"], D["w"], dbufs.scores)
         if e: e[1].record(stream)
-        dsa.dsa_topk(vd, dbufs.scores, dbufs.indices)
+        dsa.dsa_topk(vd, dbufs.scores, dbufs.indices, workspace=dbufs.topk_workspace)
         if e: e[2].record(stream)
         dsa.dsa_sparse_attn_decode(vd, D["q"], D["k"], D["v"], dbufs.indices, dout,
                                    dbufs.workspace, lse=dlse)

@@ -44,6 +44,7 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kChunk = 4 * kThreads;  // scores per step (one float4 per thread)
 constexpr int kWaveStep = 4 * kWave;  // most entries one wave appends per step
 constexpr int kDepth = 4;             // steps in flight
+constexpr int kSamples = kChunk;      // scores sampled for the start threshold
 constexpr int kCap = 4096;            // candidate buffer entries
 constexpr int kSeg = kCap / kWaves;   // one buffer segment per wave
 constexpr int kPerThread = kCap / kThreads;
@@ -341,44 +342,67 @@ __device__ void emit_sorted(TopkShared& sh, const Fill& fl, int k, int32_t n,
   for (int e = tid; e < k; e += kThreads) orow[e] = static_cast<int32_t>(sh.pos[e]);
 }
 
-// Branch-free load of scores j..j+3 (the address is clamped into the row, the
-// caller masks positions >= n): a load under a branch would make the
-// compiler wait for it right away and defeat the prefetch ring.
-__device__ __forceinline__ float4 load_step(const float* __restrict__ srow, int32_t j, int32_t n) {
-  const int32_t last = (n - 1) & ~3;
-  return *reinterpret_cast<const float4*>(srow + min(j, last));
-}
+// Element sources for the streaming select.  fetch(j) loads elements
+// j..j+3 (j a multiple of 4) with a branch-free, clamped address -- a load
+// under a branch would make the compiler wait for it right away and defeat
+// the prefetch ring; the caller masks elements >= n.  unpack() turns them
+// into (order key, position) pairs.
 
-__global__ __launch_bounds__(kThreads) void topk_kernel(
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
-    const float* __restrict__ scores, int64_t ld, int64_t row_begin, int64_t row_count, int k,
-    int32_t* __restrict__ indices) {
-  __shared__ TopkShared sh;
+// Scores of one row: element j is position pos0 + j.
+struct ScoreSource {
+  const float* row;  // score of element 0
+  int32_t n;
+  int32_t pos0;
+  using Raw = float4;
+  __device__ Raw fetch(int32_t j) const {
+    return *reinterpret_cast<const float4*>(row + min(j, (n - 1) & ~3));
+  }
+  __device__ void unpack(const Raw& r, int32_t j, uint32_t (&kv)[4], uint32_t (&pv)[4]) const {
+    kv[0] = order_key(r.x); kv[1] = order_key(r.y); kv[2] = order_key(r.z); kv[3] = order_key(r.w);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pv[e] = static_cast<uint32_t>(pos0 + j + e);
+  }
+};
+
+// Candidates left by the per-segment pass: (order key, position) pairs; key
+// 0 marks an empty slot (no finite score maps to 0, and the streaming test
+// admits only keys above the threshold, which is never below 0).
+struct CandidateSource {
+  const uint32_t* key;
+  const uint32_t* pos;
+  int32_t n;
+  struct Raw { u32x4 k, p; };
+  __device__ Raw fetch(int32_t j) const {
+    const int32_t at = min(j, (n - 1) & ~3);
+    return Raw{*reinterpret_cast<const u32x4*>(key + at), *reinterpret_cast<const u32x4*>(pos + at)};
+  }
+  __device__ void unpack(const Raw& r, int32_t, uint32_t (&kv)[4], uint32_t (&pv)[4]) const {
+    kv[0] = r.k.x; kv[1] = r.k.y; kv[2] = r.k.z; kv[3] = r.k.w;
+    pv[0] = r.p.x; pv[1] = r.p.y; pv[2] = r.p.z; pv[3] = r.p.w;
+  }
+};
+
+// Streams the n elements of src once (twice if the sampled start threshold
+// proves too high) and leaves exactly the k best of them (key desc,
+// position asc; needs n > k) as the valid entries of the candidate buffer.
+// Block-wide.
+template <class Src>
+__device__ void select_row(TopkShared& sh, const Src& src, int32_t n, int k, Fill& fl) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  // Later rows are longer: hand them out first.
-  const int64_t local = row_count - 1 - static_cast<int64_t>(blockIdx.x);
-  const RowInfo ri = row_info(cu_q, cu_k, batch, row_begin + local);
-  const int32_t n = ri.pos + 1;
-  int32_t* orow = indices + local * k;
-  if (n <= k) {
-    for (int j = tid; j < k; j += kThreads) orow[j] = j < n ? j : -1;
-    return;
-  }
-  const float* srow = scores + local * ld;
   for (int b = tid; b < kBins; b += kThreads) sh.hist[b] = 0u;
   uint32_t thr0 = 0u;  // accept key > thr; 0 admits every finite score
   if (n > kSampleMinRow) {
     // Start threshold: the m-th largest of a spread sample (thread t reads 4
-    // scores at t/256 of the row), m chosen so that about 2.5 k scores of the
-    // row are expected above it.
+    // elements at t/256 of the stream), m chosen so that about 2.5 k
+    // elements of the stream are expected above it.
     const int32_t at = (static_cast<int32_t>((static_cast<int64_t>(tid) * n) / kThreads)) & ~3;
-    const float4 v = *reinterpret_cast<const float4*>(srow + at);
-    const uint32_t sk[4] = {order_key(v.x), order_key(v.y), order_key(v.z), order_key(v.w)};
-    const int64_t want = (static_cast<int64_t>(5 * k) * kChunk + 2 * static_cast<int64_t>(n) - 1) /
+    uint32_t sk[4], sp[4];
+    src.unpack(src.fetch(at), at, sk, sp);
+    const int64_t want = (static_cast<int64_t>(5 * k) * kSamples + 2 * static_cast<int64_t>(n) - 1) /
                          (2 * static_cast<int64_t>(n));
-    const uint32_t m = static_cast<uint32_t>(want < 1 ? 1 : (want > kChunk ? kChunk : want));
+    const uint32_t m = static_cast<uint32_t>(want < 1 ? 1 : (want > kSamples ? kSamples : want));
     uint32_t tau, above, equal;
     select_kth(
         sh, m, [&](int j) { return sk[j & 3]; }, [](int j) { return j < 4; }, tau, above, equal);
@@ -386,7 +410,6 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
     thr0 = tau > 0u ? tau - 1u : 0u;
   }
   uint32_t thr = thr0;
-  Fill fl;
   uint32_t mine;  // this wave's segment fill (uniform within the wave)
   uint32_t* seg_key = sh.key + wave * kSeg;
   uint32_t* seg_pos = sh.pos + wave * kSeg;
@@ -396,28 +419,28 @@ restart:
   for (int w = 0; w < kWaves; ++w) fl.f[w] = 0u;
   mine = 0u;
   parity = 0;
-  float4 ring[kDepth];
+  typename Src::Raw ring[kDepth];
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d) ring[d] = load_step(srow, d * kChunk + 4 * tid, n);
+  for (int d = 0; d < kDepth; ++d) ring[d] = src.fetch(d * kChunk + 4 * tid);
   for (int32_t base = 0; base < n; base += kChunk) {
     const int32_t j = base + 4 * tid;
-    const float4 cur = ring[0];
+    const typename Src::Raw cur = ring[0];
 #pragma unroll
     for (int d = 0; d + 1 < kDepth; ++d) ring[d] = ring[d + 1];
-    ring[kDepth - 1] = load_step(srow, j + kDepth * kChunk, n);
-    const float xs[4] = {cur.x, cur.y, cur.z, cur.w};
+    ring[kDepth - 1] = src.fetch(j + kDepth * kChunk);
+    uint32_t kvs[4], pvs[4];
+    src.unpack(cur, j, kvs, pvs);
     // Append this wave's survivors to its own segment: slots by ballot
     // prefix counts, no shared counter.
     const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint32_t kv = order_key(xs[e]);
-      const bool acc = (j + e < n) && kv > thr;
+      const bool acc = (j + e < n) && kvs[e] > thr;
       const unsigned long long mk = __ballot(acc);
       if (acc) {
         const uint32_t s = mine + __popcll(mk & below);
-        seg_key[s] = kv;
-        seg_pos[s] = static_cast<uint32_t>(j + e);
+        seg_key[s] = kvs[e];
+        seg_pos[s] = pvs[e];
       }
       mine += __popcll(mk);
     }
@@ -446,22 +469,154 @@ restart:
     }
   }
   if (fl.total() < static_cast<uint32_t>(k)) {
-    // The sampled threshold was too high for this row (fewer than k scores
-    // beat it and no cut happened): stream the row again from zero.
+    // The sampled threshold was too high (fewer than k elements beat it and
+    // no cut happened): stream again from zero.
     thr = 0u;
     __syncthreads();
     goto restart;
   }
   if (fl.total() > static_cast<uint32_t>(k)) compact_to(sh, k, fl);
+}
+
+// Writes the k valid entries of the buffer as (key, position) candidates,
+// unordered, into ckey / cpos [k], and empty slots (key 0) into [k, kpad).
+__device__ void emit_candidates(TopkShared& sh, const Fill& fl, int k, int kpad,
+                                uint32_t* __restrict__ ckey, uint32_t* __restrict__ cpos) {
+  const int tid = threadIdx.x;
+  if (tid < kpad - k) {
+    ckey[k + tid] = 0u;
+    cpos[k + tid] = 0u;
+  }
+  if (tid == 0) sh.count = 0u;
+  __syncthreads();
+  uint32_t nv = 0;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) nv += slot_valid(fl, tid, j) ? 1u : 0u;
+  uint32_t s = nv ? atomicAdd(&sh.count, nv) : 0u;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j)
+    if (slot_valid(fl, tid, j)) {
+      ckey[s] = sh.key[tid + kThreads * j];
+      cpos[s] = sh.pos[tid + kThreads * j];
+      ++s;
+    }
+}
+
+// One workgroup per row: the whole row streamed once, k positions out.
+__global__ __launch_bounds__(kThreads) void topk_kernel(
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
+    const float* __restrict__ scores, int64_t ld, int64_t row_begin, int64_t row_count, int k,
+    int32_t* __restrict__ indices) {
+  __shared__ TopkShared sh;
+  const int tid = threadIdx.x;
+  // Later rows are longer: hand them out first.
+  const int64_t local = row_count - 1 - static_cast<int64_t>(blockIdx.x);
+  const RowInfo ri = row_info(cu_q, cu_k, batch, row_begin + local);
+  const int32_t n = ri.pos + 1;
+  int32_t* orow = indices + local * k;
+  if (n <= k) {
+    for (int j = tid; j < k; j += kThreads) orow[j] = j < n ? j : -1;
+    return;
+  }
+  Fill fl;
+  select_row(sh, ScoreSource{scores + local * ld, n, 0}, n, k, fl);
   emit_sorted(sh, fl, k, n, orow);
+}
+
+// Long rows, few of them: segment g of a row (positions [g seg, (g+1) seg))
+// keeps its own k best as candidates; a second pass selects among the
+// segments' candidates.  The row's k best are all among them, since each
+// lies in the k best of its own segment.  Each segment's candidate list is
+// kpad = k rounded up to 4 entries long (16-byte aligned lists).
+__global__ __launch_bounds__(kThreads) void topk_segment_kernel(
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
+    const float* __restrict__ scores, int64_t ld, int64_t row_begin, int64_t row_count, int k,
+    int32_t seg, int32_t segs, uint32_t* __restrict__ cand_key, uint32_t* __restrict__ cand_pos) {
+  __shared__ TopkShared sh;
+  const int tid = threadIdx.x;
+  const int64_t local = static_cast<int64_t>(blockIdx.x) / segs;
+  const int g = static_cast<int>(blockIdx.x % segs);
+  const RowInfo ri = row_info(cu_q, cu_k, batch, row_begin + local);
+  const int32_t n_row = ri.pos + 1;
+  const int kpad = (k + 3) & ~3;
+  uint32_t* ckey = cand_key + (local * segs + g) * kpad;
+  uint32_t* cpos = cand_pos + (local * segs + g) * kpad;
+  if (n_row <= k) return;  // the merge pass handles short rows alone
+  const int32_t s0 = g * seg;
+  const int32_t n = max(0, min(seg, n_row - s0));
+  if (n <= k) {
+    for (int j = tid; j < kpad; j += kThreads) {
+      ckey[j] = j < n ? order_key(scores[local * ld + s0 + j]) : 0u;
+      cpos[j] = static_cast<uint32_t>(s0 + j);
+    }
+    return;
+  }
+  Fill fl;
+  select_row(sh, ScoreSource{scores + local * ld + s0, n, s0}, n, k, fl);
+  emit_candidates(sh, fl, k, kpad, ckey, cpos);
+}
+
+__global__ __launch_bounds__(kThreads) void topk_merge_kernel(
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
+    int64_t row_begin, int64_t row_count, int k, int32_t segs,
+    const uint32_t* __restrict__ cand_key, const uint32_t* __restrict__ cand_pos,
+    int32_t* __restrict__ indices) {
+  __shared__ TopkShared sh;
+  const int tid = threadIdx.x;
+  const int64_t local = static_cast<int64_t>(blockIdx.x);
+  const RowInfo ri = row_info(cu_q, cu_k, batch, row_begin + local);
+  const int32_t n_row = ri.pos + 1;
+  int32_t* orow = indices + local * k;
+  if (n_row <= k) {
+    for (int j = tid; j < k; j += kThreads) orow[j] = j < n_row ? j : -1;
+    return;
+  }
+  const int32_t n = segs * ((k + 3) & ~3);
+  Fill fl;
+  select_row(sh, CandidateSource{cand_key + local * n, cand_pos + local * n, n}, n, k, fl);
+  emit_sorted(sh, fl, k, n_row, orow);
 }
 
 }  // namespace
 
+TopkPlan topk_plan(const dsa_varlen& vl, int64_t row_count, int k) {
+  // Split rows only when the rows alone cannot fill the chip (four rows run
+  // per CU) and each segment still holds at least 4 k scores.
+  TopkPlan plan{1, 0};
+  if (row_count <= 0 || row_count >= 512) return plan;
+  const int64_t by_rows = (512 + row_count - 1) / row_count;
+  const int64_t by_len = vl.max_seqlen_k / (4 * static_cast<int64_t>(k));
+  const int64_t segs = by_rows < by_len ? by_rows : by_len;
+  if (segs < 2) return plan;
+  int64_t seg = (vl.max_seqlen_k + segs - 1) / segs;
+  seg = ((seg + kChunk - 1) / kChunk) * kChunk;  // segments start on 16-byte boundaries
+  plan.segs = static_cast<int>((vl.max_seqlen_k + seg - 1) / seg);
+  plan.seg = static_cast<int>(seg);
+  return plan;
+}
+
+size_t topk_workspace_bytes(const TopkPlan& plan, int64_t row_count, int k) {
+  if (plan.segs <= 1) return 0;
+  return static_cast<size_t>(row_count) * plan.segs * ((k + 3) & ~3) * 2 * sizeof(uint32_t);
+}
+
 hipError_t launch_topk(const dsa_varlen& vl, const float* scores, int64_t ld, int64_t row_begin,
-                       int64_t row_count, int k, int32_t* indices, hipStream_t stream) {
+                       int64_t row_count, int k, int32_t* indices, const TopkPlan& plan,
+                       void* workspace, hipStream_t stream) {
   static_assert(kSeg - kWaveStep >= (kMaxK + kWaves - 1) / kWaves, "segments too small");
   static_assert(kBins % kThreads == 0, "bins split evenly over threads");
+  if (plan.segs > 1 && workspace != nullptr) {
+    uint32_t* cand_key = static_cast<uint32_t*>(workspace);
+    uint32_t* cand_pos = cand_key + static_cast<size_t>(row_count) * plan.segs * ((k + 3) & ~3);
+    hipLaunchKernelGGL(topk_segment_kernel, dim3(static_cast<unsigned>(row_count * plan.segs)),
+                       dim3(kThreads), 0, stream, vl.cu_seqlens_q, vl.cu_seqlens_k, vl.batch,
+                       scores, ld, row_begin, row_count, k, plan.seg, plan.segs, cand_key,
+                       cand_pos);
+    hipLaunchKernelGGL(topk_merge_kernel, dim3(static_cast<unsigned>(row_count)), dim3(kThreads),
+                       0, stream, vl.cu_seqlens_q, vl.cu_seqlens_k, vl.batch, row_begin,
+                       row_count, k, plan.segs, cand_key, cand_pos, indices);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(topk_kernel, dim3(static_cast<unsigned>(row_count)), dim3(kThreads), 0,
                      stream, vl.cu_seqlens_q, vl.cu_seqlens_k, vl.batch, scores, ld, row_begin,
                      row_count, k, indices);

@@ -10,7 +10,8 @@ from __future__ import annotations
 from dataclasses import dataclass
 
 from . import (Varlen, dsa_index_scores, dsa_sparse_attn_decode,
-               dsa_sparse_attn_decode_workspace_size, dsa_sparse_attn_prefill, dsa_topk)
+               dsa_sparse_attn_decode_workspace_size, dsa_sparse_attn_prefill, dsa_topk,
+               dsa_topk_workspace_size)
 
 
 def _torch():
@@ -57,9 +58,10 @@ def prefill(vl: Varlen, q_idx, k_idx, w, q, k, v, out, bufs: PrefillBuffers, lse
 
 @dataclass
 class DecodeBuffers:
-    scores: object     # fp32 [batch, ld]
-    indices: object    # int32 [batch, topk]
-    workspace: object  # uint8 [bytes]
+    scores: object          # fp32 [batch, ld]
+    indices: object         # int32 [batch, topk]
+    workspace: object       # uint8 [bytes], decode attention partials
+    topk_workspace: object  # uint8 [bytes] or None, per-segment top-k candidates
 
 
 def alloc_decode(vl: Varlen, n_heads_q: int, head_dim: int, topk: int,
@@ -67,15 +69,18 @@ def alloc_decode(vl: Varlen, n_heads_q: int, head_dim: int, topk: int,
     torch = _torch()
     ld = score_ld(vl.max_seqlen_k)
     ws = dsa_sparse_attn_decode_workspace_size(vl, n_heads_q, head_dim, topk)
+    tws = dsa_topk_workspace_size(vl, vl.batch, topk)
     return DecodeBuffers(torch.empty((vl.batch, ld), dtype=torch.float32, device=device),
                          torch.empty((vl.batch, topk), dtype=torch.int32, device=device),
-                         torch.empty(max(ws, 256), dtype=torch.uint8, device=device))
+                         torch.empty(max(ws, 256), dtype=torch.uint8, device=device),
+                         torch.empty(tws, dtype=torch.uint8, device=device) if tws else None)
 
 
 def decode(vl: Varlen, q_idx, k_idx_cache, w, q, k_cache, v_cache, out, bufs: DecodeBuffers,
            lse=None, softmax_scale=None, stream=None):
     dsa_index_scores(vl, q_idx, k_idx_cache, w, bufs.scores, row_begin=0, row_count=vl.batch,
                      stream=stream)
-    dsa_topk(vl, bufs.scores, bufs.indices, row_begin=0, row_count=vl.batch, stream=stream)
+    dsa_topk(vl, bufs.scores, bufs.indices, row_begin=0, row_count=vl.batch,
+             workspace=bufs.topk_workspace, stream=stream)
     dsa_sparse_attn_decode(vl, q, k_cache, v_cache, bufs.indices, out, bufs.workspace, lse=lse,
                            softmax_scale=softmax_scale, stream=stream)

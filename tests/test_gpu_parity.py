@@ -125,6 +125,48 @@ def test_topk_various_k_varlen(k):
     _topk_case(s, cu_q, cu_k, k, ld)
 
 
+@pytest.mark.parametrize("k,case", [(2048, "normal"), (2048, "integers"), (1000, "normal"),
+                                    (7, "ties")])
+def test_topk_split_path(k, case):
+    """Few long rows (decode-like, one query per sequence) take the split path
+    when given workspace: per-segment candidates, then a merge.  It must match
+    the one-pass path bit for bit and the oracle exactly; rows of ragged
+    lengths (shorter than k, shorter than one segment, not a multiple of the
+    segment, the longest) are mixed."""
+    rng = np.random.default_rng(k + len(case))
+    lk = [131072, 20000, 16385, 9000, 2048, 100, 65539, 50001, 2049, 131071]
+    B = len(lk)
+    ld = 131072
+    s = np.empty((B, ld), np.float32)
+    for b in range(B):
+        if case == "normal":
+            row = rng.standard_normal(ld) * 2
+        elif case == "integers":
+            row = rng.integers(-40, 41, ld)
+        else:  # heavy ties: a handful of values
+            row = rng.integers(0, 3, ld) * 0.5
+        s[b] = row.astype(np.float32)
+    cu_q = list(range(B + 1))
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).tolist()
+    vl = dsa.Varlen(cu_q, cu_k)
+    ws_bytes = dsa.dsa_topk_workspace_size(vl, B, k)
+    assert ws_bytes > 0, "this shape should take the split path"
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    s_dev = to_dev(s)
+    split = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+    single = torch.full((B, k), -9, dtype=torch.int32, device="cuda")
+    log(f"topk split path k={k} {case}")
+    dsa.dsa_topk(vl, s_dev, split, workspace=ws)
+    dsa.dsa_topk(vl, s_dev, single)
+    torch.cuda.synchronize()
+    assert torch.equal(split, single)
+    counts = np.array(lk, np.int64)
+    ref = oracle.topk(s, counts, k)
+    got = split.cpu().numpy()
+    bad = np.nonzero((got != ref).any(axis=1))[0]
+    assert bad.size == 0, f"rows {bad[:5]} differ"
+
+
 def test_topk_row_window():
     """A window of rows inside the packed batch writes only its own rows."""
     rng = np.random.default_rng(9)
