@@ -36,6 +36,126 @@ struct AttnCfg {
   static constexpr int VTILE = 32 * VSTRIDE;
 };
 
+// Rows of one 32-slot tile gathered by one lane: slot 16*sub + col, d range
+// of lane quarter qd, for K (kept as the A operand) and V (staged to LDS).
+template <int D>
+struct GatherTile {
+  bf16x8 k[2][AttnCfg<D>::KS];
+  u32x4 v[2][AttnCfg<D>::KS];
+  bool ok[2];  // slot holds a usable position (inside the list, 0 <= p <= pos)
+};
+
+template <int D>
+__device__ __forceinline__ void gather_tile(GatherTile<D>& t, const int32_t* idx, int s0,
+                                            int n_slots, const RowInfo& ri,
+                                            const uint16_t* __restrict__ k,
+                                            const uint16_t* __restrict__ v, int n_heads_kv, int g,
+                                            int col, int qd) {
+  using C = AttnCfg<D>;
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    const int slot = s0 + 16 * sub + col;
+    const int32_t p = slot < n_slots ? idx[slot] : -1;
+    t.ok[sub] = p >= 0 && p <= ri.pos;
+    const int64_t krow = ri.key_base + (t.ok[sub] ? p : 0);
+    const int64_t off = (krow * n_heads_kv + g) * D + qd * 8;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      t.k[sub][ks] = load_bf16x8(k + off + ks * 32);
+      t.v[sub][ks] = *reinterpret_cast<const u32x4*>(v + off + ks * 32);
+    }
+  }
+}
+
+// Online-softmax update of one tile.  m_run / l_run / acc are this lane's
+// running state (head col; O rows = heads 4 qd + r).
+template <int D>
+__device__ __forceinline__ void attend_tile(const GatherTile<D>& t, const bf16x8 (&qb)[AttnCfg<D>::KS],
+                                            uint16_t* vs, float scale_log2, int col, int qd,
+                                            float& m_run, float& l_run,
+                                            f32x4 (&acc)[AttnCfg<D>::DT]) {
+  using C = AttnCfg<D>;
+  // V rows to this wave's LDS tile (read back below in the B-operand order).
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      uint16_t* dst = vs + (16 * sub + col) * C::VSTRIDE + ks * 32 + qd * 8;
+      reinterpret_cast<uint2*>(dst)[0] = make_uint2(t.v[sub][ks].x, t.v[sub][ks].y);
+      reinterpret_cast<uint2*>(dst)[1] = make_uint2(t.v[sub][ks].z, t.v[sub][ks].w);
+    }
+  // Bit j of vm[sub] says whether slot 16*sub + j holds a usable position.
+  const unsigned long long vm0 = __ballot(t.ok[0]) & 0xFFFFull;
+  const unsigned long long vm1 = __ballot(t.ok[1]) & 0xFFFFull;
+
+  // S^T tiles: rows = slots 16*sub + 4*qd + r, column = head col.
+  f32x4 st[2];
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    st[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      st[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[sub][ks], qb[ks], st[sub], 0, 0, 0);
+  }
+  float z[2][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    const unsigned long long vm = sub ? vm1 : vm0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool ok = (vm >> (4 * qd + r)) & 1ull;
+      z[sub][r] = ok ? st[sub][r] * scale_log2 : -INFINITY;
+      mx = fmaxf(mx, z[sub][r]);
+    }
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(m_run, mx);
+  const float corr = m_new == -INFINITY ? 1.0f : exp2f(m_run - m_new);
+  float pr[2][4];
+  float psum = 0.0f;
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pr[sub][r] = z[sub][r] == -INFINITY ? 0.0f : exp2f(z[sub][r] - m_new);
+      psum += pr[sub][r];
+    }
+  l_run = l_run * corr + psum;
+  m_run = m_new;
+
+  // P as the A operand: row = head col, contraction index 8*qd + i maps to
+  // slot 4*qd + i (i < 4) and 16 + 4*qd + i - 4 (i >= 4).
+  uint4 pa_u;
+  pa_u.x = pack_bf16x2(pr[0][0], pr[0][1]);
+  pa_u.y = pack_bf16x2(pr[0][2], pr[0][3]);
+  pa_u.z = pack_bf16x2(pr[1][0], pr[1][1]);
+  pa_u.w = pack_bf16x2(pr[1][2], pr[1][3]);
+  const bf16x8 pa = __builtin_bit_cast(bf16x8, pa_u);
+
+  // Rescale O rows (heads 4*qd + r) by their head's correction.
+  float cr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * qd + r);
+  // The V tile is private to this wave and LDS operations of one wave are
+  // performed in order, so the reads below see the writes above.
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[dt][r] *= cr[r];
+    const uint16_t* src = vs + dt * 16 + col;
+    uint4 vb_u;
+    const int r0 = 4 * qd, r1 = 16 + 4 * qd;
+    vb_u.x = src[(r0 + 0) * C::VSTRIDE] | (static_cast<uint32_t>(src[(r0 + 1) * C::VSTRIDE]) << 16);
+    vb_u.y = src[(r0 + 2) * C::VSTRIDE] | (static_cast<uint32_t>(src[(r0 + 3) * C::VSTRIDE]) << 16);
+    vb_u.z = src[(r1 + 0) * C::VSTRIDE] | (static_cast<uint32_t>(src[(r1 + 1) * C::VSTRIDE]) << 16);
+    vb_u.w = src[(r1 + 2) * C::VSTRIDE] | (static_cast<uint32_t>(src[(r1 + 3) * C::VSTRIDE]) << 16);
+    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, vb_u),
+                                                      acc[dt], 0, 0, 0);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(512) void sparse_attn_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
@@ -57,15 +177,19 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(
   const RowInfo ri = row_info(cu_q, cu_k, batch, row);
   const int per_split = (topk + splits - 1) / splits;
   const int i0 = split * per_split;
-  const int i1 = min(topk, i0 + per_split);
+  const int n_slots = max(0, min(topk, i0 + per_split) - i0);
   uint16_t* vs = vs_all + g * C::VTILE;
+  // This slice of the row's index list, shared by all KV heads, in LDS.
+  int32_t* idx = reinterpret_cast<int32_t*>(vs_all + n_heads_kv * C::VTILE);
+  const int32_t* irow = indices + local * topk + i0;
+  for (int s = threadIdx.x; s < n_slots; s += blockDim.x) idx[s] = irow[s];
 
   // Q^T as the B operand: column = query head of this group, contraction d
   // ordered so that lane quarter qd covers d in [qd*QD, qd*QD + QD).
   bf16x8 qb[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks)
-    qb[ks] = col < G ? load_bf16x8(q + ((row * n_heads_q) + g * G + col) * D + qd * C::QD + ks * 8)
+    qb[ks] = col < G ? load_bf16x8(q + ((row * n_heads_q) + g * G + col) * D + ks * 32 + qd * 8)
                      : zero_bf16x8();
 
   f32x4 acc[C::DT];
@@ -73,99 +197,18 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(
   for (int dt = 0; dt < C::DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY;  // running max (log2 domain) of head `col`
   float l_run = 0.0f;       // this lane's share of the running denominator
+  __syncthreads();          // index list in LDS
 
-  const int32_t* irow = indices + local * topk;
-  for (int s0 = i0; s0 < i1; s0 += 32) {
-    // Gather: lane (col, qd) loads slot s0 + 16*sub + col, d range of quarter qd.
-    bool valid[2];
-    bf16x8 ka[2][C::KS];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int slot = s0 + 16 * sub + col;
-      const int32_t p = slot < i1 ? irow[slot] : -1;
-      valid[sub] = p >= 0 && p <= ri.pos;
-      const int64_t krow = ri.key_base + (valid[sub] ? p : 0);
-      const int64_t off = (krow * n_heads_kv + g) * D + qd * C::QD;
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) ka[sub][ks] = load_bf16x8(k + off + ks * 8);
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const uint4 vv = *reinterpret_cast<const uint4*>(v + off + ks * 8);
-        uint16_t* dst = vs + (16 * sub + col) * C::VSTRIDE + qd * C::QD + ks * 8;
-        reinterpret_cast<uint2*>(dst)[0] = make_uint2(vv.x, vv.y);
-        reinterpret_cast<uint2*>(dst)[1] = make_uint2(vv.z, vv.w);
-      }
-    }
-    // Bit j of vm[sub] says whether slot 16*sub + j holds a usable position.
-    const unsigned long long vm0 = __ballot(valid[0]) & 0xFFFFull;
-    const unsigned long long vm1 = __ballot(valid[1]) & 0xFFFFull;
-
-    // S^T tiles: rows = slots 16*sub + 4*qd + r, column = head col.
-    f32x4 st[2];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      st[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
-        st[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[sub][ks], qb[ks], st[sub], 0, 0, 0);
-    }
-    float z[2][4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const unsigned long long vm = sub ? vm1 : vm0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool ok = (vm >> (4 * qd + r)) & 1ull;
-        z[sub][r] = ok ? st[sub][r] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, z[sub][r]);
-      }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float corr = m_new == -INFINITY ? 1.0f : exp2f(m_run - m_new);
-    float pr[2][4];
-    float psum = 0.0f;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pr[sub][r] = z[sub][r] == -INFINITY ? 0.0f : exp2f(z[sub][r] - m_new);
-        psum += pr[sub][r];
-      }
-    l_run = l_run * corr + psum;
-    m_run = m_new;
-
-    // P as the A operand: row = head col, contraction index 8*qd + i maps to
-    // slot 4*qd + i (i < 4) and 16 + 4*qd + i - 4 (i >= 4).
-    uint4 pa_u;
-    pa_u.x = pack_bf16x2(pr[0][0], pr[0][1]);
-    pa_u.y = pack_bf16x2(pr[0][2], pr[0][3]);
-    pa_u.z = pack_bf16x2(pr[1][0], pr[1][1]);
-    pa_u.w = pack_bf16x2(pr[1][2], pr[1][3]);
-    const bf16x8 pa = __builtin_bit_cast(bf16x8, pa_u);
-
-    // Rescale O rows (heads 4*qd + r) by their head's correction.
-    float cr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * qd + r);
-    __syncthreads();  // V tile visible to the whole wave
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[dt][r] *= cr[r];
-      const uint16_t* src = vs + dt * 16 + col;
-      uint4 vb_u;
-      const int r0 = 4 * qd, r1 = 16 + 4 * qd;
-      vb_u.x = src[(r0 + 0) * C::VSTRIDE] | (static_cast<uint32_t>(src[(r0 + 1) * C::VSTRIDE]) << 16);
-      vb_u.y = src[(r0 + 2) * C::VSTRIDE] | (static_cast<uint32_t>(src[(r0 + 3) * C::VSTRIDE]) << 16);
-      vb_u.z = src[(r1 + 0) * C::VSTRIDE] | (static_cast<uint32_t>(src[(r1 + 1) * C::VSTRIDE]) << 16);
-      vb_u.w = src[(r1 + 2) * C::VSTRIDE] | (static_cast<uint32_t>(src[(r1 + 3) * C::VSTRIDE]) << 16);
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, vb_u),
-                                                        acc[dt], 0, 0, 0);
-    }
-    __syncthreads();  // all reads of the V tile done before it is overwritten
+  // Two tiles in flight: the next tile's rows are gathered while this one
+  // is multiplied (the loop is unrolled by two so each tile keeps its
+  // registers).  Tiles past the list gather valid rows and contribute zero.
+  GatherTile<D> ta, tb;
+  gather_tile<D>(ta, idx, 0, n_slots, ri, k, v, n_heads_kv, g, col, qd);
+  for (int s0 = 0; s0 < n_slots; s0 += 64) {
+    gather_tile<D>(tb, idx, s0 + 32, n_slots, ri, k, v, n_heads_kv, g, col, qd);
+    attend_tile<D>(ta, qb, vs, scale_log2, col, qd, m_run, l_run, acc);
+    gather_tile<D>(ta, idx, s0 + 64, n_slots, ri, k, v, n_heads_kv, g, col, qd);
+    attend_tile<D>(tb, qb, vs, scale_log2, col, qd, m_run, l_run, acc);
   }
 
   // Full denominator of head `col`: sum the four lane quarters.
@@ -263,12 +306,14 @@ hipError_t launch_sparse_attn(const dsa_varlen& vl, const uint16_t* q, const uin
   dim3 grid(static_cast<unsigned>(row_count), static_cast<unsigned>(splits));
   dim3 block(kWave * n_heads_kv);
   if (head_dim == 128) {
-    const size_t lds = n_heads_kv * AttnCfg<128>::VTILE * sizeof(uint16_t);
+    const size_t lds = n_heads_kv * AttnCfg<128>::VTILE * sizeof(uint16_t) +
+                       static_cast<size_t>((topk + splits - 1) / splits) * sizeof(int32_t);
     hipLaunchKernelGGL(sparse_attn_kernel<128>, grid, block, lds, stream, vl.cu_seqlens_q,
                        vl.cu_seqlens_k, vl.batch, q, k, v, indices, topk, row_begin, row_count,
                        n_heads_q, n_heads_kv, scale_log2, out, lse, splits, partial);
   } else {
-    const size_t lds = n_heads_kv * AttnCfg<64>::VTILE * sizeof(uint16_t);
+    const size_t lds = n_heads_kv * AttnCfg<64>::VTILE * sizeof(uint16_t) +
+                       static_cast<size_t>((topk + splits - 1) / splits) * sizeof(int32_t);
     hipLaunchKernelGGL(sparse_attn_kernel<64>, grid, block, lds, stream, vl.cu_seqlens_q,
                        vl.cu_seqlens_k, vl.batch, q, k, v, indices, topk, row_begin, row_count,
                        n_heads_q, n_heads_kv, scale_log2, out, lse, splits, partial);
