@@ -103,13 +103,7 @@ int dsa_index_scores(const dsa_varlen* vl, const void* q_idx, const void* k_idx,
                      int32_t n_heads_idx, int32_t d_idx, int64_t row_begin, int64_t row_count,
                      float* scores, int64_t ld_scores, hipStream_t stream);
 
-/*
- * Workspace bytes for dsa_topk's split path at this call shape, or 0.  Few
- * long rows (fewer than 512 rows, each at least 8 k positions long) are cut
- * into segments whose own k best are kept as candidates in the workspace,
- * then one pass per row selects among them; that fills the GPU where one
- * workgroup per row cannot.  The result is the same either way.
- */
+/* Workspace bytes dsa_topk needs for this call shape (0: it needs none). */
 int dsa_topk_workspace_size(const dsa_varlen* vl, int64_t row_count, int32_t k, size_t* bytes);
 
 /*
@@ -127,11 +121,8 @@ int dsa_topk_workspace_size(const dsa_varlen* vl, int64_t row_count, int32_t k, 
  * Supported: 1 <= k <= 2048.
  * Invalid: null pointers, scores not 16-byte aligned, ld_scores <
  * max_seqlen_k or not a multiple of 4, a window outside [0, total_q).
- * workspace: NULL selects the one-pass path (one workgroup per row, no
- * workspace).  Otherwise, when dsa_topk_workspace_size reports B > 0 bytes,
- * it must be a 16-byte aligned device buffer of at least B bytes
- * (DSA_ERR_WORKSPACE if not), owned by the caller and not used by anything
- * else until the call's work has run on `stream`.
+ * workspace may be NULL when dsa_topk_workspace_size reports 0 (it always
+ * does today; the argument keeps room for call shapes that will need one).
  */
 int dsa_topk(const dsa_varlen* vl, const float* scores, int64_t ld_scores, int64_t row_begin,
              int64_t row_count, int32_t k, int32_t* indices, void* workspace,

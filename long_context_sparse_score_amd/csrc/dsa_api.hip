@@ -129,13 +129,15 @@ int dsa_topk_workspace_size(const dsa_varlen* vl, int64_t row_count, int32_t k, 
   if (bytes == nullptr) return fail(DSA_ERR_INVALID_ARGUMENT, "bytes pointer is NULL");
   if (row_count < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "row_count < 0");
   if (k < 1 || k > 2048) return fail(DSA_ERR_UNSUPPORTED, "k %d not in 1..2048", k);
-  *bytes = dsa::topk_workspace_bytes(dsa::topk_plan(*vl, row_count, k), row_count, k);
+  *bytes = 0;
   return ok();
 }
 
 int dsa_topk(const dsa_varlen* vl, const float* scores, int64_t ld_scores, int64_t row_begin,
              int64_t row_count, int32_t k, int32_t* indices, void* workspace,
              size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
   int st;
   if ((st = check_varlen(vl))) return st;
   if ((st = check_window(vl, row_begin, row_count))) return st;
@@ -144,16 +146,7 @@ int dsa_topk(const dsa_varlen* vl, const float* scores, int64_t ld_scores, int64
     return fail(DSA_ERR_INVALID_ARGUMENT, "indices is NULL or misaligned");
   if (k < 1 || k > 2048) return fail(DSA_ERR_UNSUPPORTED, "k %d not in 1..2048", k);
   if (row_count == 0) return ok();
-  const dsa::TopkPlan plan = dsa::topk_plan(*vl, row_count, k);
-  const size_t need = dsa::topk_workspace_bytes(plan, row_count, k);
-  if (workspace != nullptr && need > 0) {
-    if (workspace_bytes < need)
-      return fail(DSA_ERR_WORKSPACE, "topk workspace %zu bytes < %zu required", workspace_bytes, need);
-    if (!aligned(workspace, 16))
-      return fail(DSA_ERR_WORKSPACE, "topk workspace not 16-byte aligned");
-  }
-  return hip_status(dsa::launch_topk(*vl, scores, ld_scores, row_begin, row_count, k, indices, plan,
-                                     need > 0 ? workspace : nullptr, stream),
+  return hip_status(dsa::launch_topk(*vl, scores, ld_scores, row_begin, row_count, k, indices, stream),
                     "topk launch");
 }
 

@@ -13,19 +13,9 @@ hipError_t launch_index_scores(const dsa_varlen& vl, const uint16_t* q_idx, cons
                                const float* w, int n_heads, int d, int64_t row_begin,
                                int64_t row_count, float* scores, int64_t ld, hipStream_t stream);
 
-// Top-k launch shape: rows split into `segs` segments of `seg` positions
-// (segs == 1: one workgroup per row, no workspace).
-struct TopkPlan {
-  int segs;
-  int seg;
-};
-TopkPlan topk_plan(const dsa_varlen& vl, int64_t row_count, int k);
-size_t topk_workspace_bytes(const TopkPlan& plan, int64_t row_count, int k);
-// With plan.segs > 1, workspace (topk_workspace_bytes, 4-byte aligned) holds
-// the per-segment candidates; a NULL workspace selects the one-pass kernel.
+// Per-row top-k; rows of the window in [row_begin, row_begin + row_count).
 hipError_t launch_topk(const dsa_varlen& vl, const float* scores, int64_t ld, int64_t row_begin,
-                       int64_t row_count, int k, int32_t* indices, const TopkPlan& plan,
-                       void* workspace, hipStream_t stream);
+                       int64_t row_count, int k, int32_t* indices, hipStream_t stream);
 
 // Attention over selected positions.  splits > 1 writes per-split partial
 // results to `partial` and merges them in a second kernel (decode).

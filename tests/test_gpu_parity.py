@@ -127,12 +127,12 @@ def test_topk_various_k_varlen(k):
 
 @pytest.mark.parametrize("k,case", [(2048, "normal"), (2048, "integers"), (1000, "normal"),
                                     (7, "ties")])
-def test_topk_split_path(k, case):
-    """Few long rows (decode-like, one query per sequence) take the split path
-    when given workspace: per-segment candidates, then a merge.  It must match
-    the one-pass path bit for bit and the oracle exactly; rows of ragged
-    lengths (shorter than k, shorter than one segment, not a multiple of the
-    segment, the longest) are mixed."""
+def test_topk_few_long_rows_both_configurations(k, case):
+    """Few long rows (decode-like, one query per sequence) run the wide
+    configuration (four 16-byte loads per thread and step, 8192 candidates);
+    the same rows inside a batch of more than 512 rows run the narrow one.
+    Both must equal the oracle exactly; row lengths are ragged (shorter than
+    k, one step, not a multiple of a step, the longest)."""
     rng = np.random.default_rng(k + len(case))
     lk = [131072, 20000, 16385, 9000, 2048, 100, 65539, 50001, 2049, 131071]
     B = len(lk)
@@ -146,25 +146,26 @@ def test_topk_split_path(k, case):
         else:  # heavy ties: a handful of values
             row = rng.integers(0, 3, ld) * 0.5
         s[b] = row.astype(np.float32)
-    cu_q = list(range(B + 1))
-    cu_k = np.concatenate([[0], np.cumsum(lk)]).tolist()
-    vl = dsa.Varlen(cu_q, cu_k)
-    ws_bytes = dsa.dsa_topk_workspace_size(vl, B, k)
-    assert ws_bytes > 0, "this shape should take the split path"
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-    s_dev = to_dev(s)
-    split = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
-    single = torch.full((B, k), -9, dtype=torch.int32, device="cuda")
-    log(f"topk split path k={k} {case}")
-    dsa.dsa_topk(vl, s_dev, split, workspace=ws)
-    dsa.dsa_topk(vl, s_dev, single)
+    ref = oracle.topk(s, np.array(lk, np.int64), k)
+    # wide: the ten rows alone
+    vl = dsa.Varlen(list(range(B + 1)), np.concatenate([[0], np.cumsum(lk)]).tolist())
+    wide = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+    log(f"topk few long rows k={k} {case}")
+    dsa.dsa_topk(vl, to_dev(s), wide)
+    # narrow: 600 one-position rows first, then the same ten rows
+    pad = 600
+    lk2 = [1] * pad + lk
+    vl2 = dsa.Varlen(list(range(B + pad + 1)), np.concatenate([[0], np.cumsum(lk2)]).tolist())
+    s2 = torch.zeros((B + pad, ld), dtype=torch.float32, device="cuda")
+    s2[pad:] = to_dev(s)
+    narrow = torch.full((B + pad, k), -9, dtype=torch.int32, device="cuda")
+    dsa.dsa_topk(vl2, s2, narrow)
     torch.cuda.synchronize()
-    assert torch.equal(split, single)
-    counts = np.array(lk, np.int64)
-    ref = oracle.topk(s, counts, k)
-    got = split.cpu().numpy()
+    got = wide.cpu().numpy()
     bad = np.nonzero((got != ref).any(axis=1))[0]
-    assert bad.size == 0, f"rows {bad[:5]} differ"
+    assert bad.size == 0, f"wide configuration: rows {bad[:5]} differ"
+    assert torch.equal(narrow[pad:], wide)
+    assert (narrow[:pad, 0] == 0).all() and (narrow[:pad, 1:] == -1).all()
 
 
 def test_topk_row_window():
