@@ -59,12 +59,24 @@ struct Fill {
   }
 };
 
-// Monotone map float -> uint32 (larger float, larger key); -0 maps like +0.
-__device__ __forceinline__ uint32_t order_key(float x) {
-  uint32_t u = __float_as_uint(x);
+// Monotone map float bits -> uint32 (larger float, larger key); -0 maps
+// like +0.
+__device__ __forceinline__ uint32_t order_key_bits(uint32_t u) {
   if ((u << 1) == 0u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+
+// "order_key_bits(u) > thr" with one integer compare, valid when thr >= 2^31
+// (the threshold is +0 or a positive float): then only positive scores can
+// pass, and for them the key is u + 2^31.
+__device__ __forceinline__ bool above_nonneg_threshold(uint32_t u, uint32_t thr) {
+  return static_cast<int32_t>(u) > static_cast<int32_t>(thr ^ 0x80000000u);
+}
+
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
 
 __device__ __forceinline__ uint32_t wave_min(uint32_t v) {
 #pragma unroll
@@ -84,7 +96,8 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 // the prefetch ring; the caller masks elements >= n.  unpack() turns them
 // into (order key, position) pairs.
 
-// Scores of one row: element j is position pos0 + j.
+// Scores of one row: element j is position pos0 + j.  unpack() leaves the
+// raw float bits; the order key is formed only for survivors.
 struct ScoreSource {
   const float* row;  // score of element 0
   int32_t n;
@@ -93,8 +106,9 @@ struct ScoreSource {
   __device__ Raw fetch(int32_t j) const {
     return *reinterpret_cast<const float4*>(row + min(j, (n - 1) & ~3));
   }
-  __device__ void unpack(const Raw& r, int32_t j, uint32_t (&kv)[4], uint32_t (&pv)[4]) const {
-    kv[0] = order_key(r.x); kv[1] = order_key(r.y); kv[2] = order_key(r.z); kv[3] = order_key(r.w);
+  __device__ void unpack(const Raw& r, int32_t j, uint32_t (&bits)[4], uint32_t (&pv)[4]) const {
+    bits[0] = __float_as_uint(r.x); bits[1] = __float_as_uint(r.y);
+    bits[2] = __float_as_uint(r.z); bits[3] = __float_as_uint(r.w);
 #pragma unroll
     for (int e = 0; e < 4; ++e) pv[e] = static_cast<uint32_t>(pos0 + j + e);
   }
@@ -394,6 +408,8 @@ struct TopkImpl {
       const int32_t at = (static_cast<int32_t>((static_cast<int64_t>(tid) * n) / kThreads)) & ~3;
       uint32_t sk[4], sp[4];
       src.unpack(src.fetch(at), at, sk, sp);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sk[e] = order_key_bits(sk[e]);
       const int64_t want = (static_cast<int64_t>(5 * k) * kSamples + 2 * static_cast<int64_t>(n) - 1) /
                            (2 * static_cast<int64_t>(n));
       const uint32_t m = static_cast<uint32_t>(want < 1 ? 1 : (want > kSamples ? kSamples : want));
@@ -428,22 +444,33 @@ struct TopkImpl {
         buf[v] = src.fetch(j + 2 * kChunk);
       }
       // Append this wave's survivors to its own segment: slots by ballot
-      // prefix counts, no shared counter.
+      // prefix counts, no shared counter.  Above a non-negative threshold one
+      // integer compare of the raw bits decides; the order key is formed only
+      // for survivors.
+      auto append = [&](auto fast) {
   #pragma unroll
-      for (int v = 0; v < kVec; ++v) {
-        const int32_t j = base + v * 4 * kThreads + 4 * tid;
+        for (int v = 0; v < kVec; ++v) {
+          const int32_t j = base + v * 4 * kThreads + 4 * tid;
   #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool acc = (j + e < n) && kvs[v][e] > thr;
-          const unsigned long long mk = __ballot(acc);
-          if (acc) {
-            const uint32_t s = mine + __popcll(mk & below);
-            seg_key[s] = kvs[v][e];
-            seg_pos[s] = pvs[v][e];
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t u = kvs[v][e];
+            const bool pass = decltype(fast)::value ? above_nonneg_threshold(u, thr)
+                                                    : order_key_bits(u) > thr;
+            const bool acc = (j + e < n) && pass;
+            const unsigned long long mk = __ballot(acc);
+            if (acc) {
+              const uint32_t s = mine + __popcll(mk & below);
+              seg_key[s] = order_key_bits(u);
+              seg_pos[s] = pvs[v][e];
+            }
+            mine += __popcll(mk);
           }
-          mine += __popcll(mk);
         }
-      }
+      };
+      if (thr >= 0x80000000u)
+        append(BoolTag<true>{});
+      else
+        append(BoolTag<false>{});
       // Publish the fill level under this step's parity; the slots of the other
       // parity are only rewritten after the next barrier, when every wave has
       // read them.
