@@ -434,7 +434,6 @@ struct TopkImpl {
     // step keeps its registers (rotating loaded values between registers would
     // make the compiler wait for the loads as soon as they are copied), and it
     // runs whole pairs of steps (steps past n admit nothing).
-    const unsigned long long below = (1ull << lane) - 1ull;
     auto step = [&](typename Src::Raw (&buf)[kVec], int32_t base) {
       uint32_t kvs[kVec][4], pvs[kVec][4];
   #pragma unroll
@@ -447,30 +446,42 @@ struct TopkImpl {
       // prefix counts, no shared counter.  Above a non-negative threshold one
       // integer compare of the raw bits decides; the order key is formed only
       // for survivors.
-      auto append = [&](auto fast) {
+      // Per element group (one element per lane) only a compare and a ballot
+      // unless the group holds survivors; a survivor's slot is the lane's
+      // rank among them (mbcnt).  Only the last step of a row needs the
+      // bound check.
+      auto append = [&](auto fast, auto tail) {
   #pragma unroll
         for (int v = 0; v < kVec; ++v) {
           const int32_t j = base + v * 4 * kThreads + 4 * tid;
   #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const uint32_t u = kvs[v][e];
-            const bool pass = decltype(fast)::value ? above_nonneg_threshold(u, thr)
-                                                    : order_key_bits(u) > thr;
-            const bool acc = (j + e < n) && pass;
+            bool acc = decltype(fast)::value ? above_nonneg_threshold(u, thr)
+                                             : order_key_bits(u) > thr;
+            if (decltype(tail)::value) acc = acc && (j + e < n);
             const unsigned long long mk = __ballot(acc);
-            if (acc) {
-              const uint32_t s = mine + __popcll(mk & below);
-              seg_key[s] = order_key_bits(u);
-              seg_pos[s] = pvs[v][e];
+            if (mk != 0ull) {
+              if (acc) {
+                const uint32_t s = mine + __builtin_amdgcn_mbcnt_hi(
+                    static_cast<uint32_t>(mk >> 32),
+                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mk), 0u));
+                seg_key[s] = order_key_bits(u);
+                seg_pos[s] = pvs[v][e];
+              }
+              mine += __popcll(mk);
             }
-            mine += __popcll(mk);
           }
         }
       };
-      if (thr >= 0x80000000u)
-        append(BoolTag<true>{});
-      else
-        append(BoolTag<false>{});
+      const bool tail = base + kChunk > n;
+      if (thr >= 0x80000000u) {
+        if (tail) append(BoolTag<true>{}, BoolTag<true>{});
+        else append(BoolTag<true>{}, BoolTag<false>{});
+      } else {
+        if (tail) append(BoolTag<false>{}, BoolTag<true>{});
+        else append(BoolTag<false>{}, BoolTag<false>{});
+      }
       // Publish the fill level under this step's parity; the slots of the other
       // parity are only rewritten after the next barrier, when every wave has
       // read them.
