@@ -6,56 +6,65 @@
 // 1 keeps the k = 2048 best positions per query token; section 8 needs the
 // selection to be deterministic so training and inference agree).
 //
-// One workgroup of 256 threads owns one row and reads it from HBM exactly
-// once, in position order, two steps in flight.  Many rows use steps of
-// 1024 scores and ~37 KB of LDS, so four rows run per CU and hide each
-// other's latencies; few long rows (decode) use steps of 4096 scores and a
-// candidate buffer twice as large, so one row alone keeps 32 KB in flight.
-// Barriers span only four waves.
+// One workgroup owns one row and reads it from HBM once, in position order,
+// with three steps of loads in flight.  Two configurations: windows of many
+// rows use 256 threads, steps of 1024 scores and ~37 KB of LDS, so several
+// rows share a CU and hide each other's latencies; few long rows (decode)
+// use 512 threads, steps of 4096 scores and a candidate buffer twice as
+// large, so one row alone keeps 48 KB in flight.
 //
-// A score survives only if its order-preserving key beats the running
-// threshold; survivors are appended to a candidate buffer in LDS (each wave
-// to its own segment, slots assigned by ballot prefix counts).  Long
-// rows start from a threshold read off a 1024-score sample of the row (256
-// spread 16-byte pieces) at the rank where about 2.5 k scores of the whole
-// row are expected above it, so the buffer is cut once or twice per row
-// instead of a dozen times.  The estimate only decides speed: if fewer than
-// k scores beat it, the row is streamed again from threshold zero, so the
-// result is exact for any input.  When
-// the buffer could overflow on the next step it is cut to exactly k entries
-// by a radix select whose digits are taken relative to the range of the
-// candidates' keys (min..max, 1024 bins): the bins spread over the values
-// actually present, so atomics rarely collide and each level shrinks the
-// range 1024-fold.  Ties at the k-th key are cut by a second select on the
-// position.  The new threshold is the k-th key: later scores equal to it sit
-// at higher positions and can never displace the kept ties, so the test
-// stays a strict "greater than".  At the end the kept positions are marked
-// in an LDS bitmask and written in ascending order by a prefix count over
-// its words (a bitonic sort serves rows too long for the bitmask).  Every
-// decision depends only on key and position values, never on the order in
-// which lanes appended, so the output is bitwise repeatable.
+// A score survives only if it beats the running threshold, which for finite
+// scores is one float compare against the smallest float whose
+// order-preserving key is above it.  Survivors (raw bits and position) are
+// appended to a candidate buffer in LDS: each wave to its own segment, slots
+// by ballot and mbcnt, lanes without a survivor writing to a dump slot, so
+// the append has no divergent branch and an element group without survivors
+// costs one compare and one scalar test.  Long rows start from a threshold
+// read off a spread sample of the row, at the rank where a set multiple of k
+// scores of the whole row are expected above it, so the buffer is rarely
+// cut before the end.  The estimate only decides speed: if fewer than k
+// scores beat it, the row is streamed again from threshold zero, so the
+// result is exact for any input.  When the buffer could overflow on the
+// next step it is cut to exactly k entries by a radix select whose digits
+// are taken relative to the range of the candidates' keys (min..max): the
+// bins spread over the values actually present, so atomics rarely collide
+// and each level shrinks the range by the bin count.  Ties at the k-th key
+// are cut by a second select on the position.  The new threshold is the
+// k-th key: the stream resumes right after the step that called for the
+// cut, so later scores equal to it sit at higher positions and can never
+// displace the kept ties, and the test stays a strict "greater than".  At
+// the end the kept positions are marked in an LDS bitmask and written in
+// ascending order by a prefix count over its words (a bitonic sort serves
+// rows too long for the bitmask).  Every decision depends only on key and
+// position values, never on the order in which lanes appended, so the
+// output is bitwise repeatable.
 #include "dsa_common.h"
 #include "dsa_internal.h"
 
 namespace dsa {
 
 namespace {
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kSamples = 4 * kThreads;  // scores sampled for the start threshold
-constexpr int kBins = 1024;
-constexpr int kBinsPerThread = kBins / kThreads;
 constexpr int kMaxK = 2048;
 constexpr int kSampleMinRow = 8192;     // shorter rows start from threshold zero
 
-// Fill levels of the four segments, held in registers (uniform).
+// Fill levels of the per-wave segments, held in registers (uniform).
+template <int W>
 struct Fill {
-  uint32_t f[kWaves];
+  uint32_t f[W];
   __device__ uint32_t total() const {
     uint32_t t = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) t += f[w];
+    for (int w = 0; w < W; ++w) t += f[w];
     return t;
+  }
+  // The fill of wave `wave`'s own segment (a select chain: no dynamic
+  // register indexing).
+  __device__ uint32_t of(int wave) const {
+    uint32_t o = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w)
+      if (w == wave) o = f[w];
+    return o;
   }
 };
 
@@ -66,11 +75,15 @@ __device__ __forceinline__ uint32_t order_key_bits(uint32_t u) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// "order_key_bits(u) > thr" with one integer compare, valid when thr >= 2^31
-// (the threshold is +0 or a positive float): then only positive scores can
-// pass, and for them the key is u + 2^31.
-__device__ __forceinline__ bool above_nonneg_threshold(uint32_t u, uint32_t thr) {
-  return static_cast<int32_t>(u) > static_cast<int32_t>(thr ^ 0x80000000u);
+// For finite x, "order_key_bits(x) > thr" is the float test x >= lim with
+// lim = the float whose order key is thr + 1: the key map is monotone, and -0
+// and +0 share a key as they compare equal.  Keys below that of -inf belong
+// to NaN bit patterns; a threshold there admits every finite score (lim =
+// -inf), and thr = 2^32 - 1 admits nothing (lim is a NaN).
+__device__ __forceinline__ float admit_limit(uint32_t thr) {
+  const uint32_t k1 = thr + 1u;
+  if (k1 != 0u && k1 <= 0x007FFFFFu) return -__builtin_inff();
+  return __uint_as_float((k1 & 0x80000000u) ? (k1 ^ 0x80000000u) : ~k1);
 }
 
 template <bool B>
@@ -114,48 +127,74 @@ struct ScoreSource {
   }
 };
 
-// One configuration of the row select: VEC 16-byte loads per thread and step
-// (a step covers 4 VEC 256 scores), a candidate buffer of CAP entries in LDS.
-// Many rows: VEC = 1, CAP = 4096 (37 KB of LDS, four rows per CU hide each
-// other's latencies).  Few long rows: VEC = 4, CAP = 8192 (69 KB), so that
-// one row keeps 32 KB of scores in flight.
-template <int VEC, int CAP>
+// One configuration of the row select: THREADS threads, VEC 16-byte loads
+// per thread and step (a step covers 4 VEC THREADS scores), a candidate
+// buffer of CAP entries in LDS, radix digits of log2(BINS) bits, and a
+// start threshold read off 4 SVEC THREADS sampled scores that TARGET2 k / 2
+// scores of a row are expected to pass.
+template <int VEC, int CAP, int THREADS, int BINS, int TARGET2, int SVEC>
 struct TopkImpl {
+  static constexpr int kThreads = THREADS;
+  static constexpr int kWaves = kThreads / kWave;
+  static constexpr int kSampleVec = SVEC;             // sampled 16-byte pieces per thread
+  static constexpr int kSamples = 4 * kSampleVec * kThreads;  // scores sampled for the start threshold
+  static constexpr int kBins = BINS;
+  static constexpr int kDigitBits = __builtin_ctz(BINS);
+  static constexpr int kBinsPerThread = kBins / kThreads;
   static constexpr int kVec = VEC;
   static constexpr int kChunk = 4 * kVec * kThreads;  // scores per step
   static constexpr int kWaveStep = 4 * kVec * kWave;  // most entries one wave appends per step
+  static constexpr int kDepth = 4;                    // step buffers: kDepth - 1 steps in flight
+  static_assert(kDepth == 4, "the stream loop names four step buffers");
   static constexpr int kCap = CAP;                    // candidate buffer entries
   static constexpr int kSeg = kCap / kWaves;          // one buffer segment per wave
-  static constexpr int kPerThread = kCap / kThreads;
-  static constexpr int kSegPerThread = kPerThread / kWaves;  // a thread's entries in one segment
+  static constexpr int kPerThread = kSeg / kWave;     // a lane's entries of its wave's segment
   static constexpr int kMaskBits = kCap * 32;         // longest row emitted through the bitmask
-  static_assert(kSeg == kThreads * kSegPerThread, "entry j of a thread lies in segment j / kSegPerThread");
+  static_assert((kBins & (kBins - 1)) == 0 && kBins % kThreads == 0,
+                "bins: a power of two, split evenly over threads");
+  static_assert(kSeg % kWave == 0, "segments split evenly over lanes");
   static_assert(kSeg - kWaveStep >= (kMaxK + kWaves - 1) / kWaves, "segments too small");
+  static_assert(kPerThread >= 4 * kSampleVec, "a thread's sample fits its select entries");
+  using FillT = Fill<kWaves>;
 
   struct Shared {
-    uint32_t key[kCap];  // reused as the position bitmask when emitting
-    uint32_t pos[kCap];
-    uint32_t hist[kBins];
-    uint32_t red[2 * kWaves];
+    // Candidates: raw score bits and position, segment w at [w kSeg, (w+1) kSeg).
+    // The kWave entries past kCap take the writes of lanes without a
+    // candidate, so an append needs no divergent branch.  key is reused as
+    // the position bitmask when emitting.
+    uint32_t key[kCap + kWave];
+    uint32_t pos[kCap + kWave];
+    uint32_t hist[kBins];      // radix histogram
+    uint32_t red[2 * kWaves];  // per-wave partials: key ranges, kept counts, prefix sums
+    uint32_t sel[5];           // one select level's outcome: lo, hi, above, remaining, equal
     uint32_t fill[2][kWaves];  // per-wave segment fill, double-buffered by step parity
     uint32_t count;
-    uint32_t lo, hi, above, remaining, equal;
   };
 
-  // Entry j of thread t is buffer slot t + 256 j, i.e. segment j / kSegPerThread
-  // at offset t + 256 (j % kSegPerThread).
-  static __device__ __forceinline__ bool slot_valid(const Fill& fl, int tid, int j) {
-    return static_cast<uint32_t>(tid + kThreads * (j % kSegPerThread)) < fl.f[j / kSegPerThread];
+  // A wave's lanes hold the entries of its own segment: entry j of lane l of
+  // wave w is buffer slot w kSeg + l + 64 j, valid below the segment's fill.
+  static __device__ __forceinline__ int slot(int tid, int j) {
+    return (tid / kWave) * kSeg + (tid & (kWave - 1)) + kWave * j;
+  }
+  static __device__ __forceinline__ bool slot_valid(uint32_t own_fill, int tid, int j) {
+    return static_cast<uint32_t>((tid & (kWave - 1)) + kWave * j) < own_fill;
   }
 
   // m-th largest value of keyf(j) over this thread's entries j = 0..kPerThread-1
-  // (slot tid + 256 j) for which pred(j) holds, across the workgroup (needs
+  // (slot(tid, j)) for which pred(j) holds, across the workgroup (needs
   // 1 <= m <= number of such entries).  Returns tau, the count of entries
   // strictly above it and the count equal to it.  Block-wide: every thread
   // calls it with the same m.
+  //
+  // Radix select with digits relative to the keys' range: each level counts
+  // the entries of the current range [lo, hi] into kBins bins of equal
+  // width; a workgroup-wide suffix count over the bins (thread t owns
+  // kBinsPerThread consecutive bins) finds the bin holding the m-th largest,
+  // whose range is the next level's.
   template <class KeyF, class Pred>
-  static __device__ __attribute__((always_inline)) void select_kth(Shared& sh, uint32_t m, KeyF keyf, Pred pred, uint32_t& tau,
-                             uint32_t& above, uint32_t& equal) {
+  static __device__ __attribute__((always_inline)) void select_kth(Shared& sh, uint32_t m, KeyF keyf,
+                                                           Pred pred, uint32_t& tau, uint32_t& above,
+                                                           uint32_t& equal) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
@@ -192,12 +231,12 @@ struct TopkImpl {
       // Histogram of (key - lo) >> shift over [lo, hi]; a single value is one bin.
       const uint32_t span = hi - lo;
       const int bits = span == 0u ? 0 : 32 - __builtin_clz(span);  // span < 2^bits
-      const int shift = bits > 10 ? bits - 10 : 0;                  // digit < 1024
+      const int shift = bits > kDigitBits ? bits - kDigitBits : 0;  // digit < kBins
   #pragma unroll
       for (int j = 0; j < kPerThread; ++j)
         if (in[j] && kv[j] >= lo && kv[j] <= hi) atomicAdd(&sh.hist[(kv[j] - lo) >> shift], 1u);
       __syncthreads();
-      // Suffix counts: thread t owns bins [t*4, t*4 + 4).
+      // Suffix counts: thread t owns bins [t kBinsPerThread, (t+1) kBinsPerThread).
       uint32_t hb[kBinsPerThread];
       uint32_t local = 0;
   #pragma unroll
@@ -225,18 +264,18 @@ struct TopkImpl {
         }
         const uint32_t nlo = lo + (static_cast<uint32_t>(digit) << shift);
         const uint32_t width_m1 = shift == 0 ? 0u : ((1u << shift) - 1u);
-        sh.lo = nlo;
-        sh.hi = (hi - nlo <= width_m1) ? hi : nlo + width_m1;  // no wrap-around
-        sh.above = gt + run;
-        sh.remaining = remaining - run;
-        sh.equal = hb[digit - tid * kBinsPerThread];
+        sh.sel[0] = nlo;
+        sh.sel[1] = (hi - nlo <= width_m1) ? hi : nlo + width_m1;  // no wrap-around
+        sh.sel[2] = gt + run;
+        sh.sel[3] = remaining - run;
+        sh.sel[4] = hb[digit - tid * kBinsPerThread];
       }
       __syncthreads();
-      lo = sh.lo;
-      hi = sh.hi;
-      gt = sh.above;
-      remaining = sh.remaining;
-      equal = sh.equal;
+      lo = sh.sel[0];
+      hi = sh.sel[1];
+      gt = sh.sel[2];
+      remaining = sh.sel[3];
+      equal = sh.sel[4];
       // Every thread has read the level's results and its bins: clear them.
       for (int b = tid; b < kBins; b += kThreads) sh.hist[b] = 0u;
       __syncthreads();
@@ -247,60 +286,68 @@ struct TopkImpl {
   }
 
   // Keep the valid entries with key > tau, or key == tau and position <=
-  // pos_cut, and lay them out round-robin over the four segments (kept/4 each).
-  // Updates the fill levels.  Block-wide.
-  static __device__ __attribute__((always_inline)) void regroup(Shared& sh, Fill& fl, uint32_t tau,
+  // pos_cut, and lay them out round-robin over the segments (kept/kWaves
+  // each).  Slots follow (wave, entry, lane) order, so the layout is
+  // deterministic.  Updates the fill levels.  Block-wide.
+  static __device__ __attribute__((always_inline)) void regroup(Shared& sh, FillT& fl, uint32_t tau,
                                                         uint32_t pos_cut) {
     const int tid = threadIdx.x;
-    uint32_t kk[kPerThread], pp[kPerThread];
-    uint32_t nk = 0;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const uint32_t own = fl.of(wave);
+    uint32_t kk[kPerThread], pp[kPerThread], at[kPerThread];
+    bool keep[kPerThread];
+    uint32_t nw = 0;  // kept entries of this wave (uniform)
   #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
-      kk[j] = 0u;
-      pp[j] = 0u;
-      if (slot_valid(fl, tid, j)) {
-        const uint32_t kv = sh.key[tid + kThreads * j], pv = sh.pos[tid + kThreads * j];
-        if (kv > tau || (kv == tau && pv <= pos_cut)) {
-          kk[j] = kv;
-          pp[j] = pv | 0x80000000u;  // mark as kept (positions < 2^31)
-          ++nk;
-        }
-      }
+      kk[j] = sh.key[slot(tid, j)];
+      pp[j] = sh.pos[slot(tid, j)];
+      const uint32_t kv = order_key_bits(kk[j]);
+      keep[j] = slot_valid(own, tid, j) && (kv > tau || (kv == tau && pp[j] <= pos_cut));
+      const unsigned long long mk = __builtin_amdgcn_ballot_w64(keep[j]);
+      at[j] = nw + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mk >> 32),
+                                             __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mk), 0u));
+      nw += static_cast<uint32_t>(__popcll(mk));
     }
-    if (tid == 0) sh.count = 0u;
-    __syncthreads();
-    uint32_t s = nk ? atomicAdd(&sh.count, nk) : 0u;
+    if (lane == 0) sh.red[wave] = nw;
+    __syncthreads();  // every entry is read and every wave's count published
+    uint32_t base = 0, kept = 0;
+  #pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const uint32_t c = sh.red[w];
+      base += w < wave ? c : 0u;
+      kept += c;
+    }
   #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
-      if (pp[j] & 0x80000000u) {
-        const int e = (s & (kWaves - 1)) * kSeg + (s >> 2);  // round-robin over segments
+      if (keep[j]) {
+        const uint32_t s2 = base + at[j];
+        const uint32_t e = (s2 % kWaves) * kSeg + s2 / kWaves;  // round-robin over segments
         sh.key[e] = kk[j];
-        sh.pos[e] = pp[j] & 0x7FFFFFFFu;
-        ++s;
+        sh.pos[e] = pp[j];
       }
     }
-    __syncthreads();
-    const uint32_t kept = sh.count;
   #pragma unroll
     for (int w = 0; w < kWaves; ++w) fl.f[w] = (kept + kWaves - 1 - w) / kWaves;
-    __syncthreads();  // everyone has read sh.count before it is reused
+    __syncthreads();  // the new layout is complete before anyone reads it
   }
 
   // Keep exactly the m best valid entries (key desc, position asc), needs more
   // than m valid entries.  Returns the m-th key, the new acceptance threshold.
-  static __device__ __attribute__((always_inline)) uint32_t compact_to(Shared& sh, uint32_t m, Fill& fl) {
+  static __device__ __attribute__((always_inline)) uint32_t compact_to(Shared& sh, uint32_t m, FillT& fl) {
     const int tid = threadIdx.x;
+    const uint32_t own = fl.of(tid / kWave);
     uint32_t tau, above, equal;
     select_kth(
-        sh, m, [&](int j) { return sh.key[tid + kThreads * j]; },
-        [&](int j) { return slot_valid(fl, tid, j); }, tau, above, equal);
+        sh, m, [&](int j) { return order_key_bits(sh.key[slot(tid, j)]); },
+        [&](int j) { return slot_valid(own, tid, j); }, tau, above, equal);
     const uint32_t need = m - above;
     uint32_t pos_cut = 0xFFFFFFFFu;
     if (equal > need) {
       uint32_t t2, a2, e2;
       select_kth(
-          sh, need, [&](int j) { return ~sh.pos[tid + kThreads * j]; },
-          [&](int j) { return slot_valid(fl, tid, j) && sh.key[tid + kThreads * j] == tau; }, t2,
+          sh, need, [&](int j) { return ~sh.pos[slot(tid, j)]; },
+          [&](int j) { return slot_valid(own, tid, j) && order_key_bits(sh.key[slot(tid, j)]) == tau; }, t2,
           a2, e2);
       pos_cut = ~t2;
     }
@@ -309,15 +356,16 @@ struct TopkImpl {
   }
 
   // Write the kept positions (valid entries, k of them) in ascending order.
-  static __device__ __attribute__((always_inline)) void emit_sorted(Shared& sh, const Fill& fl, int k, int32_t n,
+  static __device__ __attribute__((always_inline)) void emit_sorted(Shared& sh, const FillT& fl, int k, int32_t n,
                               int32_t* __restrict__ orow) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
+    const uint32_t own = fl.of(wave);
     uint32_t pv[kPerThread];
   #pragma unroll
     for (int j = 0; j < kPerThread; ++j)
-      pv[j] = slot_valid(fl, tid, j) ? sh.pos[tid + kThreads * j] : 0xFFFFFFFFu;
+      pv[j] = slot_valid(own, tid, j) ? sh.pos[slot(tid, j)] : 0xFFFFFFFFu;
     __syncthreads();  // the key array becomes the bitmask / the pos array is rewritten
     if (n <= kMaskBits) {
       // Bitmask over positions 0..n-1 in the (now free) key array.
@@ -369,7 +417,7 @@ struct TopkImpl {
     int k2 = 1;
     while (k2 < k) k2 <<= 1;
     __syncthreads();
-    for (int e = k + tid; e < k2; e += kThreads) sh.pos[e] = 0xFFFFFFFFu;
+    for (int e = static_cast<int>(sh.count) + tid; e < k2; e += kThreads) sh.pos[e] = 0xFFFFFFFFu;
     __syncthreads();
     for (int size = 2; size <= k2; size <<= 1) {
       for (int stride = size >> 1; stride > 0; stride >>= 1) {
@@ -395,92 +443,102 @@ struct TopkImpl {
   // Block-wide.
   template <class Src>
   static __device__ __attribute__((always_inline)) void select_row(Shared& sh, const Src& src, int32_t n,
-                                                           int k, Fill& fl) {
+                                                           int k, FillT& fl) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    for (int b = tid; b < kBins; b += kThreads) sh.hist[b] = 0u;
     uint32_t thr0 = 0u;  // accept key > thr; 0 admits every finite score
     if (n > kSampleMinRow) {
-      // Start threshold: the m-th largest of a spread sample (thread t reads 4
-      // elements at t/256 of the stream), m chosen so that about 2.5 k
-      // elements of the stream are expected above it.
-      const int32_t at = (static_cast<int32_t>((static_cast<int64_t>(tid) * n) / kThreads)) & ~3;
-      uint32_t sk[4], sp[4];
-      src.unpack(src.fetch(at), at, sk, sp);
+      // Start threshold: the m-th largest of a spread sample (piece i of
+      // thread t: 4 elements at (t kSampleVec + i) / (kThreads kSampleVec) of
+      // the stream), m chosen so that about TARGET2 k / 2 elements of the
+      // stream are expected above it.
+      uint32_t sk[4 * kSampleVec];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sk[e] = order_key_bits(sk[e]);
-      const int64_t want = (static_cast<int64_t>(5 * k) * kSamples + 2 * static_cast<int64_t>(n) - 1) /
-                           (2 * static_cast<int64_t>(n));
+      for (int i = 0; i < kSampleVec; ++i) {
+        const int32_t at = static_cast<int32_t>(
+                               (static_cast<int64_t>(tid * kSampleVec + i) * n) / (kThreads * kSampleVec)) &
+                           ~3;
+        uint32_t b4[4], p4[4];
+        src.unpack(src.fetch(at), at, b4, p4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sk[4 * i + e] = order_key_bits(b4[e]);
+      }
+      const int64_t want =
+          (static_cast<int64_t>(TARGET2 * k) * kSamples + 2 * static_cast<int64_t>(n) - 1) /
+          (2 * static_cast<int64_t>(n));
       const uint32_t m = static_cast<uint32_t>(want < 1 ? 1 : (want > kSamples ? kSamples : want));
       uint32_t tau, above, equal;
       select_kth(
-          sh, m, [&](int j) { return sk[j & 3]; }, [](int j) { return j < 4; }, tau, above, equal);
+          sh, m, [&](int j) { return sk[j % (4 * kSampleVec)]; },
+          [](int j) { return j < 4 * kSampleVec; }, tau, above, equal);
       // Keys equal to tau are not admitted; lower it by one so they are.
       thr0 = tau > 0u ? tau - 1u : 0u;
     }
     uint32_t thr = thr0;
-    uint32_t mine;  // this wave's segment fill (uniform within the wave)
-    uint32_t* seg_key = sh.key + wave * kSeg;
-    uint32_t* seg_pos = sh.pos + wave * kSeg;
-    int parity;
-  restart:
-  #pragma unroll
+    uint32_t mine = 0u;  // this wave's segment fill (uniform within the wave)
+    int parity = 0;
+#pragma unroll
     for (int w = 0; w < kWaves; ++w) fl.f[w] = 0u;
-    mine = 0u;
-    parity = 0;
-    // Each step covers kChunk elements: kVec 16-byte loads per thread, issued
-    // together.  Two steps are in flight; the loop is unrolled by two so each
-    // step keeps its registers (rotating loaded values between registers would
-    // make the compiler wait for the loads as soon as they are copied), and it
-    // runs whole pairs of steps (steps past n admit nothing).
-    auto step = [&](typename Src::Raw (&buf)[kVec], int32_t base) {
-      uint32_t kvs[kVec][4], pvs[kVec][4];
+    float lim = admit_limit(thr);
+    int32_t next = 0;  // first element of the next stretch
+    bool cut = false;
+    const uint32_t seg0 = static_cast<uint32_t>(wave * kSeg);
+    const uint32_t dump = static_cast<uint32_t>(kCap + lane);
+    // One step covers kChunk elements from `base`: kVec 16-byte loads per
+    // thread, held in buf.  Once they are tested, buf is refilled with the
+    // step kDepth ahead (after the test, so old and new values never share
+    // the registers' lifetime and the loop needs no copies).  When a step
+    // leaves a segment nearly full and elements remain, `cut` is set and
+    // `next` names the first element not yet tested; later steps of the same
+    // group then admit nothing.  BOUNDED steps also test the position
+    // against n (only the last steps of a row need it).
+    auto step = [&](auto bounded, typename Src::Raw (&buf)[kVec], int32_t base, bool refill) {
+      // All compares first (one ballot each, straight from the compare),
+      // then the appends: an element group (one element per lane) without
+      // survivors costs one scalar test; otherwise each lane writes its
+      // (raw bits, position) either to the wave's next free slot (rank among
+      // the survivors by mbcnt) or, without a survivor, to its own dump
+      // slot -- no divergent branch.  After a cut the limit is a NaN and
+      // nothing passes.
+      const float lim_s = cut ? __builtin_nanf("") : lim;
+      uint32_t bits[kVec][4], pv[kVec][4];
+      bool ok[kVec][4];
+      unsigned long long mk[kVec][4];
+      unsigned long long any = 0ull;
   #pragma unroll
       for (int v = 0; v < kVec; ++v) {
         const int32_t j = base + v * 4 * kThreads + 4 * tid;
-        src.unpack(buf[v], j, kvs[v], pvs[v]);
-        buf[v] = src.fetch(j + 2 * kChunk);
+        src.unpack(buf[v], j, bits[v], pv[v]);
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ok[v][e] = __uint_as_float(bits[v][e]) >= lim_s;
+          if (decltype(bounded)::value) ok[v][e] = ok[v][e] && j + e < n;
+          mk[v][e] = __builtin_amdgcn_ballot_w64(ok[v][e]);
+          any |= mk[v][e];
+        }
       }
-      // Append this wave's survivors to its own segment: slots by ballot
-      // prefix counts, no shared counter.  Above a non-negative threshold one
-      // integer compare of the raw bits decides; the order key is formed only
-      // for survivors.
-      // Per element group (one element per lane) only a compare and a ballot
-      // unless the group holds survivors; a survivor's slot is the lane's
-      // rank among them (mbcnt).  Only the last step of a row needs the
-      // bound check.
-      auto append = [&](auto fast, auto tail) {
+      if (any != 0ull) {
   #pragma unroll
         for (int v = 0; v < kVec; ++v) {
-          const int32_t j = base + v * 4 * kThreads + 4 * tid;
   #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t u = kvs[v][e];
-            bool acc = decltype(fast)::value ? above_nonneg_threshold(u, thr)
-                                             : order_key_bits(u) > thr;
-            if (decltype(tail)::value) acc = acc && (j + e < n);
-            const unsigned long long mk = __ballot(acc);
-            if (mk != 0ull) {
-              if (acc) {
-                const uint32_t s = mine + __builtin_amdgcn_mbcnt_hi(
-                    static_cast<uint32_t>(mk >> 32),
-                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mk), 0u));
-                seg_key[s] = order_key_bits(u);
-                seg_pos[s] = pvs[v][e];
-              }
-              mine += __popcll(mk);
+            if (mk[v][e] != 0ull) {
+              const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
+                  static_cast<uint32_t>(mk[v][e] >> 32),
+                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mk[v][e]), mine));
+              const uint32_t at = ok[v][e] ? seg0 + rank : dump;
+              sh.key[at] = bits[v][e];
+              sh.pos[at] = pv[v][e];
+              mine += static_cast<uint32_t>(__popcll(mk[v][e]));
             }
           }
         }
-      };
-      const bool tail = base + kChunk > n;
-      if (thr >= 0x80000000u) {
-        if (tail) append(BoolTag<true>{}, BoolTag<true>{});
-        else append(BoolTag<true>{}, BoolTag<false>{});
-      } else {
-        if (tail) append(BoolTag<false>{}, BoolTag<true>{});
-        else append(BoolTag<false>{}, BoolTag<false>{});
+      }
+      if (refill) {
+  #pragma unroll
+        for (int v = 0; v < kVec; ++v)
+          buf[v] = src.fetch(base + kDepth * kChunk + v * 4 * kThreads + 4 * tid);
       }
       // Publish the fill level under this step's parity; the slots of the other
       // parity are only rewritten after the next barrier, when every wave has
@@ -493,35 +551,78 @@ struct TopkImpl {
       bool full = false;
   #pragma unroll
       for (int w = 0; w < kWaves; ++w) full |= fl.f[w] > static_cast<uint32_t>(kSeg - kWaveStep);
-      if (full && base + kChunk < n) {
+      const bool now = !cut && full && base + kChunk < n;
+      next = now ? base + kChunk : next;
+      cut = cut || now;
+    };
+    // The stream runs in stretches: a stretch ends at the row's end or after
+    // the group of steps in which a cut was called for.  The loop holds
+    // nothing but the stream (kDepth named buffers, kDepth - 1 steps in
+    // flight while one is tested) and leaves only at its latch: an exit
+    // from the middle of the group would share the latch in the compiled
+    // control flow with loads still pending, and the loop's first wait
+    // would become a full drain.  The loads in flight when a stretch ends
+    // are dropped, and the next stretch issues them again.
+    while (true) {
+      // The loads are issued in buffer order, as the loop refills them
+      // (scheduling barriers keep that order): the wait before the loop's
+      // first test then lets the later steps stay in flight.
+      typename Src::Raw b0[kVec], b1[kVec], b2[kVec], b3[kVec];
+      const int32_t j0 = next + 4 * tid;
+  #pragma unroll
+      for (int v = 0; v < kVec; ++v) b0[v] = src.fetch(j0 + v * 4 * kThreads);
+      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+      for (int v = 0; v < kVec; ++v) b1[v] = src.fetch(j0 + kChunk + v * 4 * kThreads);
+      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+      for (int v = 0; v < kVec; ++v) b2[v] = src.fetch(j0 + 2 * kChunk + v * 4 * kThreads);
+      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+      for (int v = 0; v < kVec; ++v) b3[v] = src.fetch(j0 + 3 * kChunk + v * 4 * kThreads);
+      __builtin_amdgcn_sched_barrier(0);
+      cut = false;
+      // Whole groups of kDepth full steps, then the rest of the row (fewer
+      // than kDepth steps, the last one possibly partial) with bound checks.
+      int32_t base = next;
+      for (; base + kDepth * kChunk <= n && !cut; base += kDepth * kChunk) {
+        step(BoolTag<false>{}, b0, base, true);
+        step(BoolTag<false>{}, b1, base + kChunk, true);
+        step(BoolTag<false>{}, b2, base + 2 * kChunk, true);
+        step(BoolTag<false>{}, b3, base + 3 * kChunk, true);
+      }
+      if (!cut && base < n) {
+        step(BoolTag<true>{}, b0, base, false);
+        if (base + kChunk < n) step(BoolTag<true>{}, b1, base + kChunk, false);
+        if (base + 2 * kChunk < n) step(BoolTag<true>{}, b2, base + 2 * kChunk, false);
+        if (base + 3 * kChunk < n) step(BoolTag<true>{}, b3, base + 3 * kChunk, false);
+      }
+      if (cut) {
         // One segment is nearly full.  With more than k entries held, cut to
         // the k best and raise the threshold; otherwise (survivors crowd one
         // wave's segment) keep them all and spread them evenly.
-        if (fl.total() > static_cast<uint32_t>(k))
+        if (fl.total() > static_cast<uint32_t>(k)) {
           thr = compact_to(sh, k, fl);
-        else
+          lim = admit_limit(thr);
+        } else {
           regroup(sh, fl, 0u, 0xFFFFFFFFu);
-  #pragma unroll
-        for (int w = 0; w < kWaves; ++w)
-          if (w == wave) mine = fl.f[w];  // no dynamic register indexing
+        }
+        mine = fl.of(wave);
+        continue;
       }
-    };
-    typename Src::Raw buf_a[kVec], buf_b[kVec];
-  #pragma unroll
-    for (int v = 0; v < kVec; ++v) {
-      buf_a[v] = src.fetch(v * 4 * kThreads + 4 * tid);
-      buf_b[v] = src.fetch(kChunk + v * 4 * kThreads + 4 * tid);
-    }
-    for (int32_t base = 0; base < n; base += 2 * kChunk) {
-      step(buf_a, base);
-      step(buf_b, base + kChunk);
-    }
-    if (fl.total() < static_cast<uint32_t>(k)) {
+      // Done when k elements are held, or when the threshold was already zero
+      // (every finite score passes it, so only non-finite input can leave
+      // fewer; the row then gets fewer positions, padded, and never loops).
+      if (fl.total() >= static_cast<uint32_t>(k) || thr == 0u) break;
       // The sampled threshold was too high (fewer than k elements beat it and
       // no cut happened): stream again from zero.
       thr = 0u;
+      lim = admit_limit(thr);
+      next = 0;
+      mine = 0u;
+  #pragma unroll
+      for (int w = 0; w < kWaves; ++w) fl.f[w] = 0u;
       __syncthreads();
-      goto restart;
     }
     if (fl.total() > static_cast<uint32_t>(k)) compact_to(sh, k, fl);
   }
@@ -530,7 +631,7 @@ struct TopkImpl {
 
 // One workgroup per row: the whole row streamed once, k positions out.
 template <class Impl>
-__global__ __launch_bounds__(kThreads) void topk_kernel(
+__global__ __launch_bounds__(Impl::kThreads) void topk_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
     const float* __restrict__ scores, int64_t ld, int64_t row_begin, int64_t row_count, int k,
     int32_t* __restrict__ indices) {
@@ -542,30 +643,39 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
   const int32_t n = ri.pos + 1;
   int32_t* orow = indices + local * k;
   if (n <= k) {
-    for (int j = tid; j < k; j += kThreads) orow[j] = j < n ? j : -1;
+    for (int j = tid; j < k; j += Impl::kThreads) orow[j] = j < n ? j : -1;
     return;
   }
-  Fill fl;
+  typename Impl::FillT fl;
   Impl::select_row(sh, ScoreSource{scores + local * ld, n, 0}, n, k, fl);
   Impl::emit_sorted(sh, fl, k, n, orow);
+  // Fewer than k held only for non-finite input: pad like a short row.
+  for (int j = static_cast<int>(fl.total()) + tid; j < k; j += Impl::kThreads) orow[j] = -1;
+}
+
+template <class Impl>
+hipError_t launch_rows(const dsa_varlen& vl, const float* scores, int64_t ld, int64_t row_begin,
+                       int64_t row_count, int k, int32_t* indices, hipStream_t stream) {
+  hipLaunchKernelGGL((topk_kernel<Impl>), dim3(static_cast<unsigned>(row_count)),
+                     dim3(Impl::kThreads), 0, stream, vl.cu_seqlens_q, vl.cu_seqlens_k, vl.batch,
+                     scores, ld, row_begin, row_count, k, indices);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_topk(const dsa_varlen& vl, const float* scores, int64_t ld, int64_t row_begin,
                        int64_t row_count, int k, int32_t* indices, hipStream_t stream) {
-  static_assert(kBins % kThreads == 0, "bins split evenly over threads");
   // With fewer rows than two per CU, rows cannot hide each other's
-  // latencies: give each row the wide configuration.
+  // latencies: give each row the wide configuration, with a denser sample
+  // (4096 scores) so that a start threshold aimed at 1.5 k survivors
+  // almost never leaves fewer than k (a restart doubles that row's time,
+  // and the launch waits for its slowest row).
   if (row_count < 512)
-    hipLaunchKernelGGL((topk_kernel<TopkImpl<4, 8192>>), dim3(static_cast<unsigned>(row_count)),
-                       dim3(kThreads), 0, stream, vl.cu_seqlens_q, vl.cu_seqlens_k, vl.batch, scores,
-                       ld, row_begin, row_count, k, indices);
-  else
-    hipLaunchKernelGGL((topk_kernel<TopkImpl<1, 4096>>), dim3(static_cast<unsigned>(row_count)),
-                       dim3(kThreads), 0, stream, vl.cu_seqlens_q, vl.cu_seqlens_k, vl.batch, scores,
-                       ld, row_begin, row_count, k, indices);
-  return hipGetLastError();
+    return launch_rows<TopkImpl<2, 8192, 512, 1024, 3, 2>>(vl, scores, ld, row_begin, row_count,
+                                                           k, indices, stream);
+  return launch_rows<TopkImpl<1, 4096, 256, 1024, 5, 1>>(vl, scores, ld, row_begin, row_count, k,
+                                                         indices, stream);
 }
 
 }  // namespace dsa

@@ -168,6 +168,46 @@ def test_topk_few_long_rows_both_configurations(k, case):
     assert (narrow[:pad, 0] == 0).all() and (narrow[:pad, 1:] == -1).all()
 
 
+def _sampled_positions(n, pieces):
+    """Positions read by the start-threshold sample of a row of n scores when
+    the sample takes `pieces` 16-byte pieces spread over the row (piece i at
+    floor(i n / pieces), rounded down to a multiple of 4)."""
+    at = (np.arange(pieces, dtype=np.int64) * n // pieces) & ~3
+    return np.unique((at[:, None] + np.arange(4)[None, :]).ravel())
+
+
+@pytest.mark.parametrize("pieces", [1024, 256])
+def test_topk_sample_threshold_too_high_restarts(pieces):
+    """Rows whose largest scores sit exactly where the start-threshold sample
+    reads (1024 pieces: the few-rows configuration, 512 threads x 2; 256: the
+    many-rows one): the sampled threshold then admits far fewer than k scores
+    and the row has to be streamed again from threshold zero.  The result
+    must still equal the oracle exactly.  (Should the sampling rule change,
+    the test still checks exactness; only this path may go unexercised.)"""
+    rng = np.random.default_rng(100 + pieces)
+    k = 2048
+    lk = [131072, 65536, 40000, 20000]
+    ld = 131072
+    s = (rng.standard_normal((len(lk), ld)) * 0.1).astype(np.float32)
+    for b, n in enumerate(lk):
+        hot = _sampled_positions(n, pieces)
+        s[b, hot] = 100.0 + rng.permutation(len(hot)).astype(np.float32)
+    log(f"topk restart rows, {pieces} sample pieces")
+    if pieces == 1024:
+        cu_q = list(range(len(lk) + 1))
+        cu_k = np.concatenate([[0], np.cumsum(lk)]).tolist()
+        _topk_case(s, cu_q, cu_k, k, ld)
+    else:
+        # the many-rows configuration: 600 one-position rows before them
+        pad = 600
+        lk2 = [1] * pad + lk
+        s2 = np.zeros((pad + len(lk), ld), np.float32)
+        s2[pad:] = s
+        cu_q = list(range(len(lk2) + 1))
+        cu_k = np.concatenate([[0], np.cumsum(lk2)]).tolist()
+        _topk_case(s2, cu_q, cu_k, k, ld)
+
+
 def test_topk_row_window():
     """A window of rows inside the packed batch writes only its own rows."""
     rng = np.random.default_rng(9)
