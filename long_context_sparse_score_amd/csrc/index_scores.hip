@@ -87,7 +87,7 @@ __device__ __forceinline__ void tile_mfma(const RowState<D, MT>& st, const bf16x
   }
 }
 
-// Sum over heads of w * relu(acc); lanes 0..31 end up with the score of key
+// Sum over heads of w * relu(acc); every lane ends up with the score of key
 // (lane & 31).
 template <int D, int MT>
 __device__ __forceinline__ float tile_epilogue(const RowState<D, MT>& st,
@@ -102,7 +102,12 @@ __device__ __forceinline__ float tile_epilogue(const RowState<D, MT>& st,
     }
   }
   const float s = s0 + s1;
-  return s + __shfl_xor(s, 32);
+  // Add the other half-wave's partial sum.  v_permlane32_swap exchanges the
+  // halves in the VALU; a shuffle would go through the LDS pipeline, whose
+  // in-order counter would make this wait for the B-fragment reads just
+  // issued for the next tile.
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
 // One wave, one row, keys [c0, c1) read straight from global memory.  Two
@@ -213,14 +218,19 @@ __global__ __launch_bounds__(kBlockRows * kWave, 2) void index_scores_block(
   // Stage fill by buffer->LDS DMA: DMA instruction i of a wave writes 64
   // consecutive 16-byte LDS chunks; LDS chunk (key, s) receives global chunk
   // s ^ (key & (CHUNKS - 1)), so the B-fragment reads below are conflict free.
+  // Instruction i covers keys KPI i + (key of instruction 0); the XOR term
+  // repeats with period CHUNKS in the key and KPI is a multiple of it, so all
+  // instructions share one per-lane offset and differ by a scalar one.
+  constexpr int KPI = kBlockRows * kWave / CHUNKS;  // keys per DMA instruction of the workgroup
+  static_assert(KPI % CHUNKS == 0, "the swizzle must repeat across DMA instructions");
+  const int key0 = (wave * kWave + lane) / CHUNKS, s0 = lane % CHUNKS;
+  const int dma_off = key0 * D * 2 + (s0 ^ (key0 & (CHUNKS - 1))) * 16;
   auto fill_stage = [&](int b, int32_t t) {
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i) {
-      const int e = (i * kBlockRows + wave) * kWave + lane;
-      const int key = e / CHUNKS, s = e % CHUNKS;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           keys, (__attribute__((address_space(3))) void*)(&tile[b][(i * kBlockRows + wave) * kWave * 8]),
-          16, key * D * 2 + (s ^ (key & (CHUNKS - 1))) * 16, t * D * 2, 0, 0);
+          16, dma_off, (t + i * KPI) * D * 2, 0, 0);
     }
   };
   // One score per lane of the lower half-wave (the upper half holds copies).
@@ -248,6 +258,8 @@ __global__ __launch_bounds__(kBlockRows * kWave, 2) void index_scores_block(
       const int slot = (half * KS + ks) ^ (col & (CHUNKS - 1));
       b[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&tb[col * D + slot * 8]));
     }
+    // The first tile's fragments stay out of the interleaving pattern below.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int tj = 0; tj < TILES; ++tj) {
       f32x16 (&acc)[MT] = (tj & 1) ? acc_odd : acc_even;
@@ -265,6 +277,18 @@ __global__ __launch_bounds__(kBlockRows * kWave, 2) void index_scores_block(
       }
       store(tile_epilogue<D, MT>(st, prev), prev_pos);
       prev_pos = t0 + tj * 32 + col;
+      // Interleave this tile's MFMAs with the previous tile's epilogue (4 VALU
+      // after each MFMA) and refill each B fragment right after the MFMA pair
+      // that frees it, a full tile before its next use.  Left alone, the
+      // scheduler clusters the MFMAs and sinks the refills next to their
+      // use; with two waves per SIMD nothing then covers either gap.
+#pragma unroll
+      for (int i = 0; i < KS * MT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        if (tj + 1 < TILES && i % MT == MT - 1)
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
+      }
     }
     // Wait for the next stage's DMA only: the TILES score stores issued after
     // it may stay in flight.
