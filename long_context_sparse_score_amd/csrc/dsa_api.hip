@@ -1,5 +1,6 @@
 // dsa_api.hip -- the C ABI of libdsa.so: host-side validation and launches.
 // Behaviour of every entry point is specified in include/dsa.h.
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -78,6 +79,15 @@ int check_attn_shape(int32_t hq, int32_t hkv, int32_t d, int32_t topk, float sca
   if (hq / hkv > 16) return fail(DSA_ERR_UNSUPPORTED, "group size %d > 16", hq / hkv);
   if (topk < 1 || topk > 4096) return fail(DSA_ERR_UNSUPPORTED, "topk %d not in 1..4096", topk);
   if (!std::isfinite(scale)) return fail(DSA_ERR_INVALID_ARGUMENT, "softmax_scale is not finite");
+  return DSA_OK;
+}
+
+// The attention kernels address one sequence's K or V rows with 32-bit
+// byte offsets.
+int check_attn_extent(const dsa_varlen* vl, int32_t hkv, int32_t d) {
+  if (static_cast<int64_t>(vl->max_seqlen_k) * hkv * d * 2 > INT32_MAX)
+    return fail(DSA_ERR_UNSUPPORTED, "one sequence's K or V rows exceed 2 GiB (max_seqlen_k %d)",
+                vl->max_seqlen_k);
   return DSA_OK;
 }
 
@@ -166,6 +176,7 @@ int dsa_sparse_attn_prefill(const dsa_varlen* vl, const void* q, const void* k, 
     return fail(DSA_ERR_INVALID_ARGUMENT, "indices is NULL or misaligned");
   if (lse != nullptr && !aligned(lse, 4)) return fail(DSA_ERR_INVALID_ARGUMENT, "lse misaligned");
   if ((st = check_attn_shape(n_heads_q, n_heads_kv, head_dim, topk, softmax_scale))) return st;
+  if ((st = check_attn_extent(vl, n_heads_kv, head_dim))) return st;
   if (row_count == 0) return ok();
   return hip_status(
       dsa::launch_sparse_attn(*vl, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
@@ -206,6 +217,7 @@ int dsa_sparse_attn_decode(const dsa_varlen* vl, const void* q, const void* k_ca
     return fail(DSA_ERR_INVALID_ARGUMENT, "indices is NULL or misaligned");
   if (lse != nullptr && !aligned(lse, 4)) return fail(DSA_ERR_INVALID_ARGUMENT, "lse misaligned");
   if ((st = check_attn_shape(n_heads_q, n_heads_kv, head_dim, topk, softmax_scale))) return st;
+  if ((st = check_attn_extent(vl, n_heads_kv, head_dim))) return st;
   const int splits = dsa::attn_decode_splits(vl->batch, n_heads_kv, topk);
   const size_t need = dsa::attn_workspace_bytes(vl->batch, n_heads_q, head_dim, splits);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)))

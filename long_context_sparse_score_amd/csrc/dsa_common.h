@@ -8,6 +8,7 @@ namespace dsa {
 
 // Operand and accumulator types of the gfx950 bf16 MFMA instructions.
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 // Native 16-byte vector (HIP's uint4 is a union-based struct that register
@@ -22,6 +23,13 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
   uint4 u = *reinterpret_cast<const uint4*>(p);
   return __builtin_bit_cast(bf16x8, u);
+}
+
+// Raw buffer resource over [base, base + bytes) (gfx9-family word 3): loads
+// past the end return zero and stores past it are dropped by the hardware.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes,
+                                           0x00020000);
 }
 
 __device__ __forceinline__ bf16x8 zero_bf16x8() {

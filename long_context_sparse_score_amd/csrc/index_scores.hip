@@ -142,15 +142,6 @@ __device__ void row_direct(const RowState<D, MT>& st, const uint16_t* __restrict
 
 // ---------------------------------------------------------------- prefill kernel
 
-// Raw buffer resources (gfx9 family word 3): loads past num_records return
-// zero and stores past it are dropped by the hardware.
-constexpr int kRawBufferWord3 = 0x00020000;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes,
-                                           kRawBufferWord3);
-}
-
 // s_waitcnt immediate: vmcnt(n), expcnt and lgkmcnt left unconstrained.
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 

@@ -29,82 +29,99 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 template <int D>
 struct AttnCfg {
-  static constexpr int KS = D / 32;       // k-steps of the S product
-  static constexpr int QD = D / 4;        // d range of one lane quarter
-  static constexpr int DT = D / 16;       // 16-wide d tiles of the O product
-  static constexpr int VSTRIDE = D + 4;   // LDS row stride (bf16), spreads banks
-  static constexpr int VTILE = 32 * VSTRIDE;
+  static constexpr int KS = D / 32;           // k-steps of the S product
+  static constexpr int QD = D / 4;            // d range of one lane quarter
+  static constexpr int DT = D / 16;           // 16-wide d tiles of the O product
+  static constexpr int PIECES = D / 8;        // 16-byte pieces of one K or V row
+  static constexpr int RPI = kWave / PIECES;  // whole rows per gather instruction
+  static constexpr int LPT = 32 / RPI;        // gather instructions per 32-slot tile
+  static constexpr int TILE = 32 * D;         // elements of one K or V tile in LDS
+  static_assert(RPI * PIECES == kWave && LPT * RPI == 32, "tile shape");
 };
 
-// Rows of one 32-slot tile gathered by one lane: slot 16*sub + col, d range
-// of lane quarter qd, for K (kept as the A operand) and V (staged to LDS).
+// One 32-slot tile of one KV head as gathered by one lane: lane l reads
+// piece l % PIECES of the rows (l / PIECES) LPT + j, j < LPT, of K and V.
+// Every gather instruction thus reads RPI whole rows (RPI x 2 D bytes,
+// whole cache lines): reading the MFMA operand layout directly would touch
+// 16 rows per instruction in 64-byte pieces, which halves the rate the
+// memory path sustains for scattered rows.
 template <int D>
 struct GatherTile {
-  bf16x8 k[2][AttnCfg<D>::KS];
-  u32x4 v[2][AttnCfg<D>::KS];
-  bool ok[2];  // slot holds a usable position (inside the list, 0 <= p <= pos)
+  u32x4 k[AttnCfg<D>::LPT];
+  u32x4 v[AttnCfg<D>::LPT];
 };
 
+// kr / vr: buffer resources over this sequence's K and V rows, so a row is
+// one 32-bit offset shared by its K and V loads.
 template <int D>
 __device__ __forceinline__ void gather_tile(GatherTile<D>& t, const int32_t* idx, int s0,
                                             int n_slots, const RowInfo& ri,
-                                            const uint16_t* __restrict__ k,
-                                            const uint16_t* __restrict__ v, int n_heads_kv, int g,
-                                            int col, int qd) {
+                                            __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                            int n_heads_kv, int g, int lane) {
   using C = AttnCfg<D>;
+  const int q = lane / C::PIECES, piece = lane % C::PIECES;
 #pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-    const int slot = s0 + 16 * sub + col;
+  for (int j = 0; j < C::LPT; ++j) {
+    const int slot = s0 + q * C::LPT + j;
     const int32_t p = slot < n_slots ? idx[slot] : -1;
-    t.ok[sub] = p >= 0 && p <= ri.pos;
-    const int64_t krow = ri.key_base + (t.ok[sub] ? p : 0);
-    const int64_t off = (krow * n_heads_kv + g) * D + qd * 8;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      t.k[sub][ks] = load_bf16x8(k + off + ks * 32);
-      t.v[sub][ks] = *reinterpret_cast<const u32x4*>(v + off + ks * 32);
-    }
+    const bool ok = p >= 0 && p <= ri.pos;
+    const uint32_t off = ((static_cast<uint32_t>(ok ? p : 0) * n_heads_kv + g) * D + piece * 8) * 2;
+    t.k[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0));
+    t.v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0));
   }
 }
 
+// Position of piece p of tile row r in LDS: pieces are XOR-swizzled by row,
+// so both the row-wise stores and the column-wise operand reads below are
+// free of bank conflicts.
+template <int D>
+__device__ __forceinline__ int tile_at(int r, int piece) {
+  return r * D + ((piece ^ (r % AttnCfg<D>::PIECES)) * 8);
+}
+
 // Online-softmax update of one tile.  m_run / l_run / acc are this lane's
-// running state (head col; O rows = heads 4 qd + r).
+// running state (head col; O rows = heads 4 qd + r).  vm: bit s says whether
+// slot s of the tile holds a usable position.
 template <int D>
 __device__ __forceinline__ void attend_tile(const GatherTile<D>& t, const bf16x8 (&qb)[AttnCfg<D>::KS],
-                                            uint16_t* vs, float scale_log2, int col, int qd,
-                                            float& m_run, float& l_run,
-                                            f32x4 (&acc)[AttnCfg<D>::DT]) {
+                                            uint16_t* ks_lds, uint16_t* vs_lds, uint32_t vm,
+                                            float scale_log2, int lane, float& m_run,
+                                            float& l_run, f32x4 (&acc)[AttnCfg<D>::DT]) {
   using C = AttnCfg<D>;
-  // V rows to this wave's LDS tile (read back below in the B-operand order).
+  const int col = lane & 15, qd = lane >> 4;
+  // K and V rows to this wave's LDS tiles.  The tiles are private to the
+  // wave and LDS operations of one wave are performed in order, so the reads
+  // below see these writes and the next tile's writes come after them.
+  {
+    const int q = lane / C::PIECES, piece = lane % C::PIECES;
 #pragma unroll
-  for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      uint16_t* dst = vs + (16 * sub + col) * C::VSTRIDE + ks * 32 + qd * 8;
-      reinterpret_cast<uint2*>(dst)[0] = make_uint2(t.v[sub][ks].x, t.v[sub][ks].y);
-      reinterpret_cast<uint2*>(dst)[1] = make_uint2(t.v[sub][ks].z, t.v[sub][ks].w);
+    for (int j = 0; j < C::LPT; ++j) {
+      const int at = tile_at<D>(q * C::LPT + j, piece);
+      *reinterpret_cast<u32x4*>(ks_lds + at) = t.k[j];
+      *reinterpret_cast<u32x4*>(vs_lds + at) = t.v[j];
     }
-  // Bit j of vm[sub] says whether slot 16*sub + j holds a usable position.
-  const unsigned long long vm0 = __ballot(t.ok[0]) & 0xFFFFull;
-  const unsigned long long vm1 = __ballot(t.ok[1]) & 0xFFFFull;
+  }
 
-  // S^T tiles: rows = slots 16*sub + 4*qd + r, column = head col.
+  // S^T tiles: rows = slots 16*sub + 4*qd + r, column = head col.  A operand:
+  // slot 16*sub + col, d range [32 ks + 8 qd, +8).
   f32x4 st[2];
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
     st[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-      st[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[sub][ks], qb[ks], st[sub], 0, 0, 0);
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const bf16x8 ka = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(ks_lds + tile_at<D>(16 * sub + col, 4 * ks + qd)));
+      st[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[ks], st[sub], 0, 0, 0);
+    }
   }
   float z[2][4];
   float mx = -INFINITY;
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
-    const unsigned long long vm = sub ? vm1 : vm0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const bool ok = (vm >> (4 * qd + r)) & 1ull;
+      const bool ok = (vm >> (16 * sub + 4 * qd + r)) & 1u;
       z[sub][r] = ok ? st[sub][r] * scale_log2 : -INFINITY;
       mx = fmaxf(mx, z[sub][r]);
     }
@@ -138,22 +155,38 @@ __device__ __forceinline__ void attend_tile(const GatherTile<D>& t, const bf16x8
   float cr[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * qd + r);
-  // The V tile is private to this wave and LDS operations of one wave are
-  // performed in order, so the reads below see the writes above.
+  // B operand: column d = 16 dt + col, rows = slots 4 qd + i and 16 + 4 qd + i
+  // (i < 4), the order of P's contraction.  ds_read_b64_tr_b16 transposes
+  // within each 16-lane group: lane t receives element t % 4 of the 4-element
+  // rows addressed by lanes t / 4 + 4 i of its group.  So lane (col, qd)
+  // addresses V[4 qd + col / 4][16 dt + 4 (col % 4), +4) -- 8 contiguous
+  // bytes of one row -- and receives V[4 qd + i][16 dt + col], i < 4; a
+  // second read does the same 16 slots further on.
+  const int tr_row = 4 * qd + (col >> 2);
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[dt][r] *= cr[r];
-    const uint16_t* src = vs + dt * 16 + col;
-    uint4 vb_u;
-    const int r0 = 4 * qd, r1 = 16 + 4 * qd;
-    vb_u.x = src[(r0 + 0) * C::VSTRIDE] | (static_cast<uint32_t>(src[(r0 + 1) * C::VSTRIDE]) << 16);
-    vb_u.y = src[(r0 + 2) * C::VSTRIDE] | (static_cast<uint32_t>(src[(r0 + 3) * C::VSTRIDE]) << 16);
-    vb_u.z = src[(r1 + 0) * C::VSTRIDE] | (static_cast<uint32_t>(src[(r1 + 1) * C::VSTRIDE]) << 16);
-    vb_u.w = src[(r1 + 2) * C::VSTRIDE] | (static_cast<uint32_t>(src[(r1 + 3) * C::VSTRIDE]) << 16);
-    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, vb_u),
-                                                      acc[dt], 0, 0, 0);
+    const int d0 = dt * 16 + 4 * (col & 3);
+    const int piece = d0 / 8, e = d0 % 8;
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(vs_lds + tile_at<D>(tr_row, piece) + e));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(vs_lds + tile_at<D>(16 + tr_row, piece) + e));
+    const bf16x8 vb = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi),
+                                              0, 1, 2, 3, 4, 5, 6, 7);
+    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, acc[dt], 0, 0, 0);
   }
+}
+
+// LDS of one workgroup: K and V tiles of every KV head, the slice of the
+// index list, and one validity word per 32 slots.
+template <int D>
+__host__ __device__ constexpr size_t attn_lds_bytes(int n_heads_kv, int per_split) {
+  return static_cast<size_t>(2 * n_heads_kv) * AttnCfg<D>::TILE * sizeof(uint16_t) +
+         static_cast<size_t>(per_split) * sizeof(int32_t) +
+         static_cast<size_t>((per_split + 63) / 64 * 2) * sizeof(uint32_t);
 }
 
 template <int D>
@@ -165,7 +198,7 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(
     uint16_t* __restrict__ out, float* __restrict__ lse, int splits,
     float* __restrict__ partial) {
   using C = AttnCfg<D>;
-  extern __shared__ uint16_t vs_all[];
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds_all[];
   const int lane = lane_id();
   const int g = threadIdx.x / kWave;  // KV head of this wave
   const int G = n_heads_q / n_heads_kv;
@@ -178,11 +211,25 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(
   const int per_split = (topk + splits - 1) / splits;
   const int i0 = split * per_split;
   const int n_slots = max(0, min(topk, i0 + per_split) - i0);
-  uint16_t* vs = vs_all + g * C::VTILE;
-  // This slice of the row's index list, shared by all KV heads, in LDS.
-  int32_t* idx = reinterpret_cast<int32_t*>(vs_all + n_heads_kv * C::VTILE);
+  uint16_t* ks_lds = lds_all + g * C::TILE;
+  uint16_t* vs_lds = lds_all + (n_heads_kv + g) * C::TILE;
+  // This slice of the row's index list, shared by all KV heads, in LDS, and
+  // a bitmask of its usable slots (0 <= p <= pos), one word per 32 slots.
+  int32_t* idx = reinterpret_cast<int32_t*>(lds_all + 2 * n_heads_kv * C::TILE);
+  uint32_t* vbits = reinterpret_cast<uint32_t*>(idx + per_split);
   const int32_t* irow = indices + local * topk + i0;
-  for (int s = threadIdx.x; s < n_slots; s += blockDim.x) idx[s] = irow[s];
+  const int n_pad = (n_slots + 63) & ~63;
+  for (int base = 0; base < n_pad; base += static_cast<int>(blockDim.x)) {
+    const int s = base + static_cast<int>(threadIdx.x);
+    const int32_t p = s < n_slots ? irow[s] : -1;
+    if (s < n_slots) idx[s] = p;
+    const unsigned long long ok = __ballot(p >= 0 && p <= ri.pos);
+    const int w0 = base + (static_cast<int>(threadIdx.x) & ~(kWave - 1));
+    if (lane == 0 && w0 < n_pad) {
+      vbits[w0 / 32] = static_cast<uint32_t>(ok);
+      vbits[w0 / 32 + 1] = static_cast<uint32_t>(ok >> 32);
+    }
+  }
 
   // Q^T as the B operand: column = query head of this group, contraction d
   // ordered so that lane quarter qd covers d in [qd*QD, qd*QD + QD).
@@ -197,18 +244,23 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(
   for (int dt = 0; dt < C::DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY;  // running max (log2 domain) of head `col`
   float l_run = 0.0f;       // this lane's share of the running denominator
-  __syncthreads();          // index list in LDS
+  __syncthreads();          // index list and validity words in LDS
 
   // Two tiles in flight: the next tile's rows are gathered while this one
   // is multiplied (the loop is unrolled by two so each tile keeps its
   // registers).  Tiles past the list gather valid rows and contribute zero.
+  // The sequence's visible K and V rows (keys 0..pos; the host checks that a
+  // sequence's cache fits 32-bit offsets).
+  const int seq_bytes = (ri.pos + 1) * n_heads_kv * D * 2;
+  const __amdgpu_buffer_rsrc_t kr = raw_buffer(k + ri.key_base * n_heads_kv * D, seq_bytes);
+  const __amdgpu_buffer_rsrc_t vr = raw_buffer(v + ri.key_base * n_heads_kv * D, seq_bytes);
   GatherTile<D> ta, tb;
-  gather_tile<D>(ta, idx, 0, n_slots, ri, k, v, n_heads_kv, g, col, qd);
+  gather_tile<D>(ta, idx, 0, n_slots, ri, kr, vr, n_heads_kv, g, lane);
   for (int s0 = 0; s0 < n_slots; s0 += 64) {
-    gather_tile<D>(tb, idx, s0 + 32, n_slots, ri, k, v, n_heads_kv, g, col, qd);
-    attend_tile<D>(ta, qb, vs, scale_log2, col, qd, m_run, l_run, acc);
-    gather_tile<D>(ta, idx, s0 + 64, n_slots, ri, k, v, n_heads_kv, g, col, qd);
-    attend_tile<D>(tb, qb, vs, scale_log2, col, qd, m_run, l_run, acc);
+    gather_tile<D>(tb, idx, s0 + 32, n_slots, ri, kr, vr, n_heads_kv, g, lane);
+    attend_tile<D>(ta, qb, ks_lds, vs_lds, vbits[s0 / 32], scale_log2, lane, m_run, l_run, acc);
+    gather_tile<D>(ta, idx, s0 + 64, n_slots, ri, kr, vr, n_heads_kv, g, lane);
+    attend_tile<D>(tb, qb, ks_lds, vs_lds, vbits[s0 / 32 + 1], scale_log2, lane, m_run, l_run, acc);
   }
 
   // Full denominator of head `col`: sum the four lane quarters.
@@ -306,15 +358,26 @@ hipError_t launch_sparse_attn(const dsa_varlen& vl, const uint16_t* q, const uin
   const float scale_log2 = scale * kLog2e;
   dim3 grid(static_cast<unsigned>(row_count), static_cast<unsigned>(splits));
   dim3 block(kWave * n_heads_kv);
+  // Up to 2 x 8 KV heads x 8 KB of tiles plus a 4096-entry index list:
+  // above the default dynamic LDS limit, within the 160 KB of a CU.
+  static const hipError_t lds_ok = [] {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_attn_kernel<128>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(attn_lds_bytes<128>(8, 4096)));
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_attn_kernel<64>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              static_cast<int>(attn_lds_bytes<64>(8, 4096)));
+    return e;
+  }();
+  if (lds_ok != hipSuccess) return lds_ok;
   if (head_dim == 128) {
-    const size_t lds = n_heads_kv * AttnCfg<128>::VTILE * sizeof(uint16_t) +
-                       static_cast<size_t>((topk + splits - 1) / splits) * sizeof(int32_t);
+    const size_t lds = attn_lds_bytes<128>(n_heads_kv, (topk + splits - 1) / splits);
     hipLaunchKernelGGL(sparse_attn_kernel<128>, grid, block, lds, stream, vl.cu_seqlens_q,
                        vl.cu_seqlens_k, vl.batch, q, k, v, indices, topk, row_begin, row_count,
                        n_heads_q, n_heads_kv, scale_log2, out, lse, splits, partial);
   } else {
-    const size_t lds = n_heads_kv * AttnCfg<64>::VTILE * sizeof(uint16_t) +
-                       static_cast<size_t>((topk + splits - 1) / splits) * sizeof(int32_t);
+    const size_t lds = attn_lds_bytes<64>(n_heads_kv, (topk + splits - 1) / splits);
     hipLaunchKernelGGL(sparse_attn_kernel<64>, grid, block, lds, stream, vl.cu_seqlens_q,
                        vl.cu_seqlens_k, vl.batch, q, k, v, indices, topk, row_begin, row_count,
                        n_heads_q, n_heads_kv, scale_log2, out, lse, splits, partial);
