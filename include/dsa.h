@@ -146,7 +146,9 @@ int dsa_topk(const dsa_varlen* vl, const float* scores, int64_t ld_scores, int64
  * Arithmetic: bf16 MFMA with fp32 accumulation, fp32 softmax, probabilities
  * rounded to bf16 for the value product, bf16 output (round to nearest even).
  * Supported: head_dim in {64, 128}; n_heads_q / n_heads_kv in 1..16;
- * n_heads_kv in 1..8; 1 <= topk <= 4096.
+ * n_heads_kv in 1..8; 1 <= topk <= 4096; one sequence's K (and V) rows at
+ * most 2 GiB, i.e. max_seqlen_k * n_heads_kv * head_dim * 2 < 2^31 (the
+ * kernels address a sequence with 32-bit byte offsets).
  * Invalid: null pointers, misaligned bf16 pointers, n_heads_q % n_heads_kv,
  * a window outside [0, total_q), non-finite softmax_scale.
  */

@@ -155,6 +155,17 @@ def test_attention_validation():
     assert dec(ws=FAKE + 64) == dsa.DSA_ERR_WORKSPACE       # 256-byte alignment
     assert dec(vv=vl()) == dsa.DSA_ERR_INVALID_ARGUMENT     # more than one query per sequence
 
+    # A sequence whose K (or V) rows pass 2 GiB: the kernels address one
+    # sequence with 32-bit byte offsets, so the host refuses it (3M tokens x
+    # 4 KV heads x 128 x 2 bytes = 3 GB), even for an empty prefill window.
+    big = vl(batch=1, total_q=1, total_k=3_000_000, max_q=1, max_k=3_000_000)
+    assert lib.dsa_sparse_attn_prefill(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, 2048, 0, 0, 32,
+                                       4, 128, 0.088, FAKE, None, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert dec(vv=big) == dsa.DSA_ERR_UNSUPPORTED
+    ok_size = vl(batch=1, total_q=1, total_k=2_000_000, max_q=1, max_k=2_000_000)  # 2.05e9 bytes
+    assert lib.dsa_sparse_attn_prefill(ctypes.byref(ok_size), FAKE, FAKE, FAKE, FAKE, 2048, 0, 0,
+                                       32, 4, 128, 0.088, FAKE, None, None) == dsa.DSA_OK
+
 
 def test_varlen_struct_layout():
     assert ctypes.sizeof(dsa.dsa_varlen) == 48
