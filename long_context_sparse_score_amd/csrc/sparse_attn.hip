@@ -7,16 +7,18 @@
 //
 // Workgroup = one query row (or one slice of its index list when the list is
 // split, for decode).  Wave g = KV head g with its Hq/Hkv query heads.  The
-// selected rows are gathered straight from HBM: a key row of one KV head is
-// contiguous (head_dim * 2 bytes), and each lane loads 16-byte pieces of it.
+// selected rows are gathered straight from HBM, whole rows per load
+// instruction (a key row of one KV head is head_dim * 2 contiguous bytes),
+// and staged through the wave's own LDS tiles.
 //
 // Per tile of 32 selected positions:
 //   S^T = K_sel Q^T on v_mfma_f32_16x16x32_bf16 (keys on MFMA rows, query
 //   heads on columns, padded to 16), online softmax per head in fp32
 //   (exp2 with log2(e) folded into the scale), then O += P V_sel on the same
 //   MFMA.  The contraction order of the P V product is chosen so that every
-//   lane's probabilities are already in place as the A operand; V goes
-//   through LDS because its B operand needs 8 consecutive keys per lane.
+//   lane's probabilities are already in place as the A operand; V's B
+//   operand (8 consecutive keys of one column per lane) comes from LDS
+//   through the transposing read.
 #include "dsa_common.h"
 #include "dsa_internal.h"
 
