@@ -8,10 +8,10 @@
 //
 // One workgroup owns one row and reads it from HBM once, in position order,
 // with three steps of loads in flight.  Two configurations: windows of many
-// rows use 256 threads, steps of 1024 scores and ~37 KB of LDS, so several
-// rows share a CU and hide each other's latencies; few long rows (decode)
-// use 512 threads, steps of 4096 scores and a candidate buffer twice as
-// large, so one row alone keeps 48 KB in flight.
+// rows use 256 threads, steps of 1024 scores and ~37 KB of LDS, so four rows
+// share a CU and hide each other's latencies; few long rows (decode) use 512
+// threads, steps of 4096 scores and a candidate buffer twice as large, so one
+// row alone keeps 48 KB in flight.
 //
 // A score survives only if it beats the running threshold, which for finite
 // scores is one float compare against the smallest float whose
@@ -91,16 +91,35 @@ struct BoolTag {
   static constexpr bool value = B;
 };
 
+// Wave-wide scans and reductions by DPP (six VALU steps, no LDS round
+// trips): row shifts by 1, 2, 4, 8 build the prefix within each row of 16
+// lanes; a broadcast of lane 15 into rows 1 and 3, then of lane 31 into
+// rows 2 and 3, carries it across rows.  Lanes without a source take the
+// operation's identity.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t x, uint32_t identity, Op op) {
+  x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(identity, x, 0x111, 0xf, 0xf, false)));
+  x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(identity, x, 0x112, 0xf, 0xf, false)));
+  x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(identity, x, 0x114, 0xf, 0xf, false)));
+  x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(identity, x, 0x118, 0xf, 0xf, false)));
+  x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(identity, x, 0x142, 0xa, 0xf, false)));
+  x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(identity, x, 0x143, 0xc, 0xf, false)));
+  return x;
+}
+
+// Inclusive prefix sum over the lanes.
+__device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t x) {
+  return wave_scan(x, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+
 __device__ __forceinline__ uint32_t wave_min(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = min(v, static_cast<uint32_t>(__shfl_xor(v, off)));
-  return v;
+  return __builtin_amdgcn_readlane(
+      wave_scan(v, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return min(a, b); }), kWave - 1);
 }
 
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(v, off)));
-  return v;
+  return __builtin_amdgcn_readlane(
+      wave_scan(v, 0u, [](uint32_t a, uint32_t b) { return max(a, b); }), kWave - 1);
 }
 
 // Element source for the streaming select.  fetch(j) loads elements
@@ -244,13 +263,11 @@ struct TopkImpl {
         hb[i] = sh.hist[tid * kBinsPerThread + i];
         local += hb[i];
       }
-      uint32_t suffix = local;  // inclusive suffix sum within the wave
-  #pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t t = __shfl_down(suffix, off);
-        if (lane + off < kWave) suffix += t;
-      }
-      if (lane == 0) sh.red[wave] = suffix;  // wave total
+      // Inclusive suffix sum within the wave: wave total minus the exclusive prefix.
+      const uint32_t incl = wave_prefix_sum(local);
+      const uint32_t wave_total = __builtin_amdgcn_readlane(incl, kWave - 1);
+      uint32_t suffix = wave_total - incl + local;
+      if (lane == 0) sh.red[wave] = wave_total;
       __syncthreads();
       for (int wv = wave + 1; wv < kWaves; ++wv) suffix += sh.red[wv];
       // The owner of the crossing bin: suffix >= remaining > suffix - local.
@@ -368,38 +385,48 @@ struct TopkImpl {
       pv[j] = slot_valid(own, tid, j) ? sh.pos[slot(tid, j)] : 0xFFFFFFFFu;
     __syncthreads();  // the key array becomes the bitmask / the pos array is rewritten
     if (n <= kMaskBits) {
-      // Bitmask over positions 0..n-1 in the (now free) key array.
+      // Bitmask over positions 0..n-1 in the (now free) key array; the rank of
+      // a kept position is the number of kept positions below it.  Word
+      // prefix counts go to the (now free) position array and chunk prefix
+      // counts (64 words per chunk) to the histogram; every pass reads the
+      // words lane by lane, so no two lanes of a wave share a bank.
       uint32_t* mask = sh.key;
+      uint32_t* pre = sh.pos;
+      uint32_t* chunk = sh.hist;
       const int words = (n + 31) / 32;
+      const int chunks = (words + kWave - 1) / kWave;
+      static_assert(kCap / kWave <= kBins, "chunk prefixes fit the histogram");
       for (int i = tid; i < words; i += kThreads) mask[i] = 0u;
       __syncthreads();
   #pragma unroll
       for (int j = 0; j < kPerThread; ++j)
         if (pv[j] != 0xFFFFFFFFu) atomicOr(&mask[pv[j] >> 5], 1u << (pv[j] & 31));
       __syncthreads();
-      // Thread t owns words [t*per, t*per + per).
-      const int per = (words + kThreads - 1) / kThreads;
-      const int w0 = tid * per;
-      uint32_t cnt = 0;
-      for (int i = 0; i < per; ++i)
-        if (w0 + i < words) cnt += __popc(mask[w0 + i]);
-      uint32_t incl = cnt;  // inclusive prefix within the wave
-  #pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t t = __shfl_up(incl, off);
-        if (lane >= off) incl += t;
+      for (int c = wave; c < chunks; c += kWaves) {
+        const int i = c * kWave + lane;
+        const uint32_t cnt = i < words ? static_cast<uint32_t>(__popc(mask[i])) : 0u;
+        const uint32_t incl = wave_prefix_sum(cnt);  // inclusive prefix within the chunk
+        if (i < words) pre[i] = incl - cnt;
+        if (lane == kWave - 1) chunk[c] = incl;
       }
-      if (lane == kWave - 1) sh.red[wave] = incl;
       __syncthreads();
-      uint32_t base = incl - cnt;
-      for (int i = 0; i < wave; ++i) base += sh.red[i];
-      for (int i = 0; i < per; ++i) {
-        if (w0 + i >= words) break;
-        uint32_t bitsw = mask[w0 + i];
-        while (bitsw) {
-          const int b = __builtin_ctz(bitsw);
-          orow[base++] = (w0 + i) * 32 + b;
-          bitsw &= bitsw - 1u;
+      if (wave == 0) {
+        uint32_t carry = 0;
+        for (int c0 = 0; c0 < chunks; c0 += kWave) {
+          const int c = c0 + lane;
+          const uint32_t tot = c < chunks ? chunk[c] : 0u;
+          const uint32_t incl = wave_prefix_sum(tot);
+          if (c < chunks) chunk[c] = carry + incl - tot;
+          carry += __builtin_amdgcn_readlane(incl, kWave - 1);
+        }
+      }
+      __syncthreads();
+  #pragma unroll
+      for (int j = 0; j < kPerThread; ++j) {
+        if (pv[j] != 0xFFFFFFFFu) {
+          const uint32_t wd = pv[j] >> 5;
+          const uint32_t below = mask[wd] & ((1u << (pv[j] & 31)) - 1u);
+          orow[chunk[wd / kWave] + pre[wd] + __popc(below)] = static_cast<int32_t>(pv[j]);
         }
       }
       return;
@@ -674,7 +701,9 @@ hipError_t launch_topk(const dsa_varlen& vl, const float* scores, int64_t ld, in
   if (row_count < 512)
     return launch_rows<TopkImpl<2, 8192, 512, 1024, 3, 2>>(vl, scores, ld, row_begin, row_count,
                                                            k, indices, stream);
-  return launch_rows<TopkImpl<1, 4096, 256, 1024, 5, 1>>(vl, scores, ld, row_begin, row_count, k,
+  // Many rows: steps of 1024 scores, four rows per CU; a 2048-score sample
+  // aimed at 1.5 k survivors (a rare restart costs only its own row here).
+  return launch_rows<TopkImpl<1, 4096, 256, 1024, 3, 2>>(vl, scores, ld, row_begin, row_count, k,
                                                          indices, stream);
 }
 
