@@ -6,7 +6,9 @@ One step = one pass of the whole hot path over one batch of synthetic input:
     / 4 KV heads x 128, indexer 64 heads x 128): for each window of query rows
     dsa_index_scores -> dsa_topk -> dsa_sparse_attn_prefill;
   * decode of one new token for each of 64 sequences with 131072 cached
-    tokens: dsa_index_scores -> dsa_topk -> dsa_sparse_attn_decode.
+    tokens: dsa_index_scores -> dsa_topk -> dsa_sparse_attn_decode on one
+    stream (--decode-groups G > 1 runs G row groups alternating between two
+    streams instead).
 Inputs are resident in HBM before the timed region starts.
 
 Printed: ONE JSON line.  `value` is prefill tokens/s; decode queries/s, the
@@ -14,8 +16,8 @@ per-kernel times, the rooflines, a same-shape dense causal attention run (torch
 SDPA, flash backend) and the CPU oracle on a bounded sample of the same
 prefill are reported beside it.
 
-    python bench.py [--steps K] [--warmup W] [--window ROWS] [--no-dense]
-                    [--no-cpu-baseline] [--cpu-rows N] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--window ROWS] [--decode-groups G]
+                    [--no-dense] [--no-cpu-baseline] [--cpu-rows N] [--gpus 1]
 """
 from __future__ import annotations
 
@@ -49,6 +51,10 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-groups", type=int, default=1,
+                    help="decode row groups; more than one alternate between two streams "
+                         "(measured slower here: the attention gathers compete with the next "
+                         "group's indexer for HBM)")
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
@@ -200,7 +206,10 @@ def main():
         log(f"generating {wd.name}")
         D, _ = gen_upload(torch, wd, ("q_idx", "k_idx", "w", "q", "k", "v"))
         vd = dsa.Varlen(wd.cu_q.tolist(), wd.cu_k.tolist())
-        dbufs = pipeline.alloc_decode(vd, wd.n_heads_q, wd.head_dim, wd.topk)
+        dbufs = pipeline.alloc_decode(vd, wd.n_heads_q, wd.head_dim, wd.topk,
+                                      groups=args.decode_groups)
+        dbufs1 = pipeline.alloc_decode(vd, wd.n_heads_q, wd.head_dim, wd.topk, groups=1)
+        side = torch.cuda.Stream() if len(dbufs.groups) > 1 else None
         dout = torch.empty((wd.batch, wd.n_heads_q, wd.head_dim), dtype=torch.bfloat16,
                            device="cuda")
         dlse = torch.empty((wd.batch, wd.n_heads_q), dtype=torch.float32, device="cuda")
@@ -223,18 +232,25 @@ def main():
                 e[3].record(stream)
                 rec.append((r0, n, e))
 
-    def run_decode(rec):
-        e = [ev() for _ in range(4)] if rec is not None else None
-        if e: e[0].record(stream)
-        dsa.dsa_index_scores(vd, D["q_idx"], D["k_idx"], D["w"], dbufs.scores)
-        if e: e[1].record(stream)
-        dsa.dsa_topk(vd, dbufs.scores, dbufs.indices, workspace=dbufs.topk_workspace)
-        if e: e[2].record(stream)
-        dsa.dsa_sparse_attn_decode(vd, D["q"], D["k"], D["v"], dbufs.indices, dout,
-                                   dbufs.workspace, lse=dlse)
-        if e:
-            e[3].record(stream)
-            rec.append(e)
+    def run_decode():
+        # The timed decode step (with --decode-groups > 1: row groups alternating
+        # between two streams).
+        pipeline.decode(vd, D["q_idx"], D["k_idx"], D["w"], D["q"], D["k"], D["v"], dout, dbufs,
+                        lse=dlse, side_stream=side)
+
+    def decode_breakdown(rec):
+        # The three calls one after the other on one stream, each between events
+        # (per-kernel times; not the timed step).
+        e = [ev() for _ in range(4)]
+        e[0].record(stream)
+        dsa.dsa_index_scores(vd, D["q_idx"], D["k_idx"], D["w"], dbufs1.scores)
+        e[1].record(stream)
+        dsa.dsa_topk(vd, dbufs1.scores, dbufs1.indices, workspace=dbufs1.topk_workspace)
+        e[2].record(stream)
+        dsa.dsa_sparse_attn_decode(vd, D["q"], D["k"], D["v"], dbufs1.indices, dout,
+                                   dbufs1.workspaces[0], lse=dlse)
+        e[3].record(stream)
+        rec.append(e)
 
     log(f"warmup {args.warmup} step(s)")
     for _ in range(args.warmup):
@@ -242,7 +258,9 @@ def main():
         torch.cuda.synchronize()
         log("  warmup prefill done")
         if not args.no_decode:
-            run_decode(None)
+            run_decode()
+            torch.cuda.synchronize()
+            decode_breakdown([])
             torch.cuda.synchronize()
             log("  warmup decode done")
 
@@ -255,13 +273,17 @@ def main():
         run_prefill(prec)
         m[1].record(stream)
         if not args.no_decode:
-            run_decode(drec)
+            run_decode()
         m[2].record(stream)
         marks.append(m)
         # Waiting between steps leaves the event-timed regions unchanged.
         torch.cuda.synchronize()
         log(f"  step {step}: {m[0].elapsed_time(m[2]):.2f} ms")
     t_wall = time.time() - t_wall
+    if not args.no_decode:
+        for _ in range(args.steps):
+            decode_breakdown(drec)
+            torch.cuda.synchronize()
 
     pre_ms = sum(m[0].elapsed_time(m[1]) for m in marks)
     dec_ms = sum(m[1].elapsed_time(m[2]) for m in marks) if not args.no_decode else 0.0
@@ -344,9 +366,13 @@ def main():
             "value": round(q_per_s, 1),
             "unit": "queries/s",
             "ms": round(dec_ms / args.steps, 4),
+            "groups": len(dbufs.groups),
+            "streams": 2 if side is not None else 1,
             "index_scores_ms": round(d_idx_ms / args.steps, 4),
             "topk_ms": round(d_topk_ms / args.steps, 4),
             "sparse_attn_ms": round(d_attn_ms / args.steps, 4),
+            "breakdown": "index_scores/topk/sparse_attn ms: the three calls for the whole batch "
+                         "one after another on one stream (outside the timed step)",
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                          "bytes_per_query": per_q},

@@ -158,10 +158,11 @@ int dsa_sparse_attn_prefill(const dsa_varlen* vl, const void* q, const void* k, 
                             int32_t head_dim, float softmax_scale, void* out, float* lse,
                             hipStream_t stream);
 
-/* Workspace bytes dsa_sparse_attn_decode needs (partial results of the
-   split over the index list). */
-int dsa_sparse_attn_decode_workspace_size(const dsa_varlen* vl, int32_t n_heads_q,
-                                          int32_t head_dim, int32_t topk, size_t* bytes);
+/* Workspace bytes dsa_sparse_attn_decode needs for a window of row_count
+   queries (partial results of the split over the index list). */
+int dsa_sparse_attn_decode_workspace_size(const dsa_varlen* vl, int64_t row_count,
+                                          int32_t n_heads_q, int32_t head_dim, int32_t topk,
+                                          size_t* bytes);
 
 /*
  * dsa_sparse_attn_decode -- the same attention for one new token per
@@ -172,18 +173,23 @@ int dsa_sparse_attn_decode_workspace_size(const dsa_varlen* vl, int32_t n_heads_
  *
  *   q        bf16 [batch, n_heads_q, head_dim]
  *   k_cache, v_cache  bf16 [total_k, n_heads_kv, head_dim]
- *   indices  int32 [batch, topk]
- *   out      bf16 [batch, n_heads_q, head_dim];  lse fp32 [batch, n_heads_q] or NULL
+ *   rows     queries row_begin .. row_begin + row_count - 1 of the batch
+ *   indices  int32 [row_count, topk]: row i belongs to query row_begin + i
+ *   out      bf16 [batch, n_heads_q, head_dim];  lse fp32 [batch, n_heads_q] or
+ *            NULL; rows of the window written.
  *   workspace  device buffer of at least dsa_sparse_attn_decode_workspace_size
- *              bytes, 256-byte aligned; its contents need not be initialised
- *              and are clobbered.  Calls sharing one workspace must be ordered.
+ *              bytes for this row_count, 256-byte aligned; its contents need
+ *              not be initialised and are clobbered.  Calls sharing one
+ *              workspace must be ordered; calls on disjoint windows with
+ *              disjoint workspaces may run concurrently on different streams.
  * Supported / invalid: as dsa_sparse_attn_prefill, plus total_q == batch.
  */
 int dsa_sparse_attn_decode(const dsa_varlen* vl, const void* q, const void* k_cache,
                            const void* v_cache, const int32_t* indices, int32_t topk,
-                           int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
-                           float softmax_scale, void* out, float* lse, void* workspace,
-                           size_t workspace_bytes, hipStream_t stream);
+                           int64_t row_begin, int64_t row_count, int32_t n_heads_q,
+                           int32_t n_heads_kv, int32_t head_dim, float softmax_scale, void* out,
+                           float* lse, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -75,9 +75,9 @@ def load_library(path: str = LIB_PATH):
     lib.dsa_topk.argtypes = [vl, vp, i64, i64, i64, i32, vp, vp, ctypes.c_size_t, vp]
     lib.dsa_sparse_attn_prefill.argtypes = [vl, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, f32,
                                             vp, vp, vp]
-    lib.dsa_sparse_attn_decode_workspace_size.argtypes = [vl, i32, i32, i32, sz]
-    lib.dsa_sparse_attn_decode.argtypes = [vl, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, vp, vp,
-                                           ctypes.c_size_t, vp]
+    lib.dsa_sparse_attn_decode_workspace_size.argtypes = [vl, i64, i32, i32, i32, sz]
+    lib.dsa_sparse_attn_decode.argtypes = [vl, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, f32,
+                                           vp, vp, vp, ctypes.c_size_t, vp]
     for name in EXPORTED[2:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -213,16 +213,19 @@ def dsa_sparse_attn_prefill(vl: Varlen, q, k, v, indices, out, lse=None, softmax
 
 
 def dsa_sparse_attn_decode_workspace_size(vl: Varlen, n_heads_q: int, head_dim: int,
-                                          topk: int) -> int:
+                                          topk: int, row_count=None) -> int:
+    """Workspace bytes of a decode call over row_count queries (default: all)."""
     n = ctypes.c_size_t(0)
-    _check(load_library().dsa_sparse_attn_decode_workspace_size(vl.struct, n_heads_q, head_dim,
-                                                                 topk, ctypes.byref(n)))
+    rc = vl.batch if row_count is None else row_count
+    _check(load_library().dsa_sparse_attn_decode_workspace_size(vl.struct, rc, n_heads_q,
+                                                                 head_dim, topk, ctypes.byref(n)))
     return n.value
 
 
 def dsa_sparse_attn_decode(vl: Varlen, q, k_cache, v_cache, indices, out, workspace, lse=None,
-                           softmax_scale=None, stream=None):
-    """Sparse GQA attention of one new token per sequence over its indices."""
+                           softmax_scale=None, row_begin=0, row_count=None, stream=None):
+    """Sparse GQA attention of one new token per sequence over its indices;
+    indices[i] belongs to query row_begin + i."""
     torch = _torch()
     _need(q, "q", torch.bfloat16, 3)
     _need(k_cache, "k_cache", torch.bfloat16, 3)
@@ -234,10 +237,11 @@ def dsa_sparse_attn_decode(vl: Varlen, q, k_cache, v_cache, indices, out, worksp
     d = q.shape[2]
     scale = d ** -0.5 if softmax_scale is None else softmax_scale
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    row_count = indices.shape[0] if row_count is None else row_count
     _check(load_library().dsa_sparse_attn_decode(
         vl.struct, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(indices), indices.shape[1],
-        q.shape[1], k_cache.shape[1], d, scale, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
-        _stream(stream)))
+        row_begin, row_count, q.shape[1], k_cache.shape[1], d, scale, _ptr(out), _ptr(lse),
+        _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def build(verbose: bool = False) -> str:

@@ -186,29 +186,35 @@ int dsa_sparse_attn_prefill(const dsa_varlen* vl, const void* q, const void* k, 
       "sparse_attn_prefill launch");
 }
 
-int dsa_sparse_attn_decode_workspace_size(const dsa_varlen* vl, int32_t n_heads_q,
-                                          int32_t head_dim, int32_t topk, size_t* bytes) {
+int dsa_sparse_attn_decode_workspace_size(const dsa_varlen* vl, int64_t row_count,
+                                          int32_t n_heads_q, int32_t head_dim, int32_t topk,
+                                          size_t* bytes) {
   int st;
   if ((st = check_varlen(vl))) return st;
   if (bytes == nullptr) return fail(DSA_ERR_INVALID_ARGUMENT, "bytes pointer is NULL");
+  if (row_count < 0 || row_count > vl->batch)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "row_count %lld outside [0, batch]",
+                static_cast<long long>(row_count));
   if (n_heads_q < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "n_heads_q must be >= 1");
   if (head_dim != 64 && head_dim != 128)
     return fail(DSA_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", head_dim);
   if (topk < 1 || topk > 4096) return fail(DSA_ERR_UNSUPPORTED, "topk %d not in 1..4096", topk);
-  const int splits = dsa::attn_decode_splits(vl->batch, 1, topk);
-  *bytes = dsa::attn_workspace_bytes(vl->batch, n_heads_q, head_dim, splits);
+  const int splits = dsa::attn_decode_splits(row_count, 1, topk);
+  *bytes = dsa::attn_workspace_bytes(row_count, n_heads_q, head_dim, splits);
   return ok();
 }
 
 int dsa_sparse_attn_decode(const dsa_varlen* vl, const void* q, const void* k_cache,
                            const void* v_cache, const int32_t* indices, int32_t topk,
-                           int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
-                           float softmax_scale, void* out, float* lse, void* workspace,
-                           size_t workspace_bytes, hipStream_t stream) {
+                           int64_t row_begin, int64_t row_count, int32_t n_heads_q,
+                           int32_t n_heads_kv, int32_t head_dim, float softmax_scale, void* out,
+                           float* lse, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
   int st;
   if ((st = check_varlen(vl))) return st;
   if (vl->total_q != vl->batch || vl->max_seqlen_q != 1)
     return fail(DSA_ERR_INVALID_ARGUMENT, "decode needs exactly one query per sequence");
+  if ((st = check_window(vl, row_begin, row_count))) return st;
   if ((st = check_bf16(q, "q"))) return st;
   if ((st = check_bf16(k_cache, "k_cache"))) return st;
   if ((st = check_bf16(v_cache, "v_cache"))) return st;
@@ -218,16 +224,17 @@ int dsa_sparse_attn_decode(const dsa_varlen* vl, const void* q, const void* k_ca
   if (lse != nullptr && !aligned(lse, 4)) return fail(DSA_ERR_INVALID_ARGUMENT, "lse misaligned");
   if ((st = check_attn_shape(n_heads_q, n_heads_kv, head_dim, topk, softmax_scale))) return st;
   if ((st = check_attn_extent(vl, n_heads_kv, head_dim))) return st;
-  const int splits = dsa::attn_decode_splits(vl->batch, n_heads_kv, topk);
-  const size_t need = dsa::attn_workspace_bytes(vl->batch, n_heads_q, head_dim, splits);
+  if (row_count == 0) return ok();
+  const int splits = dsa::attn_decode_splits(row_count, n_heads_kv, topk);
+  const size_t need = dsa::attn_workspace_bytes(row_count, n_heads_q, head_dim, splits);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)))
     return fail(DSA_ERR_WORKSPACE, "decode workspace needs %zu bytes (256-byte aligned), got %zu",
                 need, workspace_bytes);
   return hip_status(
       dsa::launch_sparse_attn(*vl, static_cast<const uint16_t*>(q),
                               static_cast<const uint16_t*>(k_cache),
-                              static_cast<const uint16_t*>(v_cache), indices, topk, 0, vl->batch,
-                              n_heads_q, n_heads_kv, head_dim, softmax_scale,
+                              static_cast<const uint16_t*>(v_cache), indices, topk, row_begin,
+                              row_count, n_heads_q, n_heads_kv, head_dim, softmax_scale,
                               static_cast<uint16_t*>(out), lse, splits,
                               static_cast<float*>(workspace), stream),
       "sparse_attn_decode launch");

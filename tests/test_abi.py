@@ -142,18 +142,27 @@ def test_attention_validation():
 
     dv = vl(batch=64, total_q=64, total_k=64 * 1000, max_q=1, max_k=1000)
     need = ctypes.c_size_t(0)
-    assert lib.dsa_sparse_attn_decode_workspace_size(ctypes.byref(dv), 32, 128, 2048,
+    assert lib.dsa_sparse_attn_decode_workspace_size(ctypes.byref(dv), 64, 32, 128, 2048,
                                                      ctypes.byref(need)) == 0
     assert need.value > 0
+    half = ctypes.c_size_t(0)
+    assert lib.dsa_sparse_attn_decode_workspace_size(ctypes.byref(dv), 32, 32, 128, 2048,
+                                                     ctypes.byref(half)) == 0
+    assert 0 < half.value
+    assert lib.dsa_sparse_attn_decode_workspace_size(ctypes.byref(dv), 65, 32, 128, 2048,
+                                                     ctypes.byref(half)) == \
+        dsa.DSA_ERR_INVALID_ARGUMENT                      # more rows than the batch
 
-    def dec(ws=FAKE, ws_bytes=None, vv=dv):
+    def dec(ws=FAKE, ws_bytes=None, vv=dv, rb=0, rc=64):
         b = need.value if ws_bytes is None else ws_bytes
-        return lib.dsa_sparse_attn_decode(ctypes.byref(vv), FAKE, FAKE, FAKE, FAKE, 2048, 32, 4,
-                                          128, 0.088, FAKE, None, ws, b, None)
+        return lib.dsa_sparse_attn_decode(ctypes.byref(vv), FAKE, FAKE, FAKE, FAKE, 2048, rb, rc,
+                                          32, 4, 128, 0.088, FAKE, None, ws, b, None)
     assert dec(ws=None) == dsa.DSA_ERR_WORKSPACE
     assert dec(ws_bytes=need.value - 1) == dsa.DSA_ERR_WORKSPACE
     assert dec(ws=FAKE + 64) == dsa.DSA_ERR_WORKSPACE       # 256-byte alignment
     assert dec(vv=vl()) == dsa.DSA_ERR_INVALID_ARGUMENT     # more than one query per sequence
+    assert dec(rb=40, rc=30) == dsa.DSA_ERR_INVALID_ARGUMENT  # window past the batch
+    assert dec(rb=10, rc=0, ws=None) == dsa.DSA_OK            # empty window: nothing to do
 
     # A sequence whose K (or V) rows pass 2 GiB: the kernels address one
     # sequence with 32-bit byte offsets, so the host refuses it (3M tokens x
@@ -161,7 +170,7 @@ def test_attention_validation():
     big = vl(batch=1, total_q=1, total_k=3_000_000, max_q=1, max_k=3_000_000)
     assert lib.dsa_sparse_attn_prefill(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, 2048, 0, 0, 32,
                                        4, 128, 0.088, FAKE, None, None) == dsa.DSA_ERR_UNSUPPORTED
-    assert dec(vv=big) == dsa.DSA_ERR_UNSUPPORTED
+    assert dec(vv=big, rc=1) == dsa.DSA_ERR_UNSUPPORTED
     ok_size = vl(batch=1, total_q=1, total_k=2_000_000, max_q=1, max_k=2_000_000)  # 2.05e9 bytes
     assert lib.dsa_sparse_attn_prefill(ctypes.byref(ok_size), FAKE, FAKE, FAKE, FAKE, 2048, 0, 0,
                                        32, 4, 128, 0.088, FAKE, None, None) == dsa.DSA_OK

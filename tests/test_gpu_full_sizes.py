@@ -132,25 +132,31 @@ def test_prefill_128k_topk_property_all_rows():
 
 
 def test_decode_b64_128k_all_queries():
+    """The bench's decode step (one group, one stream) and two row groups on
+    two streams, both against the oracle on all 64 queries."""
     wl = synth.decode_b64_128k()
     log("decode_b64_128k: generate")
     host, dev = device_workload(wl)
     vl = dsa.Varlen(wl.cu_q.tolist(), wl.cu_k.tolist())
-    bufs = pipeline.alloc_decode(vl, wl.n_heads_q, wl.head_dim, wl.topk)
-    out = torch.zeros((wl.batch, wl.n_heads_q, wl.head_dim), dtype=torch.bfloat16, device="cuda")
-    lse = torch.zeros((wl.batch, wl.n_heads_q), dtype=torch.float32, device="cuda")
-    pipeline.decode(vl, dev["q_idx"], dev["k_idx"], dev["w"], dev["q"], dev["k"], dev["v"], out,
-                    bufs, lse=lse)
-    torch.cuda.synchronize()
     rows = np.arange(wl.batch)
     log("decode_b64_128k: oracle on all 64 queries")
     ref = oracle_rows(wl, host, rows)
-    same = check_topk_rows(bufs.indices.cpu().numpy(), ref["idx"], ref["scores"], ref["counts"],
-                           wl.topk)
-    mx, mean = check_attn(from_dev_bf16(out), ref["out"], rows_mask=same)
-    assert np.allclose(lse.cpu().numpy()[same], ref["lse"][same], atol=2e-3)
-    log(f"  {same.sum()}/64 identical index sets, attention max abs {mx:.2e} mean abs {mean:.2e}")
-    assert same.mean() >= 0.5
+    for groups in (1, 2):
+        bufs = pipeline.alloc_decode(vl, wl.n_heads_q, wl.head_dim, wl.topk, groups=groups)
+        out = torch.zeros((wl.batch, wl.n_heads_q, wl.head_dim), dtype=torch.bfloat16,
+                          device="cuda")
+        lse = torch.zeros((wl.batch, wl.n_heads_q), dtype=torch.float32, device="cuda")
+        side = torch.cuda.Stream() if groups > 1 else None
+        pipeline.decode(vl, dev["q_idx"], dev["k_idx"], dev["w"], dev["q"], dev["k"], dev["v"],
+                        out, bufs, lse=lse, side_stream=side)
+        torch.cuda.synchronize()
+        same = check_topk_rows(bufs.indices.cpu().numpy(), ref["idx"], ref["scores"],
+                               ref["counts"], wl.topk)
+        mx, mean = check_attn(from_dev_bf16(out), ref["out"], rows_mask=same)
+        assert np.allclose(lse.cpu().numpy()[same], ref["lse"][same], atol=2e-3)
+        log(f"  {groups} group(s): {same.sum()}/64 identical index sets, attention max abs "
+            f"{mx:.2e} mean abs {mean:.2e}")
+        assert same.mean() >= 0.5
 
 
 def test_varlen_512k_sampled():

@@ -365,19 +365,22 @@ def test_prefill_2k_int_end_to_end():
     assert np.allclose(lse.cpu().numpy(), ref["lse"], atol=2e-3)
 
 
-def test_decode_small_varlen():
+@pytest.mark.parametrize("groups", [1, 3])
+def test_decode_small_varlen(groups):
     """Decode (one query per sequence, p = Lk - 1) with ragged cache lengths,
-    including caches shorter than k."""
-    lk = [1, 100, 2048, 2049, 5000, 9000]
+    including caches shorter than k; with groups > 1 the batch runs as row
+    groups alternating between two streams (ragged last group)."""
+    lk = [1, 100, 2048, 2049, 5000, 9000, 300]
     wl = small_wl([1] * len(lk), lk, hq=32, hkv=4, d=128, hi=64, di=128, topk=2048, seed=21)
     host, dev = device_workload(wl)
     vl = varlen_for(wl)
-    bufs = pipeline.alloc_decode(vl, wl.n_heads_q, wl.head_dim, wl.topk)
+    bufs = pipeline.alloc_decode(vl, wl.n_heads_q, wl.head_dim, wl.topk, groups=groups)
     out = torch.zeros((wl.batch, 32, 128), dtype=torch.bfloat16, device="cuda")
     lse = torch.zeros((wl.batch, 32), dtype=torch.float32, device="cuda")
-    log("decode small varlen")
+    log(f"decode small varlen, {groups} group(s)")
+    side = torch.cuda.Stream() if groups > 1 else None
     pipeline.decode(vl, dev["q_idx"], dev["k_idx"], dev["w"], dev["q"], dev["k"], dev["v"], out,
-                    bufs, lse=lse)
+                    bufs, lse=lse, side_stream=side)
     torch.cuda.synchronize()
     rows = np.arange(wl.batch)
     ref = oracle_rows(wl, host, rows)
