@@ -353,6 +353,7 @@ def main():
             "algorithmic": {k: int(v) for k, v in pc.items()},
         },
         "wall_s_timed": round(t_wall, 3),
+        "device": device_info(torch),
     }
 
     if not args.no_decode:
@@ -399,6 +400,16 @@ def main():
         result["cpu_baseline"] = cpu_baseline(wl, P_host, args.cpu_rows)
 
     print(json.dumps(result), flush=True)
+
+
+def device_info(torch):
+    """GPU name and architecture, HIP version; clocks are the driver's (this
+    program neither locks nor reads back a fixed clock)."""
+    props = torch.cuda.get_device_properties(0)
+    return {"name": torch.cuda.get_device_name(0),
+            "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count,
+            "hip": torch.version.hip, "torch": torch.__version__, "clocks_locked": False}
 
 
 def dense_comparator(torch, P, wl, args, sparse_ms):

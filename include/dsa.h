@@ -21,7 +21,8 @@
  * Conventions shared by every entry point
  *   - Tensor pointers are DEVICE pointers into caller-owned, contiguous,
  *     row-major buffers.  The library never allocates, frees, copies or
- *     synchronises; it only enqueues kernels on `stream`.
+ *     synchronises; it only enqueues kernels on `stream`.  The one
+ *     exception is the opt-in device-side checking described below.
  *   - bf16 tensors are IEEE binary32 values truncated to their upper 16 bits
  *     (torch.bfloat16), passed as `const void*`, 16-byte aligned.
  *   - Calls are stateless and may be made from any host thread.
@@ -30,9 +31,19 @@
  *     the calling thread's most recent failure.  Faults during execution
  *     surface as HIP errors on the caller's next synchronisation.
  *   - Validation is host-side (pointers, sizes, shapes).  Device-resident
- *     metadata (cu_seqlens, index values) is a precondition, not checked:
- *     cu_seqlens must be non-decreasing with Lq_b <= Lk_b; indices outside
- *     0..p are treated as empty slots by the attention kernels.
+ *     metadata (cu_seqlens, index values, scores) is a precondition, not
+ *     checked by default: cu_seqlens must start at 0, be non-decreasing with
+ *     Lq_b <= Lk_b, stay within max_seqlen_q / max_seqlen_k and end at
+ *     total_q / total_k; scores must be finite; an index list holds each
+ *     position at most once.  Indices outside 0..p are treated as empty
+ *     slots by the attention kernels.
+ *   - Device-side checking (opt-in): with the environment variable DSA_CHECK
+ *     set to anything but "" or "0" (read at every call), each entry point
+ *     first runs the matching dsa_check_* call below on its own inputs and
+ *     returns its status without enqueueing the real work when it fails.
+ *     Checked calls wait for `stream` (so they cannot be captured into a
+ *     graph), and the first one on a device allocates a 256-byte report
+ *     buffer that lives until the process ends.
  *
  * Varlen layout (dsa_varlen)
  *   Sequence b owns packed query rows [cu_seqlens_q[b], cu_seqlens_q[b+1])
@@ -190,6 +201,32 @@ int dsa_sparse_attn_decode(const dsa_varlen* vl, const void* q, const void* k_ca
                            int32_t n_heads_kv, int32_t head_dim, float softmax_scale, void* out,
                            float* lse, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
+
+/*
+ * Device-side precondition checks (debugging aid; see the conventions above).
+ * Each validates its arguments on the host like the entry points, runs one
+ * or two small kernels on `stream`, waits for the stream (and so for all
+ * work enqueued before it) and returns DSA_OK, or DSA_ERR_INVALID_ARGUMENT
+ * with dsa_last_error() naming the first offending sequence or row, or
+ * DSA_ERR_HIP.  They read only the arguments they name.
+ *
+ * dsa_check_varlen   cu_seqlens_q / cu_seqlens_k against the descriptor:
+ *                    both start at 0, never decrease, Lq_b <= Lk_b,
+ *                    Lq_b <= max_seqlen_q, Lk_b <= max_seqlen_k, and they end
+ *                    at total_q / total_k.
+ * dsa_check_indices  the varlen check, then every row of an index list
+ *                    int32 [row_count, topk] for query rows row_begin ..:
+ *                    each entry is -1 or a causal position 0..p, and no
+ *                    position appears twice (the selected set is causal and
+ *                    unique, page 5 section 1).
+ * dsa_check_scores   the varlen check, then columns 0..p of every row of
+ *                    fp32 scores [row_count, ld_scores] are finite.
+ */
+int dsa_check_varlen(const dsa_varlen* vl, hipStream_t stream);
+int dsa_check_indices(const dsa_varlen* vl, const int32_t* indices, int32_t topk,
+                      int64_t row_begin, int64_t row_count, hipStream_t stream);
+int dsa_check_scores(const dsa_varlen* vl, const float* scores, int64_t ld_scores,
+                     int64_t row_begin, int64_t row_count, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -9,7 +9,10 @@ points raises.
 Entry points (same names as the C ABI):
     dsa_index_scores, dsa_topk, dsa_topk_workspace_size,
     dsa_sparse_attn_prefill, dsa_sparse_attn_decode,
-    dsa_sparse_attn_decode_workspace_size
+    dsa_sparse_attn_decode_workspace_size,
+    dsa_check_varlen, dsa_check_indices, dsa_check_scores (device-side
+    precondition checks; the entry points also run them when the environment
+    variable DSA_CHECK is set to anything but "" or "0")
 plus ``Varlen`` (the packed-batch descriptor) and ``DSAError``.
 """
 from __future__ import annotations
@@ -23,7 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 EXPORTED = (
     "dsa_status_string", "dsa_last_error", "dsa_index_scores", "dsa_topk_workspace_size",
     "dsa_topk", "dsa_sparse_attn_prefill", "dsa_sparse_attn_decode_workspace_size",
-    "dsa_sparse_attn_decode",
+    "dsa_sparse_attn_decode", "dsa_check_varlen", "dsa_check_indices", "dsa_check_scores",
 )
 
 DSA_OK = 0
@@ -78,6 +81,9 @@ def load_library(path: str = LIB_PATH):
     lib.dsa_sparse_attn_decode_workspace_size.argtypes = [vl, i64, i32, i32, i32, sz]
     lib.dsa_sparse_attn_decode.argtypes = [vl, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, f32,
                                            vp, vp, vp, ctypes.c_size_t, vp]
+    lib.dsa_check_varlen.argtypes = [vl, vp]
+    lib.dsa_check_indices.argtypes = [vl, vp, i32, i64, i64, vp]
+    lib.dsa_check_scores.argtypes = [vl, vp, i64, i64, i64, vp]
     for name in EXPORTED[2:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -242,6 +248,33 @@ def dsa_sparse_attn_decode(vl: Varlen, q, k_cache, v_cache, indices, out, worksp
         vl.struct, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(indices), indices.shape[1],
         row_begin, row_count, q.shape[1], k_cache.shape[1], d, scale, _ptr(out), _ptr(lse),
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dsa_check_varlen(vl: Varlen, stream=None):
+    """Device-side check of the packed-batch offsets (waits for the stream)."""
+    _check(load_library().dsa_check_varlen(vl.struct, _stream(stream)))
+
+
+def dsa_check_indices(vl: Varlen, indices, row_begin: int = 0, row_count: int | None = None,
+                      stream=None):
+    """Device-side check that every row of indices (int32 [row_count, topk]) is
+    causal and free of repeats (waits for the stream)."""
+    torch = _torch()
+    _need(indices, "indices", torch.int32, 2)
+    row_count = indices.shape[0] if row_count is None else row_count
+    _check(load_library().dsa_check_indices(vl.struct, _ptr(indices), indices.shape[1], row_begin,
+                                            row_count, _stream(stream)))
+
+
+def dsa_check_scores(vl: Varlen, scores, row_begin: int = 0, row_count: int | None = None,
+                     stream=None):
+    """Device-side check that columns 0..p of every score row are finite
+    (waits for the stream)."""
+    torch = _torch()
+    _need(scores, "scores", torch.float32, 2)
+    row_count = scores.shape[0] if row_count is None else row_count
+    _check(load_library().dsa_check_scores(vl.struct, _ptr(scores), scores.shape[1], row_begin,
+                                           row_count, _stream(stream)))
 
 
 def build(verbose: bool = False) -> str:

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 
 #include "dsa.h"
 #include "dsa_internal.h"
@@ -96,6 +97,69 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// DSA_CHECK set to anything but "" or "0" turns the device-side checks on
+// in every entry point.  Read at each call, so a process may toggle it.
+bool checks_enabled() {
+  const char* e = std::getenv("DSA_CHECK");
+  return e != nullptr && e[0] != '\0' && !(e[0] == '0' && e[1] == '\0');
+}
+
+int finding_status(hipError_t e, unsigned long long finding, int64_t row_begin) {
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "device check: %s", hipGetErrorString(e));
+  if (finding == dsa::kNoFinding) return ok();
+  const long long item = static_cast<long long>(finding >> 8);
+  const long long row = static_cast<long long>(row_begin) + item;
+  switch (static_cast<int>(finding & 0xff)) {
+    case dsa::kCheckOffsetStart:
+      return fail(DSA_ERR_INVALID_ARGUMENT, "cu_seqlens_q[0] and cu_seqlens_k[0] must be 0");
+    case dsa::kCheckOffsetOrder:
+      return fail(DSA_ERR_INVALID_ARGUMENT, "cu_seqlens decrease at sequence %lld", item);
+    case dsa::kCheckMoreQueriesThanKeys:
+      return fail(DSA_ERR_INVALID_ARGUMENT, "sequence %lld has more queries than keys", item);
+    case dsa::kCheckAboveMax:
+      return fail(DSA_ERR_INVALID_ARGUMENT,
+                  "sequence %lld is longer than max_seqlen_q or max_seqlen_k", item);
+    case dsa::kCheckTotal:
+      return fail(DSA_ERR_INVALID_ARGUMENT,
+                  "cu_seqlens_q[B] or cu_seqlens_k[B] differs from total_q or total_k");
+    case dsa::kCheckIndexRange:
+      return fail(DSA_ERR_INVALID_ARGUMENT, "row %lld: an index is neither -1 nor in 0..p", row);
+    case dsa::kCheckIndexDuplicate:
+      return fail(DSA_ERR_INVALID_ARGUMENT, "row %lld lists a position twice", row);
+    case dsa::kCheckScoreNotFinite:
+      return fail(DSA_ERR_INVALID_ARGUMENT, "row %lld: a score in columns 0..p is not finite",
+                  row);
+    default:
+      return fail(DSA_ERR_HIP, "device check: unknown finding %llu", finding);
+  }
+}
+
+int device_offsets(const dsa_varlen* vl, hipStream_t stream) {
+  unsigned long long f = dsa::kNoFinding;
+  const hipError_t e = dsa::check_offsets(*vl, stream, &f);
+  return finding_status(e, f, 0);
+}
+
+int device_indices(const dsa_varlen* vl, const int32_t* indices, int32_t topk, int64_t row_begin,
+                   int64_t row_count, hipStream_t stream) {
+  int st;
+  if ((st = device_offsets(vl, stream))) return st;
+  if (row_count == 0) return ok();
+  unsigned long long f = dsa::kNoFinding;
+  const hipError_t e = dsa::check_indices(*vl, indices, topk, row_begin, row_count, stream, &f);
+  return finding_status(e, f, row_begin);
+}
+
+int device_scores(const dsa_varlen* vl, const float* scores, int64_t ld, int64_t row_begin,
+                  int64_t row_count, hipStream_t stream) {
+  int st;
+  if ((st = device_offsets(vl, stream))) return st;
+  if (row_count == 0) return ok();
+  unsigned long long f = dsa::kNoFinding;
+  const hipError_t e = dsa::check_scores(*vl, scores, ld, row_begin, row_count, stream, &f);
+  return finding_status(e, f, row_begin);
+}
+
 }  // namespace
 
 extern "C" {
@@ -126,6 +190,7 @@ int dsa_index_scores(const dsa_varlen* vl, const void* q_idx, const void* k_idx,
   if (d_idx != 64 && d_idx != 128) return fail(DSA_ERR_UNSUPPORTED, "d_idx %d not in {64, 128}", d_idx);
   if (n_heads_idx < 1 || n_heads_idx > 64)
     return fail(DSA_ERR_UNSUPPORTED, "n_heads_idx %d not in 1..64", n_heads_idx);
+  if (checks_enabled() && (st = device_offsets(vl, stream))) return st;
   if (row_count == 0) return ok();
   return hip_status(dsa::launch_index_scores(*vl, static_cast<const uint16_t*>(q_idx),
                                              static_cast<const uint16_t*>(k_idx), w, n_heads_idx,
@@ -155,6 +220,9 @@ int dsa_topk(const dsa_varlen* vl, const float* scores, int64_t ld_scores, int64
   if (indices == nullptr || !aligned(indices, 4))
     return fail(DSA_ERR_INVALID_ARGUMENT, "indices is NULL or misaligned");
   if (k < 1 || k > 2048) return fail(DSA_ERR_UNSUPPORTED, "k %d not in 1..2048", k);
+  if (checks_enabled() &&
+      (st = device_scores(vl, scores, ld_scores, row_begin, row_count, stream)))
+    return st;
   if (row_count == 0) return ok();
   return hip_status(dsa::launch_topk(*vl, scores, ld_scores, row_begin, row_count, k, indices, stream),
                     "topk launch");
@@ -177,6 +245,9 @@ int dsa_sparse_attn_prefill(const dsa_varlen* vl, const void* q, const void* k, 
   if (lse != nullptr && !aligned(lse, 4)) return fail(DSA_ERR_INVALID_ARGUMENT, "lse misaligned");
   if ((st = check_attn_shape(n_heads_q, n_heads_kv, head_dim, topk, softmax_scale))) return st;
   if ((st = check_attn_extent(vl, n_heads_kv, head_dim))) return st;
+  if (checks_enabled() &&
+      (st = device_indices(vl, indices, topk, row_begin, row_count, stream)))
+    return st;
   if (row_count == 0) return ok();
   return hip_status(
       dsa::launch_sparse_attn(*vl, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
@@ -224,6 +295,9 @@ int dsa_sparse_attn_decode(const dsa_varlen* vl, const void* q, const void* k_ca
   if (lse != nullptr && !aligned(lse, 4)) return fail(DSA_ERR_INVALID_ARGUMENT, "lse misaligned");
   if ((st = check_attn_shape(n_heads_q, n_heads_kv, head_dim, topk, softmax_scale))) return st;
   if ((st = check_attn_extent(vl, n_heads_kv, head_dim))) return st;
+  if (checks_enabled() &&
+      (st = device_indices(vl, indices, topk, row_begin, row_count, stream)))
+    return st;
   if (row_count == 0) return ok();
   const int splits = dsa::attn_decode_splits(row_count, n_heads_kv, topk);
   const size_t need = dsa::attn_workspace_bytes(row_count, n_heads_q, head_dim, splits);
@@ -238,6 +312,32 @@ int dsa_sparse_attn_decode(const dsa_varlen* vl, const void* q, const void* k_ca
                               static_cast<uint16_t*>(out), lse, splits,
                               static_cast<float*>(workspace), stream),
       "sparse_attn_decode launch");
+}
+
+int dsa_check_varlen(const dsa_varlen* vl, hipStream_t stream) {
+  int st;
+  if ((st = check_varlen(vl))) return st;
+  return device_offsets(vl, stream);
+}
+
+int dsa_check_indices(const dsa_varlen* vl, const int32_t* indices, int32_t topk,
+                      int64_t row_begin, int64_t row_count, hipStream_t stream) {
+  int st;
+  if ((st = check_varlen(vl))) return st;
+  if ((st = check_window(vl, row_begin, row_count))) return st;
+  if (indices == nullptr || !aligned(indices, 4))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "indices is NULL or misaligned");
+  if (topk < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "topk must be >= 1");
+  return device_indices(vl, indices, topk, row_begin, row_count, stream);
+}
+
+int dsa_check_scores(const dsa_varlen* vl, const float* scores, int64_t ld_scores,
+                     int64_t row_begin, int64_t row_count, hipStream_t stream) {
+  int st;
+  if ((st = check_varlen(vl))) return st;
+  if ((st = check_window(vl, row_begin, row_count))) return st;
+  if ((st = check_scores(vl, scores, ld_scores))) return st;
+  return device_scores(vl, scores, ld_scores, row_begin, row_count, stream);
 }
 
 }  // extern "C"

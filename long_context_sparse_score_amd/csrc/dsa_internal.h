@@ -28,4 +28,28 @@ hipError_t launch_sparse_attn(const dsa_varlen& vl, const uint16_t* q, const uin
                               int head_dim, float scale, uint16_t* out, float* lse, int splits,
                               float* partial, hipStream_t stream);
 
+// Device-side precondition checks.  Each clears a report word, runs one
+// kernel on `stream`, waits for the stream and stores the first finding as
+// (item << 8) | code, or all ones when there is none.  The first call on a
+// device allocates its report word (kept until the process ends).
+enum CheckCode {
+  kCheckOffsetStart = 1,         // cu_seqlens_q[0] or cu_seqlens_k[0] != 0
+  kCheckOffsetOrder = 2,         // cu_seqlens decreases
+  kCheckMoreQueriesThanKeys = 3, // Lq_b > Lk_b
+  kCheckAboveMax = 4,            // Lq_b > max_seqlen_q or Lk_b > max_seqlen_k
+  kCheckTotal = 5,               // cu_seqlens[B] != total
+  kCheckIndexRange = 6,          // an entry neither -1 nor in 0..p
+  kCheckIndexDuplicate = 7,      // a position listed twice in one row
+  kCheckScoreNotFinite = 8,      // NaN or infinity among columns 0..p
+};
+constexpr unsigned long long kNoFinding = ~0ull;
+
+hipError_t check_offsets(const dsa_varlen& vl, hipStream_t stream, unsigned long long* finding);
+// Rows of the window; the offsets must already have passed check_offsets.
+hipError_t check_indices(const dsa_varlen& vl, const int32_t* indices, int topk,
+                         int64_t row_begin, int64_t row_count, hipStream_t stream,
+                         unsigned long long* finding);
+hipError_t check_scores(const dsa_varlen& vl, const float* scores, int64_t ld, int64_t row_begin,
+                        int64_t row_count, hipStream_t stream, unsigned long long* finding);
+
 }  // namespace dsa

@@ -15,6 +15,12 @@ HEADER = os.path.join(ROOT, "include", "dsa.h")
 FAKE = 0x7F0000000000  # a 256-byte aligned address; never dereferenced on these paths
 
 
+@pytest.fixture(autouse=True)
+def _no_device_checks(monkeypatch):
+    """The calls below must stop on the host: device-side checking stays off."""
+    monkeypatch.delenv("DSA_CHECK", raising=False)
+
+
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -181,3 +187,34 @@ def test_varlen_struct_layout():
     assert dsa.dsa_varlen.cu_seqlens_q.offset == 8
     assert dsa.dsa_varlen.total_q.offset == 24
     assert dsa.dsa_varlen.max_seqlen_k.offset == 44
+
+
+def test_check_entry_points_validate_on_the_host():
+    """The device-side checks reject bad descriptors, windows and pointers on
+    the host, before any HIP call."""
+    lib = dsa.load_library()
+    I = dsa.DSA_ERR_INVALID_ARGUMENT
+    v = vl()
+    assert lib.dsa_check_varlen(None, None) == I
+    assert lib.dsa_check_varlen(ctypes.byref(vl(batch=0)), None) == I
+    assert lib.dsa_check_varlen(ctypes.byref(vl(cu=0)), None) == I
+    assert lib.dsa_check_indices(ctypes.byref(v), None, 64, 0, 10, None) == I
+    assert lib.dsa_check_indices(ctypes.byref(v), FAKE + 2, 64, 0, 10, None) == I
+    assert lib.dsa_check_indices(ctypes.byref(v), FAKE, 0, 0, 10, None) == I
+    assert lib.dsa_check_indices(ctypes.byref(v), FAKE, 64, 95, 10, None) == I
+    assert b"row window" in lib.dsa_last_error()
+    assert lib.dsa_check_scores(ctypes.byref(v), None, 128, 0, 10, None) == I
+    assert lib.dsa_check_scores(ctypes.byref(v), FAKE, 96, 0, 10, None) == I
+    assert lib.dsa_check_scores(ctypes.byref(v), FAKE, 128, -1, 10, None) == I
+
+
+def test_checked_calls_still_reject_bad_arguments_on_the_host(monkeypatch):
+    """With DSA_CHECK on, host validation still comes first: these calls fail
+    before the device-side checks would run."""
+    monkeypatch.setenv("DSA_CHECK", "1")
+    lib = dsa.load_library()
+    assert call_scores(vl(), d=96) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_topk(ctypes.byref(vl()), FAKE, 64, 0, 10, 64, FAKE, None, 0, None) == \
+        dsa.DSA_ERR_INVALID_ARGUMENT
+    assert lib.dsa_sparse_attn_prefill(ctypes.byref(vl()), FAKE, FAKE, FAKE, FAKE, 0, 0, 5, 32, 4,
+                                       128, 0.088, FAKE, None, None) == dsa.DSA_ERR_UNSUPPORTED
