@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--prefill-streams", type=int, default=1, choices=(1, 2),
+                    help="2: each window's attention on a side stream, overlapping the next "
+                         "window's indexer")
     ap.add_argument("--decode-groups", type=int, default=1,
                     help="decode row groups; more than one alternate between two streams "
                          "(measured slower here: the attention gathers compete with the next "
@@ -194,7 +197,9 @@ def main():
     P, P_host = gen_upload(torch, wl, ("q_idx", "k_idx", "w", "q", "k", "v"),
                            keep_host=not args.no_cpu_baseline)
     vl = dsa.Varlen(wl.cu_q.tolist(), wl.cu_k.tolist())
-    bufs = pipeline.alloc_prefill(vl, wl.topk, args.window)
+    two = args.prefill_streams > 1
+    bufs = pipeline.alloc_prefill(vl, wl.topk, args.window, overlap=two)
+    pside = torch.cuda.Stream() if two else None
     out = torch.empty((wl.total_q, wl.n_heads_q, wl.head_dim), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((wl.total_q, wl.n_heads_q), dtype=torch.float32, device="cuda")
     window = bufs.scores.shape[0]
@@ -218,19 +223,11 @@ def main():
         return torch.cuda.Event(enable_timing=True)
 
     def run_prefill(rec):
-        for r0, n in windows:
-            e = [ev() for _ in range(4)] if rec is not None else None
-            if e: e[0].record(stream)
-            dsa.dsa_index_scores(vl, P["q_idx"], P["k_idx"], P["w"], bufs.scores, row_begin=r0,
-                                 row_count=n)
-            if e: e[1].record(stream)
-            dsa.dsa_topk(vl, bufs.scores, bufs.indices, row_begin=r0, row_count=n)
-            if e: e[2].record(stream)
-            dsa.dsa_sparse_attn_prefill(vl, P["q"], P["k"], P["v"], bufs.indices, out, lse=lse,
-                                        row_begin=r0, row_count=n)
-            if e:
-                e[3].record(stream)
-                rec.append((r0, n, e))
+        # The timed prefill: every window's index_scores -> topk -> attention
+        # (with --prefill-streams 2, each window's attention on a side stream,
+        # overlapping the next window's indexer), events around every call.
+        pipeline.prefill(vl, P["q_idx"], P["k_idx"], P["w"], P["q"], P["k"], P["v"], out, bufs,
+                         lse=lse, stream=stream, side_stream=pside, record=rec)
 
     def run_decode():
         # The timed decode step (with --decode-groups > 1: row groups alternating
@@ -288,9 +285,12 @@ def main():
     pre_ms = sum(m[0].elapsed_time(m[1]) for m in marks)
     dec_ms = sum(m[1].elapsed_time(m[2]) for m in marks) if not args.no_decode else 0.0
     step_ms = (pre_ms + dec_ms) / args.steps
-    idx_ms = sum(e[0].elapsed_time(e[1]) for _, _, e in prec)
-    topk_ms = sum(e[1].elapsed_time(e[2]) for _, _, e in prec)
-    attn_ms = sum(e[2].elapsed_time(e[3]) for _, _, e in prec)
+    def span(e, name):
+        return e[name][0].elapsed_time(e[name][1])
+
+    idx_ms = sum(span(e, "index_scores") for _, _, e in prec)
+    topk_ms = sum(span(e, "topk") for _, _, e in prec)
+    attn_ms = sum(span(e, "sparse_attn") for _, _, e in prec)
     n_idx_launches = len(prec)
 
     pc = prefill_counts(wl)
@@ -340,6 +340,7 @@ def main():
         "prefill": {
             "ms": round(pre_ms / args.steps, 3),
             "tokens_per_s": round(tokens_per_s, 1),
+            "streams": args.prefill_streams,
             "index_scores_ms": round(idx_ms / args.steps, 3),
             "topk_ms": round(topk_ms / args.steps, 3),
             "topk_score_read_GBps": round(pc["b_scores"] / 2 * args.steps / (topk_ms / 1e3) / 1e9, 1),

@@ -2,8 +2,11 @@
 
 Prefill walks the packed query rows in windows so that the fp32 score buffer
 stays bounded: for each window it enqueues dsa_index_scores -> dsa_topk ->
-dsa_sparse_attn_prefill on one stream.  Decode enqueues the same three steps
-for one query per sequence.
+dsa_sparse_attn_prefill.  On one stream the three run in order; with a side
+stream the attention of a window runs there while the next window's indexer
+runs on the main stream (the indexer is bound by the matrix cores, the
+attention by memory, so the two share the chip well).  Decode enqueues the
+same three steps for one query per sequence.
 """
 from __future__ import annotations
 
@@ -27,33 +30,86 @@ def score_ld(max_seqlen_k: int) -> int:
 
 @dataclass
 class PrefillBuffers:
-    scores: object   # fp32 [window, ld]
-    indices: object  # int32 [window, topk]
+    scores: object       # fp32 [window, ld]
+    indices: object      # int32 [window, topk]
+    spare: object = None  # a second int32 [window, topk] for the two-stream schedule
 
 
-def alloc_prefill(vl: Varlen, topk: int, window: int, device="cuda") -> PrefillBuffers:
+def alloc_prefill(vl: Varlen, topk: int, window: int, device="cuda",
+                  overlap: bool = False) -> PrefillBuffers:
+    """Buffers of a windowed prefill; `overlap` adds the second index buffer the
+    two-stream schedule alternates with."""
     torch = _torch()
     window = max(1, min(window, vl.total_q))
     ld = score_ld(vl.max_seqlen_k)
-    return PrefillBuffers(torch.empty((window, ld), dtype=torch.float32, device=device),
-                          torch.empty((window, topk), dtype=torch.int32, device=device))
+    idx = lambda: torch.empty((window, topk), dtype=torch.int32, device=device)  # noqa: E731
+    return PrefillBuffers(torch.empty((window, ld), dtype=torch.float32, device=device), idx(),
+                          idx() if overlap else None)
 
 
 def prefill(vl: Varlen, q_idx, k_idx, w, q, k, v, out, bufs: PrefillBuffers, lse=None,
-            softmax_scale=None, stream=None, keep_indices=None):
-    """Whole prefill path; `keep_indices` (int32 [total_q, topk]) receives a copy
-    of every window's selection when given (tests)."""
+            softmax_scale=None, stream=None, keep_indices=None, side_stream=None, record=None):
+    """Whole prefill path.
+
+    With `side_stream` (and `bufs.spare`), window i's attention runs on the
+    side stream and overlaps window i+1's indexer and top-k on the main
+    stream; the top-k of window i waits until the attention of window i-2 has
+    finished reading the index buffer they share.  The prefill ends on the
+    main stream (`stream`, default the current one) after every window.
+    `keep_indices` (int32 [total_q, topk]) receives every window's selection
+    (tests).  `record`, a list, receives (row_begin, rows, events) per window,
+    events being a dict of (start, end) timing-event pairs around each call:
+    "index_scores" and "topk" on the main stream (the top-k pair starts after
+    its wait for the index buffer), "sparse_attn" on the stream it runs on
+    (starting after its wait for the top-k)."""
+    torch = _torch()
+    main = torch.cuda.current_stream() if stream is None else stream
+    two = side_stream is not None and bufs.spare is not None
+    att = side_stream if two else main
+    if two:
+        side_stream.wait_stream(main)  # inputs written on the main stream
+    ibufs = [bufs.indices, bufs.spare] if two else [bufs.indices]
+    released = [None, None]  # per index buffer: attention done reading it
     window = bufs.scores.shape[0]
-    for r0 in range(0, vl.total_q, window):
+
+    def mark(st):
+        if record is None:
+            return None
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(st)
+        return e
+
+    for i, r0 in enumerate(range(0, vl.total_q, window)):
         n = min(window, vl.total_q - r0)
+        ib = ibufs[i % len(ibufs)]
+        e0 = mark(main)
         dsa_index_scores(vl, q_idx, k_idx, w, bufs.scores, row_begin=r0, row_count=n,
-                         stream=stream)
-        dsa_topk(vl, bufs.scores, bufs.indices, row_begin=r0, row_count=n, stream=stream)
-        dsa_sparse_attn_prefill(vl, q, k, v, bufs.indices, out, lse=lse,
-                                softmax_scale=softmax_scale, row_begin=r0, row_count=n,
-                                stream=stream)
+                         stream=main)
+        e1 = mark(main)
+        if two and released[i % 2] is not None:
+            main.wait_event(released[i % 2])
+        t0 = mark(main)
+        dsa_topk(vl, bufs.scores, ib, row_begin=r0, row_count=n, stream=main)
+        t1 = mark(main)
+        if two:
+            ready = torch.cuda.Event()
+            ready.record(main)
+            att.wait_event(ready)
+        a0 = mark(att)
+        dsa_sparse_attn_prefill(vl, q, k, v, ib, out, lse=lse, softmax_scale=softmax_scale,
+                                row_begin=r0, row_count=n, stream=att)
+        a1 = mark(att)
         if keep_indices is not None:
-            keep_indices[r0:r0 + n].copy_(bufs.indices[:n], non_blocking=True)
+            with torch.cuda.stream(att):
+                keep_indices[r0:r0 + n].copy_(ib[:n], non_blocking=True)
+        if two:
+            released[i % 2] = torch.cuda.Event()
+            released[i % 2].record(att)
+        if record is not None:
+            record.append((r0, n, {"index_scores": (e0, e1), "topk": (t0, t1),
+                                   "sparse_attn": (a0, a1)}))
+    if two:
+        main.wait_stream(side_stream)
 
 
 @dataclass

@@ -396,12 +396,16 @@ def test_bitwise_repeatable():
     host, dev = device_workload(wl)
     vl = varlen_for(wl)
     outs = []
-    for rep in range(3):
-        bufs = pipeline.alloc_prefill(vl, wl.topk, window=800)
+    # Three one-stream runs, then two with each window's attention on a side
+    # stream (overlapping the next window's indexer): all bitwise equal.
+    for rep in range(5):
+        two = rep >= 3
+        bufs = pipeline.alloc_prefill(vl, wl.topk, window=800 if rep < 4 else 256, overlap=two)
         out = torch.zeros((wl.total_q, 32, 128), dtype=torch.bfloat16, device="cuda")
         keep = torch.zeros((wl.total_q, wl.topk), dtype=torch.int32, device="cuda")
         pipeline.prefill(vl, dev["q_idx"], dev["k_idx"], dev["w"], dev["q"], dev["k"], dev["v"],
-                         out, bufs, keep_indices=keep)
+                         out, bufs, keep_indices=keep,
+                         side_stream=torch.cuda.Stream() if two else None)
         torch.cuda.synchronize()
         outs.append((from_dev_bf16(out), keep.cpu().numpy()))
     for o, i in outs[1:]:
