@@ -50,8 +50,17 @@ def _load():
     lib.oracle_sparse_attn.argtypes = [ctypes.c_int, p, p, p, p, p, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                        i64, p, p, ctypes.c_int, p, p]
+    lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_value.restype = ctypes.c_double
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+    lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_quantize_fp8.argtypes = [p, i64, ctypes.c_int, p, p]
+    lib.oracle_dequantize_fp8.argtypes = [p, p, i64, ctypes.c_int, p]
+    lib.oracle_dequantize_fp8.restype = None
+    lib.oracle_index_scores_f64.argtypes = [ctypes.c_int, p, p, p, p, p, ctypes.c_int,
+                                            ctypes.c_int, i64, p, p, i64]
     for f in (lib.oracle_visible_counts, lib.oracle_index_scores, lib.oracle_topk,
-              lib.oracle_sparse_attn):
+              lib.oracle_sparse_attn, lib.oracle_quantize_fp8, lib.oracle_index_scores_f64):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -106,6 +115,72 @@ def index_scores(cu_q, cu_k, q_idx, k_idx, w, rows, ld=None) -> np.ndarray:
     if lib.oracle_index_scores(len(cu_q) - 1, _ptr(cu_q), _ptr(cu_k), _ptr(q_idx),
                                _ptr(k_idx), _ptr(w), n_heads, d, rows.shape[0], _ptr(rows),
                                _ptr(out), ld):
+        raise ValueError("invalid row for the varlen layout")
+    return out
+
+
+# ---- fp8 indexer inputs (declared input transform; the pages state no indexer precision)
+
+def e4m3_value(code: int) -> float:
+    """Value of an OCP e4m3fn code (bias 7, 3 mantissa bits, no infinities,
+    S.1111.111 = NaN)."""
+    return _load().oracle_e4m3_value(int(code))
+
+
+def e4m3_encode(y: float) -> int:
+    """Nearest e4m3fn code: round to nearest, ties to even, saturating at 448."""
+    return int(_load().oracle_e4m3_encode(float(y)))
+
+
+def quantize_fp8(x):
+    """Per-row fp8 quantisation of bf16 bits x [..., d]: codes (uint8, same
+    shape) and scales (float32, shape x.shape[:-1]) with
+    inv = 448 / max|x|, code = e4m3(x * inv), scale = max|x| / 448, each step
+    in binary32 (all-zero rows: codes 0, scale 0)."""
+    lib = _load()
+    x = _bf16_bits(x)
+    d = x.shape[-1]
+    rows = x.size // d
+    codes = np.empty(x.shape, np.uint8)
+    scales = np.empty(x.shape[:-1], np.float32)
+    if lib.oracle_quantize_fp8(_ptr(x), rows, d, _ptr(codes), _ptr(scales)):
+        raise ValueError("non-finite input to the fp8 quantisation")
+    return codes, scales
+
+
+def dequantize_fp8(codes, scales) -> np.ndarray:
+    """Represented values scale * e4m3_value(code) as float64 (exact)."""
+    lib = _load()
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.float32)
+    d = codes.shape[-1]
+    if scales.shape != codes.shape[:-1]:
+        raise ValueError("one scale per row of codes")
+    out = np.empty(codes.shape, np.float64)
+    lib.oracle_dequantize_fp8(_ptr(codes), _ptr(scales), codes.size // d, d, _ptr(out))
+    return out
+
+
+def index_scores_fp8(cu_q, cu_k, q_codes, q_scales, k_codes, k_scales, w, rows,
+                     ld=None) -> np.ndarray:
+    """The indexer score of index_scores() (page 5 section 1) evaluated in
+    float64 on the values the fp8 inputs represent: queries scale[t, h] *
+    value(code) per head, keys scale[s] * value(code)."""
+    lib = _load()
+    cu_q, cu_k = _c(cu_q, np.int32), _c(cu_k, np.int32)
+    rows = _c(rows, np.int64)
+    n_heads, d = q_codes.shape[1], q_codes.shape[2]
+    if k_codes.shape[1] != d or w.shape[1] != n_heads:
+        raise ValueError("indexer shapes disagree")
+    q_rows = dequantize_fp8(np.asarray(q_codes)[rows], np.asarray(q_scales)[rows])
+    k_all = dequantize_fp8(k_codes, k_scales)
+    w = _c(w, np.float32)
+    if ld is None:
+        ld = int(np.max(np.diff(cu_k)))
+    out = np.empty((rows.shape[0], ld), np.float64)
+    if lib.oracle_index_scores_f64(len(cu_q) - 1, _ptr(cu_q), _ptr(cu_k), _ptr(q_rows),
+                                   _ptr(k_all), _ptr(w), n_heads, d, rows.shape[0], _ptr(rows),
+                                   _ptr(out), ld):
         raise ValueError("invalid row for the varlen layout")
     return out
 

@@ -233,3 +233,129 @@ int oracle_sparse_attn(int batch, const int32_t* cu_q, const int32_t* cu_k,
   }
   return bad;
 }
+
+/* ------------------------------------------------------------------------
+ * FP8 indexer inputs (a declared input transform, not on the pages: they
+ * give no indexer precision).  Format: OCP 8-bit floating point, E4M3 variant
+ * ("e4m3fn"): sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
+ * exponent field 0 encodes subnormals m/8 * 2^-6; no infinities; S.1111.111
+ * is NaN, so the largest finite magnitude is 1.75 * 2^8 = 448.
+ *
+ * Quantisation of one vector x of d values (one indexer key, or one head of
+ * one indexer query), with every step an IEEE binary32 operation:
+ *   amax  = max_j |x_j|
+ *   inv   = 448 / amax            (binary32 division)
+ *   c_j   = e4m3(x_j * inv)       (binary32 product, then round to nearest,
+ *                                  ties to even, saturating at +-448)
+ *   scale = amax / 448            (binary32 division)
+ * and x_j is represented by scale * value(c_j).  A vector of zeros gets codes
+ * 0 and scale 0.  The fp8 indexer score is the weighted-ReLU score of these
+ * represented values.
+ * ------------------------------------------------------------------------ */
+
+/* Value of an e4m3fn code (NaN for the two NaN codes). */
+double oracle_e4m3_value(uint8_t code) {
+  int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  if (e == 15 && m == 7) return NAN;
+  double v = e == 0 ? ldexp((double)m, -9) : ldexp(8.0 + m, e - 10);
+  return sign ? -v : v;
+}
+
+/* Nearest e4m3fn code to a finite y: round to nearest, ties to the even
+   mantissa, magnitudes beyond 448 saturate to 448; the sign is kept (so -0.0
+   gives the negative-zero code). */
+uint8_t oracle_e4m3_encode(double y) {
+  uint8_t sign = signbit(y) ? 0x80 : 0;
+  double a = fabs(y);
+  /* Spacing of representable values around a: 2^(e-3) for a in [2^e, 2^(e+1))
+     with e >= -6; subnormals (a < 2^-6) are spaced 2^-9. */
+  int e = a < ldexp(1.0, -6) ? -6 : ilogb(a);
+  double quantum = ldexp(1.0, e - 3);
+  double n = nearbyint(a / quantum); /* a / quantum is exact; default rounding is to even */
+  double v = n * quantum;
+  if (v > 448.0) v = 448.0;
+  /* Code of the representable magnitude v. */
+  uint8_t mag;
+  if (v < ldexp(1.0, -6)) {
+    mag = (uint8_t)(v / ldexp(1.0, -9));
+  } else {
+    int ev = ilogb(v);
+    mag = (uint8_t)(((ev + 7) << 3) | (int)(v / ldexp(1.0, ev) * 8.0 - 8.0));
+  }
+  return sign | mag;
+}
+
+/*
+ * Quantise rows of a bf16 matrix x [rows, d] to codes [rows, d] and scales
+ * [rows] as stated above.  Returns 0, or 1 if an input is not finite.
+ */
+int oracle_quantize_fp8(const uint16_t* x, int64_t rows, int d, uint8_t* codes,
+                        float* scales) {
+  int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+  for (int64_t r = 0; r < rows; ++r) {
+    float amax = 0.0f;
+    for (int j = 0; j < d; ++j) {
+      float v = (float)bf16_to_double(x[r * d + j]);
+      if (!isfinite(v)) bad = 1;
+      if (fabsf(v) > amax) amax = fabsf(v);
+    }
+    if (amax == 0.0f) {
+      for (int j = 0; j < d; ++j) codes[r * d + j] = 0;
+      scales[r] = 0.0f;
+      continue;
+    }
+    volatile float inv = 448.0f / amax;
+    for (int j = 0; j < d; ++j) {
+      volatile float y = (float)bf16_to_double(x[r * d + j]) * inv;
+      codes[r * d + j] = oracle_e4m3_encode((double)y);
+    }
+    volatile float scale = amax / 448.0f;
+    scales[r] = scale;
+  }
+  return bad;
+}
+
+/* Represented values scale[r] * value(codes[r, j]) as doubles (exact). */
+void oracle_dequantize_fp8(const uint8_t* codes, const float* scales, int64_t rows, int d,
+                           double* out) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int j = 0; j < d; ++j)
+      out[r * d + j] = (double)scales[r] * oracle_e4m3_value(codes[r * d + j]);
+}
+
+/*
+ * Indexer scores from real-valued (double) queries and keys, same definition
+ * and conventions as oracle_index_scores:
+ *   q_rows : double [n_rows, n_heads, d]  the queries of the requested rows
+ *   kI     : double [total_k, d]          w : fp32 [total_q, n_heads]
+ */
+int oracle_index_scores_f64(int batch, const int32_t* cu_q, const int32_t* cu_k,
+                            const double* q_rows, const double* kI, const float* w,
+                            int n_heads, int d, int64_t n_rows, const int64_t* rows,
+                            double* scores, int64_t ld) {
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int64_t i = 0; i < n_rows; ++i) {
+    int64_t r = rows[i];
+    double* out = scores + i * ld;
+    for (int64_t s = 0; s < ld; ++s) out[s] = NAN;
+    int b = find_seq(batch, cu_q, r);
+    if (b < 0) { bad = 1; continue; }
+    int64_t p = row_position(cu_q, cu_k, b, r);
+    if (p < 0 || p >= ld) { bad = 1; continue; }
+    const double* q = q_rows + i * (int64_t)n_heads * d;
+    for (int64_t s = 0; s <= p; ++s) {
+      const double* key = kI + (cu_k[b] + s) * d;
+      double total = 0.0;
+      for (int h = 0; h < n_heads; ++h) {
+        double dot = 0.0;
+        for (int j = 0; j < d; ++j) dot += q[h * d + j] * key[j];
+        double relu = dot > 0.0 ? dot : 0.0;
+        total += (double)w[r * n_heads + h] * relu;
+      }
+      out[s] = total + 0.0;
+    }
+  }
+  return bad;
+}

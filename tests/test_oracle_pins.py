@@ -318,3 +318,132 @@ def test_decode_equals_last_prefill_row():
     assert np.array_equal(pre["idx"], dec["idx"])
     assert np.array_equal(pre["out"], dec["out"])
     assert np.array_equal(pre["scores"], dec["scores"])
+
+
+# ---------------------------------------------------------------- fp8 indexer inputs
+
+def _torch_e4m3(values):
+    """torch's float32 -> float8_e4m3fn conversion (round to nearest even)."""
+    t = torch.tensor(np.asarray(values, np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy()
+
+
+def test_e4m3_values_match_torch_and_closed_forms():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    got = np.array([oracle.e4m3_value(c) for c in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.isnan(got).sum() == 2                       # 0x7f and 0xff only
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert oracle.e4m3_value(0x7E) == 448.0               # 1.75 * 2^8
+    assert oracle.e4m3_value(0x38) == 1.0                 # exponent field 7 = bias
+    assert oracle.e4m3_value(0x08) == 2.0 ** -6           # smallest normal
+    assert oracle.e4m3_value(0x01) == 2.0 ** -9           # smallest subnormal
+    assert oracle.e4m3_value(0xC4) == -3.0                # sign, 1.5 * 2^1
+
+
+def test_e4m3_encode_rounding_ties_and_saturation():
+    finite = [c for c in range(256) if c not in (0x7F, 0xFF)]
+    # Every code is its own value's nearest code (the sign of zero kept).
+    assert all(oracle.e4m3_encode(oracle.e4m3_value(c)) == c for c in finite)
+    vals = sorted({oracle.e4m3_value(c) for c in range(0, 0x7F)})
+    mids = [(a + b) / 2 for a, b in zip(vals, vals[1:])]
+    probes = []
+    for m in mids:
+        m32 = np.float32(m)
+        probes += [m32, np.nextafter(m32, np.float32(0)), np.nextafter(m32, np.float32(1e9))]
+    rng = np.random.default_rng(0)
+    probes += list(rng.uniform(-460, 460, 4000).astype(np.float32))
+    probes += list((rng.standard_normal(2000) * 0.01).astype(np.float32))
+    probes = np.array(probes, np.float32)
+    probes = probes[np.abs(probes) < 464]                 # torch turns larger values into NaN
+    got = np.array([oracle.e4m3_encode(float(v)) for v in probes], np.uint8)
+    assert np.array_equal(got, _torch_e4m3(probes))
+    # Ties go to the even mantissa: 1.0625 lies between 1.0 (m=0) and 1.125 (m=1).
+    assert oracle.e4m3_encode(1.0625) == 0x38 and oracle.e4m3_encode(1.1875) == 0x3A
+    for v in (448.5, 463.9, 470.0, 1e6):
+        assert oracle.e4m3_encode(v) == 0x7E and oracle.e4m3_encode(-v) == 0xFE
+
+
+def test_quantize_fp8_definition_and_error_bound():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((40, 128)).astype(np.float32) * rng.uniform(0.01, 30, (40, 1))
+    x[3] = 0.0                                            # all-zero row
+    x[5, :] = 0.0
+    x[5, 17] = -2.5                                       # one non-zero element
+    xb = bf(x)
+    codes, scales = oracle.quantize_fp8(xb)
+    xf = synth.bf16_to_float(xb).astype(np.float32)
+    amax = np.abs(xf).max(axis=1)
+    for r in range(40):
+        if amax[r] == 0:
+            assert scales[r] == 0 and not codes[r].any()
+            continue
+        inv = np.float32(448) / amax[r]                   # binary32 steps, as defined
+        assert np.array_equal(codes[r], _torch_e4m3(xf[r] * inv))
+        assert scales[r] == amax[r] / np.float32(448)
+    assert codes[5, 17] == 0xFE and scales[5] == np.float32(2.5) / np.float32(448)
+    # Error bound of the represented values: half a step of 3 mantissa bits
+    # (relative 2^-4) above 2^-6 * scale, half of 2^-9 * scale below it,
+    # plus the roundings of inv and scale.
+    deq = oracle.dequantize_fp8(codes, scales)
+    err = np.abs(deq - xf.astype(np.float64))
+    bound = np.maximum(np.abs(xf) * 2.0 ** -4, scales[:, None] * 2.0 ** -10) * (1 + 1e-6) + 1e-30
+    assert (err <= bound).all()
+    assert np.abs(deq).max(axis=1)[amax > 0] == pytest.approx(amax[amax > 0], rel=1e-6)
+
+
+def test_index_scores_fp8_equals_bf16_scores_on_exact_inputs():
+    """Vectors whose every entry is a multiple of 0.5 up to 3.5, each holding a
+    +-3.5, quantise losslessly (448 / 3.5 = 128, scale 2^-7): the fp8 score
+    must equal the bf16 score exactly."""
+    rng = np.random.default_rng(2)
+    L, H, d = 70, 5, 64
+    grid = np.arange(-7, 8) * 0.5
+    q = rng.choice(grid, (L, H, d)).astype(np.float32)
+    k = rng.choice(grid, (L, d)).astype(np.float32)
+    q[:, :, 0] = 3.5
+    k[:, 3] = -3.5
+    w = rng.uniform(-1, 2, (L, H)).astype(np.float32)
+    cu = np.array([0, 30, 70], np.int32)
+    qb, kb = bf(q), bf(k)
+    qc, qs = oracle.quantize_fp8(qb)
+    kc, ks = oracle.quantize_fp8(kb)
+    assert (qs == 2.0 ** -7).all() and (ks == 2.0 ** -7).all()
+    rows = np.arange(L)
+    ref = oracle.index_scores(cu, cu, qb, kb, w, rows)
+    got = oracle.index_scores_fp8(cu, cu, qc, qs, kc, ks, w, rows)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+
+
+def test_index_scores_fp8_within_quantisation_bound_of_bf16():
+    """Random inputs: |I_fp8 - I| <= sum_h |w_h| (|dq_h| |k^| + |q_h| |dk|)
+    (ReLU is 1-Lipschitz, Cauchy-Schwarz on each dot product), and the bound
+    is not vacuous (most scores move much less)."""
+    rng = np.random.default_rng(3)
+    L, H, d = 48, 6, 128
+    q = rng.standard_normal((L, H, d)).astype(np.float32)
+    k = (rng.standard_normal((L, d)) + rng.standard_normal((1, d))).astype(np.float32)
+    w = rng.uniform(0, 1, (L, H)).astype(np.float32)
+    cu = np.array([0, L], np.int32)
+    qb, kb = bf(q), bf(k)
+    qc, qs = oracle.quantize_fp8(qb)
+    kc, ks = oracle.quantize_fp8(kb)
+    rows = np.arange(L)
+    ref = oracle.index_scores(cu, cu, qb, kb, w, rows)
+    got = oracle.index_scores_fp8(cu, cu, qc, qs, kc, ks, w, rows)
+    qf, kf = f(qb), f(kb)
+    qd, kd = oracle.dequantize_fp8(qc, qs), oracle.dequantize_fp8(kc, ks)
+    dq = np.linalg.norm(qd - qf, axis=2)                  # [L, H]
+    dk = np.linalg.norm(kd - kf, axis=1)                  # [L]
+    nq = np.linalg.norm(qf, axis=2)
+    nk_hat = np.linalg.norm(kd, axis=1)
+    for t in range(L):
+        bound = (np.abs(w[t])[:, None] * (dq[t][:, None] * nk_hat[None, :t + 1]
+                                          + nq[t][:, None] * dk[None, :t + 1])).sum(axis=0)
+        diff = np.abs(got[t, :t + 1] - ref[t, :t + 1])
+        assert (diff <= bound * (1 + 1e-9)).all()
+        assert np.median(diff) < 0.5 * np.median(bound)
