@@ -105,7 +105,8 @@ typedef struct {
  * Arithmetic: bf16 x bf16 products accumulated in fp32 (MFMA), the ReLU,
  * weighting and head sum in fp32.  Integer-valued inputs whose partial sums
  * stay below 2^24 give exact scores.
- * Supported: d_idx in {64, 128}; 1 <= n_heads_idx <= 64.
+ * Supported: d_idx in {64, 128}; 1 <= n_heads_idx <= 64; one sequence's keys
+ * at most 2 GiB (max_seqlen_k * d_idx * 2 < 2^31).
  * Invalid: null pointers, misaligned bf16 pointers, scores not 16-byte
  * aligned, ld_scores < max_seqlen_k or not a multiple of 4, a window outside
  * [0, total_q).  row_count == 0 is a no-op.
@@ -113,6 +114,40 @@ typedef struct {
 int dsa_index_scores(const dsa_varlen* vl, const void* q_idx, const void* k_idx, const float* w,
                      int32_t n_heads_idx, int32_t d_idx, int64_t row_begin, int64_t row_count,
                      float* scores, int64_t ld_scores, hipStream_t stream);
+
+/*
+ * FP8 indexer inputs.  The pages state no indexer precision; this optional
+ * variant holds indexer queries and keys as 8-bit floats (OCP E4M3,
+ * "e4m3fn": bias 7, 3 mantissa bits, largest magnitude 448, no infinities)
+ * with one binary32 scale per vector of d_idx values:
+ *   x_j  ~  scale * value(c_j),   scale = amax / 448,   amax = max_j |x_j|.
+ *
+ * dsa_quantize_fp8 -- x bf16 [rows, dim] -> codes uint8 [rows, dim] and
+ *   scales fp32 [rows]; every step binary32: inv = 448 / amax (correctly
+ *   rounded), c_j = value x_j * inv rounded to the nearest e4m3 value, ties to
+ *   even, saturating at +-448; scale = amax / 448.  A row of zeros gets codes 0
+ *   and scale 0.  Inputs must be finite.  Supported: dim in {64, 128}.
+ *   Invalid: null pointers, x not 16-byte aligned, codes not 16-byte aligned,
+ *   rows < 0.  Queries are quantised per head: x = q_idx viewed as
+ *   [total_q * n_heads_idx, d_idx].
+ *
+ * dsa_index_scores_fp8 -- the indexer score of dsa_index_scores on the values
+ *   the codes represent:
+ *     q_codes uint8 [total_q, n_heads_idx, d_idx],  q_scales fp32 [total_q, n_heads_idx]
+ *     k_codes uint8 [total_k, d_idx],               k_scales fp32 [total_k]
+ *     I[t, s] = k_scale[s] * sum_h (w[t,h] q_scale[t,h]) max(0, codes_q[t,h] . codes_k[s])
+ *   (equal to the plain definition because scales are non-negative).  Code
+ *   products are exact; the MFMA sums them in fp32; the weighting and head
+ *   sum are fp32.  Window, scores layout, support and errors as
+ *   dsa_index_scores, with code pointers 16-byte aligned and scale pointers
+ *   4-byte aligned; one sequence's key codes at most 2 GiB.
+ */
+int dsa_quantize_fp8(const void* x, int64_t rows, int32_t dim, uint8_t* codes, float* scales,
+                     hipStream_t stream);
+int dsa_index_scores_fp8(const dsa_varlen* vl, const uint8_t* q_codes, const float* q_scales,
+                         const uint8_t* k_codes, const float* k_scales, const float* w,
+                         int32_t n_heads_idx, int32_t d_idx, int64_t row_begin, int64_t row_count,
+                         float* scores, int64_t ld_scores, hipStream_t stream);
 
 /* Workspace bytes dsa_topk needs for this call shape (0: it needs none). */
 int dsa_topk_workspace_size(const dsa_varlen* vl, int64_t row_count, int32_t k, size_t* bytes);

@@ -10,6 +10,7 @@ Entry points (same names as the C ABI):
     dsa_index_scores, dsa_topk, dsa_topk_workspace_size,
     dsa_sparse_attn_prefill, dsa_sparse_attn_decode,
     dsa_sparse_attn_decode_workspace_size,
+    dsa_quantize_fp8, dsa_index_scores_fp8 (the optional fp8 indexer),
     dsa_check_varlen, dsa_check_indices, dsa_check_scores (device-side
     precondition checks; the entry points also run them when the environment
     variable DSA_CHECK is set to anything but "" or "0")
@@ -27,6 +28,7 @@ EXPORTED = (
     "dsa_status_string", "dsa_last_error", "dsa_index_scores", "dsa_topk_workspace_size",
     "dsa_topk", "dsa_sparse_attn_prefill", "dsa_sparse_attn_decode_workspace_size",
     "dsa_sparse_attn_decode", "dsa_check_varlen", "dsa_check_indices", "dsa_check_scores",
+    "dsa_quantize_fp8", "dsa_index_scores_fp8",
 )
 
 DSA_OK = 0
@@ -81,6 +83,8 @@ def load_library(path: str = LIB_PATH):
     lib.dsa_sparse_attn_decode_workspace_size.argtypes = [vl, i64, i32, i32, i32, sz]
     lib.dsa_sparse_attn_decode.argtypes = [vl, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, f32,
                                            vp, vp, vp, ctypes.c_size_t, vp]
+    lib.dsa_quantize_fp8.argtypes = [vp, i64, i32, vp, vp, vp]
+    lib.dsa_index_scores_fp8.argtypes = [vl, vp, vp, vp, vp, vp, i32, i32, i64, i64, vp, i64, vp]
     lib.dsa_check_varlen.argtypes = [vl, vp]
     lib.dsa_check_indices.argtypes = [vl, vp, i32, i64, i64, vp]
     lib.dsa_check_scores.argtypes = [vl, vp, i64, i64, i64, vp]
@@ -177,6 +181,39 @@ def dsa_index_scores(vl: Varlen, q_idx, k_idx, w, scores, row_begin: int = 0,
     _check(load_library().dsa_index_scores(
         vl.struct, _ptr(q_idx), _ptr(k_idx), _ptr(w), q_idx.shape[1], q_idx.shape[2], row_begin,
         row_count, _ptr(scores), scores.shape[1], _stream(stream)))
+
+
+def dsa_quantize_fp8(x, codes, scales, stream=None):
+    """bf16 x [..., d] -> e4m3 codes (uint8, same shape) and one fp32 scale per
+    vector of d values (scales shape x.shape[:-1])."""
+    torch = _torch()
+    _need(x, "x", torch.bfloat16)
+    _need(codes, "codes", torch.uint8)
+    _need(scales, "scales", torch.float32)
+    d = x.shape[-1]
+    if tuple(codes.shape) != tuple(x.shape) or tuple(scales.shape) != tuple(x.shape[:-1]):
+        raise TypeError("codes must match x and scales must be x.shape[:-1]")
+    _check(load_library().dsa_quantize_fp8(_ptr(x), x.numel() // d, d, _ptr(codes), _ptr(scales),
+                                           _stream(stream)))
+
+
+def dsa_index_scores_fp8(vl: Varlen, q_codes, q_scales, k_codes, k_scales, w, scores,
+                         row_begin: int = 0, row_count: int | None = None, stream=None):
+    """Indexer scores from fp8 codes (q_codes uint8 [total_q, H, d], q_scales
+    fp32 [total_q, H], k_codes uint8 [total_k, d], k_scales fp32 [total_k]) for
+    rows [row_begin, row_begin + row_count) into scores (fp32 [row_count, ld])."""
+    torch = _torch()
+    _need(q_codes, "q_codes", torch.uint8, 3)
+    _need(q_scales, "q_scales", torch.float32, 2)
+    _need(k_codes, "k_codes", torch.uint8, 2)
+    _need(k_scales, "k_scales", torch.float32, 1)
+    _need(w, "w", torch.float32, 2)
+    _need(scores, "scores", torch.float32, 2)
+    row_count = scores.shape[0] if row_count is None else row_count
+    _check(load_library().dsa_index_scores_fp8(
+        vl.struct, _ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), _ptr(w),
+        q_codes.shape[1], q_codes.shape[2], row_begin, row_count, _ptr(scores), scores.shape[1],
+        _stream(stream)))
 
 
 def dsa_topk_workspace_size(vl: Varlen, row_count: int, k: int) -> int:

@@ -33,6 +33,7 @@ COMMON_FLAGS = [
 # head x key).
 FILE_FLAGS = {
     "index_scores.hip": ["-fno-honor-nans"],
+    "index_scores_fp8.hip": ["-fno-honor-nans"],
 }
 
 

@@ -92,6 +92,21 @@ int check_attn_extent(const dsa_varlen* vl, int32_t hkv, int32_t d) {
   return DSA_OK;
 }
 
+// The indexer kernels address one sequence's keys with 32-bit byte offsets.
+int check_index_extent(const dsa_varlen* vl, int32_t d, int elem_bytes) {
+  if (static_cast<int64_t>(vl->max_seqlen_k) * d * elem_bytes > INT32_MAX)
+    return fail(DSA_ERR_UNSUPPORTED, "one sequence's indexer keys exceed 2 GiB (max_seqlen_k %d)",
+                vl->max_seqlen_k);
+  return DSA_OK;
+}
+
+int check_index_shape(int32_t n_heads_idx, int32_t d_idx) {
+  if (d_idx != 64 && d_idx != 128) return fail(DSA_ERR_UNSUPPORTED, "d_idx %d not in {64, 128}", d_idx);
+  if (n_heads_idx < 1 || n_heads_idx > 64)
+    return fail(DSA_ERR_UNSUPPORTED, "n_heads_idx %d not in 1..64", n_heads_idx);
+  return DSA_OK;
+}
+
 int hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
@@ -187,15 +202,53 @@ int dsa_index_scores(const dsa_varlen* vl, const void* q_idx, const void* k_idx,
   if ((st = check_bf16(k_idx, "k_idx"))) return st;
   if (w == nullptr || !aligned(w, 4)) return fail(DSA_ERR_INVALID_ARGUMENT, "w is NULL or misaligned");
   if ((st = check_scores(vl, scores, ld_scores))) return st;
-  if (d_idx != 64 && d_idx != 128) return fail(DSA_ERR_UNSUPPORTED, "d_idx %d not in {64, 128}", d_idx);
-  if (n_heads_idx < 1 || n_heads_idx > 64)
-    return fail(DSA_ERR_UNSUPPORTED, "n_heads_idx %d not in 1..64", n_heads_idx);
+  if ((st = check_index_shape(n_heads_idx, d_idx))) return st;
+  if ((st = check_index_extent(vl, d_idx, 2))) return st;
   if (checks_enabled() && (st = device_offsets(vl, stream))) return st;
   if (row_count == 0) return ok();
   return hip_status(dsa::launch_index_scores(*vl, static_cast<const uint16_t*>(q_idx),
                                              static_cast<const uint16_t*>(k_idx), w, n_heads_idx,
                                              d_idx, row_begin, row_count, scores, ld_scores, stream),
                     "index_scores launch");
+}
+
+int dsa_quantize_fp8(const void* x, int64_t rows, int32_t dim, uint8_t* codes, float* scales,
+                     hipStream_t stream) {
+  int st;
+  if ((st = check_bf16(x, "x"))) return st;
+  if (codes == nullptr || !aligned(codes, 16))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "codes is NULL or not 16-byte aligned");
+  if (scales == nullptr || !aligned(scales, 4))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "scales is NULL or misaligned");
+  if (rows < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "rows < 0");
+  if (dim != 64 && dim != 128) return fail(DSA_ERR_UNSUPPORTED, "dim %d not in {64, 128}", dim);
+  if (rows == 0) return ok();
+  return hip_status(dsa::launch_quantize_fp8(static_cast<const uint16_t*>(x), rows, dim, codes,
+                                             scales, stream),
+                    "quantize_fp8 launch");
+}
+
+int dsa_index_scores_fp8(const dsa_varlen* vl, const uint8_t* q_codes, const float* q_scales,
+                         const uint8_t* k_codes, const float* k_scales, const float* w,
+                         int32_t n_heads_idx, int32_t d_idx, int64_t row_begin, int64_t row_count,
+                         float* scores, int64_t ld_scores, hipStream_t stream) {
+  int st;
+  if ((st = check_varlen(vl))) return st;
+  if ((st = check_window(vl, row_begin, row_count))) return st;
+  if (q_codes == nullptr || !aligned(q_codes, 16) || k_codes == nullptr || !aligned(k_codes, 16))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "q_codes / k_codes NULL or not 16-byte aligned");
+  if (q_scales == nullptr || !aligned(q_scales, 4) || k_scales == nullptr || !aligned(k_scales, 4))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "q_scales / k_scales NULL or misaligned");
+  if (w == nullptr || !aligned(w, 4)) return fail(DSA_ERR_INVALID_ARGUMENT, "w is NULL or misaligned");
+  if ((st = check_scores(vl, scores, ld_scores))) return st;
+  if ((st = check_index_shape(n_heads_idx, d_idx))) return st;
+  if ((st = check_index_extent(vl, d_idx, 1))) return st;
+  if (checks_enabled() && (st = device_offsets(vl, stream))) return st;
+  if (row_count == 0) return ok();
+  return hip_status(dsa::launch_index_scores_fp8(*vl, q_codes, q_scales, k_codes, k_scales, w,
+                                                 n_heads_idx, d_idx, row_begin, row_count, scores,
+                                                 ld_scores, stream),
+                    "index_scores_fp8 launch");
 }
 
 int dsa_topk_workspace_size(const dsa_varlen* vl, int64_t row_count, int32_t k, size_t* bytes) {

@@ -49,6 +49,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// s_waitcnt immediate: vmcnt(n), expcnt and lgkmcnt left unconstrained.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+
+// Workgroup barrier for LDS hand-off.  The waits it needs are explicit
+// (s_waitcnt before it); the wavefront-scope fences only keep the compiler
+// from moving LDS accesses across it, without the vmcnt(0) a workgroup
+// fence would add (that would also wait for outstanding global stores).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Sequence owning packed query row `row` (cu_q non-decreasing, cu_q[0] == 0).
 __device__ __forceinline__ int find_sequence(const int32_t* __restrict__ cu_q, int batch,
                                              int64_t row) {

@@ -13,6 +13,17 @@ hipError_t launch_index_scores(const dsa_varlen& vl, const uint16_t* q_idx, cons
                                const float* w, int n_heads, int d, int64_t row_begin,
                                int64_t row_count, float* scores, int64_t ld, hipStream_t stream);
 
+// Indexer scores from fp8 (e4m3) codes with one scale per query head and
+// per key.
+hipError_t launch_index_scores_fp8(const dsa_varlen& vl, const uint8_t* q8, const float* q_scale,
+                                   const uint8_t* k8, const float* k_scale, const float* w,
+                                   int n_heads, int d, int64_t row_begin, int64_t row_count,
+                                   float* scores, int64_t ld, hipStream_t stream);
+
+// bf16 vectors of d values -> e4m3 codes and one binary32 scale per vector.
+hipError_t launch_quantize_fp8(const uint16_t* x, int64_t rows, int d, uint8_t* codes,
+                               float* scales, hipStream_t stream);
+
 // Per-row top-k; rows of the window in [row_begin, row_begin + row_count).
 hipError_t launch_topk(const dsa_varlen& vl, const float* scores, int64_t ld, int64_t row_begin,
                        int64_t row_count, int k, int32_t* indices, hipStream_t stream);

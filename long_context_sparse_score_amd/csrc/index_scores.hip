@@ -142,19 +142,6 @@ __device__ void row_direct(const RowState<D, MT>& st, const uint16_t* __restrict
 
 // ---------------------------------------------------------------- prefill kernel
 
-// s_waitcnt immediate: vmcnt(n), expcnt and lgkmcnt left unconstrained.
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
-
-// Workgroup barrier for LDS hand-off.  The waits it needs are explicit
-// (s_waitcnt before it); the wavefront-scope fences only keep the compiler
-// from moving LDS accesses across it, without the vmcnt(0) a workgroup
-// fence would add (that would also wait for this stage's score stores).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 template <int D, int MT>
 __global__ __launch_bounds__(kBlockRows * kWave, 2) void index_scores_block(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,

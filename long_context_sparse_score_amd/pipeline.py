@@ -12,9 +12,9 @@ from __future__ import annotations
 
 from dataclasses import dataclass
 
-from . import (Varlen, dsa_index_scores, dsa_sparse_attn_decode,
-               dsa_sparse_attn_decode_workspace_size, dsa_sparse_attn_prefill, dsa_topk,
-               dsa_topk_workspace_size)
+from . import (Varlen, dsa_index_scores, dsa_index_scores_fp8, dsa_quantize_fp8,
+               dsa_sparse_attn_decode, dsa_sparse_attn_decode_workspace_size,
+               dsa_sparse_attn_prefill, dsa_topk, dsa_topk_workspace_size)
 
 
 def _torch():
@@ -26,6 +26,43 @@ def _torch():
 def score_ld(max_seqlen_k: int) -> int:
     """Leading dimension of a score buffer: a multiple of 64 floats (256 B)."""
     return (max_seqlen_k + 63) // 64 * 64
+
+
+@dataclass
+class Fp8Indexer:
+    """Indexer inputs as e4m3 codes with one scale per vector (the optional fp8
+    indexer)."""
+    q_codes: object   # uint8 [total_q, n_heads_idx, d_idx]
+    q_scales: object  # fp32 [total_q, n_heads_idx]
+    k_codes: object   # uint8 [total_k, d_idx]
+    k_scales: object  # fp32 [total_k]
+
+
+def alloc_fp8_indexer(total_q: int, total_k: int, n_heads_idx: int, d_idx: int,
+                      device="cuda") -> Fp8Indexer:
+    torch = _torch()
+    return Fp8Indexer(
+        torch.empty((total_q, n_heads_idx, d_idx), dtype=torch.uint8, device=device),
+        torch.empty((total_q, n_heads_idx), dtype=torch.float32, device=device),
+        torch.empty((total_k, d_idx), dtype=torch.uint8, device=device),
+        torch.empty((total_k,), dtype=torch.float32, device=device))
+
+
+def quantize_queries(q_idx, fp8: Fp8Indexer, stream=None):
+    dsa_quantize_fp8(q_idx, fp8.q_codes, fp8.q_scales, stream=stream)
+
+
+def quantize_keys(k_idx, fp8: Fp8Indexer, stream=None):
+    dsa_quantize_fp8(k_idx, fp8.k_codes, fp8.k_scales, stream=stream)
+
+
+def _scores(vl, q_idx, k_idx, w, scores, fp8, row_begin, row_count, stream):
+    if fp8 is None:
+        dsa_index_scores(vl, q_idx, k_idx, w, scores, row_begin=row_begin, row_count=row_count,
+                         stream=stream)
+    else:
+        dsa_index_scores_fp8(vl, fp8.q_codes, fp8.q_scales, fp8.k_codes, fp8.k_scales, w, scores,
+                             row_begin=row_begin, row_count=row_count, stream=stream)
 
 
 @dataclass
@@ -48,8 +85,13 @@ def alloc_prefill(vl: Varlen, topk: int, window: int, device="cuda",
 
 
 def prefill(vl: Varlen, q_idx, k_idx, w, q, k, v, out, bufs: PrefillBuffers, lse=None,
-            softmax_scale=None, stream=None, keep_indices=None, side_stream=None, record=None):
+            softmax_scale=None, stream=None, keep_indices=None, side_stream=None, record=None,
+            fp8: Fp8Indexer | None = None):
     """Whole prefill path.
+
+    With `fp8` (buffers from alloc_fp8_indexer) the indexer queries and keys
+    are first quantised into it and every window's scores come from the fp8
+    indexer.
 
     With `side_stream` (and `bufs.spare`), window i's attention runs on the
     side stream and overlaps window i+1's indexer and top-k on the main
@@ -71,6 +113,9 @@ def prefill(vl: Varlen, q_idx, k_idx, w, q, k, v, out, bufs: PrefillBuffers, lse
     ibufs = [bufs.indices, bufs.spare] if two else [bufs.indices]
     released = [None, None]  # per index buffer: attention done reading it
     window = bufs.scores.shape[0]
+    if fp8 is not None:
+        quantize_queries(q_idx, fp8, stream=main)
+        quantize_keys(k_idx, fp8, stream=main)
 
     def mark(st):
         if record is None:
@@ -83,8 +128,7 @@ def prefill(vl: Varlen, q_idx, k_idx, w, q, k, v, out, bufs: PrefillBuffers, lse
         n = min(window, vl.total_q - r0)
         ib = ibufs[i % len(ibufs)]
         e0 = mark(main)
-        dsa_index_scores(vl, q_idx, k_idx, w, bufs.scores, row_begin=r0, row_count=n,
-                         stream=main)
+        _scores(vl, q_idx, k_idx, w, bufs.scores, fp8, r0, n, main)
         e1 = mark(main)
         if two and released[i % 2] is not None:
             main.wait_event(released[i % 2])
@@ -141,8 +185,13 @@ def alloc_decode(vl: Varlen, n_heads_q: int, head_dim: int, topk: int, groups: i
 
 
 def decode(vl: Varlen, q_idx, k_idx_cache, w, q, k_cache, v_cache, out, bufs: DecodeBuffers,
-           lse=None, softmax_scale=None, stream=None, side_stream=None):
+           lse=None, softmax_scale=None, stream=None, side_stream=None,
+           fp8: Fp8Indexer | None = None):
     """One decode step: index scores -> top-k -> sparse attention per row group.
+
+    With `fp8`, the indexer key cache is the one held in fp8.k_codes /
+    fp8.k_scales (quantised when its tokens were appended, see quantize_keys;
+    k_idx_cache is not read) and the step quantises its new indexer queries.
 
     The indexer streams the whole key cache and keeps HBM busy; the top-k and
     the attention of a group do not.  With a side stream the groups alternate
@@ -153,6 +202,8 @@ def decode(vl: Varlen, q_idx, k_idx_cache, w, q, k_cache, v_cache, out, bufs: De
     torch = _torch()
     main = torch.cuda.current_stream() if stream is None else stream
     streams = [main] if side_stream is None or len(bufs.groups) == 1 else [main, side_stream]
+    if fp8 is not None:
+        quantize_queries(q_idx, fp8, stream=main)
     if len(streams) > 1:
         side_stream.wait_stream(main)  # inputs written on the main stream
     prev_idx = None
@@ -160,8 +211,7 @@ def decode(vl: Varlen, q_idx, k_idx_cache, w, q, k_cache, v_cache, out, bufs: De
         st = streams[i % len(streams)]
         if prev_idx is not None and len(streams) > 1:
             st.wait_event(prev_idx)
-        dsa_index_scores(vl, q_idx, k_idx_cache, w, bufs.scores[r0:r0 + n], row_begin=r0,
-                         row_count=n, stream=st)
+        _scores(vl, q_idx, k_idx_cache, w, bufs.scores[r0:r0 + n], fp8, r0, n, st)
         if len(streams) > 1:
             prev_idx = torch.cuda.Event()
             prev_idx.record(st)

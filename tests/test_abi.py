@@ -218,3 +218,43 @@ def test_checked_calls_still_reject_bad_arguments_on_the_host(monkeypatch):
         dsa.DSA_ERR_INVALID_ARGUMENT
     assert lib.dsa_sparse_attn_prefill(ctypes.byref(vl()), FAKE, FAKE, FAKE, FAKE, 0, 0, 5, 32, 4,
                                        128, 0.088, FAKE, None, None) == dsa.DSA_ERR_UNSUPPORTED
+
+
+def test_fp8_entry_points_validate_on_the_host():
+    lib = dsa.load_library()
+    I, U = dsa.DSA_ERR_INVALID_ARGUMENT, dsa.DSA_ERR_UNSUPPORTED
+    q = lib.dsa_quantize_fp8
+    assert q(FAKE, 0, 128, FAKE, FAKE, None) == dsa.DSA_OK          # nothing to do
+    assert q(None, 10, 128, FAKE, FAKE, None) == I
+    assert q(FAKE + 2, 10, 128, FAKE, FAKE, None) == I
+    assert q(FAKE, 10, 128, FAKE + 8, FAKE, None) == I              # codes 16-byte aligned
+    assert q(FAKE, 10, 128, FAKE, FAKE + 2, None) == I
+    assert q(FAKE, -1, 128, FAKE, FAKE, None) == I
+    assert q(FAKE, 10, 96, FAKE, FAKE, None) == U
+
+    def s8(v=None, qc=FAKE, qs=FAKE, kc=FAKE, ks=FAKE, w=FAKE, heads=64, d=128, rb=0, rc=10,
+           sc=FAKE, ld=128):
+        v = vl() if v is None else v
+        return lib.dsa_index_scores_fp8(ctypes.byref(v), qc, qs, kc, ks, w, heads, d, rb, rc, sc,
+                                        ld, None)
+    assert s8(rc=0) == dsa.DSA_OK
+    assert s8(qc=FAKE + 8) == I
+    assert s8(kc=None) == I
+    assert s8(ks=FAKE + 1) == I
+    assert s8(w=None) == I
+    assert s8(ld=96) == I
+    assert s8(rb=95) == I
+    assert s8(d=32) == U
+    assert s8(heads=65) == U
+    # One sequence's key codes beyond 2 GiB: 20M keys x 128 bytes.
+    big = vl(total_q=1, total_k=20_000_000, max_q=1, max_k=20_000_000)
+    assert s8(v=big, rc=1, ld=20_000_000) == U
+
+
+def test_index_scores_key_extent_limit():
+    """The bf16 indexer addresses one sequence's keys with 32-bit offsets:
+    9M keys x 128 x 2 bytes pass 2 GiB and are refused on the host."""
+    big = vl(total_q=1, total_k=9_000_000, max_q=1, max_k=9_000_000)
+    assert call_scores(big, rc=1, ld=9_000_000) == dsa.DSA_ERR_UNSUPPORTED
+    ok_size = vl(total_q=1, total_k=8_000_000, max_q=1, max_k=8_000_000)
+    assert call_scores(ok_size, rc=0, ld=8_000_000) == dsa.DSA_OK
