@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 
 
 def log(msg):
@@ -51,6 +52,8 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the optional fp8-indexer variant (reported beside the headline)")
     ap.add_argument("--prefill-streams", type=int, default=1, choices=(1, 2),
                     help="2: each window's attention on a side stream, overlapping the next "
                          "window's indexer")
@@ -113,6 +116,21 @@ def window_flops(wl, r0, n):
     """Indexer flops of packed rows [r0, r0 + n) of a single-sequence prefill."""
     pairs = sum(p + 1 for p in range(r0, r0 + n))
     return pairs * 2 * wl.n_heads_idx * wl.d_idx
+
+
+def decode_bytes_fp8(wd):
+    """Bytes per decode query with the fp8 indexer: the key cache is e4m3 codes
+    plus one fp32 scale per key; the new queries are quantised in the step."""
+    N = wd.seqlens_k[0]
+    k = min(wd.topk, N)
+    per = (N * (wd.d_idx + 4)                              # indexer key codes + scales
+           + k * 2 * wd.n_heads_kv * wd.head_dim * 2       # gathered K and V rows
+           + N * 4 * 2                                     # score write + read
+           + wd.topk * 4 * 2                               # indices write + read
+           + wd.n_heads_idx * wd.d_idx * (2 + 1 + 1)       # qI read, codes write + read
+           + wd.n_heads_idx * 4 * 3                        # w, query scales write + read
+           + 2 * wd.n_heads_q * wd.head_dim * 2)           # q, out
+    return per * wd.batch, per
 
 
 def decode_bytes(wd):
@@ -393,6 +411,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if not args.no_fp8:
+        result["fp8_indexer"] = fp8_variant(torch, pipeline, args, stream, wl, vl, P, out, lse,
+                                            None if args.no_decode else (wd, vd, D, dout, dlse))
+
     if not args.no_dense:
         result["dense"] = dense_comparator(torch, P, wl, args, pre_ms / args.steps)
 
@@ -401,6 +423,81 @@ def main():
         result["cpu_baseline"] = cpu_baseline(wl, P_host, args.cpu_rows)
 
     print(json.dumps(result), flush=True)
+
+
+def fp8_variant(torch, pipeline, args, stream, wl, vl, P, out, lse, dec):
+    """The same prefill and decode steps with the optional fp8 indexer
+    (e4m3 codes, one scale per vector).  Not the headline: the configuration's
+    indexer is bf16.  Prefill steps include quantising qI and kI; the decode
+    key cache is quantised once beforehand (as it would be when tokens are
+    appended) and each step quantises its new queries."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    res = {"note": "optional fp8 (e4m3, per-vector scales) indexer variant; the workload's "
+                   "indexer is bf16, so this is reported beside the headline, not as it"}
+    bufs = pipeline.alloc_prefill(vl, wl.topk, args.window)
+    fp8 = pipeline.alloc_fp8_indexer(wl.total_q, wl.total_k, wl.n_heads_idx, wl.d_idx)
+    run = lambda rec: pipeline.prefill(vl, P["q_idx"], P["k_idx"], P["w"], P["q"], P["k"],  # noqa: E731
+                                       P["v"], out, bufs, lse=lse, stream=stream, record=rec,
+                                       fp8=fp8)
+    log("fp8 indexer: prefill")
+    for _ in range(args.warmup):
+        run(None)
+    torch.cuda.synchronize()
+    rec, marks = [], []
+    for _ in range(args.steps):
+        m0, m1 = ev(), ev()
+        m0.record(stream)
+        n0 = len(rec)
+        run(rec)
+        m1.record(stream)
+        marks.append((m0, m1, n0))
+        torch.cuda.synchronize()
+    pre_ms = sum(a.elapsed_time(b) for a, b, _ in marks) / args.steps
+    quant_ms = sum(a.elapsed_time(rec[n0][2]["index_scores"][0]) for a, _, n0 in marks) / args.steps
+    span = lambda name: sum(e[name][0].elapsed_time(e[name][1]) for _, _, e in rec) / args.steps  # noqa: E731
+    idx_ms = span("index_scores")
+    pc = prefill_counts(wl)
+    tflops = pc["f_idx"] / (idx_ms / 1e3) / 1e12
+    res["prefill"] = {
+        "ms": round(pre_ms, 3), "tokens_per_s": round(wl.total_q / (pre_ms / 1e3), 1),
+        "quantize_ms": round(quant_ms, 3), "index_scores_ms": round(idx_ms, 3),
+        "topk_ms": round(span("topk"), 3), "sparse_attn_ms": round(span("sparse_attn"), 3),
+        "roofline": {"bound": "mfma", "kernel": "index_scores_fp8 (prefill)",
+                     "achieved": round(tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_FP8_TFLOPS, 4),
+                     "avg_launch_ms": round(idx_ms / max(1, len(rec) // args.steps), 3)},
+    }
+    del bufs, fp8
+    if dec is not None:
+        wd, vd, D, dout, dlse = dec
+        dbufs = pipeline.alloc_decode(vd, wd.n_heads_q, wd.head_dim, wd.topk)
+        fp8d = pipeline.alloc_fp8_indexer(wd.total_q, wd.total_k, wd.n_heads_idx, wd.d_idx)
+        pipeline.quantize_keys(D["k_idx"], fp8d, stream=stream)
+        step = lambda: pipeline.decode(vd, D["q_idx"], None, D["w"], D["q"], D["k"], D["v"],  # noqa: E731
+                                       dout, dbufs, lse=dlse, stream=stream, fp8=fp8d)
+        log("fp8 indexer: decode")
+        for _ in range(max(1, args.warmup)):
+            step()
+        torch.cuda.synchronize()
+        tot = 0.0
+        for _ in range(args.steps):
+            a, b = ev(), ev()
+            a.record(stream)
+            step()
+            b.record(stream)
+            torch.cuda.synchronize()
+            tot += a.elapsed_time(b)
+        ms = tot / args.steps
+        b_dec, per_q = decode_bytes_fp8(wd)
+        gbs = b_dec / (ms / 1e3) / 1e9
+        res["decode"] = {"ms": round(ms, 4), "queries_per_s": round(wd.batch / (ms / 1e3), 1),
+                         "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                      "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                      "bytes_per_query": per_q}}
+        del dbufs, fp8d
+    torch.cuda.empty_cache()
+    return res
 
 
 def device_info(torch):

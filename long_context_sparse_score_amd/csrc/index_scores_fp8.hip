@@ -17,7 +17,8 @@
 // one MFMA covering 64 of the d_idx products instead of 16, so a 32-key tile
 // of 64 heads at d_idx = 128 is 4 MFMAs.  Key tiles arrive by buffer->LDS DMA
 // with the same XOR swizzle of 16-byte chunks; the key scales travel with
-// them, and each tile's scale is read with its B fragments.
+// them, and each tile's scale is read with its B fragments.  The LDS swizzle
+// differs from the bf16 kernels' because a key row is half as long.
 #include "dsa_common.h"
 #include "dsa_internal.h"
 
@@ -28,9 +29,19 @@ namespace {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kBlockRows8 = 8;    // query rows (waves) per prefill workgroup
-constexpr int kStageKeys8 = 256;  // keys per LDS stage
+constexpr int kStageKeys8 = 512;  // keys per LDS stage
 constexpr int kStreamRows8 = 4;   // waves per decode workgroup
 constexpr int kRing8 = 4;         // 32-key tiles in a decode wave's LDS ring
+
+// LDS layout of a key tile: 16-byte chunk s of key row r sits in slot
+// s ^ swz(r).  LDS serves 16 lanes (256 bytes, all 64 banks) per cycle; rows
+// are D bytes, so 256 / D consecutive rows share one bank pattern and the
+// swizzle must differ between rows 256 / D apart: swz(r) = (r / (256 / D)) mod
+// (D / 16).  The 16 rows read together then cover all 64 banks once.
+template <int D>
+__host__ __device__ constexpr int swz(int r) {
+  return (r / (256 / D)) & (D / 16 - 1);
+}
 
 __device__ __forceinline__ i32x8 join(u32x4 lo, u32x4 hi) {
   return i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
@@ -156,7 +167,7 @@ __global__ __launch_bounds__(kBlockRows8 * kWave, 2) void index_scores_fp8_block
   constexpr int TILES = kStageKeys8 / 32;
   static_assert(TILES % 2 == 0 && DMA_PER_WAVE * kBlockRows8 * kWave == kStageKeys8 * CHUNKS,
                 "stage shape");
-  static_assert(kStageKeys8 == 4 * kWave, "four waves carry a stage's key scales");
+  static_assert(kStageKeys8 == kBlockRows8 * kWave, "every lane carries one key scale");
   __shared__ __attribute__((aligned(16))) uint8_t tile[2][kStageKeys8 * D];
   __shared__ float tscale[2][kStageKeys8];
 
@@ -195,12 +206,13 @@ __global__ __launch_bounds__(kBlockRows8 * kWave, 2) void index_scores_fp8_block
   const __amdgpu_buffer_rsrc_t outs = raw_buffer(out_row, my_end * 4);
 
   // Stage fill: DMA instruction i of a wave writes 64 consecutive 16-byte LDS
-  // chunks; LDS chunk (key, s) receives global chunk s ^ (key & (CHUNKS - 1)).
-  // Waves 0..3 also copy the stage's 256 key scales (4 bytes per lane).
+  // chunks; LDS chunk (key, s) receives global chunk s ^ swz(key).  Every
+  // lane also copies one of the stage's key scales (4 bytes).
   constexpr int KPI = kBlockRows8 * kWave / CHUNKS;
-  static_assert(KPI % CHUNKS == 0, "the swizzle must repeat across DMA instructions");
+  static_assert((KPI / (256 / D)) % CHUNKS == 0 && KPI % (256 / D) == 0,
+                "the swizzle must repeat across DMA instructions");
   const int key0 = (wave * kWave + lane) / CHUNKS, s0 = lane % CHUNKS;
-  const int dma_off = key0 * D + (s0 ^ (key0 & (CHUNKS - 1))) * 16;
+  const int dma_off = key0 * D + (s0 ^ swz<D>(key0)) * 16;
   auto fill_stage = [&](int b, int32_t t) {
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i) {
@@ -208,20 +220,20 @@ __global__ __launch_bounds__(kBlockRows8 * kWave, 2) void index_scores_fp8_block
           keys, (__attribute__((address_space(3))) void*)(&tile[b][(i * kBlockRows8 + wave) * kWave * 16]),
           16, dma_off, (t + i * KPI) * D, 0, 0);
     }
-    if (wave < 4)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
           kscl, (__attribute__((address_space(3))) void*)(&tscale[b][wave * kWave]), 4, lane * 4,
           (t + wave * kWave) * 4, 0, 0);
   };
   auto store = [&](float v, int32_t pos) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), outs, half == 0 ? pos * 4 : 0x7FFFFFF0, 0, 0);
   };
-  // B fragment ks of key row r of a stage: chunks c and c + 1 of this lane's
-  // half of the row ((32 tj + col) & (CHUNKS - 1) == col & (CHUNKS - 1)).
+  // B fragment ks of key row r = 32 tj + col of a stage: chunks c and c + 1 of
+  // this lane's half of the row (swz(32 tj + col) == swz(col)).
+  const int sw = swz<D>(col);
   auto read_b = [&](const uint8_t* tb, int r, int ks) {
     const int c = half * (CHUNKS / 2) + 2 * ks;
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(&tb[r * D + ((c ^ (col & (CHUNKS - 1))) * 16)]);
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(&tb[r * D + (((c + 1) ^ (col & (CHUNKS - 1))) * 16)]);
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(&tb[r * D + ((c ^ sw) * 16)]);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(&tb[r * D + (((c + 1) ^ sw) * 16)]);
     return join(lo, hi);
   };
 
@@ -331,7 +343,7 @@ __global__ __launch_bounds__(kStreamRows8 * kWave) void index_scores_fp8_stream(
       const int key = e / CHUNKS, s = e % CHUNKS;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           keys, (__attribute__((address_space(3))) void*)(&ring[wave][slot][i * kWave * 16]), 16,
-          key * D + (s ^ (key & (CHUNKS - 1))) * 16, t * D, 0, 0);
+          key * D + (s ^ ((key / (256 / D)) & (CHUNKS - 1))) * 16, t * D, 0, 0);  // s ^ swz(key)
     }
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         kscl, (__attribute__((address_space(3))) void*)(&sring[wave][slot][0]), 4, col * 4, t * 4,
@@ -363,8 +375,8 @@ __global__ __launch_bounds__(kStreamRows8 * kWave) void index_scores_fp8_stream(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int c = half * (CHUNKS / 2) + 2 * ks;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(&tb[col * D + ((c ^ (col & (CHUNKS - 1))) * 16)]);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(&tb[col * D + (((c + 1) ^ (col & (CHUNKS - 1))) * 16)]);
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(&tb[col * D + ((c ^ swz<D>(col)) * 16)]);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(&tb[col * D + (((c + 1) ^ swz<D>(col)) * 16)]);
       b[ks] = join(lo, hi);
     }
     const float sk = sring[wave][j % kRing8][col];
