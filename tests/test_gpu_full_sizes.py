@@ -13,6 +13,7 @@ Acceptance (per sampled row):
 import numpy as np
 import pytest
 
+import oracle
 import synth
 
 from _gpu import check_attn, check_topk_rows, device_workload, from_dev_bf16, log, oracle_rows
@@ -29,21 +30,39 @@ from long_context_sparse_score_amd import pipeline  # noqa: E402
 BENCH_WINDOW = 8192  # bench.py's default score window
 
 
-def run_prefill(wl, dev, window=BENCH_WINDOW):
+def run_prefill(wl, dev, window=BENCH_WINDOW, fp8=False):
     vl = dsa.Varlen(wl.cu_q.tolist(), wl.cu_k.tolist())
     bufs = pipeline.alloc_prefill(vl, wl.topk, window)
+    f8 = (pipeline.alloc_fp8_indexer(wl.total_q, wl.total_k, wl.n_heads_idx, wl.d_idx)
+          if fp8 else None)
     out = torch.zeros((wl.total_q, wl.n_heads_q, wl.head_dim), dtype=torch.bfloat16,
                       device="cuda")
     lse = torch.zeros((wl.total_q, wl.n_heads_q), dtype=torch.float32, device="cuda")
     keep = torch.full((wl.total_q, wl.topk), -7, dtype=torch.int32, device="cuda")
     pipeline.prefill(vl, dev["q_idx"], dev["k_idx"], dev["w"], dev["q"], dev["k"], dev["v"], out,
-                     bufs, lse=lse, keep_indices=keep)
+                     bufs, lse=lse, keep_indices=keep, fp8=f8)
     torch.cuda.synchronize()
     return out, lse, keep
 
 
-def check_rows(wl, host, rows, out, lse, idx):
-    ref = oracle_rows(wl, host, rows)
+def fp8_oracle_rows(wl, host, rows):
+    """The oracle path with the fp8-represented indexer inputs (queries are
+    quantised per vector, so only the sampled rows' need quantising)."""
+    qc_rows, qs_rows = oracle.quantize_fp8(host["q_idx"][rows])
+    qc = np.zeros((wl.total_q, wl.n_heads_idx, wl.d_idx), np.uint8)
+    qs = np.zeros((wl.total_q, wl.n_heads_idx), np.float32)
+    qc[rows], qs[rows] = qc_rows, qs_rows
+    kc, ks = oracle.quantize_fp8(host["k_idx"])
+    counts = oracle.visible_counts(wl.cu_q, wl.cu_k, rows)
+    sc = oracle.index_scores_fp8(wl.cu_q, wl.cu_k, qc, qs, kc, ks, host["w"], rows)
+    sel = oracle.topk(sc, counts, wl.topk)
+    o, l = oracle.sparse_attn(wl.cu_q, wl.cu_k, host["q"], host["k"], host["v"], sel, rows,
+                              wl.softmax_scale)
+    return {"scores": sc, "counts": counts, "idx": sel, "out": o, "lse": l}
+
+
+def check_rows(wl, host, rows, out, lse, idx, fp8=False):
+    ref = fp8_oracle_rows(wl, host, rows) if fp8 else oracle_rows(wl, host, rows)
     got_idx = idx[torch.from_numpy(rows).cuda()].cpu().numpy()
     same = check_topk_rows(got_idx, ref["idx"], ref["scores"], ref["counts"], wl.topk)
     got_out = from_dev_bf16(out[torch.from_numpy(rows).cuda()])
@@ -71,6 +90,17 @@ def test_prefill_128k_sampled():
     out, lse, idx = run_prefill(wl, dev)
     rows = synth_rows(wl, 24, seed=3)
     check_rows(wl, host, rows, out, lse, idx)
+
+
+def test_prefill_128k_fp8_indexer_sampled():
+    """The optional fp8 indexer at the bench's full prefill size and windows,
+    against the oracle on the same fp8-represented inputs."""
+    wl = synth.prefill_128k()
+    log("prefill_128k fp8 indexer: generate")
+    host, dev = device_workload(wl)
+    out, lse, idx = run_prefill(wl, dev, fp8=True)
+    rows = synth_rows(wl, 24, seed=4)
+    check_rows(wl, host, rows, out, lse, idx, fp8=True)
 
 
 def test_prefill_128k_repeatable():
@@ -157,6 +187,31 @@ def test_decode_b64_128k_all_queries():
         log(f"  {groups} group(s): {same.sum()}/64 identical index sets, attention max abs "
             f"{mx:.2e} mean abs {mean:.2e}")
         assert same.mean() >= 0.5
+
+
+def test_decode_b64_128k_fp8_indexer_all_queries():
+    """The bench's fp8-indexer decode step (key cache held as e4m3 codes)
+    against the oracle on the same fp8-represented inputs, all 64 queries."""
+    wl = synth.decode_b64_128k()
+    host, dev = device_workload(wl)
+    vl = dsa.Varlen(wl.cu_q.tolist(), wl.cu_k.tolist())
+    rows = np.arange(wl.batch)
+    log("decode_b64_128k fp8: oracle on all 64 queries")
+    ref = fp8_oracle_rows(wl, host, rows)
+    bufs = pipeline.alloc_decode(vl, wl.n_heads_q, wl.head_dim, wl.topk)
+    f8 = pipeline.alloc_fp8_indexer(wl.total_q, wl.total_k, wl.n_heads_idx, wl.d_idx)
+    pipeline.quantize_keys(dev["k_idx"], f8)
+    out = torch.zeros((wl.batch, wl.n_heads_q, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((wl.batch, wl.n_heads_q), dtype=torch.float32, device="cuda")
+    pipeline.decode(vl, dev["q_idx"], None, dev["w"], dev["q"], dev["k"], dev["v"], out, bufs,
+                    lse=lse, fp8=f8)
+    torch.cuda.synchronize()
+    same = check_topk_rows(bufs.indices.cpu().numpy(), ref["idx"], ref["scores"], ref["counts"],
+                           wl.topk)
+    mx, mean = check_attn(from_dev_bf16(out), ref["out"], rows_mask=same)
+    assert np.allclose(lse.cpu().numpy()[same], ref["lse"][same], atol=2e-3)
+    log(f"  {same.sum()}/64 identical index sets, attention max abs {mx:.2e} mean abs {mean:.2e}")
+    assert same.mean() >= 0.5
 
 
 def test_varlen_512k_sampled():
