@@ -204,6 +204,42 @@ int dsa_sparse_attn_prefill(const dsa_varlen* vl, const void* q, const void* k, 
                             int32_t head_dim, float softmax_scale, void* out, float* lse,
                             hipStream_t stream);
 
+/* Workspace bytes dsa_sparse_attn_prefill_grouped needs for a window of
+   row_count rows (the unions of up to ceil(row_count / 16) groups). */
+int dsa_sparse_attn_prefill_grouped_workspace_size(const dsa_varlen* vl, int64_t row_count,
+                                                   int32_t topk, size_t* bytes);
+
+/*
+ * dsa_sparse_attn_prefill_grouped -- the attention of dsa_sparse_attn_prefill
+ * computed for groups of 16 adjacent query rows at once (page 5 section 8:
+ * adjacent queries select largely the same positions, so the 16 index sets
+ * are de-duplicated before attention).  Rows row_begin + 16 j .. + 15 form
+ * group j; the union of their index rows is gathered once per group and a
+ * per-(row, position) mask keeps every query to its own set, so the result
+ * is that of dsa_sparse_attn_prefill on the same indices (same arithmetic per
+ * query; the group may span sequences).  Pays off when the sets overlap: the
+ * K/V rows gathered per group are the union's, the matrix work is 16 rows
+ * times the union.
+ *
+ *   q, k, v, out, lse, softmax_scale, window: as dsa_sparse_attn_prefill.
+ *   indices int32 [row_count, topk]: every row ascending, with its valid
+ *           positions (0..p) first and -1 after them, as dsa_topk writes
+ *           them.  (Other orders are not detected; they drop positions from
+ *           the union.)
+ *   workspace  device buffer of at least
+ *              dsa_sparse_attn_prefill_grouped_workspace_size bytes for this
+ *              row_count and topk, 256-byte aligned, contents clobbered; calls
+ *              sharing it must be ordered.
+ * Supported: as dsa_sparse_attn_prefill, plus all K (and V) rows at most
+ * 2 GiB (total_k * n_heads_kv * head_dim * 2 < 2^31).
+ */
+int dsa_sparse_attn_prefill_grouped(const dsa_varlen* vl, const void* q, const void* k,
+                                    const void* v, const int32_t* indices, int32_t topk,
+                                    int64_t row_begin, int64_t row_count, int32_t n_heads_q,
+                                    int32_t n_heads_kv, int32_t head_dim, float softmax_scale,
+                                    void* out, float* lse, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes dsa_sparse_attn_decode needs for a window of row_count
    queries (partial results of the split over the index list). */
 int dsa_sparse_attn_decode_workspace_size(const dsa_varlen* vl, int64_t row_count,

@@ -11,6 +11,8 @@ Entry points (same names as the C ABI):
     dsa_sparse_attn_prefill, dsa_sparse_attn_decode,
     dsa_sparse_attn_decode_workspace_size,
     dsa_quantize_fp8, dsa_index_scores_fp8 (the optional fp8 indexer),
+    dsa_sparse_attn_prefill_grouped (+ workspace size; 16 adjacent rows per
+    union of index sets),
     dsa_check_varlen, dsa_check_indices, dsa_check_scores (device-side
     precondition checks; the entry points also run them when the environment
     variable DSA_CHECK is set to anything but "" or "0")
@@ -28,7 +30,8 @@ EXPORTED = (
     "dsa_status_string", "dsa_last_error", "dsa_index_scores", "dsa_topk_workspace_size",
     "dsa_topk", "dsa_sparse_attn_prefill", "dsa_sparse_attn_decode_workspace_size",
     "dsa_sparse_attn_decode", "dsa_check_varlen", "dsa_check_indices", "dsa_check_scores",
-    "dsa_quantize_fp8", "dsa_index_scores_fp8",
+    "dsa_quantize_fp8", "dsa_index_scores_fp8", "dsa_sparse_attn_prefill_grouped_workspace_size",
+    "dsa_sparse_attn_prefill_grouped",
 )
 
 DSA_OK = 0
@@ -85,6 +88,9 @@ def load_library(path: str = LIB_PATH):
                                            vp, vp, vp, ctypes.c_size_t, vp]
     lib.dsa_quantize_fp8.argtypes = [vp, i64, i32, vp, vp, vp]
     lib.dsa_index_scores_fp8.argtypes = [vl, vp, vp, vp, vp, vp, i32, i32, i64, i64, vp, i64, vp]
+    lib.dsa_sparse_attn_prefill_grouped_workspace_size.argtypes = [vl, i64, i32, sz]
+    lib.dsa_sparse_attn_prefill_grouped.argtypes = [vl, vp, vp, vp, vp, i32, i64, i64, i32, i32,
+                                                    i32, f32, vp, vp, vp, ctypes.c_size_t, vp]
     lib.dsa_check_varlen.argtypes = [vl, vp]
     lib.dsa_check_indices.argtypes = [vl, vp, i32, i64, i64, vp]
     lib.dsa_check_scores.argtypes = [vl, vp, i64, i64, i64, vp]
@@ -253,6 +259,36 @@ def dsa_sparse_attn_prefill(vl: Varlen, q, k, v, indices, out, lse=None, softmax
     _check(load_library().dsa_sparse_attn_prefill(
         vl.struct, _ptr(q), _ptr(k), _ptr(v), _ptr(indices), indices.shape[1], row_begin,
         row_count, q.shape[1], k.shape[1], d, scale, _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def dsa_sparse_attn_prefill_grouped_workspace_size(vl: Varlen, row_count: int, topk: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().dsa_sparse_attn_prefill_grouped_workspace_size(vl.struct, row_count, topk,
+                                                                          ctypes.byref(n)))
+    return n.value
+
+
+def dsa_sparse_attn_prefill_grouped(vl: Varlen, q, k, v, indices, out, workspace, lse=None,
+                                    softmax_scale=None, row_begin: int = 0,
+                                    row_count: int | None = None, stream=None):
+    """dsa_sparse_attn_prefill for groups of 16 adjacent rows served from the
+    union of their (ascending) index rows."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k, "k", torch.bfloat16, 3)
+    _need(v, "v", torch.bfloat16, 3)
+    _need(indices, "indices", torch.int32, 2)
+    _need(out, "out", torch.bfloat16, 3)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2)
+    d = q.shape[2]
+    scale = d ** -0.5 if softmax_scale is None else softmax_scale
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    row_count = indices.shape[0] if row_count is None else row_count
+    _check(load_library().dsa_sparse_attn_prefill_grouped(
+        vl.struct, _ptr(q), _ptr(k), _ptr(v), _ptr(indices), indices.shape[1], row_begin,
+        row_count, q.shape[1], k.shape[1], d, scale, _ptr(out), _ptr(lse), _ptr(workspace),
+        ws_bytes, _stream(stream)))
 
 
 def dsa_sparse_attn_decode_workspace_size(vl: Varlen, n_heads_q: int, head_dim: int,

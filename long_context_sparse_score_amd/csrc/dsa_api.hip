@@ -310,6 +310,57 @@ int dsa_sparse_attn_prefill(const dsa_varlen* vl, const void* q, const void* k, 
       "sparse_attn_prefill launch");
 }
 
+int dsa_sparse_attn_prefill_grouped_workspace_size(const dsa_varlen* vl, int64_t row_count,
+                                                   int32_t topk, size_t* bytes) {
+  int st;
+  if ((st = check_varlen(vl))) return st;
+  if (bytes == nullptr) return fail(DSA_ERR_INVALID_ARGUMENT, "bytes pointer is NULL");
+  if (row_count < 0 || row_count > vl->total_q)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "row_count %lld outside [0, total_q]",
+                static_cast<long long>(row_count));
+  if (topk < 1 || topk > 4096) return fail(DSA_ERR_UNSUPPORTED, "topk %d not in 1..4096", topk);
+  *bytes = row_count == 0 ? 0 : dsa::grouped_attn_workspace_bytes(row_count, topk);
+  return ok();
+}
+
+int dsa_sparse_attn_prefill_grouped(const dsa_varlen* vl, const void* q, const void* k,
+                                    const void* v, const int32_t* indices, int32_t topk,
+                                    int64_t row_begin, int64_t row_count, int32_t n_heads_q,
+                                    int32_t n_heads_kv, int32_t head_dim, float softmax_scale,
+                                    void* out, float* lse, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  int st;
+  if ((st = check_varlen(vl))) return st;
+  if ((st = check_window(vl, row_begin, row_count))) return st;
+  if ((st = check_bf16(q, "q"))) return st;
+  if ((st = check_bf16(k, "k"))) return st;
+  if ((st = check_bf16(v, "v"))) return st;
+  if ((st = check_bf16(out, "out"))) return st;
+  if (indices == nullptr || !aligned(indices, 4))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "indices is NULL or misaligned");
+  if (lse != nullptr && !aligned(lse, 4)) return fail(DSA_ERR_INVALID_ARGUMENT, "lse misaligned");
+  if ((st = check_attn_shape(n_heads_q, n_heads_kv, head_dim, topk, softmax_scale))) return st;
+  // The grouped kernels address all K (and V) rows with 32-bit offsets.
+  if (vl->total_k * n_heads_kv * head_dim * 2 > INT32_MAX)
+    return fail(DSA_ERR_UNSUPPORTED, "K or V rows exceed 2 GiB (total_k %lld)",
+                static_cast<long long>(vl->total_k));
+  if (checks_enabled() &&
+      (st = device_indices(vl, indices, topk, row_begin, row_count, stream)))
+    return st;
+  if (row_count == 0) return ok();
+  const size_t need = dsa::grouped_attn_workspace_bytes(row_count, topk);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
+    return fail(DSA_ERR_WORKSPACE, "grouped workspace needs %zu bytes (256-byte aligned), got %zu",
+                need, workspace_bytes);
+  return hip_status(
+      dsa::launch_grouped_attn(*vl, static_cast<const uint16_t*>(q),
+                               static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                               indices, topk, row_begin, row_count, n_heads_q, n_heads_kv,
+                               head_dim, softmax_scale, static_cast<uint16_t*>(out), lse,
+                               workspace, stream),
+      "sparse_attn_prefill_grouped launch");
+}
+
 int dsa_sparse_attn_decode_workspace_size(const dsa_varlen* vl, int64_t row_count,
                                           int32_t n_heads_q, int32_t head_dim, int32_t topk,
                                           size_t* bytes) {

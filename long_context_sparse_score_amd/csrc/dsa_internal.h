@@ -39,6 +39,15 @@ hipError_t launch_sparse_attn(const dsa_varlen& vl, const uint16_t* q, const uin
                               int head_dim, float scale, uint16_t* out, float* lse, int splits,
                               float* partial, hipStream_t stream);
 
+// Grouped prefill attention: 16 adjacent rows served from the union of their
+// (ascending) index rows; `workspace` holds the unions.
+size_t grouped_attn_workspace_bytes(int64_t row_count, int topk);
+hipError_t launch_grouped_attn(const dsa_varlen& vl, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, const int32_t* indices, int topk,
+                               int64_t row_begin, int64_t row_count, int n_heads_q,
+                               int n_heads_kv, int head_dim, float scale, uint16_t* out,
+                               float* lse, void* workspace, hipStream_t stream);
+
 // Device-side precondition checks.  Each clears a report word, runs one
 // kernel on `stream`, waits for the stream and stores the first finding as
 // (item << 8) | code, or all ones when there is none.  The first call on a

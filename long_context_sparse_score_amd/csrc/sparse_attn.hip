@@ -19,6 +19,8 @@
 //   lane's probabilities are already in place as the A operand; V's B
 //   operand (8 consecutive keys of one column per lane) comes from LDS
 //   through the transposing read.
+#include <type_traits>
+
 #include "dsa_common.h"
 #include "dsa_internal.h"
 
@@ -81,29 +83,17 @@ __device__ __forceinline__ int tile_at(int r, int piece) {
   return r * D + ((piece ^ (r % AttnCfg<D>::PIECES)) * 8);
 }
 
-// Online-softmax update of one tile.  m_run / l_run / acc are this lane's
-// running state (head col; O rows = heads 4 qd + r).  vm: bit s says whether
-// slot s of the tile holds a usable position.
+// Online-softmax update of one tile held in LDS.  m_run / l_run / acc are
+// this lane's running state (query column col; O rows = columns 4 qd + r).
+// vm: bit s says whether slot s of the tile is usable for this lane's column.
 template <int D>
-__device__ __forceinline__ void attend_tile(const GatherTile<D>& t, const bf16x8 (&qb)[AttnCfg<D>::KS],
-                                            uint16_t* ks_lds, uint16_t* vs_lds, uint32_t vm,
-                                            float scale_log2, int lane, float& m_run,
-                                            float& l_run, f32x4 (&acc)[AttnCfg<D>::DT]) {
+__device__ __forceinline__ void compute_tile(const bf16x8 (&qb)[AttnCfg<D>::KS],
+                                             const uint16_t* ks_lds, const uint16_t* vs_lds,
+                                             uint32_t vm, float scale_log2, int lane,
+                                             float& m_run, float& l_run,
+                                             f32x4 (&acc)[AttnCfg<D>::DT]) {
   using C = AttnCfg<D>;
   const int col = lane & 15, qd = lane >> 4;
-  // K and V rows to this wave's LDS tiles.  The tiles are private to the
-  // wave and LDS operations of one wave are performed in order, so the reads
-  // below see these writes and the next tile's writes come after them.
-  {
-    const int q = lane / C::PIECES, piece = lane % C::PIECES;
-#pragma unroll
-    for (int j = 0; j < C::LPT; ++j) {
-      const int at = tile_at<D>(q * C::LPT + j, piece);
-      *reinterpret_cast<u32x4*>(ks_lds + at) = t.k[j];
-      *reinterpret_cast<u32x4*>(vs_lds + at) = t.v[j];
-    }
-  }
-
   // S^T tiles: rows = slots 16*sub + 4*qd + r, column = head col.  A operand:
   // slot 16*sub + col, d range [32 ks + 8 qd, +8).
   f32x4 st[2];
@@ -180,6 +170,27 @@ __device__ __forceinline__ void attend_tile(const GatherTile<D>& t, const bf16x8
                                               0, 1, 2, 3, 4, 5, 6, 7);
     acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, acc[dt], 0, 0, 0);
   }
+}
+
+// A wave's own tile: its K and V rows to its private LDS tiles, then the
+// update.  LDS operations of one wave are performed in order, so the reads
+// see these writes and the next tile's writes come after them.
+template <int D>
+__device__ __forceinline__ void attend_tile(const GatherTile<D>& t, const bf16x8 (&qb)[AttnCfg<D>::KS],
+                                            uint16_t* ks_lds, uint16_t* vs_lds, uint32_t vm,
+                                            float scale_log2, int lane, float& m_run,
+                                            float& l_run, f32x4 (&acc)[AttnCfg<D>::DT]) {
+  using C = AttnCfg<D>;
+  {
+    const int q = lane / C::PIECES, piece = lane % C::PIECES;
+#pragma unroll
+    for (int j = 0; j < C::LPT; ++j) {
+      const int at = tile_at<D>(q * C::LPT + j, piece);
+      *reinterpret_cast<u32x4*>(ks_lds + at) = t.k[j];
+      *reinterpret_cast<u32x4*>(vs_lds + at) = t.v[j];
+    }
+  }
+  compute_tile<D>(qb, ks_lds, vs_lds, vm, scale_log2, lane, m_run, l_run, acc);
 }
 
 // LDS of one workgroup: K and V tiles of every KV head, the slice of the
@@ -335,7 +346,337 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(const float* __restrict__
   if (lse != nullptr && d == 0) lse[row * n_heads_q + hq] = den > 0.0f ? (m + log2f(den)) * kLn2 : -INFINITY;
 }
 
+// ---------------------------------------------------------------- grouped prefill
+//
+// Adjacent query rows select largely the same positions when their queries
+// are alike (page 5 section 8: the index sets of 16 adjacent queries are
+// de-duplicated before attention).  A group of kGroupRows consecutive rows
+// of the window is served from the union of their index sets: each K/V row
+// of the union is gathered once for the group, and a per-(row, position)
+// mask restricts every query to its own set, so each query's result is the
+// one of its own set.
+//
+// Pass 1 (union_kernel, one workgroup per group): the union as packed key
+// rows (sequence key base + position, ascending) with a 16-bit row mask per
+// entry, in the caller's workspace.  The index rows must be ascending with
+// -1 padding after the valid entries (as dsa_topk writes them): a cursor per
+// row then walks its list once while the packed-key range is swept in spans
+// of kUnionSpan, each marked in an LDS bitmap and compacted in order.
+// Pass 2 (grouped_attn_kernel, one workgroup per (group, KV head), one wave
+// per 16 of the group's 16 * G queries): every union tile of 32 entries is
+// gathered into LDS by the whole workgroup and used by every wave with the
+// tile update of the per-row kernel, the validity bits taken from the masks.
+
+constexpr int kGroupRows = 16;
+constexpr int kUnionSpan = 8192;
+constexpr int kUnionThreads = 256;
+
+// Workspace of the grouped path for `groups` groups: union keys (int32), row
+// masks (uint16), one count per group.
+struct GroupedWorkspace {
+  int32_t* keys;
+  uint16_t* masks;
+  int32_t* counts;
+};
+
+__host__ __device__ inline size_t grouped_ws_entries(int topk) {
+  return static_cast<size_t>(kGroupRows) * topk;
+}
+
+inline GroupedWorkspace grouped_ws_layout(void* base, int64_t groups, int topk) {
+  char* p = static_cast<char*>(base);
+  GroupedWorkspace w;
+  const size_t n = static_cast<size_t>(groups) * grouped_ws_entries(topk);
+  w.keys = reinterpret_cast<int32_t*>(p);
+  p += (n * sizeof(int32_t) + 255) / 256 * 256;
+  w.masks = reinterpret_cast<uint16_t*>(p);
+  p += (n * sizeof(uint16_t) + 255) / 256 * 256;
+  w.counts = reinterpret_cast<int32_t*>(p);
+  return w;
+}
+
+__global__ __launch_bounds__(kUnionThreads) void union_kernel(
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
+    const int32_t* __restrict__ indices, int topk, int64_t row_begin, int64_t row_count,
+    int32_t* __restrict__ ukeys, uint16_t* __restrict__ umasks, int32_t* __restrict__ ucount) {
+  constexpr int kWavesU = kUnionThreads / kWave;
+  constexpr int kPer = kUnionSpan / kUnionThreads;  // bitmap entries per thread
+  static_assert(kPer % 4 == 0, "bitmap entries are read 4 at a time");
+  __shared__ __attribute__((aligned(16))) uint32_t bits[kUnionSpan / 2];  // 16-bit masks, paired
+  __shared__ int64_t rbase[kGroupRows];
+  __shared__ int32_t rlim[kGroupRows];
+  __shared__ int32_t rcur[kGroupRows];
+  __shared__ int32_t wsum[kWavesU];
+  __shared__ int64_t span[2];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int64_t g = blockIdx.x;
+  const int64_t first = g * kGroupRows;
+  const int nrows = static_cast<int>(min<int64_t>(kGroupRows, row_count - first));
+  if (tid < kGroupRows) {
+    if (tid < nrows) {
+      const RowInfo ri = row_info(cu_q, cu_k, batch, row_begin + first + tid);
+      rbase[tid] = ri.key_base;
+      rlim[tid] = ri.pos;
+    }
+    rcur[tid] = 0;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int64_t lo = rbase[0], hi = rbase[0] + rlim[0];
+    for (int r = 1; r < nrows; ++r) {
+      lo = min(lo, rbase[r]);
+      hi = max(hi, rbase[r] + rlim[r]);
+    }
+    span[0] = lo;
+    span[1] = hi;
+  }
+  __syncthreads();
+  const int64_t lo = span[0], hi = span[1];
+  int32_t* keys = ukeys + g * grouped_ws_entries(topk);
+  uint16_t* masks = umasks + g * grouped_ws_entries(topk);
+  int32_t out = 0;
+  for (int64_t x0 = lo; x0 <= hi; x0 += kUnionSpan) {
+    for (int i = tid; i < kUnionSpan / 2; i += kUnionThreads) bits[i] = 0u;
+    __syncthreads();
+    // Mark: wave w walks rows w, w + kWavesU, ... from their cursors while
+    // the packed keys stay below x0 + kUnionSpan.
+    for (int r = wave; r < nrows; r += kWavesU) {
+      const int32_t* irow = indices + (first + r) * topk;
+      const int64_t base = rbase[r];
+      const int32_t lim = rlim[r];
+      int32_t c = rcur[r];
+      while (c < topk) {
+        const int32_t e = c + lane < topk ? irow[c + lane] : -1;
+        const bool valid = e >= 0 && e <= lim;
+        const int64_t key = base + e;
+        const bool in = valid && key < x0 + kUnionSpan;
+        if (in && key >= x0) {
+          const int off = static_cast<int>(key - x0);
+          atomicOr(&bits[off >> 1], (1u << r) << (16 * (off & 1)));
+        }
+        const int n_in = __popcll(__ballot(in));
+        c += n_in;
+        if (n_in < kWave) break;
+      }
+      if (lane == 0) rcur[r] = c;
+    }
+    __syncthreads();
+    // Compact the marked entries in key order: thread t owns entries
+    // [t kPer, (t + 1) kPer).
+    uint32_t m[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer / 2; i += 2) {
+      const uint2 w2 = *reinterpret_cast<const uint2*>(&bits[tid * (kPer / 2) + i]);
+      m[2 * i] = w2.x & 0xFFFFu;
+      m[2 * i + 1] = w2.x >> 16;
+      m[2 * i + 2] = w2.y & 0xFFFFu;
+      m[2 * i + 3] = w2.y >> 16;
+    }
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) cnt += m[i] != 0u;
+    // Exclusive prefix over the workgroup.
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == kWave - 1) wsum[wave] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesU; ++w) {
+      before += w < wave ? wsum[w] : 0;
+      total += wsum[w];
+    }
+    int at = out + before + incl - cnt;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (m[i] != 0u) {
+        keys[at] = static_cast<int32_t>(x0 + tid * kPer + i);
+        masks[at] = static_cast<uint16_t>(m[i]);
+        ++at;
+      }
+    }
+    out += total;
+    __syncthreads();
+  }
+  if (tid == 0) ucount[g] = out;
+}
+
+// One workgroup per (group, KV head); wave w serves the group's queries
+// 16 w .. 16 w + 15 of this KV head (query c = row c / G, head c mod G).
+// JOBS: 16-byte gather loads per lane and tile (32 rows x D x 2 bytes of K,
+// and of V, over the workgroup), the smallest power of two that covers the
+// tile; a workgroup of 64 G threads then has at most 1024 / JOBS threads.
+template <int D, int JOBS>
+__global__ __launch_bounds__(1024 / JOBS) void grouped_attn_kernel(
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, int64_t total_k, int topk, int64_t row_begin,
+    int64_t row_count, int n_heads_q, int n_heads_kv, float scale_log2,
+    uint16_t* __restrict__ out, float* __restrict__ lse, const int32_t* __restrict__ ukeys,
+    const uint16_t* __restrict__ umasks, const int32_t* __restrict__ ucount) {
+  using C = AttnCfg<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t kt[2][C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[2][C::TILE];
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int nthreads = blockDim.x;
+  const int G = n_heads_q / n_heads_kv;
+  const int col = lane & 15, qd = lane >> 4;
+  const int64_t g = blockIdx.x;
+  const int h = blockIdx.y;
+  const int64_t first = g * kGroupRows;
+  // This lane's query column.
+  const int cq = 16 * wave + col;
+  const int rl = cq / G;
+  const bool active = first + rl < row_count;
+  const int64_t row = row_begin + first + rl;
+  const int hq = h * G + cq % G;
+  bf16x8 qb[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks)
+    qb[ks] = active ? load_bf16x8(q + (row * n_heads_q + hq) * D + ks * 32 + qd * 8) : zero_bf16x8();
+  // Rows of this wave's 16 columns: rl_first .. rl_first + nrw - 1.
+  const int rl_first = (16 * wave) / G;
+  const int nrw = (16 * wave + 15) / G - rl_first + 1;
+
+  const int32_t count = ucount[g];
+  const int32_t* keys = ukeys + g * grouped_ws_entries(topk);
+  const uint16_t* masks = umasks + g * grouped_ws_entries(topk);
+  const int kv_bytes = static_cast<int>(total_k * n_heads_kv * D * 2);
+  const __amdgpu_buffer_rsrc_t kr = raw_buffer(k, kv_bytes);
+  const __amdgpu_buffer_rsrc_t vr = raw_buffer(v, kv_bytes);
+  // Gather job j of thread t: tile row (t + j nthreads) / PIECES, piece
+  // (t + j nthreads) mod PIECES.
+  u32x4 rk[JOBS], rv[JOBS];
+  auto gather = [&](int t0) {
+#pragma unroll
+    for (int j = 0; j < JOBS; ++j) {
+      const int e = static_cast<int>(threadIdx.x) + j * nthreads;
+      const int slot = t0 + e / C::PIECES, piece = e % C::PIECES;
+      const bool ok = e < 32 * C::PIECES && slot < count;
+      const int32_t key = ok ? keys[slot] : 0;
+      const uint32_t off = ((static_cast<uint32_t>(key) * n_heads_kv + h) * D + piece * 8) * 2;
+      rk[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0));
+      rv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0));
+    }
+  };
+  auto store = [&](int b) {
+#pragma unroll
+    for (int j = 0; j < JOBS; ++j) {
+      const int e = static_cast<int>(threadIdx.x) + j * nthreads;
+      if (e < 32 * C::PIECES) {
+        const int at = tile_at<D>(e / C::PIECES, e % C::PIECES);
+        *reinterpret_cast<u32x4*>(&kt[b][at]) = rk[j];
+        *reinterpret_cast<u32x4*>(&vt[b][at]) = rv[j];
+      }
+    }
+  };
+
+  f32x4 acc[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;
+  const int ntiles = (count + 31) / 32;
+  gather(0);
+  for (int t = 0; t < ntiles; ++t) {
+    const int b = t & 1;
+    store(b);
+    const int slot = t * 32 + (lane & 31);
+    const uint32_t m16 = slot < count ? masks[slot] : 0u;
+    __syncthreads();  // tile t in LDS; every wave is done with tile t - 1
+    if (t + 1 < ntiles) gather((t + 1) * 32);
+    // Validity of the 32 slots for this lane's row.
+    uint32_t vm = 0u;
+    for (int i = 0; i < nrw; ++i) {
+      const uint32_t w = static_cast<uint32_t>(__ballot((m16 >> (rl_first + i)) & 1u));
+      if (rl == rl_first + i) vm = w;
+    }
+    compute_tile<D>(qb, kt[b], vt[b], vm, scale_log2, lane, m_run, l_run, acc);
+  }
+
+  // Normalise; O rows of this lane are columns 4 qd + r.
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float lr = __shfl(l_tot, 4 * qd + r);
+    const float mr = __shfl(m_run, 4 * qd + r);
+    const int c = 16 * wave + 4 * qd + r;
+    const int rr = c / G;
+    if (first + rr >= row_count) continue;
+    const int64_t orow_i = row_begin + first + rr;
+    const int ohq = h * G + c % G;
+    const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+    uint16_t* orow = out + (orow_i * n_heads_q + ohq) * D;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+      orow[dt * 16 + col] = static_cast<uint16_t>(f32_to_bf16_bits(acc[dt][r] * inv));
+    if (lse != nullptr && col == 0)
+      lse[orow_i * n_heads_q + ohq] = lr > 0.0f ? (mr + log2f(lr)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int D, int JOBS>
+void launch_grouped_attn_d(dim3 grid, dim3 block, hipStream_t stream, const dsa_varlen& vl,
+                           const uint16_t* q, const uint16_t* k, const uint16_t* v, int topk,
+                           int64_t row_begin, int64_t row_count, int n_heads_q, int n_heads_kv,
+                           float scale_log2, uint16_t* out, float* lse,
+                           const GroupedWorkspace& ws) {
+  hipLaunchKernelGGL((grouped_attn_kernel<D, JOBS>), grid, block, 0, stream, vl.cu_seqlens_q,
+                     vl.cu_seqlens_k, vl.batch, q, k, v, vl.total_k, topk, row_begin, row_count,
+                     n_heads_q, n_heads_kv, scale_log2, out, lse, ws.keys, ws.masks, ws.counts);
+}
+
 }  // namespace
+
+size_t grouped_attn_workspace_bytes(int64_t row_count, int topk) {
+  const int64_t groups = (row_count + kGroupRows - 1) / kGroupRows;
+  const size_t n = static_cast<size_t>(groups) * grouped_ws_entries(topk);
+  return (n * sizeof(int32_t) + 255) / 256 * 256 + (n * sizeof(uint16_t) + 255) / 256 * 256 +
+         static_cast<size_t>(groups) * sizeof(int32_t);
+}
+
+hipError_t launch_grouped_attn(const dsa_varlen& vl, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, const int32_t* indices, int topk,
+                               int64_t row_begin, int64_t row_count, int n_heads_q,
+                               int n_heads_kv, int head_dim, float scale, uint16_t* out,
+                               float* lse, void* workspace, hipStream_t stream) {
+  const int64_t groups = (row_count + kGroupRows - 1) / kGroupRows;
+  const GroupedWorkspace ws = grouped_ws_layout(workspace, groups, topk);
+  hipLaunchKernelGGL(union_kernel, dim3(static_cast<unsigned>(groups)), dim3(kUnionThreads), 0,
+                     stream, vl.cu_seqlens_q, vl.cu_seqlens_k, vl.batch, indices, topk, row_begin,
+                     row_count, ws.keys, ws.masks, ws.counts);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int G = n_heads_q / n_heads_kv;
+  const dim3 grid(static_cast<unsigned>(groups), static_cast<unsigned>(n_heads_kv));
+  const dim3 block(kWave * G);  // 16 G queries per KV head, 16 per wave
+  const float scale_log2 = scale * kLog2e;
+  const int jobs = (32 * (head_dim / 8) + kWave * G - 1) / (kWave * G);
+  auto go = [&](auto d_tag, auto jobs_tag) {
+    launch_grouped_attn_d<decltype(d_tag)::value, decltype(jobs_tag)::value>(
+        grid, block, stream, vl, q, k, v, topk, row_begin, row_count, n_heads_q, n_heads_kv,
+        scale_log2, out, lse, ws);
+  };
+  using I64 = std::integral_constant<int, 64>;
+  using I128 = std::integral_constant<int, 128>;
+  // The smallest compiled JOBS that covers the tile.
+  if (head_dim == 128) {
+    if (jobs > 4) go(I128{}, std::integral_constant<int, 8>{});
+    else if (jobs > 2) go(I128{}, std::integral_constant<int, 4>{});
+    else if (jobs > 1) go(I128{}, std::integral_constant<int, 2>{});
+    else go(I128{}, std::integral_constant<int, 1>{});
+  } else {
+    if (jobs > 2) go(I64{}, std::integral_constant<int, 4>{});
+    else if (jobs > 1) go(I64{}, std::integral_constant<int, 2>{});
+    else go(I64{}, std::integral_constant<int, 1>{});
+  }
+  return hipGetLastError();
+}
 
 size_t attn_workspace_bytes(int64_t rows, int n_heads_q, int head_dim, int splits) {
   if (splits <= 1) return 0;

@@ -14,7 +14,9 @@ from dataclasses import dataclass
 
 from . import (Varlen, dsa_index_scores, dsa_index_scores_fp8, dsa_quantize_fp8,
                dsa_sparse_attn_decode, dsa_sparse_attn_decode_workspace_size,
-               dsa_sparse_attn_prefill, dsa_topk, dsa_topk_workspace_size)
+               dsa_sparse_attn_prefill, dsa_sparse_attn_prefill_grouped,
+               dsa_sparse_attn_prefill_grouped_workspace_size, dsa_topk,
+               dsa_topk_workspace_size)
 
 
 def _torch():
@@ -70,18 +72,25 @@ class PrefillBuffers:
     scores: object       # fp32 [window, ld]
     indices: object      # int32 [window, topk]
     spare: object = None  # a second int32 [window, topk] for the two-stream schedule
+    grouped: object = None  # uint8 workspace of the grouped attention (one per index buffer)
+    grouped_spare: object = None
 
 
-def alloc_prefill(vl: Varlen, topk: int, window: int, device="cuda",
-                  overlap: bool = False) -> PrefillBuffers:
+def alloc_prefill(vl: Varlen, topk: int, window: int, device="cuda", overlap: bool = False,
+                  grouped: bool = False) -> PrefillBuffers:
     """Buffers of a windowed prefill; `overlap` adds the second index buffer the
-    two-stream schedule alternates with."""
+    two-stream schedule alternates with; `grouped` selects the grouped attention
+    (16 adjacent rows per union of index sets) and adds its workspace."""
     torch = _torch()
     window = max(1, min(window, vl.total_q))
     ld = score_ld(vl.max_seqlen_k)
     idx = lambda: torch.empty((window, topk), dtype=torch.int32, device=device)  # noqa: E731
+    gws = lambda: torch.empty(  # noqa: E731
+        max(256, dsa_sparse_attn_prefill_grouped_workspace_size(vl, window, topk)),
+        dtype=torch.uint8, device=device)
     return PrefillBuffers(torch.empty((window, ld), dtype=torch.float32, device=device), idx(),
-                          idx() if overlap else None)
+                          idx() if overlap else None, gws() if grouped else None,
+                          gws() if grouped and overlap else None)
 
 
 def prefill(vl: Varlen, q_idx, k_idx, w, q, k, v, out, bufs: PrefillBuffers, lse=None,
@@ -111,6 +120,7 @@ def prefill(vl: Varlen, q_idx, k_idx, w, q, k, v, out, bufs: PrefillBuffers, lse
     if two:
         side_stream.wait_stream(main)  # inputs written on the main stream
     ibufs = [bufs.indices, bufs.spare] if two else [bufs.indices]
+    gbufs = [bufs.grouped, bufs.grouped_spare] if two else [bufs.grouped]
     released = [None, None]  # per index buffer: attention done reading it
     window = bufs.scores.shape[0]
     if fp8 is not None:
@@ -140,8 +150,13 @@ def prefill(vl: Varlen, q_idx, k_idx, w, q, k, v, out, bufs: PrefillBuffers, lse
             ready.record(main)
             att.wait_event(ready)
         a0 = mark(att)
-        dsa_sparse_attn_prefill(vl, q, k, v, ib, out, lse=lse, softmax_scale=softmax_scale,
-                                row_begin=r0, row_count=n, stream=att)
+        if bufs.grouped is None:
+            dsa_sparse_attn_prefill(vl, q, k, v, ib, out, lse=lse, softmax_scale=softmax_scale,
+                                    row_begin=r0, row_count=n, stream=att)
+        else:
+            dsa_sparse_attn_prefill_grouped(vl, q, k, v, ib, out, gbufs[i % len(gbufs)], lse=lse,
+                                            softmax_scale=softmax_scale, row_begin=r0,
+                                            row_count=n, stream=att)
         a1 = mark(att)
         if keep_indices is not None:
             with torch.cuda.stream(att):

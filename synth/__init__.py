@@ -42,7 +42,7 @@ LIB_PATH = os.path.join(_HERE, "libsynth.so")
 _lib = None
 
 # Stream ids (one independent counter stream per tensor).
-S_QIDX, S_KIDX, S_W, S_Q, S_K, S_V, S_KIDX_MEAN, S_K_MEAN, S_LENGTHS = range(1, 10)
+S_QIDX, S_KIDX, S_W, S_Q, S_K, S_V, S_KIDX_MEAN, S_K_MEAN, S_LENGTHS, S_QIDX_MEAN = range(1, 11)
 
 
 def build(verbose: bool = False) -> str:
@@ -184,6 +184,9 @@ class Workload:
     block: int = 256
     mean_std: float = 0.5
     ts_scale: float = 2.0
+    # > 0: indexer queries get a per-(block, head) mean of this std, shared by
+    # the block's tokens, so that adjacent queries select similar positions
+    query_mean_std: float = 0.0
     notes: str = field(default="", compare=False)
 
     # -- layout ---------------------------------------------------------------
@@ -243,6 +246,17 @@ class Workload:
     def q_idx(self, rows=None) -> np.ndarray:
         rows = (0, self.total_q) if rows is None else rows
         per = self.n_heads_idx * self.d_idx
+        if self.query_mean_std > 0 and not self.integer_indexer:
+            spans = [rows] if isinstance(rows, tuple) else [(int(r), int(r) + 1) for r in rows]
+            parts = []
+            cu = self.cu_q  # kept alive across the calls
+            for a, b in spans:
+                out = np.empty((b - a) * per, np.uint16)
+                _load().synth_clustered_bf16(self.seed, S_QIDX, S_QIDX_MEAN, self.batch, _ptr(cu),
+                                             per, self.block, self.query_mean_std, 0, 1.0, a, b - a,
+                                             _ptr(out))
+                parts.append(out)
+            return np.concatenate(parts).reshape(self._n(rows), self.n_heads_idx, self.d_idx)
         if self.integer_indexer:
             f = _Fill(np.uint16, lambda s, c, o: int_bf16(self.seed, S_QIDX, s, c, -3, 3, o))
         else:

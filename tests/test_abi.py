@@ -258,3 +258,34 @@ def test_index_scores_key_extent_limit():
     assert call_scores(big, rc=1, ld=9_000_000) == dsa.DSA_ERR_UNSUPPORTED
     ok_size = vl(total_q=1, total_k=8_000_000, max_q=1, max_k=8_000_000)
     assert call_scores(ok_size, rc=0, ld=8_000_000) == dsa.DSA_OK
+
+
+def test_grouped_attention_validation():
+    lib = dsa.load_library()
+    v = vl(total_q=100, total_k=100, max_q=100, max_k=100)
+    n = ctypes.c_size_t(0)
+    assert lib.dsa_sparse_attn_prefill_grouped_workspace_size(ctypes.byref(v), 100, 2048,
+                                                              ctypes.byref(n)) == 0
+    assert n.value > 0
+    need = n.value
+    assert lib.dsa_sparse_attn_prefill_grouped_workspace_size(ctypes.byref(v), 0, 2048,
+                                                              ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert lib.dsa_sparse_attn_prefill_grouped_workspace_size(ctypes.byref(v), 101, 2048,
+                                                              ctypes.byref(n)) == \
+        dsa.DSA_ERR_INVALID_ARGUMENT
+
+    def call(ws=FAKE, ws_bytes=None, vv=v, rc=100, hq=32, hkv=4, topk=2048):
+        b = need if ws_bytes is None else ws_bytes
+        return lib.dsa_sparse_attn_prefill_grouped(ctypes.byref(vv), FAKE, FAKE, FAKE, FAKE, topk,
+                                                   0, rc, hq, hkv, 128, 0.088, FAKE, None, ws, b,
+                                                   None)
+    assert call(rc=0, ws=None) == dsa.DSA_OK
+    assert call(ws=None) == dsa.DSA_ERR_WORKSPACE
+    assert call(ws_bytes=need - 1) == dsa.DSA_ERR_WORKSPACE
+    assert call(ws=FAKE + 64) == dsa.DSA_ERR_WORKSPACE
+    assert call(hq=30) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert call(topk=5000) == dsa.DSA_ERR_UNSUPPORTED
+    # all K rows beyond 2 GiB (the grouped kernels use one 32-bit offset space)
+    big = vl(total_q=100, total_k=3_000_000, max_q=100, max_k=3_000_000)
+    assert call(vv=big) == dsa.DSA_ERR_UNSUPPORTED

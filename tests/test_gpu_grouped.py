@@ -1,0 +1,124 @@
+"""GPU parity of the grouped prefill attention (16 adjacent rows served from
+the union of their index sets) against the CPU oracle's per-row attention,
+and of the union itself against numpy on the same index rows.  Every call
+goes through the C ABI (libdsa.so)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+from _gpu import check_attn, device_workload, from_dev_bf16, log, oracle_rows, to_dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - collected on CPU-only hosts
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import long_context_sparse_score_amd as dsa  # noqa: E402
+from long_context_sparse_score_amd import pipeline  # noqa: E402
+
+GROUP = 16
+
+
+def small_wl(lq, lk, hq, hkv, d, topk, qstd=0.0, seed=11, hi=8, di=64):
+    return synth.Workload(name="test", seed=seed, seqlens_q=tuple(lq), seqlens_k=tuple(lk),
+                          n_heads_q=hq, n_heads_kv=hkv, head_dim=d, n_heads_idx=hi, d_idx=di,
+                          topk=topk, clustered=True, query_mean_std=qstd)
+
+
+def run_grouped(wl, dev, idx, row_begin=0, row_count=None):
+    vl = dsa.Varlen(wl.cu_q.tolist(), wl.cu_k.tolist())
+    row_count = idx.shape[0] if row_count is None else row_count
+    nbytes = dsa.dsa_sparse_attn_prefill_grouped_workspace_size(vl, row_count, wl.topk)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+    out = torch.full((wl.total_q, wl.n_heads_q, wl.head_dim), 7.0, dtype=torch.bfloat16,
+                     device="cuda")
+    lse = torch.zeros((wl.total_q, wl.n_heads_q), dtype=torch.float32, device="cuda")
+    dsa.dsa_sparse_attn_prefill_grouped(vl, dev["q"], dev["k"], dev["v"], to_dev(idx), out, ws,
+                                        lse=lse, row_begin=row_begin, row_count=row_count)
+    torch.cuda.synchronize()
+    return out, lse, ws
+
+
+def workspace_counts(ws, row_count, topk):
+    """The per-group union sizes at the end of the workspace (keys int32 and
+    masks uint16 regions, each rounded up to 256 bytes, then one int32 per group)."""
+    groups = (row_count + GROUP - 1) // GROUP
+    n = groups * GROUP * topk
+    off = -(-n * 4 // 256) * 256 + -(-n * 2 // 256) * 256
+    raw = ws[off:off + 4 * groups].cpu().numpy()
+    return raw.view(np.int32)
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(32, 4, 128), (16, 1, 128), (8, 2, 64), (8, 8, 64),
+                                      (8, 4, 128), (24, 8, 128)])
+def test_grouped_matches_oracle_varlen(hq, hkv, d):
+    """Groups straddling sequences, a partial last group, rows shorter than k
+    (-1 padding), query heads per KV head from 1 to 16."""
+    wl = small_wl([37, 100, 1, 250], [60, 100, 5, 250], hq, hkv, d, topk=64, qstd=3.0,
+                  seed=hq + d)
+    host, dev = device_workload(wl)
+    rows = np.arange(wl.total_q)
+    ref = oracle_rows(wl, host, rows)
+    log(f"grouped attention hq={hq} hkv={hkv} d={d}")
+    out, lse, ws = run_grouped(wl, dev, ref["idx"])
+    mx, mean = check_attn(from_dev_bf16(out), ref["out"])
+    log(f"  max abs {mx:.2e} mean abs {mean:.2e}")
+    assert np.allclose(lse.cpu().numpy(), ref["lse"], atol=2e-3)
+    # The union sizes: distinct packed keys over each group's rows.
+    counts = workspace_counts(ws, wl.total_q, wl.topk)
+    cu_k = wl.cu_k
+    seq = np.searchsorted(wl.cu_q, rows, side="right") - 1
+    for g in range(len(counts)):
+        rr = rows[g * GROUP:(g + 1) * GROUP]
+        keys = set()
+        for r in rr:
+            sel = ref["idx"][r]
+            keys |= set((cu_k[seq[r]] + sel[sel >= 0]).tolist())
+        assert counts[g] == len(keys), f"group {g}: {counts[g]} != {len(keys)}"
+
+
+def test_grouped_row_window_and_long_rows():
+    """A window that starts mid-sequence (groups are formed from row_begin),
+    rows longer than one union span (8192 keys) and k = 2048."""
+    wl = small_wl([9000], [9000], 32, 4, 128, topk=2048, qstd=4.0, seed=5, hi=16, di=64)
+    host, dev = device_workload(wl)
+    rows = np.arange(8700, 9000)
+    ref = oracle_rows(wl, host, rows)
+    log("grouped attention, window of 300 rows at 8700 over 9000 keys")
+    out, lse, ws = run_grouped(wl, dev, ref["idx"], row_begin=8700, row_count=300)
+    got = from_dev_bf16(out)[8700:9000]
+    mx, mean = check_attn(got, ref["out"])
+    log(f"  max abs {mx:.2e} mean abs {mean:.2e}")
+    assert np.allclose(lse.cpu().numpy()[8700:9000], ref["lse"], atol=2e-3)
+    untouched = from_dev_bf16(out)[:8700]
+    assert (untouched == 0x40E0).all()  # 7.0 in bf16: rows outside the window stay
+    counts = workspace_counts(ws, 300, wl.topk)
+    for g in range(len(counts)):
+        sel = ref["idx"][g * GROUP:(g + 1) * GROUP]
+        assert counts[g] == np.unique(sel[sel >= 0]).size
+
+
+def test_grouped_equals_per_row_pipeline_end_to_end():
+    """The prefill pipeline with the grouped attention against the oracle on a
+    correlated-query clustered workload (indices from the GPU top-k)."""
+    wl = small_wl([1500, 700], [1500, 700], 32, 4, 128, topk=512, qstd=4.0, seed=8, hi=64,
+                  di=128)
+    host, dev = device_workload(wl)
+    vl = dsa.Varlen(wl.cu_q.tolist(), wl.cu_k.tolist())
+    bufs = pipeline.alloc_prefill(vl, wl.topk, window=800, grouped=True)
+    out = torch.zeros((wl.total_q, 32, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((wl.total_q, 32), dtype=torch.float32, device="cuda")
+    keep = torch.zeros((wl.total_q, wl.topk), dtype=torch.int32, device="cuda")
+    pipeline.prefill(vl, dev["q_idx"], dev["k_idx"], dev["w"], dev["q"], dev["k"], dev["v"], out,
+                     bufs, lse=lse, keep_indices=keep)
+    torch.cuda.synchronize()
+    rows = np.arange(wl.total_q)
+    sel = keep.cpu().numpy()
+    ref_out, ref_lse = oracle.sparse_attn(wl.cu_q, wl.cu_k, host["q"], host["k"], host["v"], sel,
+                                          rows, wl.softmax_scale)
+    mx, mean = check_attn(from_dev_bf16(out), ref_out)
+    log(f"  pipeline grouped: max abs {mx:.2e} mean abs {mean:.2e}")
+    assert np.allclose(lse.cpu().numpy(), ref_lse, atol=2e-3)
