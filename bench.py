@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-grouped", action="store_true",
+                    help="skip the grouped-attention comparison on the correlated-query workload")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the optional fp8-indexer variant (reported beside the headline)")
     ap.add_argument("--prefill-streams", type=int, default=1, choices=(1, 2),
@@ -415,6 +417,10 @@ def main():
         result["fp8_indexer"] = fp8_variant(torch, pipeline, args, stream, wl, vl, P, out, lse,
                                             None if args.no_decode else (wd, vd, D, dout, dlse))
 
+    if not args.no_grouped:
+        result["grouped_attention"] = grouped_variant(torch, dsa, pipeline, args, stream, wl, vl, P,
+                                                      out, lse, attn_ms / args.steps)
+
     if not args.no_dense:
         result["dense"] = dense_comparator(torch, P, wl, args, pre_ms / args.steps)
 
@@ -496,6 +502,83 @@ def fp8_variant(torch, pipeline, args, stream, wl, vl, P, out, lse, dec):
                                       "frac": round(gbs / PEAK_HBM_GBS, 4),
                                       "bytes_per_query": per_q}}
         del dbufs, fp8d
+    torch.cuda.empty_cache()
+    return res
+
+
+def grouped_variant(torch, dsa, pipeline, args, stream, wl, vl, P, out, lse, iid_attn_ms):
+    """Adjacent-query de-duplication (grouped attention, 16 rows per union of
+    index sets) against the per-row attention, on prefill_128k_corr: the same
+    tensors as the headline prefill except the indexer queries, which share a
+    per-block mean.  Both whole prefills are timed; the union sizes come from
+    an untimed pass.  The grouped attention on the headline (i.i.d.-query)
+    workload is timed too, where the sets barely overlap."""
+    import synth
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    wc = synth.prefill_128k_corr()
+    log(f"grouped attention: generating {wc.name} indexer queries")
+    qc = upload_bf16(torch, wc.q_idx())
+    res = {"workload": f"{wc.name} (indexer query block means of std {wc.query_mean_std})",
+           "group_rows": 16}
+    modes = {}
+    for name, grouped in (("per_row", False), ("grouped", True)):
+        bufs = pipeline.alloc_prefill(vl, wl.topk, args.window, grouped=grouped)
+        run = lambda rec: pipeline.prefill(vl, qc, P["k_idx"], P["w"], P["q"], P["k"], P["v"],  # noqa: E731
+                                           out, bufs, lse=lse, stream=stream, record=rec)
+        for _ in range(args.warmup):
+            run(None)
+        torch.cuda.synchronize()
+        rec, tot = [], 0.0
+        for _ in range(args.steps):
+            a, b = ev(), ev()
+            a.record(stream)
+            run(rec)
+            b.record(stream)
+            torch.cuda.synchronize()
+            tot += a.elapsed_time(b)
+        attn = sum(e["sparse_attn"][0].elapsed_time(e["sparse_attn"][1]) for _, _, e in rec)
+        modes[name] = {"prefill_ms": round(tot / args.steps, 3),
+                       "tokens_per_s": round(wl.total_q / (tot / args.steps / 1e3), 1),
+                       "sparse_attn_ms": round(attn / args.steps, 3)}
+        if grouped:
+            # Union sizes of every group, one window at a time (untimed).
+            counts = []
+            window = bufs.scores.shape[0]
+            for r0 in range(0, wl.total_q, window):
+                n = min(window, wl.total_q - r0)
+                dsa.dsa_index_scores(vl, qc, P["k_idx"], P["w"], bufs.scores, row_begin=r0,
+                                     row_count=n)
+                dsa.dsa_topk(vl, bufs.scores, bufs.indices, row_begin=r0, row_count=n)
+                dsa.dsa_sparse_attn_prefill_grouped(vl, P["q"], P["k"], P["v"], bufs.indices, out,
+                                                    bufs.grouped, row_begin=r0, row_count=n)
+                groups = (n + 15) // 16
+                ent = groups * 16 * wl.topk
+                off = -(-ent * 4 // 256) * 256 + -(-ent * 2 // 256) * 256
+                counts.append(bufs.grouped[off:off + 4 * groups].view(torch.int32).cpu())
+            c = torch.cat(counts).double()
+            res["unique_kv_per_16_rows"] = {"mean": round(float(c.mean()), 1),
+                                            "min": int(c.min()), "max": int(c.max()),
+                                            "without_dedup": 16 * wl.topk}
+            # The grouped attention on the headline workload's own indices.
+            tot_iid = 0.0
+            for r0 in range(0, wl.total_q, window):
+                n = min(window, wl.total_q - r0)
+                dsa.dsa_index_scores(vl, P["q_idx"], P["k_idx"], P["w"], bufs.scores, row_begin=r0,
+                                     row_count=n)
+                dsa.dsa_topk(vl, bufs.scores, bufs.indices, row_begin=r0, row_count=n)
+                a, b = ev(), ev()
+                a.record(stream)
+                dsa.dsa_sparse_attn_prefill_grouped(vl, P["q"], P["k"], P["v"], bufs.indices, out,
+                                                    bufs.grouped, row_begin=r0, row_count=n)
+                b.record(stream)
+                torch.cuda.synchronize()
+                tot_iid += a.elapsed_time(b)
+            res["headline_workload_attention_ms"] = {"per_row": round(iid_attn_ms, 3),
+                                                     "grouped": round(tot_iid, 3)}
+        del bufs
+    res.update(modes)
+    del qc
     torch.cuda.empty_cache()
     return res
 

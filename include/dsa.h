@@ -230,8 +230,9 @@ int dsa_sparse_attn_prefill_grouped_workspace_size(const dsa_varlen* vl, int64_t
  *              dsa_sparse_attn_prefill_grouped_workspace_size bytes for this
  *              row_count and topk, 256-byte aligned, contents clobbered; calls
  *              sharing it must be ordered.
- * Supported: as dsa_sparse_attn_prefill, plus all K (and V) rows at most
- * 2 GiB (total_k * n_heads_kv * head_dim * 2 < 2^31).
+ * Supported: as dsa_sparse_attn_prefill with n_heads_q / n_heads_kv in
+ * {1, 2, 4, 8}, plus all K (and V) rows at most 2 GiB
+ * (total_k * n_heads_kv * head_dim * 2 < 2^31).
  */
 int dsa_sparse_attn_prefill_grouped(const dsa_varlen* vl, const void* q, const void* k,
                                     const void* v, const int32_t* indices, int32_t topk,

@@ -340,6 +340,10 @@ int dsa_sparse_attn_prefill_grouped(const dsa_varlen* vl, const void* q, const v
     return fail(DSA_ERR_INVALID_ARGUMENT, "indices is NULL or misaligned");
   if (lse != nullptr && !aligned(lse, 4)) return fail(DSA_ERR_INVALID_ARGUMENT, "lse misaligned");
   if ((st = check_attn_shape(n_heads_q, n_heads_kv, head_dim, topk, softmax_scale))) return st;
+  const int32_t group_heads = n_heads_q / n_heads_kv;
+  if ((group_heads & (group_heads - 1)) != 0 || group_heads > 8)
+    return fail(DSA_ERR_UNSUPPORTED, "n_heads_q / n_heads_kv = %d is not 1, 2, 4 or 8",
+                group_heads);
   // The grouped kernels address all K (and V) rows with 32-bit offsets.
   if (vl->total_k * n_heads_kv * head_dim * 2 > INT32_MAX)
     return fail(DSA_ERR_UNSUPPORTED, "K or V rows exceed 2 GiB (total_k %lld)",

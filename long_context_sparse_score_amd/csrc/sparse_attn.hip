@@ -30,6 +30,9 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Growth of a head's maximum (log2 units) that the running softmax
+// reference absorbs before it is moved (P terms stay below 2^8).
+constexpr float kRescaleLog2 = 8.0f;
 
 template <int D>
 struct AttnCfg {
@@ -59,17 +62,17 @@ struct GatherTile {
 // one 32-bit offset shared by its K and V loads.
 template <int D>
 __device__ __forceinline__ void gather_tile(GatherTile<D>& t, const int32_t* idx, int s0,
-                                            int n_slots, const RowInfo& ri,
                                             __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
                                             int n_heads_kv, int g, int lane) {
   using C = AttnCfg<D>;
   const int q = lane / C::PIECES, piece = lane % C::PIECES;
 #pragma unroll
   for (int j = 0; j < C::LPT; ++j) {
-    const int slot = s0 + q * C::LPT + j;
-    const int32_t p = slot < n_slots ? idx[slot] : -1;
-    const bool ok = p >= 0 && p <= ri.pos;
-    const uint32_t off = ((static_cast<uint32_t>(ok ? p : 0) * n_heads_kv + g) * D + piece * 8) * 2;
+    // idx holds -1 past the slice.  A row outside 0..pos (-1 included:
+    // (g - n_heads_kv) D 2 wraps to at least 2^32 - 2^31) lies past the
+    // buffer's range and reads zeros; its slot is masked anyway.
+    const int32_t p = idx[s0 + q * C::LPT + j];
+    const uint32_t off = ((static_cast<uint32_t>(p) * n_heads_kv + g) * D + piece * 8) * 2;
     t.k[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0));
     t.v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0));
   }
@@ -120,33 +123,46 @@ __device__ __forceinline__ void compute_tile(const bf16x8 (&qb)[AttnCfg<D>::KS],
   }
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(m_run, mx);
-  const float corr = m_new == -INFINITY ? 1.0f : exp2f(m_run - m_new);
+  // Lazy rescaling: the reference m_run (log2 domain) moves only when some
+  // head's tile maximum exceeds it by more than kRescaleLog2, so most tiles
+  // skip the rescale of l and O.  Otherwise P is taken against the older
+  // reference (terms up to 2^kRescaleLog2); O, l and the log-sum-exp all
+  // use the same reference, so the normalised result is unchanged.
+  if (__any(mx > m_run + kRescaleLog2)) {
+    const float m_new = fmaxf(m_run, mx);
+    const float corr = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= corr;
+    m_run = m_new;
+    // O rows (heads 4*qd + r) take their head's correction.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float cr = __shfl(corr, 4 * qd + r);
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) acc[dt][r] *= cr;
+    }
+  }
+  // Masked slots hold -inf, whose exp2 is 0; a reference still at -inf
+  // means every slot so far was masked, and 0 then serves as well.
+  const float m_use = m_run == -INFINITY ? 0.0f : m_run;
   float pr[2][4];
   float psum = 0.0f;
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      pr[sub][r] = z[sub][r] == -INFINITY ? 0.0f : exp2f(z[sub][r] - m_new);
+      pr[sub][r] = __builtin_amdgcn_exp2f(z[sub][r] - m_use);
       psum += pr[sub][r];
     }
-  l_run = l_run * corr + psum;
-  m_run = m_new;
+  l_run += psum;
 
   // P as the A operand: row = head col, contraction index 8*qd + i maps to
-  // slot 4*qd + i (i < 4) and 16 + 4*qd + i - 4 (i >= 4).
-  uint4 pa_u;
-  pa_u.x = pack_bf16x2(pr[0][0], pr[0][1]);
-  pa_u.y = pack_bf16x2(pr[0][2], pr[0][3]);
-  pa_u.z = pack_bf16x2(pr[1][0], pr[1][1]);
-  pa_u.w = pack_bf16x2(pr[1][2], pr[1][3]);
-  const bf16x8 pa = __builtin_bit_cast(bf16x8, pa_u);
+  // slot 4*qd + i (i < 4) and 16 + 4*qd + i - 4 (i >= 4); converted with
+  // round-to-nearest-even.
+  typedef float f32x8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 bf16x8n __attribute__((ext_vector_type(8)));
+  const f32x8 pf = {pr[0][0], pr[0][1], pr[0][2], pr[0][3], pr[1][0], pr[1][1], pr[1][2], pr[1][3]};
+  const bf16x8 pa = __builtin_bit_cast(bf16x8, __builtin_convertvector(pf, bf16x8n));
 
-  // Rescale O rows (heads 4*qd + r) by their head's correction.
-  float cr[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * qd + r);
   // B operand: column d = 16 dt + col, rows = slots 4 qd + i and 16 + 4 qd + i
   // (i < 4), the order of P's contraction.  ds_read_b64_tr_b16 transposes
   // within each 16-lane group: lane t receives element t % 4 of the 4-element
@@ -157,8 +173,6 @@ __device__ __forceinline__ void compute_tile(const bf16x8 (&qb)[AttnCfg<D>::KS],
   const int tr_row = 4 * qd + (col >> 2);
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[dt][r] *= cr[r];
     const int d0 = dt * 16 + 4 * (col & 3);
     const int piece = d0 / 8, e = d0 % 8;
     typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -193,12 +207,18 @@ __device__ __forceinline__ void attend_tile(const GatherTile<D>& t, const bf16x8
   compute_tile<D>(qb, ks_lds, vs_lds, vm, scale_log2, lane, m_run, l_run, acc);
 }
 
+// Entries of the LDS index slice: the slice rounded up to 64 plus the 64
+// that the look-ahead gather reads past it, all -1 beyond the slice.
+__host__ __device__ constexpr int attn_idx_entries(int per_split) {
+  return (per_split + 63) / 64 * 64 + 64;
+}
+
 // LDS of one workgroup: K and V tiles of every KV head, the slice of the
 // index list, and one validity word per 32 slots.
 template <int D>
 __host__ __device__ constexpr size_t attn_lds_bytes(int n_heads_kv, int per_split) {
   return static_cast<size_t>(2 * n_heads_kv) * AttnCfg<D>::TILE * sizeof(uint16_t) +
-         static_cast<size_t>(per_split) * sizeof(int32_t) +
+         static_cast<size_t>(attn_idx_entries(per_split)) * sizeof(int32_t) +
          static_cast<size_t>((per_split + 63) / 64 * 2) * sizeof(uint32_t);
 }
 
@@ -228,14 +248,15 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(
   uint16_t* vs_lds = lds_all + (n_heads_kv + g) * C::TILE;
   // This slice of the row's index list, shared by all KV heads, in LDS, and
   // a bitmask of its usable slots (0 <= p <= pos), one word per 32 slots.
+  const int n_idx = attn_idx_entries(per_split);
   int32_t* idx = reinterpret_cast<int32_t*>(lds_all + 2 * n_heads_kv * C::TILE);
-  uint32_t* vbits = reinterpret_cast<uint32_t*>(idx + per_split);
+  uint32_t* vbits = reinterpret_cast<uint32_t*>(idx + n_idx);
   const int32_t* irow = indices + local * topk + i0;
   const int n_pad = (n_slots + 63) & ~63;
-  for (int base = 0; base < n_pad; base += static_cast<int>(blockDim.x)) {
+  for (int base = 0; base < n_pad + 64; base += static_cast<int>(blockDim.x)) {
     const int s = base + static_cast<int>(threadIdx.x);
     const int32_t p = s < n_slots ? irow[s] : -1;
-    if (s < n_slots) idx[s] = p;
+    if (s < n_pad + 64) idx[s] = p;
     const unsigned long long ok = __ballot(p >= 0 && p <= ri.pos);
     const int w0 = base + (static_cast<int>(threadIdx.x) & ~(kWave - 1));
     if (lane == 0 && w0 < n_pad) {
@@ -268,11 +289,11 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(
   const __amdgpu_buffer_rsrc_t kr = raw_buffer(k + ri.key_base * n_heads_kv * D, seq_bytes);
   const __amdgpu_buffer_rsrc_t vr = raw_buffer(v + ri.key_base * n_heads_kv * D, seq_bytes);
   GatherTile<D> ta, tb;
-  gather_tile<D>(ta, idx, 0, n_slots, ri, kr, vr, n_heads_kv, g, lane);
+  gather_tile<D>(ta, idx, 0, kr, vr, n_heads_kv, g, lane);
   for (int s0 = 0; s0 < n_slots; s0 += 64) {
-    gather_tile<D>(tb, idx, s0 + 32, n_slots, ri, kr, vr, n_heads_kv, g, lane);
+    gather_tile<D>(tb, idx, s0 + 32, kr, vr, n_heads_kv, g, lane);
     attend_tile<D>(ta, qb, ks_lds, vs_lds, vbits[s0 / 32], scale_log2, lane, m_run, l_run, acc);
-    gather_tile<D>(ta, idx, s0 + 64, n_slots, ri, kr, vr, n_heads_kv, g, lane);
+    gather_tile<D>(ta, idx, s0 + 64, kr, vr, n_heads_kv, g, lane);
     attend_tile<D>(tb, qb, ks_lds, vs_lds, vbits[s0 / 32 + 1], scale_log2, lane, m_run, l_run, acc);
   }
 
@@ -507,11 +528,58 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(
 
 // One workgroup per (group, KV head); wave w serves the group's queries
 // 16 w .. 16 w + 15 of this KV head (query c = row c / G, head c mod G).
-// JOBS: 16-byte gather loads per lane and tile (32 rows x D x 2 bytes of K,
-// and of V, over the workgroup), the smallest power of two that covers the
-// tile; a workgroup of 64 G threads then has at most 1024 / JOBS threads.
-template <int D, int JOBS>
-__global__ __launch_bounds__(1024 / JOBS) void grouped_attn_kernel(
+// Union tiles of 32 entries stream through an LDS ring of R slots by
+// buffer->LDS DMA, so R - 1 tiles are in flight while one is used: the
+// K and V rows of the tile's entries (2 x 32 x D / 8 16-byte chunks, COPIES
+// per lane: G is a power of two, so every wave issues the same copies),
+// while each wave loads the tile's 32 row masks into a register.  The union
+// keys that address a tile's copies are loaded into registers R - 1 tiles
+// earlier, so they have landed by the ring's counted wait that precedes the
+// copies (a key read at copy time would stall every wave on a miss each
+// tile).  Every step issues the same loads (past the union's end they read
+// zeros, copied into a slot nobody reads), which keeps the counts fixed.
+//
+// R = grouped_ring: as many slots as leave room in LDS (at most
+// kMaxRingG), bounded so that the counted wait ((R - 2) (COPIES + 2) loads)
+// fits its 6-bit field.  Four slots measured as fast as eight, at fewer
+// registers.
+constexpr int kMaxRingG = 4;
+template <int D, int COPIES>
+constexpr int grouped_ring() {
+  constexpr int by_wait = 2 + 63 / (COPIES + 2);
+  constexpr int by_lds = (128 * 1024) / (2 * AttnCfg<D>::TILE * 2 + 512);
+  constexpr int r = by_wait < by_lds ? by_wait : by_lds;
+  return r < kMaxRingG ? r : kMaxRingG;
+}
+
+// Ring slot B: K tile, V tile, then 128 union masks from the tile's first
+// (only its 32 are read); and key slot B: 64 union keys from a tile's first.
+// One LDS variable each: the compiler then sees that a slot being read is
+// not the one a copy in flight writes, and places no wait for those copies
+// before the reads.
+template <int D, int B>
+__device__ __forceinline__ uint16_t* grouped_slot() {
+  __shared__ __attribute__((aligned(16))) uint16_t buf[2 * AttnCfg<D>::TILE + 2 * kWave];
+  return buf;
+}
+template <int B>
+__device__ __forceinline__ int32_t* grouped_keyslot() {
+  __shared__ __attribute__((aligned(16))) int32_t buf[kWave];
+  return buf;
+}
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, i>) for i = 0 .. N - 1, in order.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <int D, int COPIES>
+__global__ __launch_bounds__(8 * D / COPIES) void grouped_attn_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int64_t total_k, int topk, int64_t row_begin,
@@ -519,11 +587,12 @@ __global__ __launch_bounds__(1024 / JOBS) void grouped_attn_kernel(
     uint16_t* __restrict__ out, float* __restrict__ lse, const int32_t* __restrict__ ukeys,
     const uint16_t* __restrict__ umasks, const int32_t* __restrict__ ucount) {
   using C = AttnCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t kt[2][C::TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[2][C::TILE];
+  constexpr int CH = 32 * C::PIECES;      // 16-byte chunks of one K (or V) tile
+  constexpr int RPI = kWave / C::PIECES;  // tile rows per copy instruction
+  constexpr int R = grouped_ring<D, COPIES>();
   const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
-  const int nthreads = blockDim.x;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  constexpr int NTHREADS = 8 * D / COPIES;  // the launch's block size, 64 G
   const int G = n_heads_q / n_heads_kv;
   const int col = lane & 15, qd = lane >> 4;
   const int64_t g = blockIdx.x;
@@ -539,6 +608,9 @@ __global__ __launch_bounds__(1024 / JOBS) void grouped_attn_kernel(
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks)
     qb[ks] = active ? load_bf16x8(q + (row * n_heads_q + hq) * D + ks * 32 + qd * 8) : zero_bf16x8();
+  // The queries have landed before the ring starts, so the ring's counted
+  // waits below are the only vector-memory waits in the loop.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   // Rows of this wave's 16 columns: rl_first .. rl_first + nrw - 1.
   const int rl_first = (16 * wave) / G;
   const int nrw = (16 * wave + 15) / G - rl_first + 1;
@@ -547,33 +619,45 @@ __global__ __launch_bounds__(1024 / JOBS) void grouped_attn_kernel(
   const int32_t* keys = ukeys + g * grouped_ws_entries(topk);
   const uint16_t* masks = umasks + g * grouped_ws_entries(topk);
   const int kv_bytes = static_cast<int>(total_k * n_heads_kv * D * 2);
-  const __amdgpu_buffer_rsrc_t kr = raw_buffer(k, kv_bytes);
-  const __amdgpu_buffer_rsrc_t vr = raw_buffer(v, kv_bytes);
-  // Gather job j of thread t: tile row (t + j nthreads) / PIECES, piece
-  // (t + j nthreads) mod PIECES.
-  u32x4 rk[JOBS], rv[JOBS];
-  auto gather = [&](int t0) {
-#pragma unroll
-    for (int j = 0; j < JOBS; ++j) {
-      const int e = static_cast<int>(threadIdx.x) + j * nthreads;
-      const int slot = t0 + e / C::PIECES, piece = e % C::PIECES;
-      const bool ok = e < 32 * C::PIECES && slot < count;
-      const int32_t key = ok ? keys[slot] : 0;
-      const uint32_t off = ((static_cast<uint32_t>(key) * n_heads_kv + h) * D + piece * 8) * 2;
-      rk[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0));
-      rv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0));
-    }
+  // Whole words up to the union's end (a word read partly past the range
+  // would come back as zero); the group's mask region always holds them.
+  const __amdgpu_buffer_rsrc_t mr = raw_buffer(masks, (count * 2 + 3) & ~3);
+  // Copies of tile t into a ring slot.  Copy j of this wave covers chunks
+  // cbase .. cbase + 63 (cbase uniform); chunk c is piece c mod PIECES of
+  // tile row c / PIECES in LDS, filled from global piece
+  // (c mod PIECES) ^ (row mod PIECES) (the tile_at swizzle).  The tile's 32
+  // row masks come with them into a register: lane l gets the word holding
+  // the masks of slots 2 (l mod 32) / 2 and the one after (zero past the
+  // union's end).
+  const __amdgpu_buffer_rsrc_t kyr = raw_buffer(keys, count * 4);
+  // Union keys u*32 .. u*32 + 63 into a key slot (4 bytes a lane; zero past
+  // the union's end).  Every wave copies the same words, so every wave
+  // issues the same loads.
+  auto copy_keys = [&](int u, int32_t* ks) __attribute__((always_inline)) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        kyr, (__attribute__((address_space(3))) void*)ks, 4, lane * 4, u * 128, 0, 0);
   };
-  auto store = [&](int b) {
+  // Copies of tile u into ring slot rs, addressed by the keys in key slot ks;
+  // then its masks (4 bytes a lane, from entry u*32) behind the V tile.
+  auto issue = [&](int u, uint16_t* rs, const int32_t* ks) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < JOBS; ++j) {
-      const int e = static_cast<int>(threadIdx.x) + j * nthreads;
-      if (e < 32 * C::PIECES) {
-        const int at = tile_at<D>(e / C::PIECES, e % C::PIECES);
-        *reinterpret_cast<u32x4*>(&kt[b][at]) = rk[j];
-        *reinterpret_cast<u32x4*>(&vt[b][at]) = rv[j];
-      }
+    for (int j = 0; j < COPIES; ++j) {
+      // Chunks 0 .. CH - 1 are the K tile's, CH .. 2 CH - 1 the V tile's
+      // (CH is a multiple of 64, so a copy is all K or all V).
+      const int cc = j * NTHREADS + kWave * wave;
+      const bool is_v = cc >= CH;
+      const int cbase = is_v ? cc - CH : cc;
+      const int c = cbase + lane;
+      const int r = c / C::PIECES;
+      const int piece = (c % C::PIECES) ^ (r % C::PIECES);
+      const int off = ((ks[r] * n_heads_kv + h) * D + piece * 8) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          raw_buffer(is_v ? v : k, kv_bytes),
+          (__attribute__((address_space(3))) void*)(&rs[(is_v ? C::TILE : 0) + cbase * 8]), 16,
+          off, 0, 0, 0);
     }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        mr, (__attribute__((address_space(3))) void*)(&rs[2 * C::TILE]), 4, lane * 4, u * 64, 0, 0);
   };
 
   f32x4 acc[C::DT];
@@ -581,22 +665,60 @@ __global__ __launch_bounds__(1024 / JOBS) void grouped_attn_kernel(
   for (int dt = 0; dt < C::DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;
   const int ntiles = (count + 31) / 32;
-  gather(0);
-  for (int t = 0; t < ntiles; ++t) {
-    const int b = t & 1;
-    store(b);
-    const int slot = t * 32 + (lane & 31);
-    const uint32_t m16 = slot < count ? masks[slot] : 0u;
-    __syncthreads();  // tile t in LDS; every wave is done with tile t - 1
-    if (t + 1 < ntiles) gather((t + 1) * 32);
+  // Every step issues, in order, the keys of tile u + R - 1, the copies of
+  // tile u and its masks (COPIES + 2 loads); the loop's step t is such a step
+  // with u = t + R - 1.  The prologue runs it for u = 0 .. R - 2 once the
+  // first tiles' keys are in.
+  static_for<R - 1>([&](auto b) __attribute__((always_inline)) {
+    copy_keys(decltype(b)::value, grouped_keyslot<decltype(b)::value>());
+  });
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  lds_barrier();
+  static_for<R - 1>([&](auto b) __attribute__((always_inline)) {
+    constexpr int U = decltype(b)::value;
+    // Key slot (U + R - 1) mod R held tile U - 1's keys: every wave has
+    // read them once past this barrier.
+    if constexpr (U > 0) lds_barrier();
+    copy_keys(U + R - 1, grouped_keyslot<(U + R - 1) % R>());
+    issue(U, grouped_slot<D, U>(), grouped_keyslot<U>());
+  });
+  // Tile t from ring slot B = t mod R; the copies of tile t + R - 1 go to
+  // slot (B + R - 1) mod R, the one tile t - 1 used.
+  auto step = [&](auto tag, int t) __attribute__((always_inline)) {
+    constexpr int B = decltype(tag)::value;
+    constexpr int BN = (B + R - 1) % R;
+    // Tile t has landed once only the R - 2 younger steps' loads are
+    // outstanding, and so have the keys of tile t + R - 1, copied before
+    // tile t; the barrier makes every wave's copies visible and frees slot
+    // BN and key slot (B + R - 2) mod R (all waves are done with tile t - 1).
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((R - 2) * (COPIES + 2)));
+    lds_barrier();
+    const uint16_t* rs = grouped_slot<D, B>();
+    const uint32_t mw = reinterpret_cast<const uint32_t*>(rs + 2 * C::TILE)[(lane & 31) >> 1];
+    copy_keys(t + 2 * R - 2, grouped_keyslot<(B + 2 * R - 2) % R>());
+    issue(t + R - 1, grouped_slot<D, BN>(), grouped_keyslot<BN>());
+    const uint32_t m16 = t * 32 + (lane & 31) >= count ? 0u
+                         : (lane & 1)                   ? (mw >> 16)
+                                                        : (mw & 0xFFFFu);
     // Validity of the 32 slots for this lane's row.
     uint32_t vm = 0u;
     for (int i = 0; i < nrw; ++i) {
       const uint32_t w = static_cast<uint32_t>(__ballot((m16 >> (rl_first + i)) & 1u));
       if (rl == rl_first + i) vm = w;
     }
-    compute_tile<D>(qb, kt[b], vt[b], vm, scale_log2, lane, m_run, l_run, acc);
-  }
+    // The index sets come in runs of nearby positions, so a tile often holds
+    // none of this wave's rows: the wave then skips it (a fully masked tile
+    // changes nothing).
+    if (__any(vm != 0u))
+      compute_tile<D>(qb, rs, rs + C::TILE, vm, scale_log2, lane, m_run, l_run, acc);
+  };
+  // Whole rounds of R tiles: a tile past the union's end has all masks zero
+  // and changes nothing, and straight-line rounds let the compiler see which
+  // loads each register waits for.
+  for (int t = 0; t < ntiles; t += R)
+    static_for<R>([&](auto b) __attribute__((always_inline)) { step(b, t + decltype(b)::value); });
+  // No copy may still be writing LDS when the wave ends.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   // Normalise; O rows of this lane are columns 4 qd + r.
   float l_tot = l_run + __shfl_xor(l_run, 16);
@@ -604,7 +726,7 @@ __global__ __launch_bounds__(1024 / JOBS) void grouped_attn_kernel(
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float lr = __shfl(l_tot, 4 * qd + r);
-    const float mr = __shfl(m_run, 4 * qd + r);
+    const float mrun = __shfl(m_run, 4 * qd + r);
     const int c = 16 * wave + 4 * qd + r;
     const int rr = c / G;
     if (first + rr >= row_count) continue;
@@ -616,17 +738,17 @@ __global__ __launch_bounds__(1024 / JOBS) void grouped_attn_kernel(
     for (int dt = 0; dt < C::DT; ++dt)
       orow[dt * 16 + col] = static_cast<uint16_t>(f32_to_bf16_bits(acc[dt][r] * inv));
     if (lse != nullptr && col == 0)
-      lse[orow_i * n_heads_q + ohq] = lr > 0.0f ? (mr + log2f(lr)) * kLn2 : -INFINITY;
+      lse[orow_i * n_heads_q + ohq] = lr > 0.0f ? (mrun + log2f(lr)) * kLn2 : -INFINITY;
   }
 }
 
-template <int D, int JOBS>
+template <int D, int COPIES>
 void launch_grouped_attn_d(dim3 grid, dim3 block, hipStream_t stream, const dsa_varlen& vl,
                            const uint16_t* q, const uint16_t* k, const uint16_t* v, int topk,
                            int64_t row_begin, int64_t row_count, int n_heads_q, int n_heads_kv,
                            float scale_log2, uint16_t* out, float* lse,
                            const GroupedWorkspace& ws) {
-  hipLaunchKernelGGL((grouped_attn_kernel<D, JOBS>), grid, block, 0, stream, vl.cu_seqlens_q,
+  hipLaunchKernelGGL((grouped_attn_kernel<D, COPIES>), grid, block, 0, stream, vl.cu_seqlens_q,
                      vl.cu_seqlens_k, vl.batch, q, k, v, vl.total_k, topk, row_begin, row_count,
                      n_heads_q, n_heads_kv, scale_log2, out, lse, ws.keys, ws.masks, ws.counts);
 }
@@ -656,24 +778,30 @@ hipError_t launch_grouped_attn(const dsa_varlen& vl, const uint16_t* q, const ui
   const dim3 grid(static_cast<unsigned>(groups), static_cast<unsigned>(n_heads_kv));
   const dim3 block(kWave * G);  // 16 G queries per KV head, 16 per wave
   const float scale_log2 = scale * kLog2e;
-  const int jobs = (32 * (head_dim / 8) + kWave * G - 1) / (kWave * G);
-  auto go = [&](auto d_tag, auto jobs_tag) {
-    launch_grouped_attn_d<decltype(d_tag)::value, decltype(jobs_tag)::value>(
+  // Copies per lane and tile: 2 x 32 rows x head_dim / 8 chunks over 64 G
+  // lanes (G in {1, 2, 4, 8}, checked by the caller): head_dim / (8 G).
+  const int copies = head_dim / (8 * G);
+  auto go = [&](auto d_tag, auto copies_tag) {
+    launch_grouped_attn_d<decltype(d_tag)::value, decltype(copies_tag)::value>(
         grid, block, stream, vl, q, k, v, topk, row_begin, row_count, n_heads_q, n_heads_kv,
         scale_log2, out, lse, ws);
   };
   using I64 = std::integral_constant<int, 64>;
   using I128 = std::integral_constant<int, 128>;
-  // The smallest compiled JOBS that covers the tile.
   if (head_dim == 128) {
-    if (jobs > 4) go(I128{}, std::integral_constant<int, 8>{});
-    else if (jobs > 2) go(I128{}, std::integral_constant<int, 4>{});
-    else if (jobs > 1) go(I128{}, std::integral_constant<int, 2>{});
-    else go(I128{}, std::integral_constant<int, 1>{});
+    switch (copies) {
+      case 16: go(I128{}, std::integral_constant<int, 16>{}); break;
+      case 8: go(I128{}, std::integral_constant<int, 8>{}); break;
+      case 4: go(I128{}, std::integral_constant<int, 4>{}); break;
+      default: go(I128{}, std::integral_constant<int, 2>{}); break;
+    }
   } else {
-    if (jobs > 2) go(I64{}, std::integral_constant<int, 4>{});
-    else if (jobs > 1) go(I64{}, std::integral_constant<int, 2>{});
-    else go(I64{}, std::integral_constant<int, 1>{});
+    switch (copies) {
+      case 8: go(I64{}, std::integral_constant<int, 8>{}); break;
+      case 4: go(I64{}, std::integral_constant<int, 4>{}); break;
+      case 2: go(I64{}, std::integral_constant<int, 2>{}); break;
+      default: go(I64{}, std::integral_constant<int, 1>{}); break;
+    }
   }
   return hipGetLastError();
 }

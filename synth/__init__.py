@@ -346,6 +346,14 @@ def prefill_128k() -> Workload:
     return _prefill("prefill_128k", 3, [131072], clustered=True, **_BIG)
 
 
+def prefill_128k_corr() -> Workload:
+    """prefill_128k with correlated indexer queries: a per-(256-token block,
+    head) mean of std 8 shared by the block's queries, so that 16 adjacent
+    queries select about 7-10 K distinct positions between them (the page's
+    figure for real data is about 8000) instead of 19-26 K."""
+    return prefill_128k().with_(name="prefill_128k_corr", query_mean_std=8.0)
+
+
 def decode_b64_128k() -> Workload:
     return Workload(name="decode_b64_128k", seed=4, seqlens_q=(1,) * 64,
                     seqlens_k=(131072,) * 64, **_BIG)

@@ -285,6 +285,8 @@ def test_grouped_attention_validation():
     assert call(ws_bytes=need - 1) == dsa.DSA_ERR_WORKSPACE
     assert call(ws=FAKE + 64) == dsa.DSA_ERR_WORKSPACE
     assert call(hq=30) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert call(hq=24, hkv=8) == dsa.DSA_ERR_UNSUPPORTED   # 3 query heads per KV head
+    assert call(hq=64, hkv=4) == dsa.DSA_ERR_UNSUPPORTED   # 16 query heads per KV head
     assert call(topk=5000) == dsa.DSA_ERR_UNSUPPORTED
     # all K rows beyond 2 GiB (the grouped kernels use one 32-bit offset space)
     big = vl(total_q=100, total_k=3_000_000, max_q=100, max_k=3_000_000)
