@@ -48,7 +48,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--window", type=int, default=8192, help="prefill query rows per score window")
+    ap.add_argument("--window", type=int, default=2048,
+                    help="prefill query rows per score window (2048 measured fastest of 512..8192)")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -149,9 +150,10 @@ def decode_bytes(wd):
 
 # ---------------------------------------------------------------- CPU baseline
 
-def counter_traffic(kernel_source, record):
+def counter_traffic(kernel_source, record, window_rows):
     """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE counter
-    record, or None once the kernel source differs from the one measured."""
+    record, or None once the kernel source or the window size differs from
+    the one measured."""
     import hashlib
 
     try:
@@ -161,7 +163,7 @@ def counter_traffic(kernel_source, record):
             digest = hashlib.sha256(f.read()).hexdigest()
     except OSError:
         return None
-    if rec.get("source_sha256") != digest:
+    if rec.get("source_sha256") != digest or rec.get("window_rows") != window_rows:
         return None
     return int(rec["fetch_bytes_per_dispatch"] + rec["write_bytes_per_dispatch"])
 
@@ -350,7 +352,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(idx_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": counter_traffic("long_context_sparse_score_amd/csrc/index_scores.hip",
-                                       "profiles/index_scores_traffic.json"),
+                                       "profiles/index_scores_traffic.json", window),
             "traffic_unit": "HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
             "algorithmic_bytes_per_launch": int(pc["b_idx"] / max(1, n_idx_launches // args.steps)),
             "launches_per_step": n_idx_launches // args.steps,
