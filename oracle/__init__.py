@@ -59,8 +59,11 @@ def _load():
     lib.oracle_dequantize_fp8.restype = None
     lib.oracle_index_scores_f64.argtypes = [ctypes.c_int, p, p, p, p, p, ctypes.c_int,
                                             ctypes.c_int, i64, p, p, i64]
+    lib.oracle_indexer_kl.argtypes = [ctypes.c_int, p, p, p, p, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_double, i64, p, p, i64, p, p]
     for f in (lib.oracle_visible_counts, lib.oracle_index_scores, lib.oracle_topk,
-              lib.oracle_sparse_attn, lib.oracle_quantize_fp8, lib.oracle_index_scores_f64):
+              lib.oracle_sparse_attn, lib.oracle_quantize_fp8, lib.oracle_index_scores_f64,
+              lib.oracle_indexer_kl):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -223,6 +226,37 @@ def sparse_attn(cu_q, cu_k, q, k, v, idx, rows, scale: float):
                               idx.shape[1], _ptr(out), _ptr(lse)):
         raise ValueError("invalid row or index outside the causal prefix")
     return out, lse
+
+
+def indexer_kl(cu_q, cu_k, q, k, scores, rows, scale: float, want_grad: bool = True):
+    """Indexer warm-up loss per query row (page 5 section 1, training stages:
+    the dense warm-up trains the indexer so that its distribution over
+    positions approaches the full attention's, the gap measured by KL
+    divergence).  With P = the per-head dense softmax over the visible keys,
+    averaged over query heads, and Pi = the softmax of the row's indexer
+    scores: loss = KL(P || Pi) and grad = d loss / d I = Pi - P.
+    scores: float [n, ld] for the listed rows (columns 0..p used).
+    Returns (loss float64 [n], grad float64 [n, ld] or None; grad columns
+    past p are 0)."""
+    lib = _load()
+    cu_q, cu_k = _c(cu_q, np.int32), _c(cu_k, np.int32)
+    q, k = _bf16_bits(q), _bf16_bits(k)
+    scores = _c(scores, np.float64)
+    rows = _c(rows, np.int64)
+    hq, d = q.shape[1], q.shape[2]
+    hkv = k.shape[1]
+    if hq % hkv or k.shape[2] != d:
+        raise ValueError("attention shapes disagree")
+    n, ld = scores.shape
+    if rows.shape[0] != n:
+        raise ValueError("one score row per listed row")
+    loss = np.empty(n, np.float64)
+    grad = np.zeros((n, ld), np.float64) if want_grad else None
+    if lib.oracle_indexer_kl(len(cu_q) - 1, _ptr(cu_q), _ptr(cu_k), _ptr(q), _ptr(k), hq, hkv,
+                             d, float(scale), n, _ptr(rows), _ptr(scores), ld, _ptr(loss),
+                             _ptr(grad) if want_grad else None):
+        raise ValueError("invalid row or score rows shorter than the causal prefix")
+    return loss, grad
 
 
 def dsa_rows(cu_q, cu_k, q_idx, k_idx, w, q, k, v, rows, topk_k: int, scale: float,

@@ -359,3 +359,74 @@ int oracle_index_scores_f64(int batch, const int32_t* cu_q, const int32_t* cu_k,
   }
   return bad;
 }
+
+/* ------------------------------------------------------------------------
+ * Indexer warm-up loss (page 5 section 1, the paragraph on the two training
+ * stages: in the dense warm-up the rest of the model is frozen and only the
+ * indexer is trained, so that its judgement of which positions matter comes
+ * close to the full attention's distribution, the gap measured by the KL
+ * divergence).  The pages print no formula.  Read plainly, for query row t
+ * at position p (keys s = 0..p):
+ *   z_h[s]  = scale * Q[t,h] . K[s, h / G]                  (G = Hq / Hkv)
+ *   A_h[s]  = exp(z_h[s]) / sum_{s'} exp(z_h[s'])           (dense attention, head h)
+ *   P[s]    = (1/Hq) sum_h A_h[s]                           (the target: heads averaged)
+ *   Pi[s]   = exp(I[t,s]) / sum_{s'} exp(I[t,s'])           (the indexer's distribution)
+ *   loss[t] = sum_s P[s] (ln P[s] - ln Pi[s])               (KL(P || Pi); P[s] = 0 adds 0)
+ *   grad[t,s] = Pi[s] - P[s]                                (d loss[t] / d I[t,s]; P is a
+ *                                                            fixed target)
+ * scores holds I for the listed rows (row i at scores + i ld, columns 0..p);
+ * grad, when not NULL, receives columns 0..p of each row in the same layout.
+ * ------------------------------------------------------------------------ */
+int oracle_indexer_kl(int batch, const int32_t* cu_q, const int32_t* cu_k,
+                      const uint16_t* Q, const uint16_t* K, int n_heads_q, int n_heads_kv,
+                      int d, double scale, int64_t n_rows, const int64_t* rows,
+                      const double* scores, int64_t ld, double* loss, double* grad) {
+  int bad = 0;
+  int group = n_heads_q / n_heads_kv;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int64_t i = 0; i < n_rows; ++i) {
+    int64_t r = rows[i];
+    int b = find_seq(batch, cu_q, r);
+    loss[i] = 0.0;
+    if (b < 0) { bad = 1; continue; }
+    int64_t p = row_position(cu_q, cu_k, b, r);
+    if (p + 1 > ld) { bad = 1; continue; }
+    int64_t n = p + 1;
+    const double* I = scores + i * ld;
+    double* P = (double*)calloc((size_t)n, sizeof(double));
+    double* z = (double*)malloc(sizeof(double) * (size_t)n);
+    /* P: the per-head softmax over all visible keys, averaged over heads. */
+    for (int h = 0; h < n_heads_q; ++h) {
+      int g = h / group;
+      const uint16_t* q = Q + (r * n_heads_q + h) * (int64_t)d;
+      double m = -INFINITY;
+      for (int64_t s = 0; s < n; ++s) {
+        const uint16_t* key = K + ((cu_k[b] + s) * (int64_t)n_heads_kv + g) * d;
+        double dot = 0.0;
+        for (int c = 0; c < d; ++c) dot += bf16_to_double(q[c]) * bf16_to_double(key[c]);
+        z[s] = scale * dot;
+        if (z[s] > m) m = z[s];
+      }
+      double denom = 0.0;
+      for (int64_t s = 0; s < n; ++s) denom += exp(z[s] - m);
+      for (int64_t s = 0; s < n; ++s) P[s] += exp(z[s] - m) / denom / n_heads_q;
+    }
+    /* ln Pi[s] = I[s] - (mI + ln sum exp(I - mI)). */
+    double mI = -INFINITY;
+    for (int64_t s = 0; s < n; ++s)
+      if (I[s] > mI) mI = I[s];
+    double lI = 0.0;
+    for (int64_t s = 0; s < n; ++s) lI += exp(I[s] - mI);
+    double log_norm = mI + log(lI);
+    double kl = 0.0;
+    for (int64_t s = 0; s < n; ++s) {
+      double log_pi = I[s] - log_norm;
+      if (P[s] > 0.0) kl += P[s] * (log(P[s]) - log_pi);
+      if (grad) grad[i * ld + s] = exp(log_pi) - P[s];
+    }
+    loss[i] = kl;
+    free(P);
+    free(z);
+  }
+  return bad;
+}
