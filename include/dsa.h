@@ -204,6 +204,39 @@ int dsa_sparse_attn_prefill(const dsa_varlen* vl, const void* q, const void* k, 
                             int32_t head_dim, float softmax_scale, void* out, float* lse,
                             hipStream_t stream);
 
+/*
+ * dsa_indexer_kl -- the indexer's warm-up loss and its gradient with respect
+ * to the indexer scores (page 5 section 1, the two training stages: in the
+ * dense warm-up only the indexer is trained, so that its distribution over
+ * positions approaches the full attention's, the gap measured by KL
+ * divergence).  For window row t at position p, keys s = 0..p, G = Hq / Hkv:
+ *   A_h[s]    = softmax_s(softmax_scale * q[t,h] . k[s, h / G])  dense attention of head h
+ *   P[s]      = (1 / n_heads_q) sum_h A_h[s]                    the target, heads averaged
+ *   Pi[s]     = softmax_s(scores[t, s])                         the indexer's distribution
+ *   loss[t]   = sum_s P[s] (ln P[s] - ln Pi[s])                 KL(P || Pi), natural log
+ *   grad[t,s] = Pi[s] - P[s]                                    d loss[t] / d scores[t, s]
+ *
+ *   q       bf16 [total_q, n_heads_q, head_dim]; k bf16 [total_k, n_heads_kv, head_dim]
+ *   scores  fp32 [row_count, ld_scores]: the window's indexer scores as
+ *           dsa_index_scores writes them (columns 0..p read), 16-byte aligned
+ *   loss    fp32 [row_count], one value per window row (caller sums or averages)
+ *   grad    fp32 [row_count, ld_grad] or NULL; columns 0..p written, others
+ *           untouched.  grad == scores (with ld_grad == ld_scores) overwrites
+ *           the scores in place.
+ * Arithmetic: bf16 products with fp32 accumulation (MFMA), fp32 softmax
+ * statistics; every dense logit is computed twice (statistics, then P).
+ * Supported: head_dim in {64, 128}, n_heads_q in {1, 2, 4, ..., 64},
+ * n_heads_kv <= 8 dividing it, one sequence's K rows within 2 GiB.
+ * Invalid: null q, k, scores or loss, misaligned pointers, ld_scores or
+ * ld_grad < max_seqlen_k, ld_scores not a multiple of 4, a window outside
+ * [0, total_q), grad == scores with ld_grad != ld_scores, non-finite scale.
+ * Under DSA_CHECK the scores of the window are checked to be finite first.
+ */
+int dsa_indexer_kl(const dsa_varlen* vl, const void* q, const void* k, const float* scores,
+                   int64_t ld_scores, int64_t row_begin, int64_t row_count, int32_t n_heads_q,
+                   int32_t n_heads_kv, int32_t head_dim, float softmax_scale, float* loss,
+                   float* grad, int64_t ld_grad, hipStream_t stream);
+
 /* Workspace bytes dsa_sparse_attn_prefill_grouped needs for a window of
    row_count rows (the unions of up to ceil(row_count / 16) groups). */
 int dsa_sparse_attn_prefill_grouped_workspace_size(const dsa_varlen* vl, int64_t row_count,

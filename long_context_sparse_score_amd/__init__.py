@@ -13,6 +13,7 @@ Entry points (same names as the C ABI):
     dsa_quantize_fp8, dsa_index_scores_fp8 (the optional fp8 indexer),
     dsa_sparse_attn_prefill_grouped (+ workspace size; 16 adjacent rows per
     union of index sets),
+    dsa_indexer_kl (the indexer's warm-up KL loss and its score gradient),
     dsa_check_varlen, dsa_check_indices, dsa_check_scores (device-side
     precondition checks; the entry points also run them when the environment
     variable DSA_CHECK is set to anything but "" or "0")
@@ -31,7 +32,7 @@ EXPORTED = (
     "dsa_topk", "dsa_sparse_attn_prefill", "dsa_sparse_attn_decode_workspace_size",
     "dsa_sparse_attn_decode", "dsa_check_varlen", "dsa_check_indices", "dsa_check_scores",
     "dsa_quantize_fp8", "dsa_index_scores_fp8", "dsa_sparse_attn_prefill_grouped_workspace_size",
-    "dsa_sparse_attn_prefill_grouped",
+    "dsa_sparse_attn_prefill_grouped", "dsa_indexer_kl",
 )
 
 DSA_OK = 0
@@ -91,6 +92,8 @@ def load_library(path: str = LIB_PATH):
     lib.dsa_sparse_attn_prefill_grouped_workspace_size.argtypes = [vl, i64, i32, sz]
     lib.dsa_sparse_attn_prefill_grouped.argtypes = [vl, vp, vp, vp, vp, i32, i64, i64, i32, i32,
                                                     i32, f32, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.dsa_indexer_kl.argtypes = [vl, vp, vp, vp, i64, i64, i64, i32, i32, i32, f32, vp, vp,
+                                   i64, vp]
     lib.dsa_check_varlen.argtypes = [vl, vp]
     lib.dsa_check_indices.argtypes = [vl, vp, i32, i64, i64, vp]
     lib.dsa_check_scores.argtypes = [vl, vp, i64, i64, i64, vp]
@@ -289,6 +292,27 @@ def dsa_sparse_attn_prefill_grouped(vl: Varlen, q, k, v, indices, out, workspace
         vl.struct, _ptr(q), _ptr(k), _ptr(v), _ptr(indices), indices.shape[1], row_begin,
         row_count, q.shape[1], k.shape[1], d, scale, _ptr(out), _ptr(lse), _ptr(workspace),
         ws_bytes, _stream(stream)))
+
+
+def dsa_indexer_kl(vl: Varlen, q, k, scores, loss, grad=None, softmax_scale=None,
+                   row_begin: int = 0, row_count: int | None = None, stream=None):
+    """Per-row KL divergence of the indexer's softmax (over the window's
+    scores) from the head-averaged dense attention distribution, into loss
+    [row_count]; with grad, also d loss / d scores (grad may be scores)."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k, "k", torch.bfloat16, 3)
+    _need(scores, "scores", torch.float32, 2)
+    _need(loss, "loss", torch.float32, 1)
+    if grad is not None:
+        _need(grad, "grad", torch.float32, 2)
+    d = q.shape[2]
+    scale = d ** -0.5 if softmax_scale is None else softmax_scale
+    row_count = scores.shape[0] if row_count is None else row_count
+    _check(load_library().dsa_indexer_kl(
+        vl.struct, _ptr(q), _ptr(k), _ptr(scores), scores.stride(0), row_begin, row_count,
+        q.shape[1], k.shape[1], d, scale, _ptr(loss), _ptr(grad),
+        0 if grad is None else grad.stride(0), _stream(stream)))
 
 
 def dsa_sparse_attn_decode_workspace_size(vl: Varlen, n_heads_q: int, head_dim: int,

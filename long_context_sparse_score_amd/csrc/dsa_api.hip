@@ -365,6 +365,41 @@ int dsa_sparse_attn_prefill_grouped(const dsa_varlen* vl, const void* q, const v
       "sparse_attn_prefill_grouped launch");
 }
 
+int dsa_indexer_kl(const dsa_varlen* vl, const void* q, const void* k, const float* scores,
+                   int64_t ld_scores, int64_t row_begin, int64_t row_count, int32_t n_heads_q,
+                   int32_t n_heads_kv, int32_t head_dim, float softmax_scale, float* loss,
+                   float* grad, int64_t ld_grad, hipStream_t stream) {
+  int st;
+  if ((st = check_varlen(vl))) return st;
+  if ((st = check_window(vl, row_begin, row_count))) return st;
+  if ((st = check_bf16(q, "q"))) return st;
+  if ((st = check_bf16(k, "k"))) return st;
+  if ((st = check_scores(vl, scores, ld_scores))) return st;
+  if (loss == nullptr || !aligned(loss, 4))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "loss is NULL or misaligned");
+  if (grad != nullptr) {
+    if (!aligned(grad, 4)) return fail(DSA_ERR_INVALID_ARGUMENT, "grad misaligned");
+    if (ld_grad < vl->max_seqlen_k)
+      return fail(DSA_ERR_INVALID_ARGUMENT, "ld_grad (%lld) < max_seqlen_k (%d)",
+                  static_cast<long long>(ld_grad), vl->max_seqlen_k);
+    if (grad == scores && ld_grad != ld_scores)
+      return fail(DSA_ERR_INVALID_ARGUMENT, "grad may replace scores only with ld_grad == ld_scores");
+  }
+  if ((st = check_attn_shape(n_heads_q, n_heads_kv, head_dim, 1, softmax_scale))) return st;
+  if (n_heads_q > 64 || (n_heads_q & (n_heads_q - 1)) != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "n_heads_q %d not in {1, 2, 4, ..., 64}", n_heads_q);
+  if ((st = check_attn_extent(vl, n_heads_kv, head_dim))) return st;
+  if (checks_enabled() &&
+      (st = device_scores(vl, scores, ld_scores, row_begin, row_count, stream)))
+    return st;
+  if (row_count == 0) return ok();
+  return hip_status(
+      dsa::launch_indexer_kl(*vl, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                             scores, ld_scores, row_begin, row_count, n_heads_q, n_heads_kv,
+                             head_dim, softmax_scale, loss, grad, ld_grad, stream),
+      "indexer_kl launch");
+}
+
 int dsa_sparse_attn_decode_workspace_size(const dsa_varlen* vl, int64_t row_count,
                                           int32_t n_heads_q, int32_t head_dim, int32_t topk,
                                           size_t* bytes) {

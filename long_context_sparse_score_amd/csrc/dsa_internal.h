@@ -48,6 +48,14 @@ hipError_t launch_grouped_attn(const dsa_varlen& vl, const uint16_t* q, const ui
                                int n_heads_kv, int head_dim, float scale, uint16_t* out,
                                float* lse, void* workspace, hipStream_t stream);
 
+// Indexer warm-up loss per query row and its gradient with respect to the
+// scores (grad may be null, or equal to scores with the same ld).
+hipError_t launch_indexer_kl(const dsa_varlen& vl, const uint16_t* q, const uint16_t* k,
+                             const float* scores, int64_t ld, int64_t row_begin,
+                             int64_t row_count, int n_heads_q, int n_heads_kv, int head_dim,
+                             float scale, float* loss, float* grad, int64_t ld_grad,
+                             hipStream_t stream);
+
 // Device-side precondition checks.  Each clears a report word, runs one
 // kernel on `stream`, waits for the stream and stores the first finding as
 // (item << 8) | code, or all ones when there is none.  The first call on a

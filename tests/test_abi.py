@@ -291,3 +291,26 @@ def test_grouped_attention_validation():
     # all K rows beyond 2 GiB (the grouped kernels use one 32-bit offset space)
     big = vl(total_q=100, total_k=3_000_000, max_q=100, max_k=3_000_000)
     assert call(vv=big) == dsa.DSA_ERR_UNSUPPORTED
+
+
+def test_indexer_kl_validation():
+    """Host-side checks of dsa_indexer_kl (no kernel is launched: every call
+    below fails before, or has an empty window)."""
+    lib = dsa.load_library()
+    v = vl(total_q=100, total_k=100, max_q=100, max_k=100)
+
+    def call(q=FAKE, scores=FAKE, ld=128, loss=FAKE, grad=None, ld_grad=0, rc=100, hq=32, hkv=4,
+             d=128, scale=0.088):
+        return lib.dsa_indexer_kl(ctypes.byref(v), q, FAKE, scores, ld, 0, rc, hq, hkv, d, scale,
+                                  loss, grad, ld_grad, None)
+    assert call(rc=0) == dsa.DSA_OK
+    assert call(q=None) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert call(scores=None) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert call(loss=None) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert call(ld=96) == dsa.DSA_ERR_INVALID_ARGUMENT           # < max_seqlen_k
+    assert call(grad=FAKE, ld_grad=64) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert call(grad=FAKE, ld_grad=132) == dsa.DSA_ERR_INVALID_ARGUMENT  # in place, other ld
+    assert call(hq=24, hkv=8) == dsa.DSA_ERR_UNSUPPORTED         # not a power of two
+    assert call(hq=128, hkv=8) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(d=96) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(scale=float("nan")) == dsa.DSA_ERR_INVALID_ARGUMENT
