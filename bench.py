@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-grouped", action="store_true",
                     help="skip the grouped-attention comparison on the correlated-query workload")
+    ap.add_argument("--no-kl", action="store_true",
+                    help="skip the indexer warm-up KL loss measurement (a training-side kernel)")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the optional fp8-indexer variant (reported beside the headline)")
     ap.add_argument("--prefill-streams", type=int, default=1, choices=(1, 2),
@@ -419,6 +421,9 @@ def main():
         result["fp8_indexer"] = fp8_variant(torch, pipeline, args, stream, wl, vl, P, out, lse,
                                             None if args.no_decode else (wd, vd, D, dout, dlse))
 
+    if not args.no_kl:
+        result["indexer_kl"] = kl_variant(torch, dsa, args, stream, wl, vl, P, bufs)
+
     if not args.no_grouped:
         result["grouped_attention"] = grouped_variant(torch, dsa, pipeline, args, stream, wl, vl, P,
                                                       out, lse, attn_ms / args.steps)
@@ -506,6 +511,45 @@ def fp8_variant(torch, pipeline, args, stream, wl, vl, P, out, lse, dec):
         del dbufs, fp8d
     torch.cuda.empty_cache()
     return res
+
+
+def kl_variant(torch, dsa, args, stream, wl, vl, P, bufs):
+    """The indexer's warm-up loss (dsa_indexer_kl) over the whole prefill: per
+    window the indexer scores (untimed), then the KL loss with the gradient
+    written over the scores (timed by HIP events on the launch stream).  Its
+    work is two dense logit passes over every causal pair: 2 x 2 Hq d flops
+    per pair, an MFMA-bound kernel.  Windows of 8192 rows: one workgroup
+    serves 16 rows, so a 2048-row window would fill only 128 of the 256 CUs."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    pc = prefill_counts(wl)
+    flops = pc["pairs"] * 4 * wl.n_heads_q * wl.head_dim
+    window = min(8192, wl.total_q)
+    ld = bufs.scores.shape[1]
+    scores = torch.empty((window, ld), dtype=torch.float32, device="cuda")
+    loss = torch.empty(wl.total_q, dtype=torch.float32, device="cuda")
+    log("indexer KL: one pass over the prefill")
+    tot, n_launch = 0.0, 0
+    for r0 in range(0, wl.total_q, window):
+        n = min(window, wl.total_q - r0)
+        dsa.dsa_index_scores(vl, P["q_idx"], P["k_idx"], P["w"], scores, row_begin=r0,
+                             row_count=n)
+        a, b = ev(), ev()
+        a.record(stream)
+        dsa.dsa_indexer_kl(vl, P["q"], P["k"], scores, loss[r0:r0 + n], grad=scores,
+                           row_begin=r0, row_count=n)
+        b.record(stream)
+        torch.cuda.synchronize()
+        tot += a.elapsed_time(b)
+        n_launch += 1
+    tflops = flops / (tot / 1e3) / 1e12
+    del scores
+    torch.cuda.empty_cache()
+    return {"ms": round(tot, 3), "launches": n_launch, "window_rows": window,
+            "mean_loss_per_row": round(float(loss.mean()), 5),
+            "roofline": {"bound": "mfma", "kernel": "indexer_kl", "achieved": round(tflops, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                         "flops_per_causal_pair": 4 * wl.n_heads_q * wl.head_dim}}
 
 
 def grouped_variant(torch, dsa, pipeline, args, stream, wl, vl, P, out, lse, iid_attn_ms):

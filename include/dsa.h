@@ -226,7 +226,8 @@ int dsa_sparse_attn_prefill(const dsa_varlen* vl, const void* q, const void* k, 
  * Arithmetic: bf16 products with fp32 accumulation (MFMA), fp32 softmax
  * statistics; every dense logit is computed twice (statistics, then P).
  * Supported: head_dim in {64, 128}, n_heads_q in {1, 2, 4, ..., 64},
- * n_heads_kv <= 8 dividing it, one sequence's K rows within 2 GiB.
+ * n_heads_kv <= 8 dividing it, softmax_scale > 0, one sequence's K rows
+ * within 2 GiB.
  * Invalid: null q, k, scores or loss, misaligned pointers, ld_scores or
  * ld_grad < max_seqlen_k, ld_scores not a multiple of 4, a window outside
  * [0, total_q), grad == scores with ld_grad != ld_scores, non-finite scale.

@@ -386,6 +386,8 @@ int dsa_indexer_kl(const dsa_varlen* vl, const void* q, const void* k, const flo
       return fail(DSA_ERR_INVALID_ARGUMENT, "grad may replace scores only with ld_grad == ld_scores");
   }
   if ((st = check_attn_shape(n_heads_q, n_heads_kv, head_dim, 1, softmax_scale))) return st;
+  if (!(softmax_scale > 0.0f))
+    return fail(DSA_ERR_UNSUPPORTED, "softmax_scale %g is not positive", softmax_scale);
   if (n_heads_q > 64 || (n_heads_q & (n_heads_q - 1)) != 0)
     return fail(DSA_ERR_UNSUPPORTED, "n_heads_q %d not in {1, 2, 4, ..., 64}", n_heads_q);
   if ((st = check_attn_extent(vl, n_heads_kv, head_dim))) return st;

@@ -51,16 +51,16 @@ __device__ __forceinline__ int kl_at(int key, int g, int n_heads_kv, int piece) 
   return (key * n_heads_kv + g) * D + ((piece ^ (key % KlCfg<D>::PIECES)) * 8);
 }
 
-// LDS layout (dynamic): the K tile (32 keys x Hkv x D bf16), then the
-// waves' partial sums [W][16 rows][kPStride] fp32 (32 keys, padded), then
-// per-row words.
+// LDS layout (dynamic): the K tile (32 keys x Hkv x D bf16), a 1 KB dump
+// for the stores of lanes without a chunk, the waves' partial sums
+// [W][16 rows][kPStride] fp32 (32 keys, padded), then per-row words.
 constexpr int kPStride = kKlKeys + 1;
 __host__ __device__ constexpr size_t kl_lds_bytes(int d, int n_heads_kv, int waves) {
-  return static_cast<size_t>(kKlKeys) * n_heads_kv * d * 2 +
+  return static_cast<size_t>(kKlKeys) * n_heads_kv * d * 2 + kWave * 16 +
          static_cast<size_t>(waves) * kKlRows * kPStride * 4 + 4 * kKlRows * 4;
 }
 
-template <int D, int HPW, int W>
+template <int D, int HPW, int W, int CPT>
 __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -73,7 +73,8 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
   static_assert(RI * NT == kKlRows * kKlKeys, "entries split evenly");
   extern __shared__ __attribute__((aligned(16))) uint16_t kl_lds[];
   uint16_t* ktile = kl_lds;
-  float* ppart = reinterpret_cast<float*>(kl_lds + kKlKeys * n_heads_kv * D);
+  uint16_t* dump = kl_lds + kKlKeys * n_heads_kv * D;
+  float* ppart = reinterpret_cast<float*>(dump + kWave * 8);
   int32_t* rowkb = reinterpret_cast<int32_t*>(ppart + W * kKlRows * kPStride);  // key base per row
   int32_t* rowpos = rowkb + kKlRows;                                           // position per row
 
@@ -114,13 +115,14 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
       qb[j][ks] = load_bf16x8(q + ((row_begin + lr) * n_heads_q + h) * D + ks * 32 + qd * 8);
   }
 
-  // 16-byte chunks of one K tile; with Hkv <= W (the caller checks it) a
-  // thread moves at most PIECES / 2 of them.  Indices past the tile are
-  // clamped to its last chunk (a repeated copy), so the loads carry no
-  // branch and stay in flight during the tile's products.
+  // 16-byte chunks of one K tile, CPT per thread (the launcher picks CPT =
+  // ceil(chunks / NT)).  Load indices past the
+  // tile are clamped to its last chunk, so the loads carry no branch and
+  // stay in flight during the tile's products (a wave's lanes then share
+  // one address, one request); their stores go to a per-lane dump slot
+  // (a branch there would again make the compiler drain the loads).
   const int chunks = kKlKeys * n_heads_kv * C::PIECES;
-  constexpr int kMaxCpt = C::PIECES / 2;
-  static_assert(kKlKeys * (W < 8 ? W : 8) * C::PIECES <= NT * kMaxCpt, "chunks per thread");
+  constexpr int kMaxCpt = CPT;
 
   // Serve the rows one sequence at a time (key bases ascend with the row).
   int32_t seg_kb = rowkb[0];
@@ -147,34 +149,69 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
     auto store_tile = [&]() {
 #pragma unroll
       for (int i = 0; i < kMaxCpt; ++i) {
-        const int c = min(tid + NT * i, chunks - 1);
-        const int key = c / (n_heads_kv * C::PIECES);
-        const int rest = c % (n_heads_kv * C::PIECES);
-        *reinterpret_cast<u32x4*>(ktile + kl_at<D>(key, rest / C::PIECES, n_heads_kv,
-                                                   rest % C::PIECES)) = pre[i];
+        const int c = tid + NT * i;
+        const int cc = min(c, chunks - 1);
+        const int key = cc / (n_heads_kv * C::PIECES);
+        const int rest = cc % (n_heads_kv * C::PIECES);
+        const int at = c < chunks ? kl_at<D>(key, rest / C::PIECES, n_heads_kv, rest % C::PIECES)
+                                  : kKlKeys * n_heads_kv * D + lane * 8;
+        *reinterpret_cast<u32x4*>(kl_lds + at) = pre[i];
+      }
+    };
+    // Scores of this thread's entries of the tile at t (-inf when not
+    // visible); the address is clamped into the row, so the load carries no
+    // branch.
+    auto load_scores = [&](int t, float (&sv)[RI]) {
+#pragma unroll
+      for (int i = 0; i < RI; ++i) {
+        const int r = min(e_row[i], n_rows - 1);
+        const int s = t * kKlKeys + e_key[i];
+        const bool vis = e_row[i] < n_rows && rowkb[r] == seg_kb && s <= rowpos[r];
+        const float x = scores[(first + r) * ld + min(s, max(rowpos[r], 0))];
+        sv[i] = vis ? x : -INFINITY;
       }
     };
     // Logits (log2 domain) of head j for the tile at t: z[sub][r] is key
     // 16 sub + 4 qd + r of this lane's row, -inf when not visible.
-    auto logits = [&](int t, int j, float (&z)[2][4]) {
+    // Raw dot products of head j for the tile: st[sub][r] is key
+    // 16 sub + 4 qd + r of this lane's row.
+    auto dots = [&](int j, f32x4 (&st)[2]) {
       const int g = (wave * HPW + j) / G;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
-        f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
+        st[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
           const bf16x8 ka = __builtin_bit_cast(
               bf16x8, *reinterpret_cast<const u32x4*>(
                           ktile + kl_at<D>(16 * sub + col, g, n_heads_kv, 4 * ks + qd)));
-          st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[j][ks], st, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int s = t * kKlKeys + 16 * sub + 4 * qd + r;
-          z[sub][r] = col_in && s <= my_pos ? st[r] * scale_log2 : -INFINITY;
+          st[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[j][ks], st[sub], 0, 0, 0);
         }
       }
     };
+    // Logits (log2 domain) of head j for the tile at t, -inf when not
+    // visible.
+    auto logits = [&](int t, int j, float (&z)[2][4]) {
+      f32x4 st[2];
+      dots(j, st);
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int s = t * kKlKeys + 16 * sub + 4 * qd + r;
+          z[sub][r] = col_in && s <= my_pos ? st[sub][r] * scale_log2 : -INFINITY;
+        }
+    };
+    // A tile is full when all 16 rows belong to this sequence and see all
+    // of its keys: no masking then, and the scale folds into the exponent's
+    // FMA (softmax_scale > 0, which the caller checks).
+    bool all_in = n_rows == kKlRows;
+    int32_t min_pos = pmax;
+    for (int r = 0; r < kKlRows; ++r) {
+      all_in = all_in && rowkb[r] == seg_kb;
+      min_pos = min(min_pos, rowpos[r]);
+    }
+    const int full_tiles = all_in ? (min_pos + 1) / kKlKeys : 0;
 
     // ---- pass 1: per-(row, head) softmax statistics, per-row indexer ones.
     float hm[HPW], hl[HPW];
@@ -183,38 +220,64 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
     float im[RI], il[RI];
 #pragma unroll
     for (int i = 0; i < RI; ++i) { im[i] = -INFINITY; il[i] = 0.0f; }
+    // The scores and the K rows of tile t + 1 are loaded while tile t is
+    // used, unconditionally (the last tile reloads itself): a branch would
+    // make the compiler drain the loads at the first use of any of them.
+    float sv_next[RI];
+    load_scores(0, sv_next);
     load_tile(0);
     for (int t = 0; t < ntiles; ++t) {
       __syncthreads();  // every wave is done with the previous tile
       store_tile();
       __syncthreads();
-      if (t + 1 < ntiles) load_tile(t + 1);
+      float sv[RI];
 #pragma unroll
-      for (int j = 0; j < HPW; ++j) {
-        float z[2][4];
-        logits(t, j, z);
-        float mx = -INFINITY;
+      for (int i = 0; i < RI; ++i) sv[i] = sv_next[i];
+      load_scores(min(t + 1, ntiles - 1), sv_next);
+      load_tile(min(t + 1, ntiles - 1));
+      if (t < full_tiles) {
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, z[sub][r]);
-        const float mn = fmaxf(hm[j], mx);
-        if (mn != -INFINITY) {
+        for (int j = 0; j < HPW; ++j) {
+          f32x4 st[2];
+          dots(j, st);
+          float mx = fmaxf(fmaxf(fmaxf(st[0][0], st[0][1]), fmaxf(st[0][2], st[0][3])),
+                           fmaxf(fmaxf(st[1][0], st[1][1]), fmaxf(st[1][2], st[1][3])));
+          const float mn = fmaxf(hm[j], mx * scale_log2);
           float sum = 0.0f;
 #pragma unroll
           for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sum += __builtin_amdgcn_exp2f(z[sub][r] - mn);
+            for (int r = 0; r < 4; ++r)
+              sum += __builtin_amdgcn_exp2f(__builtin_fmaf(st[sub][r], scale_log2, -mn));
           hl[j] = hl[j] * __builtin_amdgcn_exp2f(hm[j] - mn) + sum;
           hm[j] = mn;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) {
+          float z[2][4];
+          logits(t, j, z);
+          float mx = -INFINITY;
+#pragma unroll
+          for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, z[sub][r]);
+          const float mn = fmaxf(hm[j], mx);
+          if (mn != -INFINITY) {
+            float sum = 0.0f;
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) sum += __builtin_amdgcn_exp2f(z[sub][r] - mn);
+            hl[j] = hl[j] * __builtin_amdgcn_exp2f(hm[j] - mn) + sum;
+            hm[j] = mn;
+          }
         }
       }
 #pragma unroll
       for (int i = 0; i < RI; ++i) {
-        const int r = e_row[i];
-        const int s = t * kKlKeys + e_key[i];
-        if (r < n_rows && rowkb[r] == seg_kb && s <= rowpos[r]) {
-          const float x = scores[(first + r) * ld + s] * kKlLog2e;
+        if (sv[i] != -INFINITY) {
+          const float x = sv[i] * kKlLog2e;
           const float mn = fmaxf(im[i], x);
           il[i] = il[i] * exp2f(im[i] - mn) + exp2f(x - mn);
           im[i] = mn;
@@ -222,7 +285,8 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
       }
     }
     // Whole-row statistics: the four lane quarters hold one row's keys.
-    float hinv[HPW];
+    // hb[j] = log2 of the normaliser of head j: A = exp2(z - hb[j]).
+    float hb[HPW];
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
       float m = fmaxf(hm[j], __shfl_xor(hm[j], 16));
@@ -230,8 +294,7 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
       float l = hm[j] == -INFINITY ? 0.0f : hl[j] * exp2f(hm[j] - m);
       l += __shfl_xor(l, 16);
       l += __shfl_xor(l, 32);
-      hm[j] = m;
-      hinv[j] = l > 0.0f ? 1.0f / l : 0.0f;
+      hb[j] = l > 0.0f ? m + log2f(l) : INFINITY;  // no visible key: A = 0
     }
     // The 32 entries of one row sit in 32 consecutive lanes.
     float lnorm[RI];
@@ -251,22 +314,39 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
 #pragma unroll
     for (int i = 0; i < RI; ++i) kl[i] = 0.0f;
     const float inv_hq = 1.0f / static_cast<float>(n_heads_q);
+    load_scores(0, sv_next);
     load_tile(0);
     for (int t = 0; t < ntiles; ++t) {
       __syncthreads();  // tile t-1's reads of K and of the partial sums are done
       store_tile();
       __syncthreads();
-      if (t + 1 < ntiles) load_tile(t + 1);
+      float sv[RI];
+#pragma unroll
+      for (int i = 0; i < RI; ++i) sv[i] = sv_next[i];
+      load_scores(min(t + 1, ntiles - 1), sv_next);
+      load_tile(min(t + 1, ntiles - 1));
       float acc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      if (t < full_tiles) {
 #pragma unroll
-      for (int j = 0; j < HPW; ++j) {
-        float z[2][4];
-        logits(t, j, z);
+        for (int j = 0; j < HPW; ++j) {
+          f32x4 st[2];
+          dots(j, st);
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
+          for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            acc[sub][r] += __builtin_amdgcn_exp2f(z[sub][r] - hm[j]) * hinv[j];
+            for (int r = 0; r < 4; ++r)
+              acc[sub][r] += __builtin_amdgcn_exp2f(__builtin_fmaf(st[sub][r], scale_log2, -hb[j]));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) {
+          float z[2][4];
+          logits(t, j, z);
+#pragma unroll
+          for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[sub][r] += __builtin_amdgcn_exp2f(z[sub][r] - hb[j]);
+        }
       }
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
@@ -278,12 +358,12 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
       for (int i = 0; i < RI; ++i) {
         const int r = e_row[i];
         const int s = t * kKlKeys + e_key[i];
-        if (r < n_rows && rowkb[r] == seg_kb && s <= rowpos[r]) {
+        if (sv[i] != -INFINITY) {
           float psum = 0.0f;
 #pragma unroll
           for (int w = 0; w < W; ++w) psum += ppart[(w * kKlRows + r) * kPStride + e_key[i]];
           const float P = psum * inv_hq;
-          const float lpi = scores[(first + r) * ld + s] - lnorm[i];
+          const float lpi = sv[i] - lnorm[i];
           const float pi = __expf(lpi);
           if (P > 0.0f) kl[i] += P * (__logf(P) - lpi);
           if (grad != nullptr) grad[(first + r) * ld_grad + s] = pi - P;
@@ -310,7 +390,7 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
   }
 }
 
-template <int D, int HPW, int W>
+template <int D, int HPW, int W, int CPT>
 hipError_t launch_kl_d(const dsa_varlen& vl, const uint16_t* q, const uint16_t* k,
                        const float* scores, int64_t ld, int64_t row_begin, int64_t row_count,
                        int n_heads_q, int n_heads_kv, float scale, float* loss, float* grad,
@@ -319,13 +399,13 @@ hipError_t launch_kl_d(const dsa_varlen& vl, const uint16_t* q, const uint16_t* 
   static bool configured = false;
   if (!configured) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&indexer_kl_kernel<D, HPW, W>),
+        reinterpret_cast<const void*>(&indexer_kl_kernel<D, HPW, W, CPT>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kl_lds_bytes(D, 8, W)));
     if (e != hipSuccess) return e;
     configured = true;
   }
   const unsigned blocks = static_cast<unsigned>((row_count + kKlRows - 1) / kKlRows);
-  hipLaunchKernelGGL((indexer_kl_kernel<D, HPW, W>), dim3(blocks), dim3(W * kWave), lds, stream,
+  hipLaunchKernelGGL((indexer_kl_kernel<D, HPW, W, CPT>), dim3(blocks), dim3(W * kWave), lds, stream,
                      vl.cu_seqlens_q, vl.cu_seqlens_k, vl.batch, q, k, scores, ld, row_begin,
                      row_count, n_heads_q, n_heads_kv, scale * kKlLog2e, loss, grad, ld_grad);
   return hipGetLastError();
@@ -337,10 +417,25 @@ hipError_t launch_kl_heads(const dsa_varlen& vl, const uint16_t* q, const uint16
                            int n_heads_q, int n_heads_kv, float scale, float* loss, float* grad,
                            int64_t ld_grad, hipStream_t stream) {
   // W = min(8, Hq) waves, Hq / W heads each (the caller checks Hq in
-  // {1, 2, 4, 8, 16, 32, 64}).
+  // {1, 2, 4, 8, 16, 32, 64}); CPT = the K-tile chunks each thread moves,
+  // 32 Hkv D / 8 over 64 W threads (Hkv <= min(Hq, 8): 1, 2, 4 or 8).
+  const int waves = n_heads_q < 8 ? n_heads_q : 8;
+  const int cpt = (kKlKeys * n_heads_kv * (D / 8) + kWave * waves - 1) / (kWave * waves);
 #define DSA_KL(HPW, W)                                                                        \
-  return launch_kl_d<D, HPW, W>(vl, q, k, scores, ld, row_begin, row_count, n_heads_q,        \
-                                n_heads_kv, scale, loss, grad, ld_grad, stream)
+  switch (cpt) {                                                                              \
+    case 1: return launch_kl_d<D, HPW, W, 1>(vl, q, k, scores, ld, row_begin, row_count,      \
+                                             n_heads_q, n_heads_kv, scale, loss, grad,        \
+                                             ld_grad, stream);                                \
+    case 2: return launch_kl_d<D, HPW, W, 2>(vl, q, k, scores, ld, row_begin, row_count,      \
+                                             n_heads_q, n_heads_kv, scale, loss, grad,        \
+                                             ld_grad, stream);                                \
+    case 4: return launch_kl_d<D, HPW, W, 4>(vl, q, k, scores, ld, row_begin, row_count,      \
+                                             n_heads_q, n_heads_kv, scale, loss, grad,        \
+                                             ld_grad, stream);                                \
+    default: return launch_kl_d<D, HPW, W, 8>(vl, q, k, scores, ld, row_begin, row_count,     \
+                                              n_heads_q, n_heads_kv, scale, loss, grad,       \
+                                              ld_grad, stream);                               \
+  }
   switch (n_heads_q) {
     case 1: DSA_KL(1, 1);
     case 2: DSA_KL(1, 2);

@@ -314,3 +314,4 @@ def test_indexer_kl_validation():
     assert call(hq=128, hkv=8) == dsa.DSA_ERR_UNSUPPORTED
     assert call(d=96) == dsa.DSA_ERR_UNSUPPORTED
     assert call(scale=float("nan")) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert call(scale=-0.1) == dsa.DSA_ERR_UNSUPPORTED
