@@ -189,6 +189,38 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
         }
       }
     };
+    // Raw dot products of all HPW heads for half sub of the tile (keys
+    // 16 sub + 4 qd + r): when the heads share one KV head (G a multiple of
+    // HPW) each K fragment is read from LDS once for all of them.
+    auto dots_sub = [&](int sub, bool one_g, f32x4 (&st)[HPW]) {
+#pragma unroll
+      for (int j = 0; j < HPW; ++j) st[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (one_g) {
+        const int g = (wave * HPW) / G;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+          const bf16x8 ka = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(
+                          ktile + kl_at<D>(16 * sub + col, g, n_heads_kv, 4 * ks + qd)));
+#pragma unroll
+          for (int j = 0; j < HPW; ++j)
+            st[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[j][ks], st[j], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) {
+          const int g = (wave * HPW + j) / G;
+#pragma unroll
+          for (int ks = 0; ks < C::KS; ++ks) {
+            const bf16x8 ka = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(
+                            ktile + kl_at<D>(16 * sub + col, g, n_heads_kv, 4 * ks + qd)));
+            st[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[j][ks], st[j], 0, 0, 0);
+          }
+        }
+      }
+    };
+    const bool one_g = G % HPW == 0;
     // Logits (log2 domain) of head j for the tile at t, -inf when not
     // visible.
     auto logits = [&](int t, int j, float (&z)[2][4]) {
@@ -236,21 +268,22 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
       load_scores(min(t + 1, ntiles - 1), sv_next);
       load_tile(min(t + 1, ntiles - 1));
       if (t < full_tiles) {
+        // Each half tile of 16 keys updates the running statistics.
 #pragma unroll
-        for (int j = 0; j < HPW; ++j) {
-          f32x4 st[2];
-          dots(j, st);
-          float mx = fmaxf(fmaxf(fmaxf(st[0][0], st[0][1]), fmaxf(st[0][2], st[0][3])),
-                           fmaxf(fmaxf(st[1][0], st[1][1]), fmaxf(st[1][2], st[1][3])));
-          const float mn = fmaxf(hm[j], mx * scale_log2);
-          float sum = 0.0f;
+        for (int sub = 0; sub < 2; ++sub) {
+          f32x4 st[HPW];
+          dots_sub(sub, one_g, st);
 #pragma unroll
-          for (int sub = 0; sub < 2; ++sub)
+          for (int j = 0; j < HPW; ++j) {
+            const float mx = fmaxf(fmaxf(st[j][0], st[j][1]), fmaxf(st[j][2], st[j][3]));
+            const float mn = fmaxf(hm[j], mx * scale_log2);
+            float sum = 0.0f;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              sum += __builtin_amdgcn_exp2f(__builtin_fmaf(st[sub][r], scale_log2, -mn));
-          hl[j] = hl[j] * __builtin_amdgcn_exp2f(hm[j] - mn) + sum;
-          hm[j] = mn;
+              sum += __builtin_amdgcn_exp2f(__builtin_fmaf(st[j][r], scale_log2, -mn));
+            hl[j] = hl[j] * __builtin_amdgcn_exp2f(hm[j] - mn) + sum;
+            hm[j] = mn;
+          }
         }
       } else {
 #pragma unroll
@@ -328,14 +361,14 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
       float acc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
       if (t < full_tiles) {
 #pragma unroll
-        for (int j = 0; j < HPW; ++j) {
-          f32x4 st[2];
-          dots(j, st);
+        for (int sub = 0; sub < 2; ++sub) {
+          f32x4 st[HPW];
+          dots_sub(sub, one_g, st);
 #pragma unroll
-          for (int sub = 0; sub < 2; ++sub)
+          for (int j = 0; j < HPW; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              acc[sub][r] += __builtin_amdgcn_exp2f(__builtin_fmaf(st[sub][r], scale_log2, -hb[j]));
+              acc[sub][r] += __builtin_amdgcn_exp2f(__builtin_fmaf(st[j][r], scale_log2, -hb[j]));
         }
       } else {
 #pragma unroll
