@@ -140,3 +140,34 @@ def test_kl_on_indexer_scores_full_size_sampled():
 def to_dev_bf16_(bits):
     t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
     return t.to("cuda").view(torch.bfloat16)
+
+
+def test_kl_separate_grad_stride_and_checked_scores(monkeypatch):
+    """A gradient buffer with its own leading dimension; with DSA_CHECK set,
+    a NaN among a row's visible scores is reported before any launch and a
+    NaN past the row's position is not."""
+    wl = small_wl([70], [90], 8, 2, 64, seed=13)
+    host, dev = device_workload(wl, parts=("q", "k"))
+    vl = dsa.Varlen(wl.cu_q.tolist(), wl.cu_k.tolist())
+    n, ld = wl.total_q, 96
+    rng = np.random.default_rng(2)
+    scores = rng.standard_normal((n, ld)).astype(np.float32)
+    sc = to_dev(scores)
+    loss = torch.zeros(n, dtype=torch.float32, device="cuda")
+    grad = torch.full((n, 100), 3.0, dtype=torch.float32, device="cuda")
+    dsa.dsa_indexer_kl(vl, dev["q"], dev["k"], sc, loss, grad=grad)
+    torch.cuda.synchronize()
+    rows = np.arange(n)
+    lo, go = oracle.indexer_kl(wl.cu_q, wl.cu_k, host["q"], host["k"], scores.astype(np.float64),
+                               rows, wl.softmax_scale)
+    counts = oracle.visible_counts(wl.cu_q, wl.cu_k, rows)
+    check(loss.cpu().numpy(), grad.cpu().numpy()[:, :ld], lo, go, counts, scores)
+    assert (grad.cpu().numpy()[:, ld:] == 3.0).all()
+    monkeypatch.setenv("DSA_CHECK", "1")
+    bad = scores.copy()
+    bad[5, counts[5] + 2] = np.nan          # past row 5's position: never read
+    dsa.dsa_indexer_kl(vl, dev["q"], dev["k"], to_dev(bad), loss)
+    torch.cuda.synchronize()
+    bad[7, 3] = np.nan                      # visible to row 7
+    with pytest.raises(dsa.DSAError):
+        dsa.dsa_indexer_kl(vl, dev["q"], dev["k"], to_dev(bad), loss)
