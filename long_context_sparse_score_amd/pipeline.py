@@ -95,7 +95,7 @@ def alloc_prefill(vl: Varlen, topk: int, window: int, device="cuda", overlap: bo
 
 def prefill(vl: Varlen, q_idx, k_idx, w, q, k, v, out, bufs: PrefillBuffers, lse=None,
             softmax_scale=None, stream=None, keep_indices=None, side_stream=None, record=None,
-            fp8: Fp8Indexer | None = None):
+            fp8: Fp8Indexer | None = None, attn_rows: int | None = None):
     """Whole prefill path.
 
     With `fp8` (buffers from alloc_fp8_indexer) the indexer queries and keys
@@ -151,8 +151,14 @@ def prefill(vl: Varlen, q_idx, k_idx, w, q, k, v, out, bufs: PrefillBuffers, lse
             att.wait_event(ready)
         a0 = mark(att)
         if bufs.grouped is None:
-            dsa_sparse_attn_prefill(vl, q, k, v, ib, out, lse=lse, softmax_scale=softmax_scale,
-                                    row_begin=r0, row_count=n, stream=att)
+            # `attn_rows` splits a window's attention into launches of that
+            # many rows (same results; a timing knob).
+            step = n if attn_rows is None else max(1, attn_rows)
+            for j in range(0, n, step):
+                m = min(step, n - j)
+                dsa_sparse_attn_prefill(vl, q, k, v, ib[j:j + m], out, lse=lse,
+                                        softmax_scale=softmax_scale, row_begin=r0 + j, row_count=m,
+                                        stream=att)
         else:
             dsa_sparse_attn_prefill_grouped(vl, q, k, v, ib, out, gbufs[i % len(gbufs)], lse=lse,
                                             softmax_scale=softmax_scale, row_begin=r0,
