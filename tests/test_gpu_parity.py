@@ -398,14 +398,16 @@ def test_bitwise_repeatable():
     outs = []
     # Three one-stream runs, then two with each window's attention on a side
     # stream (overlapping the next window's indexer): all bitwise equal.
-    for rep in range(5):
-        two = rep >= 3
-        bufs = pipeline.alloc_prefill(vl, wl.topk, window=800 if rep < 4 else 256, overlap=two)
+    # A sixth run splits every window's attention into launches of 300 rows.
+    for rep in range(6):
+        two = rep in (3, 4)
+        bufs = pipeline.alloc_prefill(vl, wl.topk, window=800 if rep != 4 else 256, overlap=two)
         out = torch.zeros((wl.total_q, 32, 128), dtype=torch.bfloat16, device="cuda")
         keep = torch.zeros((wl.total_q, wl.topk), dtype=torch.int32, device="cuda")
         pipeline.prefill(vl, dev["q_idx"], dev["k_idx"], dev["w"], dev["q"], dev["k"], dev["v"],
                          out, bufs, keep_indices=keep,
-                         side_stream=torch.cuda.Stream() if two else None)
+                         side_stream=torch.cuda.Stream() if two else None,
+                         attn_rows=300 if rep == 5 else None)
         torch.cuda.synchronize()
         outs.append((from_dev_bf16(out), keep.cpu().numpy()))
     for o, i in outs[1:]:
