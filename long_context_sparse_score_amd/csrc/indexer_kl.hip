@@ -429,14 +429,13 @@ hipError_t launch_kl_d(const dsa_varlen& vl, const uint16_t* q, const uint16_t* 
                        int n_heads_q, int n_heads_kv, float scale, float* loss, float* grad,
                        int64_t ld_grad, hipStream_t stream) {
   const size_t lds = kl_lds_bytes(D, n_heads_kv, W);
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&indexer_kl_kernel<D, HPW, W, CPT>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kl_lds_bytes(D, 8, W)));
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  // Up to 64 KB of K tile (8 KV heads at d = 128) plus the partial sums:
+  // above the default dynamic LDS limit, within the 160 KB of a CU.  Set
+  // once per instantiation (thread-safe static initialisation).
+  static const hipError_t lds_ok = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&indexer_kl_kernel<D, HPW, W, CPT>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kl_lds_bytes(D, 8, W)));
+  if (lds_ok != hipSuccess) return lds_ok;
   const unsigned blocks = static_cast<unsigned>((row_count + kKlRows - 1) / kKlRows);
   hipLaunchKernelGGL((indexer_kl_kernel<D, HPW, W, CPT>), dim3(blocks), dim3(W * kWave), lds, stream,
                      vl.cu_seqlens_q, vl.cu_seqlens_k, vl.batch, q, k, scores, ld, row_begin,
