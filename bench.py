@@ -48,9 +48,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--window", type=int, default=2048,
+    from long_context_sparse_score_amd.pipeline import BENCH_PREFILL
+
+    ap.add_argument("--window", type=int, default=BENCH_PREFILL.window,
                     help="prefill query rows per score window (2048 measured fastest of 512..8192)")
-    ap.add_argument("--attn-rows", type=int, default=1024,
+    ap.add_argument("--attn-rows", type=int, default=BENCH_PREFILL.attn_rows,
                     help="split each window's attention into launches of this many rows "
                          "(1024: 51.0 ms against 52.9 ms in one launch per 2048-row window)")
     ap.add_argument("--no-dense", action="store_true")

@@ -43,7 +43,12 @@
  *     returns its status without enqueueing the real work when it fails.
  *     Checked calls wait for `stream` (so they cannot be captured into a
  *     graph), and the first one on a device allocates a 256-byte report
- *     buffer that lives until the process ends.
+ *     buffer that lives until the process ends.  Checks share that buffer,
+ *     so checked calls from several host threads run one after another.
+ *     The attention entry points check their index lists with their own
+ *     reading (an entry outside 0..p is an empty slot; a position listed
+ *     twice is an error), so a call that is valid unchecked stays valid
+ *     checked.
  *
  * Varlen layout (dsa_varlen)
  *   Sequence b owns packed query rows [cu_seqlens_q[b], cu_seqlens_q[b+1])
@@ -72,6 +77,11 @@ typedef enum {
   DSA_ERR_WORKSPACE = 3,        /* workspace missing or too small             */
   DSA_ERR_HIP = 4               /* a HIP launch call failed                   */
 } dsa_status;
+
+/* softmax_scale value that selects the default scale 1 / sqrt(head_dim) in
+   the attention and warm-up-loss entry points (a scale of exactly zero has no
+   use: it would make every selected position equally likely). */
+#define DSA_SCALE_DEFAULT 0.0f
 
 /* Static text for a status code. */
 const char* dsa_status_string(int status);
@@ -189,6 +199,7 @@ int dsa_topk(const dsa_varlen* vl, const float* scores, int64_t ld_scores, int64
  *           lse = -inf.
  * Query head h reads KV head h / (n_heads_q / n_heads_kv).
  *   O[h] = sum_s softmax_s(softmax_scale * q[h] . k[s, g]) v[s, g].
+ * softmax_scale: DSA_SCALE_DEFAULT (0) selects 1 / sqrt(head_dim).
  * Arithmetic: bf16 MFMA with fp32 accumulation, fp32 softmax, probabilities
  * rounded to bf16 for the value product, bf16 output (round to nearest even).
  * Supported: head_dim in {64, 128}; n_heads_q / n_heads_kv in 1..16;
@@ -225,9 +236,10 @@ int dsa_sparse_attn_prefill(const dsa_varlen* vl, const void* q, const void* k, 
  *           the scores in place.
  * Arithmetic: bf16 products with fp32 accumulation (MFMA), fp32 softmax
  * statistics; every dense logit is computed twice (statistics, then P).
+ * softmax_scale: DSA_SCALE_DEFAULT (0) selects 1 / sqrt(head_dim).
  * Supported: head_dim in {64, 128}, n_heads_q in {1, 2, 4, ..., 64},
- * n_heads_kv <= 8 dividing it, softmax_scale > 0, one sequence's K rows
- * within 2 GiB.
+ * n_heads_kv <= 8 dividing it, softmax_scale > 0 (after the default is
+ * applied), one sequence's K rows within 2 GiB.
  * Invalid: null q, k, scores or loss, misaligned pointers, ld_scores or
  * ld_grad < max_seqlen_k, ld_scores not a multiple of 4, a window outside
  * [0, total_q), grad == scores with ld_grad != ld_scores, non-finite scale.

@@ -128,17 +128,56 @@ def _ptr(t) -> int | None:
 
 
 def _need(t, name, dtype, ndim=None):
+    """Type, dtype, rank and contiguity of one tensor argument (the device is
+    checked last, by _on_device, after the extents)."""
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if not t.is_cuda:
-        raise TypeError(f"{name} must be a device tensor")
     if not t.is_contiguous():
         raise TypeError(f"{name} must be contiguous")
     if ndim is not None and t.dim() != ndim:
         raise TypeError(f"{name} must have {ndim} dimensions, got {t.dim()}")
+
+
+def _on_device(**tensors):
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise TypeError(f"{name} must be a device tensor")
+
+
+# Extent checks: the C ABI addresses every buffer from the packed-batch
+# descriptor and the window alone, so an undersized tensor would become an
+# out-of-bounds device access.  These raise ValueError before any call.
+
+def _extent(ok: bool, msg: str):
+    if not ok:
+        raise ValueError(msg)
+
+
+def _window(vl, row_begin: int, row_count: int):
+    _extent(row_begin >= 0 and row_count >= 0 and row_begin + row_count <= vl.total_q,
+            f"row window [{row_begin}, {row_begin + row_count}) outside [0, {vl.total_q})")
+
+
+def _rows(t, name: str, need: int):
+    _extent(t.shape[0] >= need, f"{name} has {t.shape[0]} rows, the window needs {need}")
+
+
+def _shape(t, name: str, want: tuple):
+    _extent(tuple(t.shape) == tuple(want), f"{name} has shape {tuple(t.shape)}, expected {want}")
+
+
+def _score_cols(t, name: str, vl):
+    _extent(t.shape[1] >= vl.max_seqlen_k,
+            f"{name} has {t.shape[1]} columns, fewer than max_seqlen_k = {vl.max_seqlen_k}")
+
+
+def _scale(softmax_scale) -> float:
+    """None selects the library's default scale (DSA_SCALE_DEFAULT = 0: the C
+    ABI applies 1 / sqrt(head_dim)); the binding computes nothing."""
+    return 0.0 if softmax_scale is None else float(softmax_scale)
 
 
 def _stream(stream) -> int:
@@ -187,6 +226,14 @@ def dsa_index_scores(vl: Varlen, q_idx, k_idx, w, scores, row_begin: int = 0,
     _need(w, "w", torch.float32, 2)
     _need(scores, "scores", torch.float32, 2)
     row_count = scores.shape[0] if row_count is None else row_count
+    _window(vl, row_begin, row_count)
+    h, d = q_idx.shape[1], q_idx.shape[2]
+    _shape(q_idx, "q_idx", (vl.total_q, h, d))
+    _shape(k_idx, "k_idx", (vl.total_k, d))
+    _shape(w, "w", (vl.total_q, h))
+    _rows(scores, "scores", row_count)
+    _score_cols(scores, "scores", vl)
+    _on_device(q_idx=q_idx, k_idx=k_idx, w=w, scores=scores)
     _check(load_library().dsa_index_scores(
         vl.struct, _ptr(q_idx), _ptr(k_idx), _ptr(w), q_idx.shape[1], q_idx.shape[2], row_begin,
         row_count, _ptr(scores), scores.shape[1], _stream(stream)))
@@ -201,7 +248,8 @@ def dsa_quantize_fp8(x, codes, scales, stream=None):
     _need(scales, "scales", torch.float32)
     d = x.shape[-1]
     if tuple(codes.shape) != tuple(x.shape) or tuple(scales.shape) != tuple(x.shape[:-1]):
-        raise TypeError("codes must match x and scales must be x.shape[:-1]")
+        raise ValueError("codes must match x and scales must be x.shape[:-1]")
+    _on_device(x=x, codes=codes, scales=scales)
     _check(load_library().dsa_quantize_fp8(_ptr(x), x.numel() // d, d, _ptr(codes), _ptr(scales),
                                            _stream(stream)))
 
@@ -219,6 +267,17 @@ def dsa_index_scores_fp8(vl: Varlen, q_codes, q_scales, k_codes, k_scales, w, sc
     _need(w, "w", torch.float32, 2)
     _need(scores, "scores", torch.float32, 2)
     row_count = scores.shape[0] if row_count is None else row_count
+    _window(vl, row_begin, row_count)
+    h, d = q_codes.shape[1], q_codes.shape[2]
+    _shape(q_codes, "q_codes", (vl.total_q, h, d))
+    _shape(q_scales, "q_scales", (vl.total_q, h))
+    _shape(k_codes, "k_codes", (vl.total_k, d))
+    _shape(k_scales, "k_scales", (vl.total_k,))
+    _shape(w, "w", (vl.total_q, h))
+    _rows(scores, "scores", row_count)
+    _score_cols(scores, "scores", vl)
+    _on_device(q_codes=q_codes, q_scales=q_scales, k_codes=k_codes, k_scales=k_scales, w=w,
+               scores=scores)
     _check(load_library().dsa_index_scores_fp8(
         vl.struct, _ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), _ptr(w),
         q_codes.shape[1], q_codes.shape[2], row_begin, row_count, _ptr(scores), scores.shape[1],
@@ -238,10 +297,28 @@ def dsa_topk(vl: Varlen, scores, indices, row_begin: int = 0, row_count: int | N
     _need(scores, "scores", torch.float32, 2)
     _need(indices, "indices", torch.int32, 2)
     row_count = indices.shape[0] if row_count is None else row_count
+    _window(vl, row_begin, row_count)
+    _rows(scores, "scores", row_count)
+    _rows(indices, "indices", row_count)
+    _score_cols(scores, "scores", vl)
+    _on_device(scores=scores, indices=indices, workspace=workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().dsa_topk(
         vl.struct, _ptr(scores), scores.shape[1], row_begin, row_count, indices.shape[1],
         _ptr(indices), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def _attn_extents(vl, q, k, v, indices, out, lse, row_begin, row_count, q_rows=None):
+    hq, d = q.shape[1], q.shape[2]
+    _window(vl, row_begin, row_count)
+    _shape(q, "q", (vl.total_q if q_rows is None else q_rows, hq, d))
+    _extent(k.shape[0] == vl.total_k and k.shape[2] == d,
+            f"k has shape {tuple(k.shape)}, expected ({vl.total_k}, n_heads_kv, {d})")
+    _shape(v, "v", tuple(k.shape))
+    _rows(indices, "indices", row_count)
+    _shape(out, "out", tuple(q.shape))
+    if lse is not None:
+        _shape(lse, "lse", (q.shape[0], hq))
 
 
 def dsa_sparse_attn_prefill(vl: Varlen, q, k, v, indices, out, lse=None, softmax_scale=None,
@@ -256,12 +333,14 @@ def dsa_sparse_attn_prefill(vl: Varlen, q, k, v, indices, out, lse=None, softmax
     _need(out, "out", torch.bfloat16, 3)
     if lse is not None:
         _need(lse, "lse", torch.float32, 2)
-    d = q.shape[2]
-    scale = d ** -0.5 if softmax_scale is None else softmax_scale
     row_count = indices.shape[0] if row_count is None else row_count
+    _attn_extents(vl, q, k, v, indices, out, lse, row_begin, row_count)
+    _on_device(q=q, k=k, v=v, indices=indices, out=out, lse=lse)
+    d = q.shape[2]
     _check(load_library().dsa_sparse_attn_prefill(
         vl.struct, _ptr(q), _ptr(k), _ptr(v), _ptr(indices), indices.shape[1], row_begin,
-        row_count, q.shape[1], k.shape[1], d, scale, _ptr(out), _ptr(lse), _stream(stream)))
+        row_count, q.shape[1], k.shape[1], d, _scale(softmax_scale), _ptr(out), _ptr(lse),
+        _stream(stream)))
 
 
 def dsa_sparse_attn_prefill_grouped_workspace_size(vl: Varlen, row_count: int, topk: int) -> int:
@@ -284,14 +363,15 @@ def dsa_sparse_attn_prefill_grouped(vl: Varlen, q, k, v, indices, out, workspace
     _need(out, "out", torch.bfloat16, 3)
     if lse is not None:
         _need(lse, "lse", torch.float32, 2)
-    d = q.shape[2]
-    scale = d ** -0.5 if softmax_scale is None else softmax_scale
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     row_count = indices.shape[0] if row_count is None else row_count
+    _attn_extents(vl, q, k, v, indices, out, lse, row_begin, row_count)
+    _on_device(q=q, k=k, v=v, indices=indices, out=out, lse=lse, workspace=workspace)
+    d = q.shape[2]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().dsa_sparse_attn_prefill_grouped(
         vl.struct, _ptr(q), _ptr(k), _ptr(v), _ptr(indices), indices.shape[1], row_begin,
-        row_count, q.shape[1], k.shape[1], d, scale, _ptr(out), _ptr(lse), _ptr(workspace),
-        ws_bytes, _stream(stream)))
+        row_count, q.shape[1], k.shape[1], d, _scale(softmax_scale), _ptr(out), _ptr(lse),
+        _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def dsa_indexer_kl(vl: Varlen, q, k, scores, loss, grad=None, softmax_scale=None,
@@ -306,12 +386,22 @@ def dsa_indexer_kl(vl: Varlen, q, k, scores, loss, grad=None, softmax_scale=None
     _need(loss, "loss", torch.float32, 1)
     if grad is not None:
         _need(grad, "grad", torch.float32, 2)
-    d = q.shape[2]
-    scale = d ** -0.5 if softmax_scale is None else softmax_scale
     row_count = scores.shape[0] if row_count is None else row_count
+    _window(vl, row_begin, row_count)
+    hq, d = q.shape[1], q.shape[2]
+    _shape(q, "q", (vl.total_q, hq, d))
+    _extent(k.shape[0] == vl.total_k and k.shape[2] == d,
+            f"k has shape {tuple(k.shape)}, expected ({vl.total_k}, n_heads_kv, {d})")
+    _rows(scores, "scores", row_count)
+    _score_cols(scores, "scores", vl)
+    _rows(loss, "loss", row_count)
+    if grad is not None:
+        _rows(grad, "grad", row_count)
+        _score_cols(grad, "grad", vl)
+    _on_device(q=q, k=k, scores=scores, loss=loss, grad=grad)
     _check(load_library().dsa_indexer_kl(
         vl.struct, _ptr(q), _ptr(k), _ptr(scores), scores.stride(0), row_begin, row_count,
-        q.shape[1], k.shape[1], d, scale, _ptr(loss), _ptr(grad),
+        q.shape[1], k.shape[1], d, _scale(softmax_scale), _ptr(loss), _ptr(grad),
         0 if grad is None else grad.stride(0), _stream(stream)))
 
 
@@ -337,14 +427,17 @@ def dsa_sparse_attn_decode(vl: Varlen, q, k_cache, v_cache, indices, out, worksp
     _need(out, "out", torch.bfloat16, 3)
     if lse is not None:
         _need(lse, "lse", torch.float32, 2)
-    d = q.shape[2]
-    scale = d ** -0.5 if softmax_scale is None else softmax_scale
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     row_count = indices.shape[0] if row_count is None else row_count
+    _attn_extents(vl, q, k_cache, v_cache, indices, out, lse, row_begin, row_count,
+                  q_rows=vl.batch)
+    _on_device(q=q, k_cache=k_cache, v_cache=v_cache, indices=indices, out=out, lse=lse,
+               workspace=workspace)
+    d = q.shape[2]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().dsa_sparse_attn_decode(
         vl.struct, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(indices), indices.shape[1],
-        row_begin, row_count, q.shape[1], k_cache.shape[1], d, scale, _ptr(out), _ptr(lse),
-        _ptr(workspace), ws_bytes, _stream(stream)))
+        row_begin, row_count, q.shape[1], k_cache.shape[1], d, _scale(softmax_scale), _ptr(out),
+        _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def dsa_check_varlen(vl: Varlen, stream=None):
@@ -359,6 +452,9 @@ def dsa_check_indices(vl: Varlen, indices, row_begin: int = 0, row_count: int | 
     torch = _torch()
     _need(indices, "indices", torch.int32, 2)
     row_count = indices.shape[0] if row_count is None else row_count
+    _window(vl, row_begin, row_count)
+    _rows(indices, "indices", row_count)
+    _on_device(indices=indices)
     _check(load_library().dsa_check_indices(vl.struct, _ptr(indices), indices.shape[1], row_begin,
                                             row_count, _stream(stream)))
 
@@ -370,6 +466,10 @@ def dsa_check_scores(vl: Varlen, scores, row_begin: int = 0, row_count: int | No
     torch = _torch()
     _need(scores, "scores", torch.float32, 2)
     row_count = scores.shape[0] if row_count is None else row_count
+    _window(vl, row_begin, row_count)
+    _rows(scores, "scores", row_count)
+    _score_cols(scores, "scores", vl)
+    _on_device(scores=scores)
     _check(load_library().dsa_check_scores(vl.struct, _ptr(scores), scores.shape[1], row_begin,
                                            row_count, _stream(stream)))
 

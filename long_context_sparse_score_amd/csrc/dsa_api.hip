@@ -70,6 +70,11 @@ int check_bf16(const void* p, const char* name) {
   return DSA_OK;
 }
 
+// DSA_SCALE_DEFAULT (0) selects the usual 1 / sqrt(head_dim).
+float resolve_scale(float scale, int32_t head_dim) {
+  return scale == 0.0f && head_dim > 0 ? 1.0f / std::sqrt(static_cast<float>(head_dim)) : scale;
+}
+
 int check_attn_shape(int32_t hq, int32_t hkv, int32_t d, int32_t topk, float scale) {
   if (hq < 1 || hkv < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "head counts must be >= 1");
   if (hq % hkv != 0)
@@ -155,13 +160,17 @@ int device_offsets(const dsa_varlen* vl, hipStream_t stream) {
   return finding_status(e, f, 0);
 }
 
+// empty_outside: the attention entry points treat an index outside 0..p
+// as an empty slot, so their checked calls accept it (dsa_check_indices
+// itself holds lists to the -1-or-causal form dsa_topk writes).
 int device_indices(const dsa_varlen* vl, const int32_t* indices, int32_t topk, int64_t row_begin,
-                   int64_t row_count, hipStream_t stream) {
+                   int64_t row_count, hipStream_t stream, bool empty_outside) {
   int st;
   if ((st = device_offsets(vl, stream))) return st;
   if (row_count == 0) return ok();
   unsigned long long f = dsa::kNoFinding;
-  const hipError_t e = dsa::check_indices(*vl, indices, topk, row_begin, row_count, stream, &f);
+  const hipError_t e =
+      dsa::check_indices(*vl, indices, topk, row_begin, row_count, empty_outside, stream, &f);
   return finding_status(e, f, row_begin);
 }
 
@@ -286,6 +295,7 @@ int dsa_sparse_attn_prefill(const dsa_varlen* vl, const void* q, const void* k, 
                             int64_t row_count, int32_t n_heads_q, int32_t n_heads_kv,
                             int32_t head_dim, float softmax_scale, void* out, float* lse,
                             hipStream_t stream) {
+  softmax_scale = resolve_scale(softmax_scale, head_dim);
   int st;
   if ((st = check_varlen(vl))) return st;
   if ((st = check_window(vl, row_begin, row_count))) return st;
@@ -299,7 +309,7 @@ int dsa_sparse_attn_prefill(const dsa_varlen* vl, const void* q, const void* k, 
   if ((st = check_attn_shape(n_heads_q, n_heads_kv, head_dim, topk, softmax_scale))) return st;
   if ((st = check_attn_extent(vl, n_heads_kv, head_dim))) return st;
   if (checks_enabled() &&
-      (st = device_indices(vl, indices, topk, row_begin, row_count, stream)))
+      (st = device_indices(vl, indices, topk, row_begin, row_count, stream, true)))
     return st;
   if (row_count == 0) return ok();
   return hip_status(
@@ -329,6 +339,7 @@ int dsa_sparse_attn_prefill_grouped(const dsa_varlen* vl, const void* q, const v
                                     int32_t n_heads_kv, int32_t head_dim, float softmax_scale,
                                     void* out, float* lse, void* workspace,
                                     size_t workspace_bytes, hipStream_t stream) {
+  softmax_scale = resolve_scale(softmax_scale, head_dim);
   int st;
   if ((st = check_varlen(vl))) return st;
   if ((st = check_window(vl, row_begin, row_count))) return st;
@@ -349,7 +360,7 @@ int dsa_sparse_attn_prefill_grouped(const dsa_varlen* vl, const void* q, const v
     return fail(DSA_ERR_UNSUPPORTED, "K or V rows exceed 2 GiB (total_k %lld)",
                 static_cast<long long>(vl->total_k));
   if (checks_enabled() &&
-      (st = device_indices(vl, indices, topk, row_begin, row_count, stream)))
+      (st = device_indices(vl, indices, topk, row_begin, row_count, stream, true)))
     return st;
   if (row_count == 0) return ok();
   const size_t need = dsa::grouped_attn_workspace_bytes(row_count, topk);
@@ -369,6 +380,7 @@ int dsa_indexer_kl(const dsa_varlen* vl, const void* q, const void* k, const flo
                    int64_t ld_scores, int64_t row_begin, int64_t row_count, int32_t n_heads_q,
                    int32_t n_heads_kv, int32_t head_dim, float softmax_scale, float* loss,
                    float* grad, int64_t ld_grad, hipStream_t stream) {
+  softmax_scale = resolve_scale(softmax_scale, head_dim);
   int st;
   if ((st = check_varlen(vl))) return st;
   if ((st = check_window(vl, row_begin, row_count))) return st;
@@ -426,6 +438,7 @@ int dsa_sparse_attn_decode(const dsa_varlen* vl, const void* q, const void* k_ca
                            int32_t n_heads_kv, int32_t head_dim, float softmax_scale, void* out,
                            float* lse, void* workspace, size_t workspace_bytes,
                            hipStream_t stream) {
+  softmax_scale = resolve_scale(softmax_scale, head_dim);
   int st;
   if ((st = check_varlen(vl))) return st;
   if (vl->total_q != vl->batch || vl->max_seqlen_q != 1)
@@ -441,7 +454,7 @@ int dsa_sparse_attn_decode(const dsa_varlen* vl, const void* q, const void* k_ca
   if ((st = check_attn_shape(n_heads_q, n_heads_kv, head_dim, topk, softmax_scale))) return st;
   if ((st = check_attn_extent(vl, n_heads_kv, head_dim))) return st;
   if (checks_enabled() &&
-      (st = device_indices(vl, indices, topk, row_begin, row_count, stream)))
+      (st = device_indices(vl, indices, topk, row_begin, row_count, stream, true)))
     return st;
   if (row_count == 0) return ok();
   const int splits = dsa::attn_decode_splits(row_count, n_heads_kv, topk);
@@ -473,7 +486,7 @@ int dsa_check_indices(const dsa_varlen* vl, const int32_t* indices, int32_t topk
   if (indices == nullptr || !aligned(indices, 4))
     return fail(DSA_ERR_INVALID_ARGUMENT, "indices is NULL or misaligned");
   if (topk < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "topk must be >= 1");
-  return device_indices(vl, indices, topk, row_begin, row_count, stream);
+  return device_indices(vl, indices, topk, row_begin, row_count, stream, false);
 }
 
 int dsa_check_scores(const dsa_varlen* vl, const float* scores, int64_t ld_scores,

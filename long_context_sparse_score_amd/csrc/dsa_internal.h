@@ -59,7 +59,8 @@ hipError_t launch_indexer_kl(const dsa_varlen& vl, const uint16_t* q, const uint
 // Device-side precondition checks.  Each clears a report word, runs one
 // kernel on `stream`, waits for the stream and stores the first finding as
 // (item << 8) | code, or all ones when there is none.  The first call on a
-// device allocates its report word (kept until the process ends).
+// device allocates its report word (kept until the process ends); checks
+// are serialised by a lock held until their finding is read back.
 enum CheckCode {
   kCheckOffsetStart = 1,         // cu_seqlens_q[0] or cu_seqlens_k[0] != 0
   kCheckOffsetOrder = 2,         // cu_seqlens decreases
@@ -74,9 +75,11 @@ constexpr unsigned long long kNoFinding = ~0ull;
 
 hipError_t check_offsets(const dsa_varlen& vl, hipStream_t stream, unsigned long long* finding);
 // Rows of the window; the offsets must already have passed check_offsets.
+// empty_outside: entries outside 0..p are empty slots (the attention
+// kernels' reading) rather than errors; repeats among 0..p are still errors.
 hipError_t check_indices(const dsa_varlen& vl, const int32_t* indices, int topk,
-                         int64_t row_begin, int64_t row_count, hipStream_t stream,
-                         unsigned long long* finding);
+                         int64_t row_begin, int64_t row_count, bool empty_outside,
+                         hipStream_t stream, unsigned long long* finding);
 hipError_t check_scores(const dsa_varlen& vl, const float* scores, int64_t ld, int64_t row_begin,
                         int64_t row_count, hipStream_t stream, unsigned long long* finding);
 

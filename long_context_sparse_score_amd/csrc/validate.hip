@@ -40,11 +40,12 @@ __global__ void check_offsets_kernel(const int32_t* __restrict__ cu_q,
 }
 
 // One workgroup per row of the window: every entry is -1 or a position in
-// 0..p, and no position appears twice.  Duplicates are found with an LDS
-// bitmap, one span of positions per pass.
+// 0..p (unless empty_outside: then any entry outside 0..p is an empty slot,
+// as the attention kernels treat it), and no position appears twice.
+// Duplicates are found with an LDS bitmap, one span of positions per pass.
 __global__ __launch_bounds__(kCheckThreads) void check_indices_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
-    const int32_t* __restrict__ indices, int topk, int64_t row_begin,
+    const int32_t* __restrict__ indices, int topk, int64_t row_begin, int empty_outside,
     unsigned long long* rep) {
   __shared__ uint32_t bits[kBitmapWords];
   __shared__ int found;
@@ -55,7 +56,7 @@ __global__ __launch_bounds__(kCheckThreads) void check_indices_kernel(
   __syncthreads();
   for (int j = threadIdx.x; j < topk; j += kCheckThreads) {
     const int32_t p = irow[j];
-    if (p != -1 && (p < 0 || p > ri.pos)) found = 1;
+    if (!empty_outside && p != -1 && (p < 0 || p > ri.pos)) found = 1;
   }
   __syncthreads();
   if (found) {
@@ -67,6 +68,7 @@ __global__ __launch_bounds__(kCheckThreads) void check_indices_kernel(
     for (int i = threadIdx.x; i < words; i += kCheckThreads) bits[i] = 0u;
     __syncthreads();
     for (int j = threadIdx.x; j < topk; j += kCheckThreads) {
+      if (irow[j] < 0 || irow[j] > ri.pos) continue;  // empty slot (empty_outside only)
       const int64_t p = irow[j] - span0;
       if (p < 0 || p >= kBitmapSpan) continue;
       const uint32_t bit = 1u << (p & 31);
@@ -93,12 +95,12 @@ __global__ __launch_bounds__(kCheckThreads) void check_scores_kernel(
 std::mutex g_report_mutex;
 unsigned long long* g_report[kMaxDevices] = {};
 
+// Caller holds g_report_mutex.
 hipError_t report_buffer(unsigned long long** rep) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(g_report_mutex);
   if (g_report[dev] == nullptr) {
     e = hipMalloc(reinterpret_cast<void**>(&g_report[dev]), 256);
     if (e != hipSuccess) return e;
@@ -108,9 +110,13 @@ hipError_t report_buffer(unsigned long long** rep) {
 }
 
 // Clears the report, enqueues `launch`, waits for the stream and reads the
-// smallest finding back (~0 when there is none).
+// smallest finding back (~0 when there is none).  One report word serves a
+// device, so checks run one at a time: the lock is held until the finding
+// has been read back, and checks from several host threads or streams
+// queue behind each other instead of mixing their findings.
 template <class Launch>
 hipError_t run_check(hipStream_t stream, unsigned long long* finding, Launch launch) {
+  std::lock_guard<std::mutex> lock(g_report_mutex);
   unsigned long long* rep = nullptr;
   hipError_t e = report_buffer(&rep);
   if (e != hipSuccess) return e;
@@ -134,12 +140,12 @@ hipError_t check_offsets(const dsa_varlen& vl, hipStream_t stream, unsigned long
 }
 
 hipError_t check_indices(const dsa_varlen& vl, const int32_t* indices, int topk,
-                         int64_t row_begin, int64_t row_count, hipStream_t stream,
-                         unsigned long long* finding) {
+                         int64_t row_begin, int64_t row_count, bool empty_outside,
+                         hipStream_t stream, unsigned long long* finding) {
   return run_check(stream, finding, [&](unsigned long long* rep) {
     hipLaunchKernelGGL(check_indices_kernel, dim3(static_cast<unsigned>(row_count)),
                        dim3(kCheckThreads), 0, stream, vl.cu_seqlens_q, vl.cu_seqlens_k,
-                       vl.batch, indices, topk, row_begin, rep);
+                       vl.batch, indices, topk, row_begin, empty_outside ? 1 : 0, rep);
   });
 }
 

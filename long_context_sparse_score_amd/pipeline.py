@@ -25,6 +25,17 @@ def _torch():
     return torch
 
 
+@dataclass(frozen=True)
+class PrefillConfig:
+    """Launch shape of a windowed prefill.  BENCH_PREFILL is the one bench.py
+    times by default; the full-size parity tests run the same object."""
+    window: int = 2048      # query rows per score window (fp32 scores of one window in HBM)
+    attn_rows: int = 1024   # rows per attention launch inside a window
+
+
+BENCH_PREFILL = PrefillConfig()
+
+
 def score_ld(max_seqlen_k: int) -> int:
     """Leading dimension of a score buffer: a multiple of 64 floats (256 B)."""
     return (max_seqlen_k + 63) // 64 * 64

@@ -315,3 +315,118 @@ def test_indexer_kl_validation():
     assert call(d=96) == dsa.DSA_ERR_UNSUPPORTED
     assert call(scale=float("nan")) == dsa.DSA_ERR_INVALID_ARGUMENT
     assert call(scale=-0.1) == dsa.DSA_ERR_UNSUPPORTED
+
+
+# ---- binding extent checks (host only: CPU tensors, the device check comes last)
+
+def _bf(*shape):
+    import torch
+
+    return torch.zeros(shape, dtype=torch.bfloat16)
+
+
+def _f32(*shape):
+    import torch
+
+    return torch.zeros(shape, dtype=torch.float32)
+
+
+def _i32(*shape):
+    import torch
+
+    return torch.zeros(shape, dtype=torch.int32)
+
+
+def _cpu_varlen(cq=(0, 40, 100), ck=(0, 40, 100)):
+    return dsa.Varlen(cq, ck, device="cpu")
+
+
+def _expect(fn, exc=ValueError):
+    with pytest.raises(exc):
+        fn()
+
+
+def test_binding_index_scores_extents():
+    v = _cpu_varlen()
+    good = dict(q_idx=_bf(100, 4, 64), k_idx=_bf(100, 64), w=_f32(100, 4), scores=_f32(16, 64))
+    call = lambda **kw: dsa.dsa_index_scores(v, **{**good, **kw}, row_begin=80)  # noqa: E731
+    _expect(lambda: call(), TypeError)                     # extents fine: stops at the device check
+    _expect(lambda: call(q_idx=_bf(99, 4, 64)))            # q_idx rows != total_q
+    _expect(lambda: call(k_idx=_bf(100, 128)))             # key width != d_idx
+    _expect(lambda: call(k_idx=_bf(90, 64)))               # k_idx rows != total_k
+    _expect(lambda: call(w=_f32(100, 3)))                  # w heads != n_heads_idx
+    _expect(lambda: call(scores=_f32(16, 32)))             # fewer columns than max_seqlen_k
+    _expect(lambda: dsa.dsa_index_scores(v, **good, row_begin=90))          # window past total_q
+    _expect(lambda: dsa.dsa_index_scores(v, **good, row_begin=0, row_count=17))  # > scores rows
+
+
+def test_binding_topk_extents():
+    v = _cpu_varlen()
+    call = lambda s, i, **kw: dsa.dsa_topk(v, s, i, **kw)  # noqa: E731
+    _expect(lambda: call(_f32(8, 64), _i32(8, 16)), TypeError)
+    _expect(lambda: call(_f32(8, 64), _i32(8, 16), row_count=9))
+    _expect(lambda: call(_f32(4, 64), _i32(8, 16)))
+    _expect(lambda: call(_f32(8, 59), _i32(8, 16)))    # fewer columns than max_seqlen_k (60)
+    _expect(lambda: call(_f32(8, 64), _i32(8, 16), row_begin=95))
+
+
+def test_binding_attention_extents():
+    v = _cpu_varlen()
+    good = dict(q=_bf(100, 8, 64), k=_bf(100, 2, 64), v=_bf(100, 2, 64), indices=_i32(10, 32),
+                out=_bf(100, 8, 64), lse=_f32(100, 8))
+    call = lambda **kw: dsa.dsa_sparse_attn_prefill(v, **{**good, **kw})  # noqa: E731
+    _expect(lambda: call(), TypeError)
+    _expect(lambda: call(q=_bf(50, 8, 64)))
+    _expect(lambda: call(k=_bf(99, 2, 64)))
+    _expect(lambda: call(v=_bf(100, 4, 64)))
+    _expect(lambda: call(out=_bf(100, 8, 32)))
+    _expect(lambda: call(lse=_f32(100, 4)))
+    _expect(lambda: call(row_count=11))
+    _expect(lambda: call(row_begin=95))
+    ws = torch_u8(1024)
+    _expect(lambda: dsa.dsa_sparse_attn_prefill_grouped(v, **{**good, "q": _bf(10, 8, 64)},
+                                                        workspace=ws))
+    _expect(lambda: dsa.dsa_sparse_attn_prefill_grouped(v, **good, workspace=ws), TypeError)
+
+
+def torch_u8(n):
+    import torch
+
+    return torch.zeros(n, dtype=torch.uint8)
+
+
+def test_binding_decode_extents():
+    v = _cpu_varlen((0, 1, 2), (0, 300, 700))
+    good = dict(q=_bf(2, 8, 64), k_cache=_bf(700, 2, 64), v_cache=_bf(700, 2, 64),
+                indices=_i32(2, 32), out=_bf(2, 8, 64), workspace=torch_u8(1024))
+    call = lambda **kw: dsa.dsa_sparse_attn_decode(v, **{**good, **kw})  # noqa: E731
+    _expect(lambda: call(), TypeError)
+    _expect(lambda: call(q=_bf(3, 8, 64)))
+    _expect(lambda: call(k_cache=_bf(600, 2, 64)))
+    _expect(lambda: call(indices=_i32(1, 32), row_count=2))
+    _expect(lambda: call(lse=_f32(2, 4)))
+
+
+def test_binding_kl_and_check_extents():
+    v = _cpu_varlen()
+    good = dict(q=_bf(100, 8, 64), k=_bf(100, 2, 64), scores=_f32(10, 64), loss=_f32(10))
+    call = lambda **kw: dsa.dsa_indexer_kl(v, **{**good, **kw})  # noqa: E731
+    _expect(lambda: call(), TypeError)
+    _expect(lambda: call(loss=_f32(9)))
+    _expect(lambda: call(grad=_f32(9, 64)))
+    _expect(lambda: call(grad=_f32(10, 32)))
+    _expect(lambda: call(k=_bf(100, 2, 32)))
+    _expect(lambda: dsa.dsa_check_indices(v, _i32(10, 32), row_count=11))
+    _expect(lambda: dsa.dsa_check_scores(v, _f32(10, 64), row_begin=95))
+    _expect(lambda: dsa.dsa_check_scores(v, _f32(10, 64)), TypeError)
+
+
+def test_binding_passes_no_computed_scale(monkeypatch):
+    """With softmax_scale=None the binding hands the library its default
+    sentinel (0) and computes nothing; the library applies 1 / sqrt(d)."""
+    assert dsa._scale(None) == 0.0
+    assert dsa._scale(0.25) == 0.25
+    src = open(os.path.join(ROOT, "long_context_sparse_score_amd", "__init__.py")).read()
+    assert "** -0.5" not in src and "math.sqrt" not in src and "** 0.5" not in src
+    assert "#define DSA_SCALE_DEFAULT 0.0f" in open(HEADER).read()
+

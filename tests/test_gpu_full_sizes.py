@@ -1,14 +1,21 @@
 """GPU parity at the full workload sizes, in the launch configuration bench.py
-times (score windows of 8192 query rows), checked on sampled rows the oracle
-computes one by one.  Every call goes through the C ABI (libdsa.so).
+times by default (pipeline.BENCH_PREFILL: score windows and attention launch
+rows), checked on sampled rows the oracle computes one by one.  Every call
+goes through the C ABI (libdsa.so).
 
 Acceptance (per sampled row):
   * indices: causal, unique, ascending, -1 padded; any disagreement with the
     oracle's set only at positions whose fp64 score lies within 1e-3
     (relative) of the oracle's k-th score;
-  * attention output, on rows whose index set equals the oracle's:
-    max |err| <= 2e-2, mean |err| <= 2e-3 against the fp64 oracle;
-  * lse within 2e-3 on the same rows.
+  * attention output on EVERY sampled row: max |err| <= 2e-2 and mean
+    |err| <= 2e-3 against the fp64 oracle, which attends over the oracle's
+    own set where the sets agree and over the GPU's set where they differ
+    (the selection itself is held to the rule above);
+  * lse within 2e-3 on every sampled row.
+
+The 32K prefill is checked on 2048 stratified rows rather than in full: the
+oracle's whole-path time for all 32768 rows (minutes on the GPU host's
+cores) does not fit a test's time limit.
 """
 import numpy as np
 import pytest
@@ -16,7 +23,8 @@ import pytest
 import oracle
 import synth
 
-from _gpu import check_attn, check_topk_rows, device_workload, from_dev_bf16, log, oracle_rows
+from _gpu import (check_attn_every_row, check_topk_rows, device_workload, from_dev_bf16, log,
+                  oracle_rows)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -27,12 +35,12 @@ if not torch.cuda.is_available():  # pragma: no cover
 import long_context_sparse_score_amd as dsa  # noqa: E402
 from long_context_sparse_score_amd import pipeline  # noqa: E402
 
-BENCH_WINDOW = 8192  # bench.py's default score window
+CFG = pipeline.BENCH_PREFILL
 
 
-def run_prefill(wl, dev, window=BENCH_WINDOW, fp8=False):
+def run_prefill(wl, dev, fp8=False, cfg=CFG):
     vl = dsa.Varlen(wl.cu_q.tolist(), wl.cu_k.tolist())
-    bufs = pipeline.alloc_prefill(vl, wl.topk, window)
+    bufs = pipeline.alloc_prefill(vl, wl.topk, cfg.window)
     f8 = (pipeline.alloc_fp8_indexer(wl.total_q, wl.total_k, wl.n_heads_idx, wl.d_idx)
           if fp8 else None)
     out = torch.zeros((wl.total_q, wl.n_heads_q, wl.head_dim), dtype=torch.bfloat16,
@@ -40,9 +48,19 @@ def run_prefill(wl, dev, window=BENCH_WINDOW, fp8=False):
     lse = torch.zeros((wl.total_q, wl.n_heads_q), dtype=torch.float32, device="cuda")
     keep = torch.full((wl.total_q, wl.topk), -7, dtype=torch.int32, device="cuda")
     pipeline.prefill(vl, dev["q_idx"], dev["k_idx"], dev["w"], dev["q"], dev["k"], dev["v"], out,
-                     bufs, lse=lse, keep_indices=keep, fp8=f8)
+                     bufs, lse=lse, keep_indices=keep, fp8=f8, attn_rows=cfg.attn_rows)
     torch.cuda.synchronize()
     return out, lse, keep
+
+
+def stratified_rows(total, k, n, seed):
+    """n rows, one seeded row from each of n equal strata of [0, total), plus
+    rows 0, 1, k-2, k-1, k, k+1, the middle and the last two."""
+    rng = np.random.default_rng(seed)
+    edges = np.linspace(0, total, n + 1).astype(np.int64)
+    picked = {int(rng.integers(a, max(a + 1, b))) for a, b in zip(edges[:-1], edges[1:])}
+    fixed = {0, 1, k - 2, k - 1, k, k + 1, total // 2, total - 2, total - 1}
+    return np.array(sorted(r for r in picked | fixed if 0 <= r < total), dtype=np.int64)
 
 
 def fp8_oracle_rows(wl, host, rows):
@@ -63,43 +81,42 @@ def fp8_oracle_rows(wl, host, rows):
 
 def check_rows(wl, host, rows, out, lse, idx, fp8=False):
     ref = fp8_oracle_rows(wl, host, rows) if fp8 else oracle_rows(wl, host, rows)
-    got_idx = idx[torch.from_numpy(rows).cuda()].cpu().numpy()
+    rows_dev = torch.from_numpy(rows).cuda()
+    got_idx = idx[rows_dev].cpu().numpy()
     same = check_topk_rows(got_idx, ref["idx"], ref["scores"], ref["counts"], wl.topk)
-    got_out = from_dev_bf16(out[torch.from_numpy(rows).cuda()])
-    mx, mean = check_attn(got_out, ref["out"], rows_mask=same)
-    got_lse = lse[torch.from_numpy(rows).cuda()].cpu().numpy()
-    assert np.allclose(got_lse[same], ref["lse"][same], atol=2e-3)
-    log(f"  {len(rows)} rows: {same.sum()} identical index sets, attention max abs {mx:.2e} "
-        f"mean abs {mean:.2e}")
-    assert same.mean() >= 0.5, "most sampled rows should select exactly the oracle's set"
+    mx, mean, nd = check_attn_every_row(wl, host, rows, got_idx, same,
+                                        from_dev_bf16(out[rows_dev]), lse[rows_dev].cpu().numpy(),
+                                        ref)
+    log(f"  {len(rows)} rows: {same.sum()} identical index sets, {nd} checked on the GPU's own "
+        f"set; attention max abs {mx:.2e} mean abs {mean:.2e}")
 
 
-def test_prefill_32k_sampled():
+def test_prefill_32k_stratified_2048_rows():
     wl = synth.prefill_32k()
-    log("prefill_32k: generate")
+    log(f"prefill_32k (window {CFG.window}, attention launches of {CFG.attn_rows}): generate")
     host, dev = device_workload(wl)
     out, lse, idx = run_prefill(wl, dev)
-    rows = synth_rows(wl, 40, seed=2)
+    rows = stratified_rows(wl.total_q, wl.topk, 2048, seed=2)
     check_rows(wl, host, rows, out, lse, idx)
 
 
 def test_prefill_128k_sampled():
     wl = synth.prefill_128k()
-    log("prefill_128k: generate")
+    log(f"prefill_128k (window {CFG.window}, attention launches of {CFG.attn_rows}): generate")
     host, dev = device_workload(wl)
     out, lse, idx = run_prefill(wl, dev)
-    rows = synth_rows(wl, 24, seed=3)
+    rows = stratified_rows(wl.total_q, wl.topk, 128, seed=3)
     check_rows(wl, host, rows, out, lse, idx)
 
 
 def test_prefill_128k_fp8_indexer_sampled():
-    """The optional fp8 indexer at the bench's full prefill size and windows,
-    against the oracle on the same fp8-represented inputs."""
+    """The optional fp8 indexer at the full prefill size, in the bench's launch
+    configuration, against the oracle on the same fp8-represented inputs."""
     wl = synth.prefill_128k()
     log("prefill_128k fp8 indexer: generate")
     host, dev = device_workload(wl)
     out, lse, idx = run_prefill(wl, dev, fp8=True)
-    rows = synth_rows(wl, 24, seed=4)
+    rows = stratified_rows(wl.total_q, wl.topk, 48, seed=4)
     check_rows(wl, host, rows, out, lse, idx, fp8=True)
 
 
@@ -114,20 +131,21 @@ def test_prefill_128k_repeatable():
 
 
 def test_prefill_128k_topk_property_all_rows():
-    """Every row of the 128K prefill, at the bench's window size: the selection
-    is causal, ascending, unique, min(k, p + 1) long, and exact for the GPU's own
-    fp32 scores -- each selected score beats each unselected visible score, and
-    on an equal score the selected position is the lower one.  (A property of
-    the top-k that holds at any size; the fp32 scores are the kernel's.)"""
+    """Every row of the 128K prefill, in the bench's score windows: the
+    selection is causal, ascending, unique, min(k, p + 1) long, and exact for
+    the GPU's own fp32 scores -- each selected score beats each unselected
+    visible score, and on an equal score the selected position is the lower
+    one.  (A property of the top-k that holds at any size; the fp32 scores
+    are the kernel's.)"""
     wl = synth.prefill_128k()
     _, dev = device_workload(wl, ("q_idx", "k_idx", "w"))
     vl = dsa.Varlen(wl.cu_q.tolist(), wl.cu_k.tolist())
-    bufs = pipeline.alloc_prefill(vl, wl.topk, BENCH_WINDOW)
+    bufs = pipeline.alloc_prefill(vl, wl.topk, CFG.window)
     ld = bufs.scores.shape[1]
     cols = torch.arange(ld, device="cuda")
     bad_rows = 0
-    for r0 in range(0, wl.total_q, BENCH_WINDOW):
-        n = min(BENCH_WINDOW, wl.total_q - r0)
+    for r0 in range(0, wl.total_q, CFG.window):
+        n = min(CFG.window, wl.total_q - r0)
         dsa.dsa_index_scores(vl, dev["q_idx"], dev["k_idx"], dev["w"], bufs.scores,
                              row_begin=r0, row_count=n)
         dsa.dsa_topk(vl, bufs.scores, bufs.indices, row_begin=r0, row_count=n)
@@ -180,13 +198,12 @@ def test_decode_b64_128k_all_queries():
         pipeline.decode(vl, dev["q_idx"], dev["k_idx"], dev["w"], dev["q"], dev["k"], dev["v"],
                         out, bufs, lse=lse, side_stream=side)
         torch.cuda.synchronize()
-        same = check_topk_rows(bufs.indices.cpu().numpy(), ref["idx"], ref["scores"],
-                               ref["counts"], wl.topk)
-        mx, mean = check_attn(from_dev_bf16(out), ref["out"], rows_mask=same)
-        assert np.allclose(lse.cpu().numpy()[same], ref["lse"][same], atol=2e-3)
-        log(f"  {groups} group(s): {same.sum()}/64 identical index sets, attention max abs "
-            f"{mx:.2e} mean abs {mean:.2e}")
-        assert same.mean() >= 0.5
+        got_idx = bufs.indices.cpu().numpy()
+        same = check_topk_rows(got_idx, ref["idx"], ref["scores"], ref["counts"], wl.topk)
+        mx, mean, nd = check_attn_every_row(wl, host, rows, got_idx, same, from_dev_bf16(out),
+                                            lse.cpu().numpy(), ref)
+        log(f"  {groups} group(s): {same.sum()}/64 identical index sets ({nd} on the GPU's own "
+            f"set), attention max abs {mx:.2e} mean abs {mean:.2e}")
 
 
 def test_decode_b64_128k_fp8_indexer_all_queries():
@@ -206,12 +223,12 @@ def test_decode_b64_128k_fp8_indexer_all_queries():
     pipeline.decode(vl, dev["q_idx"], None, dev["w"], dev["q"], dev["k"], dev["v"], out, bufs,
                     lse=lse, fp8=f8)
     torch.cuda.synchronize()
-    same = check_topk_rows(bufs.indices.cpu().numpy(), ref["idx"], ref["scores"], ref["counts"],
-                           wl.topk)
-    mx, mean = check_attn(from_dev_bf16(out), ref["out"], rows_mask=same)
-    assert np.allclose(lse.cpu().numpy()[same], ref["lse"][same], atol=2e-3)
-    log(f"  {same.sum()}/64 identical index sets, attention max abs {mx:.2e} mean abs {mean:.2e}")
-    assert same.mean() >= 0.5
+    got_idx = bufs.indices.cpu().numpy()
+    same = check_topk_rows(got_idx, ref["idx"], ref["scores"], ref["counts"], wl.topk)
+    mx, mean, nd = check_attn_every_row(wl, host, rows, got_idx, same, from_dev_bf16(out),
+                                        lse.cpu().numpy(), ref)
+    log(f"  {same.sum()}/64 identical index sets ({nd} on the GPU's own set), attention max abs "
+        f"{mx:.2e} mean abs {mean:.2e}")
 
 
 def test_varlen_512k_sampled():
@@ -219,18 +236,13 @@ def test_varlen_512k_sampled():
     log(f"varlen_512k: {len(wl.seqlens_q)} sequences, max {wl.max_seqlen_k}: generate")
     host, dev = device_workload(wl)
     out, lse, idx = run_prefill(wl, dev)
-    # rows from every sequence: first, around k, last, plus random
+    # rows from every sequence: first, around k, last, plus seeded stratified rows
     rng = np.random.default_rng(5)
     rows = set()
     for b in range(wl.batch):
         a, e = int(wl.cu_q[b]), int(wl.cu_q[b + 1])
-        rows |= {a, min(a + wl.topk, e - 1), e - 1}
-        rows |= set(rng.integers(a, e, size=2).tolist())
+        rows |= {a, min(a + wl.topk - 1, e - 1), min(a + wl.topk, e - 1), e - 1}
+        edges = np.linspace(a, e, 5).astype(np.int64)
+        rows |= {int(rng.integers(x, max(x + 1, y))) for x, y in zip(edges[:-1], edges[1:])}
     rows = np.array(sorted(rows), dtype=np.int64)
     check_rows(wl, host, rows, out, lse, idx)
-
-
-def synth_rows(wl, n_random, seed):
-    from _gpu import sample_rows
-
-    return sample_rows(wl.total_q, wl.topk, n_random, seed)

@@ -7,7 +7,7 @@ import pytest
 import oracle
 import synth
 
-from _gpu import (check_attn, check_topk_rows, device_workload, from_dev_bf16, log, oracle_rows,
+from _gpu import (check_attn, check_attn_every_row, check_topk_rows, device_workload, from_dev_bf16, log, oracle_rows,
                   to_dev, to_dev_bf16)
 
 torch = pytest.importorskip("torch")
@@ -311,9 +311,12 @@ def test_sparse_attn_prefill_given_indices(hq, hkv, d):
     assert np.allclose(lse.cpu().numpy(), ref["lse"], rtol=0, atol=2e-3)
 
 
-def test_sparse_attn_shuffled_and_invalid_slots():
+def test_sparse_attn_shuffled_and_invalid_slots(monkeypatch):
     """Index order does not matter; -1 and out-of-range slots are empty; a row
-    with no valid slot gives zeros and -inf."""
+    with no valid slot gives zeros and -inf.  The same call under DSA_CHECK
+    (which reads out-of-range entries as empty slots for attention) is
+    accepted and bitwise equal; the default scale (softmax_scale=None, the C
+    ABI's DSA_SCALE_DEFAULT) is bitwise the explicit 1/sqrt(d)."""
     wl = small_wl([64], [64], hq=8, hkv=2, d=128, topk=32, seed=4)
     host, dev = device_workload(wl)
     rng = np.random.default_rng(0)
@@ -338,6 +341,18 @@ def test_sparse_attn_shuffled_and_invalid_slots():
     assert np.isneginf(l[10]).all()
     ok = np.arange(64) != 10
     assert np.allclose(l[ok], ref_lse[ok], atol=2e-3)
+    out2 = torch.zeros_like(out)
+    lse2 = torch.zeros_like(lse)
+    dsa.dsa_sparse_attn_prefill(vl, dev["q"], dev["k"], dev["v"], to_dev(idx), out2, lse=lse2,
+                                softmax_scale=float(np.float32(1) / np.sqrt(np.float32(128))))
+    monkeypatch.setenv("DSA_CHECK", "1")
+    out3 = torch.zeros_like(out)
+    dsa.dsa_sparse_attn_prefill(vl, dev["q"], dev["k"], dev["v"], to_dev(idx), out3)
+    monkeypatch.delenv("DSA_CHECK")
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse, lse2)
+    assert torch.equal(out.view(torch.int16), out3.view(torch.int16))
 
 
 # ---------------------------------------------------------------- whole path
@@ -384,10 +399,9 @@ def test_decode_small_varlen(groups):
     torch.cuda.synchronize()
     rows = np.arange(wl.batch)
     ref = oracle_rows(wl, host, rows)
-    same = check_topk_rows(bufs.indices.cpu().numpy(), ref["idx"], ref["scores"], ref["counts"],
-                           wl.topk)
-    check_attn(from_dev_bf16(out), ref["out"], rows_mask=same)
-    assert np.allclose(lse.cpu().numpy()[same], ref["lse"][same], atol=2e-3)
+    got_idx = bufs.indices.cpu().numpy()
+    same = check_topk_rows(got_idx, ref["idx"], ref["scores"], ref["counts"], wl.topk)
+    check_attn_every_row(wl, host, rows, got_idx, same, from_dev_bf16(out), lse.cpu().numpy(), ref)
 
 
 def test_bitwise_repeatable():
