@@ -321,6 +321,31 @@ int dsa_sparse_attn_decode(const dsa_varlen* vl, const void* q, const void* k_ca
                            hipStream_t stream);
 
 /*
+ * dsa_sparse_attn_decode_noalloc -- dsa_sparse_attn_decode without a
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under graph capture, serving loops or harnesses that forbid hipMalloc).
+ * The split partials live in a fixed 16 MiB device array inside the library
+ * (one per GPU, held until the process ends; its address is looked up on the
+ * first call on each device).  The call allocates nothing and is otherwise
+ * identical to dsa_sparse_attn_decode: same kernels, same split of the index
+ * list, bitwise the same results.
+ *
+ * Limit: the partials, row_count * splits * n_heads_q * (head_dim + 2) * 4
+ * bytes, must fit the 16 MiB (every shape with n_heads_q * (head_dim + 2) <=
+ * 8192, i.e. up to 63 query heads at head_dim 128); larger calls return
+ * DSA_ERR_UNSUPPORTED before enqueueing anything.
+ * Every call on one GPU shares that GPU's array and leaves its partials in
+ * it; nothing in it needs to start at zero.  Calls that overlap in time on
+ * one GPU (different streams or host threads) race on the array and must be
+ * ordered by the caller.
+ */
+int dsa_sparse_attn_decode_noalloc(const dsa_varlen* vl, const void* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* indices, int32_t topk,
+                                   int64_t row_begin, int64_t row_count, int32_t n_heads_q,
+                                   int32_t n_heads_kv, int32_t head_dim, float softmax_scale,
+                                   void* out, float* lse, hipStream_t stream);
+
+/*
  * Device-side precondition checks (debugging aid; see the conventions above).
  * Each validates its arguments on the host like the entry points, runs one
  * or two small kernels on `stream`, waits for the stream (and so for all

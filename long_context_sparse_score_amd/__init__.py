@@ -14,6 +14,8 @@ Entry points (same names as the C ABI):
     dsa_sparse_attn_prefill_grouped (+ workspace size; 16 adjacent rows per
     union of index sets),
     dsa_indexer_kl (the indexer's warm-up KL loss and its score gradient),
+    dsa_sparse_attn_decode_noalloc (decode attention with the partials in the
+    library's fixed per-GPU scratch, for callers that cannot allocate),
     dsa_check_varlen, dsa_check_indices, dsa_check_scores (device-side
     precondition checks; the entry points also run them when the environment
     variable DSA_CHECK is set to anything but "" or "0")
@@ -32,7 +34,7 @@ EXPORTED = (
     "dsa_topk", "dsa_sparse_attn_prefill", "dsa_sparse_attn_decode_workspace_size",
     "dsa_sparse_attn_decode", "dsa_check_varlen", "dsa_check_indices", "dsa_check_scores",
     "dsa_quantize_fp8", "dsa_index_scores_fp8", "dsa_sparse_attn_prefill_grouped_workspace_size",
-    "dsa_sparse_attn_prefill_grouped", "dsa_indexer_kl",
+    "dsa_sparse_attn_prefill_grouped", "dsa_indexer_kl", "dsa_sparse_attn_decode_noalloc",
 )
 
 DSA_OK = 0
@@ -87,6 +89,8 @@ def load_library(path: str = LIB_PATH):
     lib.dsa_sparse_attn_decode_workspace_size.argtypes = [vl, i64, i32, i32, i32, sz]
     lib.dsa_sparse_attn_decode.argtypes = [vl, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, f32,
                                            vp, vp, vp, ctypes.c_size_t, vp]
+    lib.dsa_sparse_attn_decode_noalloc.argtypes = [vl, vp, vp, vp, vp, i32, i64, i64, i32, i32,
+                                                   i32, f32, vp, vp, vp]
     lib.dsa_quantize_fp8.argtypes = [vp, i64, i32, vp, vp, vp]
     lib.dsa_index_scores_fp8.argtypes = [vl, vp, vp, vp, vp, vp, i32, i32, i64, i64, vp, i64, vp]
     lib.dsa_sparse_attn_prefill_grouped_workspace_size.argtypes = [vl, i64, i32, sz]
@@ -438,6 +442,29 @@ def dsa_sparse_attn_decode(vl: Varlen, q, k_cache, v_cache, indices, out, worksp
         vl.struct, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(indices), indices.shape[1],
         row_begin, row_count, q.shape[1], k_cache.shape[1], d, _scale(softmax_scale), _ptr(out),
         _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dsa_sparse_attn_decode_noalloc(vl: Varlen, q, k_cache, v_cache, indices, out, lse=None,
+                                   softmax_scale=None, row_begin=0, row_count=None, stream=None):
+    """dsa_sparse_attn_decode with the split partials in the library's fixed
+    per-GPU scratch (no workspace, nothing allocated; calls that overlap on
+    one GPU race on that scratch)."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 3)
+    _need(v_cache, "v_cache", torch.bfloat16, 3)
+    _need(indices, "indices", torch.int32, 2)
+    _need(out, "out", torch.bfloat16, 3)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2)
+    row_count = indices.shape[0] if row_count is None else row_count
+    _attn_extents(vl, q, k_cache, v_cache, indices, out, lse, row_begin, row_count,
+                  q_rows=vl.batch)
+    _on_device(q=q, k_cache=k_cache, v_cache=v_cache, indices=indices, out=out, lse=lse)
+    _check(load_library().dsa_sparse_attn_decode_noalloc(
+        vl.struct, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(indices), indices.shape[1],
+        row_begin, row_count, q.shape[1], k_cache.shape[1], q.shape[2], _scale(softmax_scale),
+        _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def dsa_check_varlen(vl: Varlen, stream=None):

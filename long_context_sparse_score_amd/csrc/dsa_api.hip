@@ -472,6 +472,51 @@ int dsa_sparse_attn_decode(const dsa_varlen* vl, const void* q, const void* k_ca
       "sparse_attn_decode launch");
 }
 
+int dsa_sparse_attn_decode_noalloc(const dsa_varlen* vl, const void* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* indices, int32_t topk,
+                                   int64_t row_begin, int64_t row_count, int32_t n_heads_q,
+                                   int32_t n_heads_kv, int32_t head_dim, float softmax_scale,
+                                   void* out, float* lse, hipStream_t stream) {
+  softmax_scale = resolve_scale(softmax_scale, head_dim);
+  int st;
+  if ((st = check_varlen(vl))) return st;
+  if (vl->total_q != vl->batch || vl->max_seqlen_q != 1)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "decode needs exactly one query per sequence");
+  if ((st = check_window(vl, row_begin, row_count))) return st;
+  if ((st = check_bf16(q, "q"))) return st;
+  if ((st = check_bf16(k_cache, "k_cache"))) return st;
+  if ((st = check_bf16(v_cache, "v_cache"))) return st;
+  if ((st = check_bf16(out, "out"))) return st;
+  if (indices == nullptr || !aligned(indices, 4))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "indices is NULL or misaligned");
+  if (lse != nullptr && !aligned(lse, 4)) return fail(DSA_ERR_INVALID_ARGUMENT, "lse misaligned");
+  if ((st = check_attn_shape(n_heads_q, n_heads_kv, head_dim, topk, softmax_scale))) return st;
+  if ((st = check_attn_extent(vl, n_heads_kv, head_dim))) return st;
+  const int splits = dsa::attn_decode_splits(row_count, n_heads_kv, topk);
+  const size_t need = dsa::attn_workspace_bytes(row_count, n_heads_q, head_dim, splits);
+  if (need > dsa::attn_scratch_bytes())
+    return fail(DSA_ERR_UNSUPPORTED,
+                "decode partials need %zu bytes, above the fixed scratch of %zu bytes; use "
+                "dsa_sparse_attn_decode with a workspace",
+                need, dsa::attn_scratch_bytes());
+  if (checks_enabled() &&
+      (st = device_indices(vl, indices, topk, row_begin, row_count, stream, true)))
+    return st;
+  if (row_count == 0) return ok();
+  float* scratch = nullptr;
+  if (need > 0) {
+    const hipError_t e = dsa::attn_scratch(&scratch);
+    if (e != hipSuccess) return hip_status(e, "decode scratch lookup");
+  }
+  return hip_status(
+      dsa::launch_sparse_attn(*vl, static_cast<const uint16_t*>(q),
+                              static_cast<const uint16_t*>(k_cache),
+                              static_cast<const uint16_t*>(v_cache), indices, topk, row_begin,
+                              row_count, n_heads_q, n_heads_kv, head_dim, softmax_scale,
+                              static_cast<uint16_t*>(out), lse, splits, scratch, stream),
+      "sparse_attn_decode_noalloc launch");
+}
+
 int dsa_check_varlen(const dsa_varlen* vl, hipStream_t stream) {
   int st;
   if ((st = check_varlen(vl))) return st;

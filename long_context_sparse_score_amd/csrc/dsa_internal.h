@@ -33,6 +33,12 @@ hipError_t launch_topk(const dsa_varlen& vl, const float* scores, int64_t ld, in
 size_t attn_workspace_bytes(int64_t rows, int n_heads_q, int head_dim, int splits);
 int attn_decode_splits(int64_t rows, int n_heads_kv, int topk);
 
+// The decode partials' fixed device scratch (the entry point that allocates
+// nothing): its size, and its address on the current device (looked up on
+// the first call per device).
+size_t attn_scratch_bytes();
+hipError_t attn_scratch(float** ptr);
+
 hipError_t launch_sparse_attn(const dsa_varlen& vl, const uint16_t* q, const uint16_t* k,
                               const uint16_t* v, const int32_t* indices, int topk,
                               int64_t row_begin, int64_t row_count, int n_heads_q, int n_heads_kv,

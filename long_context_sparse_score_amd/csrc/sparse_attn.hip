@@ -19,6 +19,7 @@
 //   lane's probabilities are already in place as the A operand; V's B
 //   operand (8 consecutive keys of one column per lane) comes from LDS
 //   through the transposing read.
+#include <mutex>
 #include <type_traits>
 
 #include "dsa_common.h"
@@ -804,6 +805,41 @@ hipError_t launch_grouped_attn(const dsa_varlen& vl, const uint16_t* q, const ui
     }
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- fixed scratch
+//
+// Device-resident scratch for the decode split partials, for callers that
+// cannot allocate (code under graph capture, serving loops that forbid
+// hipMalloc).  Each GPU the library runs on holds one copy until the process
+// ends; host code never passes `scratch` itself to a kernel (on the host the
+// name is only a stand-in), but the device address hipGetSymbolAddress
+// returns for the current device, looked up once per device.
+constexpr size_t kAttnScratchBytes = size_t{16} << 20;
+static __device__ __align__(256) float scratch[kAttnScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+float* g_scratch[kMaxScratchDevices] = {};
+}  // namespace
+
+size_t attn_scratch_bytes() { return kAttnScratchBytes; }
+
+hipError_t attn_scratch(float** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = static_cast<float*>(p);
+  }
+  *ptr = g_scratch[dev];
+  return hipSuccess;
 }
 
 size_t attn_workspace_bytes(int64_t rows, int n_heads_q, int head_dim, int splits) {

@@ -430,3 +430,23 @@ def test_binding_passes_no_computed_scale(monkeypatch):
     assert "** -0.5" not in src and "math.sqrt" not in src and "** 0.5" not in src
     assert "#define DSA_SCALE_DEFAULT 0.0f" in open(HEADER).read()
 
+
+def test_noalloc_decode_validation_and_limit():
+    """The no-alloc decode rejects bad arguments and partials beyond its
+    fixed 16 MiB scratch on the host, before touching any device."""
+    lib = dsa.load_library()
+    U, I = dsa.DSA_ERR_UNSUPPORTED, dsa.DSA_ERR_INVALID_ARGUMENT
+
+    def call(batch=64, hq=32, hkv=4, d=128, topk=2048, q=FAKE, rc=None):
+        v = vl(batch=batch, total_q=batch, total_k=batch * 1000, max_q=1, max_k=1000)
+        return lib.dsa_sparse_attn_decode_noalloc(ctypes.byref(v), q, FAKE, FAKE, FAKE, topk, 0,
+                                                  batch if rc is None else rc, hq, hkv, d, 0.0,
+                                                  FAKE, None, None)
+
+    # 64 rows x 4 splits x 128 heads x 130 x 4 B = 17.0 MB > 16 MiB
+    assert call(hq=128, hkv=8) == U
+    assert b"fixed scratch" in lib.dsa_last_error()
+    assert call(q=None) == I
+    assert call(rc=65) == I
+    assert call(hq=30, hkv=4) == I
+    assert call(rc=0) == dsa.DSA_OK  # empty window: nothing enqueued, no device touched
