@@ -64,6 +64,8 @@ def parse():
                     help="skip the indexer warm-up KL loss measurement (a training-side kernel)")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the optional fp8-indexer variant (reported beside the headline)")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the fused indexer -> top-k variant (reported beside the headline)")
     ap.add_argument("--prefill-streams", type=int, default=1, choices=(1, 2),
                     help="2: each window's attention on a side stream, overlapping the next "
                          "window's indexer")
@@ -427,6 +429,13 @@ def main():
         result["fp8_indexer"] = fp8_variant(torch, pipeline, args, stream, wl, vl, P, out, lse,
                                             None if args.no_decode else (wd, vd, D, dout, dlse))
 
+    if not args.no_fused:
+        result["fused_index_topk"] = fused_variant(
+            torch, dsa, pipeline, args, stream, wl, vl, P, out, lse, pre_ms / args.steps,
+            idx_ms / args.steps + topk_ms / args.steps,
+            None if args.no_decode else (wd, vd, D, dout, dlse, dec_ms / args.steps,
+                                         (d_idx_ms + d_topk_ms) / args.steps))
+
     if not args.no_kl:
         result["indexer_kl"] = kl_variant(torch, dsa, args, stream, wl, vl, P, bufs)
 
@@ -515,6 +524,90 @@ def fp8_variant(torch, pipeline, args, stream, wl, vl, P, out, lse, dec):
                                       "frac": round(gbs / PEAK_HBM_GBS, 4),
                                       "bytes_per_query": per_q}}
         del dbufs, fp8d
+    torch.cuda.empty_cache()
+    return res
+
+
+def fused_variant(torch, dsa, pipeline, args, stream, wl, vl, P, out, lse, unfused_prefill_ms,
+                  unfused_select_ms, dec):
+    """The same prefill and decode steps with the indexer and the top-k fused
+    (dsa_index_topk: the indexer keeps only candidates above a threshold read
+    off a sample of each row, an exact select runs over them, rows it cannot
+    settle are recomputed unfused).  Same windows and attention launches as
+    the headline; the selection is bitwise the headline's."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    res = {"note": "fused indexer -> top-k (no score rows); same selection, reported beside the "
+                   "unfused headline"}
+    bufs = pipeline.alloc_prefill(vl, wl.topk, args.window, fused=True)
+    run = lambda rec: pipeline.prefill(vl, P["q_idx"], P["k_idx"], P["w"], P["q"], P["k"],  # noqa: E731
+                                       P["v"], out, bufs, lse=lse, stream=stream, record=rec,
+                                       attn_rows=args.attn_rows)
+    log("fused indexer -> top-k: prefill")
+    for _ in range(args.warmup):
+        run(None)
+    torch.cuda.synchronize()
+    rec, tot = [], 0.0
+    for _ in range(args.steps):
+        a, b = ev(), ev()
+        a.record(stream)
+        run(rec)
+        b.record(stream)
+        torch.cuda.synchronize()
+        tot += a.elapsed_time(b)
+    pre_ms = tot / args.steps
+    span = lambda name: sum(e[name][0].elapsed_time(e[name][1]) for _, _, e in rec) / args.steps  # noqa: E731
+    # Candidate counts and fallbacks of every window (an untimed pass).
+    counts, fallbacks = [], 0
+    window = bufs.window
+    for r0 in range(0, wl.total_q, window):
+        n = min(window, wl.total_q - r0)
+        dsa.dsa_index_topk(vl, P["q_idx"], P["k_idx"], P["w"], bufs.indices[:n], bufs.fused,
+                           row_begin=r0, row_count=n)
+        off = (n * 4 + 255) // 256 * 256
+        counts.append(bufs.fused[:4 * n].view(torch.int32).cpu())
+        fallbacks += int(bufs.fused[off:off + 4 * n].view(torch.int32).sum())
+    c = torch.cat(counts).double()
+    long_rows = c[torch.arange(wl.total_q) + 1 > 10240]
+    res["prefill"] = {
+        "ms": round(pre_ms, 3), "tokens_per_s": round(wl.total_q / (pre_ms / 1e3), 1),
+        "unfused_ms": round(unfused_prefill_ms, 3),
+        "index_topk_ms": round(span("index_scores"), 3),
+        "unfused_index_scores_plus_topk_ms": round(unfused_select_ms, 3),
+        "sparse_attn_ms": round(span("sparse_attn"), 3),
+        "candidates_long_rows": {"mean": round(float(long_rows.mean()), 1),
+                                 "min": int(long_rows.min()), "max": int(long_rows.max())},
+        "fallback_rows": fallbacks,
+    }
+    del bufs
+    if dec is not None:
+        wd, vd, D, dout, dlse, unfused_dec_ms, unfused_dec_sel_ms = dec
+        dbufs = pipeline.alloc_decode(vd, wd.n_heads_q, wd.head_dim, wd.topk, fused=True)
+        step = lambda: pipeline.decode(vd, D["q_idx"], D["k_idx"], D["w"], D["q"], D["k"], D["v"],  # noqa: E731
+                                       dout, dbufs, lse=dlse, stream=stream)
+        log("fused indexer -> top-k: decode")
+        for _ in range(max(1, args.warmup)):
+            step()
+        torch.cuda.synchronize()
+        tot, sel = 0.0, 0.0
+        for _ in range(args.steps):
+            a, b = ev(), ev()
+            a.record(stream)
+            step()
+            b.record(stream)
+            torch.cuda.synchronize()
+            tot += a.elapsed_time(b)
+            a, b = ev(), ev()
+            a.record(stream)
+            dsa.dsa_index_topk(vd, D["q_idx"], D["k_idx"], D["w"], dbufs.indices, dbufs.fused[0])
+            b.record(stream)
+            torch.cuda.synchronize()
+            sel += a.elapsed_time(b)
+        ms = tot / args.steps
+        res["decode"] = {"ms": round(ms, 4), "queries_per_s": round(wd.batch / (ms / 1e3), 1),
+                         "unfused_ms": round(unfused_dec_ms, 4),
+                         "index_topk_ms": round(sel / args.steps, 4),
+                         "unfused_index_scores_plus_topk_ms": round(unfused_dec_sel_ms, 4)}
+        del dbufs
     torch.cuda.empty_cache()
     return res
 

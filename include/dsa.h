@@ -184,6 +184,43 @@ int dsa_topk(const dsa_varlen* vl, const float* scores, int64_t ld_scores, int64
              int64_t row_count, int32_t k, int32_t* indices, void* workspace,
              size_t workspace_bytes, hipStream_t stream);
 
+/* Workspace bytes dsa_index_topk needs for a window of row_count rows. */
+int dsa_index_topk_workspace_size(const dsa_varlen* vl, int64_t row_count, int32_t k,
+                                  size_t* bytes);
+
+/*
+ * dsa_index_topk -- dsa_index_scores followed by dsa_topk, fused: the k best
+ * positions of every window row by indexer score (page 5 section 1: the
+ * scout scores every position and the k best are kept; section 8: the
+ * selection is deterministic) without writing the row's scores out.
+ *
+ *   q_idx, k_idx, w, n_heads_idx, d_idx, row window: as dsa_index_scores
+ *   indices   int32 [row_count, k]: exactly what dsa_index_scores ->
+ *             dsa_topk write for the same inputs (bitwise: the scores are
+ *             computed by the same kernel arithmetic and the same tie rule
+ *             selects among them).
+ *   workspace device buffer of at least dsa_index_topk_workspace_size bytes,
+ *             256-byte aligned, contents clobbered; calls sharing it must be
+ *             ordered.  After the call, its first row_count uint32 words are
+ *             the rows' candidate counts, and row_count words starting at
+ *             byte offset 256 * ceil(4 * row_count / 256) are 1 for rows
+ *             that took the exact fallback below, else 0 (diagnostics).
+ *
+ * How: a sample pass scores every S-th key of each row (S = 64, or more for
+ * rows beyond 262144 keys) and reads off a per-row threshold that about
+ * 5120 scores of the row are expected to reach; the indexer then keeps only
+ * the scores at or above it, as (score, position) candidates, and an exact
+ * top-k runs over those.  When a row has fewer than k candidates, or more
+ * than its list holds (10240), its scores are recomputed and selected the
+ * unfused way, so the result never depends on the estimate.  Rows of at most
+ * 10240 positions keep every score as a candidate.
+ * Supported / invalid: as dsa_index_scores and dsa_topk (1 <= k <= 2048).
+ */
+int dsa_index_topk(const dsa_varlen* vl, const void* q_idx, const void* k_idx, const float* w,
+                   int32_t n_heads_idx, int32_t d_idx, int64_t row_begin, int64_t row_count,
+                   int32_t k, int32_t* indices, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+
 /*
  * dsa_sparse_attn_prefill -- GQA softmax attention of each query row over its
  * selected positions only (page 5 section 1: attention among the chosen

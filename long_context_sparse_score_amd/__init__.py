@@ -8,6 +8,7 @@ points raises.
 
 Entry points (same names as the C ABI):
     dsa_index_scores, dsa_topk, dsa_topk_workspace_size,
+    dsa_index_topk (+ workspace size; the indexer and top-k fused: no score rows),
     dsa_sparse_attn_prefill, dsa_sparse_attn_decode,
     dsa_sparse_attn_decode_workspace_size,
     dsa_quantize_fp8, dsa_index_scores_fp8 (the optional fp8 indexer),
@@ -35,6 +36,7 @@ EXPORTED = (
     "dsa_sparse_attn_decode", "dsa_check_varlen", "dsa_check_indices", "dsa_check_scores",
     "dsa_quantize_fp8", "dsa_index_scores_fp8", "dsa_sparse_attn_prefill_grouped_workspace_size",
     "dsa_sparse_attn_prefill_grouped", "dsa_indexer_kl", "dsa_sparse_attn_decode_noalloc",
+    "dsa_index_topk_workspace_size", "dsa_index_topk",
 )
 
 DSA_OK = 0
@@ -91,6 +93,9 @@ def load_library(path: str = LIB_PATH):
                                            vp, vp, vp, ctypes.c_size_t, vp]
     lib.dsa_sparse_attn_decode_noalloc.argtypes = [vl, vp, vp, vp, vp, i32, i64, i64, i32, i32,
                                                    i32, f32, vp, vp, vp]
+    lib.dsa_index_topk_workspace_size.argtypes = [vl, i64, i32, sz]
+    lib.dsa_index_topk.argtypes = [vl, vp, vp, vp, i32, i32, i64, i64, i32, vp, vp,
+                                   ctypes.c_size_t, vp]
     lib.dsa_quantize_fp8.argtypes = [vp, i64, i32, vp, vp, vp]
     lib.dsa_index_scores_fp8.argtypes = [vl, vp, vp, vp, vp, vp, i32, i32, i64, i64, vp, i64, vp]
     lib.dsa_sparse_attn_prefill_grouped_workspace_size.argtypes = [vl, i64, i32, sz]
@@ -241,6 +246,36 @@ def dsa_index_scores(vl: Varlen, q_idx, k_idx, w, scores, row_begin: int = 0,
     _check(load_library().dsa_index_scores(
         vl.struct, _ptr(q_idx), _ptr(k_idx), _ptr(w), q_idx.shape[1], q_idx.shape[2], row_begin,
         row_count, _ptr(scores), scores.shape[1], _stream(stream)))
+
+
+def dsa_index_topk_workspace_size(vl: Varlen, row_count: int, k: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().dsa_index_topk_workspace_size(vl.struct, row_count, k, ctypes.byref(n)))
+    return n.value
+
+
+def dsa_index_topk(vl: Varlen, q_idx, k_idx, w, indices, workspace, row_begin: int = 0,
+                   row_count: int | None = None, stream=None):
+    """Fused indexer scores -> top-k (k = indices.shape[1]) of rows
+    [row_begin, row_begin + row_count) into indices (int32 [row_count, k]),
+    without writing score rows; bitwise what dsa_index_scores -> dsa_topk give."""
+    torch = _torch()
+    _need(q_idx, "q_idx", torch.bfloat16, 3)
+    _need(k_idx, "k_idx", torch.bfloat16, 2)
+    _need(w, "w", torch.float32, 2)
+    _need(indices, "indices", torch.int32, 2)
+    _need(workspace, "workspace", torch.uint8, 1)
+    row_count = indices.shape[0] if row_count is None else row_count
+    _window(vl, row_begin, row_count)
+    h, d = q_idx.shape[1], q_idx.shape[2]
+    _shape(q_idx, "q_idx", (vl.total_q, h, d))
+    _shape(k_idx, "k_idx", (vl.total_k, d))
+    _shape(w, "w", (vl.total_q, h))
+    _rows(indices, "indices", row_count)
+    _on_device(q_idx=q_idx, k_idx=k_idx, w=w, indices=indices, workspace=workspace)
+    _check(load_library().dsa_index_topk(
+        vl.struct, _ptr(q_idx), _ptr(k_idx), _ptr(w), h, d, row_begin, row_count,
+        indices.shape[1], _ptr(indices), _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 def dsa_quantize_fp8(x, codes, scales, stream=None):

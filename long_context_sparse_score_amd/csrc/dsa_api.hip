@@ -290,6 +290,47 @@ int dsa_topk(const dsa_varlen* vl, const float* scores, int64_t ld_scores, int64
                     "topk launch");
 }
 
+int dsa_index_topk_workspace_size(const dsa_varlen* vl, int64_t row_count, int32_t k,
+                                  size_t* bytes) {
+  int st;
+  if ((st = check_varlen(vl))) return st;
+  if (bytes == nullptr) return fail(DSA_ERR_INVALID_ARGUMENT, "bytes pointer is NULL");
+  if (row_count < 0 || row_count > vl->total_q)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "row_count %lld outside [0, total_q]",
+                static_cast<long long>(row_count));
+  if (k < 1 || k > 2048) return fail(DSA_ERR_UNSUPPORTED, "k %d not in 1..2048", k);
+  *bytes = dsa::index_topk_workspace_bytes(*vl, row_count, k);
+  return ok();
+}
+
+int dsa_index_topk(const dsa_varlen* vl, const void* q_idx, const void* k_idx, const float* w,
+                   int32_t n_heads_idx, int32_t d_idx, int64_t row_begin, int64_t row_count,
+                   int32_t k, int32_t* indices, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+  int st;
+  if ((st = check_varlen(vl))) return st;
+  if ((st = check_window(vl, row_begin, row_count))) return st;
+  if ((st = check_bf16(q_idx, "q_idx"))) return st;
+  if ((st = check_bf16(k_idx, "k_idx"))) return st;
+  if (w == nullptr || !aligned(w, 4)) return fail(DSA_ERR_INVALID_ARGUMENT, "w is NULL or misaligned");
+  if (indices == nullptr || !aligned(indices, 4))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "indices is NULL or misaligned");
+  if ((st = check_index_shape(n_heads_idx, d_idx))) return st;
+  if ((st = check_index_extent(vl, d_idx, 2))) return st;
+  if (k < 1 || k > 2048) return fail(DSA_ERR_UNSUPPORTED, "k %d not in 1..2048", k);
+  if (checks_enabled() && (st = device_offsets(vl, stream))) return st;
+  if (row_count == 0) return ok();
+  const size_t need = dsa::index_topk_workspace_bytes(*vl, row_count, k);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
+    return fail(DSA_ERR_WORKSPACE, "index_topk workspace needs %zu bytes (256-byte aligned), got %zu",
+                need, workspace_bytes);
+  return hip_status(dsa::launch_index_topk(*vl, static_cast<const uint16_t*>(q_idx),
+                                           static_cast<const uint16_t*>(k_idx), w, n_heads_idx,
+                                           d_idx, row_begin, row_count, k, indices, workspace,
+                                           stream),
+                    "index_topk launch");
+}
+
 int dsa_sparse_attn_prefill(const dsa_varlen* vl, const void* q, const void* k, const void* v,
                             const int32_t* indices, int32_t topk, int64_t row_begin,
                             int64_t row_count, int32_t n_heads_q, int32_t n_heads_kv,

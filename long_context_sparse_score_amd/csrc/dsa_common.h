@@ -14,6 +14,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 // Native 16-byte vector (HIP's uint4 is a union-based struct that register
 // promotion of local arrays does not always see through).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 

@@ -13,6 +13,38 @@ hipError_t launch_index_scores(const dsa_varlen& vl, const uint16_t* q_idx, cons
                                const float* w, int n_heads, int d, int64_t row_begin,
                                int64_t row_count, float* scores, int64_t ld, hipStream_t stream);
 
+// Where one indexer launch sends its scores (rows are window-local).
+// Score mode writes rows of `scores`; key j of a row is position
+// j * key_stride (1 but for sampling every key_stride-th key).  Candidate
+// mode (key_stride 1) keeps only the scores >= tau[row] and appends them as
+// (score bits, position) to the row's list of `cap` entries, counting every
+// survivor in count[row] (a count above cap means entries were dropped; the
+// stream kernel adds to count, which must start at zero).
+struct IndexOut {
+  float* scores = nullptr;
+  int64_t ld = 0;
+  int32_t key_stride = 1;
+  const float* tau = nullptr;
+  uint32_t* count = nullptr;
+  uint2* cand = nullptr;
+  int32_t cap = 0;
+};
+hipError_t launch_index_scores_to(const dsa_varlen& vl, const uint16_t* q_idx,
+                                  const uint16_t* k_idx, const float* w, int n_heads, int d,
+                                  int64_t row_begin, int64_t row_count, const IndexOut& out,
+                                  bool candidates, hipStream_t stream);
+
+// Fused indexer -> top-k over a window (the indexer keeps only candidates
+// above a per-row threshold read off a sample of the row's scores; rows it
+// cannot settle exactly are recomputed unfused).  `workspace` as sized by
+// index_topk_workspace_bytes; it starts with the rows' candidate counts,
+// then (256-byte aligned) their fallback flags.
+size_t index_topk_workspace_bytes(const dsa_varlen& vl, int64_t row_count, int k);
+hipError_t launch_index_topk(const dsa_varlen& vl, const uint16_t* q_idx, const uint16_t* k_idx,
+                             const float* w, int n_heads, int d, int64_t row_begin,
+                             int64_t row_count, int k, int32_t* indices, void* workspace,
+                             hipStream_t stream);
+
 // Indexer scores from fp8 (e4m3) codes with one scale per query head and
 // per key.
 hipError_t launch_index_scores_fp8(const dsa_varlen& vl, const uint8_t* q8, const float* q_scale,

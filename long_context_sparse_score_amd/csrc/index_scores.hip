@@ -2,15 +2,9 @@
 //
 // I[t, s] = sum_h w[t, h] * max(0, qI[t, h, :] . kI[s, :])  for s = 0..p(t)
 // (Keye-VL-2.0 report summary, page 5 section 1: a lightweight scout scores
-// every position with one MQA key shared by all of its heads.)
-//
-// For one query row the head-by-key product is a small GEMM with M = indexer
-// heads (up to 64), N = keys, K = d_idx.  Heads sit on the MFMA rows so that
-// after v_mfma_f32_32x32x16_bf16 every lane holds one key column and 16 heads
-// of it: the ReLU, the weight and the head sum happen in registers, and one
-// exchange between the two half-waves finishes the sum.  The contraction over
-// d_idx is ordered so that each half-wave covers one contiguous half of every
-// qI / kI row, which keeps every load a full 16-byte vector.
+// every position with one MQA key shared by all of its heads).  The per-row
+// MFMA core (heads on the MFMA rows, ReLU / weight / head sum in registers)
+// is in index_core.h.
 //
 // Two kernels share that core:
 //  * index_scores_block (prefill): a 512-thread workgroup owns 8 consecutive
@@ -22,7 +16,7 @@
 //    the previous tile's epilogue, and scores leave through range-checked
 //    buffer stores, so a stage waits only for the next stage's DMA.
 //    A workgroup whose rows straddle a sequence boundary falls back to the
-//    per-wave path below.
+//    per-wave path of index_core.h.
 //  * index_scores_stream (decode / few rows): each wave streams its own key
 //    range of one row through a private LDS ring filled by coalesced
 //    buffer->LDS DMA, three 32-key tiles in flight; long rows are split into
@@ -30,130 +24,105 @@
 // Every global load is issued unconditionally (addresses are clamped into
 // the sequence instead): a load under a branch makes the compiler wait for
 // it on the spot, which would serialise the prefetch.
+//
+// Both kernels have a candidate mode for the fused indexer -> top-k: instead
+// of writing every score, the epilogue keeps the scores at or above the
+// row's threshold.  The two tiles of a pair finish their head sums together
+// (index_core.h), so each 64-key step ranks its survivors with one ballot and
+// writes them to the wave's LDS staging area with one LDS write per lane and
+// no branch.  The prefill kernel runs its rows whole (one key chunk), so a
+// wave owns its row's list: its staging ring is drained twice per stage from
+// inside the tile schedule, two range-checked stores per lane, the same
+// store count per stage as score mode, and no atomics.  The decode kernel
+// splits rows into chunks: each group of 8 tiles reserves room in the row's
+// list with one atomic whose result is used a group later.  In score mode
+// both kernels can also score only every key_stride-th key (the fused path's
+// sample).
 #include "dsa_common.h"
 #include "dsa_internal.h"
+#include "index_core.h"
 
 namespace dsa {
 
 namespace {
 
+using namespace core;
+
 constexpr int kBlockRows = 8;        // query rows (waves) per prefill workgroup
 constexpr int kStageKeys = 256;      // keys per LDS stage (2 stages: 128 KB at d_idx = 128)
 constexpr int kStreamRows = 4;       // waves per stream workgroup
-
-// Per-wave stationary state: this row's indexer queries (A operand, heads on
-// MFMA rows, MT tiles of 32 heads) and its head weights laid out like the
-// accumulator rows.
-template <int D, int MT>
-struct RowState {
-  static constexpr int KS = D / 16;
-  bf16x8 a[MT][KS];
-  float wv[MT][16];
+constexpr int kStreamGroup = 8;      // stream-kernel tiles per candidate reservation
+// One wave's candidate staging: N halves of HALF entries, each followed by
+// one dump slot per lane.  With two halves (stream kernel) the survivors of
+// the current tile group go to half `cur` while the other half waits for
+// its reservation.
+template <int HALF, int N>
+struct CandStage {
+  static constexpr int kSlots = HALF + kWave;
+  uint2 e[N][kSlots];
 };
 
-template <int D, int MT>
-__device__ __forceinline__ void load_row_state(RowState<D, MT>& st,
-                                               const uint16_t* __restrict__ q_idx,
-                                               const float* __restrict__ w, int64_t row,
-                                               int n_heads, int col, int half) {
-  constexpr int KS = D / 16, HALF = D / 2;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int h = mt * 32 + col;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      st.a[mt][ks] = h < n_heads ? load_bf16x8(q_idx + (row * n_heads + h) * D + half * HALF + ks * 8)
-                                 : zero_bf16x8();
-    // Accumulator element v of this lane is MFMA row 8*(v/4) + 4*half + v%4.
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int hr = mt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-      st.wv[mt][v] = hr < n_heads ? w[row * n_heads + hr] : 0.0f;
-    }
-  }
+// Appends the survivors among 64 consecutive keys (lane l: the score v of
+// key pos; a survivor has v >= tau and pos < end) to half `cur` of the
+// staging area: survivors rank by ballot, every other lane writes its own
+// dump slot -- one LDS write per lane, no branch.  The ballot itself is the
+// lane condition (inverse ballot), so the append is two compares, the rank
+// and one select.
+// RING: the half is a ring (slot = count mod HALF, HALF a power of two) that
+// the caller drains as it goes; otherwise slots count up from 0.
+template <bool RING = false, int HALF, int N>
+__device__ __forceinline__ void cand_append(CandStage<HALF, N>& cs, int cur, uint32_t& fill, float v,
+                                            int32_t pos, int32_t end, float tau, int lane) {
+  static_assert(!RING || (HALF & (HALF - 1)) == 0, "ring size");
+  const unsigned long long m =
+      __builtin_amdgcn_ballot_w64(pos < end) & __builtin_amdgcn_ballot_w64(v >= tau);
+  const bool ok = __builtin_amdgcn_inverse_ballot_w64(m);
+  const uint32_t rank = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+  const uint32_t at = RING ? (fill + rank) & (HALF - 1) : fill + rank;
+  cs.e[cur][ok ? at : HALF + static_cast<uint32_t>(lane)] =
+      make_uint2(__float_as_uint(v), static_cast<uint32_t>(pos));
+  fill += static_cast<uint32_t>(__popcll(m));
 }
 
-// Head products of one 32-key tile.
-template <int D, int MT>
-__device__ __forceinline__ void tile_mfma(const RowState<D, MT>& st, const bf16x8 (&b)[D / 16],
-                                          f32x16 (&acc)[MT]) {
-  constexpr int KS = D / 16;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    acc[mt] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(st.a[mt][ks], b[ks], acc[mt], 0, 0, 0);
-  }
+// Copies n staged entries of half h to the row's list at `base` (entries
+// past the list's capacity are dropped; the count records them).
+template <int HALF, int N>
+__device__ __forceinline__ void cand_copy(const CandStage<HALF, N>& cs, int h, uint32_t n,
+                                          uint32_t base, uint2* __restrict__ list, int cap,
+                                          int lane) {
+  for (uint32_t i = lane; i < n; i += kWave)
+    if (base + i < static_cast<uint32_t>(cap)) list[base + i] = cs.e[h][i];
 }
 
-// Sum over heads of w * relu(acc); every lane ends up with the score of key
-// (lane & 31).
-template <int D, int MT>
-__device__ __forceinline__ float tile_epilogue(const RowState<D, MT>& st,
-                                               const f32x16 (&acc)[MT]) {
-  float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-    for (int v = 0; v < 16; v += 2) {
-      s0 += st.wv[mt][v] * fmaxf(acc[mt][v], 0.0f);
-      s1 += st.wv[mt][v + 1] * fmaxf(acc[mt][v + 1], 0.0f);
-    }
-  }
-  const float s = s0 + s1;
-  // Add the other half-wave's partial sum.  v_permlane32_swap exchanges the
-  // halves in the VALU; a shuffle would go through the LDS pipeline, whose
-  // in-order counter would make this wait for the B-fragment reads just
-  // issued for the next tile.
-  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-}
-
-// One wave, one row, keys [c0, c1) read straight from global memory.  Two
-// register buffers alternate roles (the loop is unrolled by two tiles), so
-// the next tile's load is always in flight while one is multiplied.
-template <int D, int MT>
-__device__ void row_direct(const RowState<D, MT>& st, const uint16_t* __restrict__ k_idx,
-                           const RowInfo& ri, int32_t c0, int32_t c1,
-                           float* __restrict__ out_row, int col, int half) {
-  constexpr int KS = D / 16, HALF = D / 2;
-  const uint16_t* kbase = k_idx + ri.key_base * D + half * HALF;
-  auto fetch = [&](bf16x8 (&dst)[KS], int32_t t0) {
-    const int32_t key_ld = min(t0 + col, ri.pos);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) dst[ks] = load_bf16x8(kbase + static_cast<int64_t>(key_ld) * D + ks * 8);
-  };
-  bf16x8 x[KS], y[KS];
-  fetch(x, c0);
-  fetch(y, c0 + 32);
-  for (int32_t t0 = c0; t0 < c1; t0 += 64) {
-    f32x16 acc[MT];
-    tile_mfma<D, MT>(st, x, acc);
-    fetch(x, t0 + 64);
-    float s = tile_epilogue<D, MT>(st, acc);
-    if (half == 0 && t0 + col < c1) out_row[t0 + col] = s;
-    tile_mfma<D, MT>(st, y, acc);
-    fetch(y, t0 + 96);
-    s = tile_epilogue<D, MT>(st, acc);
-    if (half == 0 && t0 + 32 + col < c1) out_row[t0 + 32 + col] = s;
-  }
+// Reserves n entries of the row's list (returns the old count; lane 0 only).
+__device__ __forceinline__ uint32_t cand_reserve(uint32_t* count, uint32_t n, int lane) {
+  uint32_t base = 0;
+  if (lane == 0 && n != 0) base = atomicAdd(count, n);
+  return base;
 }
 
 // ---------------------------------------------------------------- prefill kernel
 
-template <int D, int MT>
+// SK keys per LDS stage; CAND selects the candidate mode (no score rows):
+// the 8 waves' staging areas (SK entries plus 64 dump slots each, 20 KB at
+// SK = 256) sit beside the key stages (148 KB at d_idx = 128).  Candidate mode runs with
+// one key chunk (gridDim.y == 1): each wave then owns its row's list and
+// counter, so no atomics are needed.
+template <int D, int MT, int SK, bool CAND>
 __global__ __launch_bounds__(kBlockRows * kWave, 2) void index_scores_block(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
     const uint16_t* __restrict__ q_idx, const uint16_t* k_idx,
     const float* __restrict__ w, int n_heads, int64_t row_begin, int64_t row_count,
-    float* __restrict__ scores, int64_t ld, int key_chunk) {
+    IndexOut o, int key_chunk) {
   constexpr int KS = D / 16;
   constexpr int CHUNKS = D / 8;                                     // 16-byte chunks per key row
-  constexpr int DMA_PER_WAVE = kStageKeys * CHUNKS / (kBlockRows * kWave);
-  constexpr int TILES = kStageKeys / 32;                            // 32-key MFMA tiles per stage
-  static_assert(TILES % 2 == 0 && DMA_PER_WAVE * kBlockRows * kWave == kStageKeys * CHUNKS, "stage shape");
-  __shared__ __attribute__((aligned(16))) uint16_t tile[2][kStageKeys * D];
+  constexpr int DMA_PER_WAVE = SK * CHUNKS / (kBlockRows * kWave);
+  constexpr int TILES = SK / 32;                                    // 32-key MFMA tiles per stage
+  static_assert(TILES % 2 == 0 && DMA_PER_WAVE * kBlockRows * kWave == SK * CHUNKS, "stage shape");
+  __shared__ __attribute__((aligned(16))) uint16_t tile[2][SK * D];
+  __shared__ CandStage<CAND ? SK : 1, 1> cstage[CAND ? kBlockRows : 1];
+  static_assert(!CAND || TILES * 32 <= SK, "a stage's survivors fit one half");
 
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
@@ -166,32 +135,64 @@ __global__ __launch_bounds__(kBlockRows * kWave, 2) void index_scores_block(
   const int64_t local = first + wave;
   const bool active = local < row_count;
   const int64_t row = row_begin + (active ? local : last);
+  const int stride = o.key_stride;
 
   const RowInfo ri = row_info(cu_q, cu_k, batch, row);
   const RowInfo r_first = row_info(cu_q, cu_k, batch, row_begin + first);
   const RowInfo r_last = row_info(cu_q, cu_k, batch, row_begin + last);
   const int32_t c0 = blockIdx.y * key_chunk;
+  const int32_t nv = visible_keys(ri.pos, stride);
 
   RowState<D, MT> st;
   load_row_state<D, MT>(st, q_idx, w, row, n_heads, col, half);
-  float* out_row = scores + local * ld;
+  float* out_row = CAND ? nullptr : o.scores + local * o.ld;
+  const float tau = CAND && active ? o.tau[local] : 0.0f;
+  uint2* list = CAND ? o.cand + local * o.cap : nullptr;
+  uint32_t* counter = CAND ? o.count + local : nullptr;
 
   if (r_first.key_base != r_last.key_base) {
     // Rows of several sequences: every wave walks its own keys.
-    const int32_t c1 = min(c0 + key_chunk, ri.pos + 1);
-    if (active && c0 < c1) row_direct<D, MT>(st, k_idx, ri, c0, c1, out_row, col, half);
+    const int32_t c1 = min(c0 + key_chunk, nv);
+    if (!active || c0 >= c1) return;
+    if constexpr (CAND) {
+      // One staging half, copied to the row's list whenever a further 64
+      // survivors might not fit.
+      CandStage<SK, 1>& cs = cstage[wave];
+      uint32_t fill = 0, written = 0;
+      auto flush = [&]() {
+        cand_copy(cs, 0, fill, written, list, o.cap, lane);
+        written += fill;
+        fill = 0;
+      };
+      row_direct<D, MT>(st, k_idx, ri, stride, c0, c1, col, half,
+                        [&](float v, int32_t pos) {
+                          cand_append(cs, 0, fill, v, pos, c1, tau, lane);
+                        },
+                        [&]() {
+                          if (fill > static_cast<uint32_t>(SK - 64)) flush();
+                        });
+      flush();
+      if (lane == 0) *counter = written;
+    } else {
+      row_direct<D, MT>(st, k_idx, ri, stride, c0, c1, col, half,
+                        [&](float v, int32_t pos) {
+                          if (pos < c1) out_row[pos] = v;
+                        },
+                        []() {});
+    }
     return;
   }
 
   // All rows share one sequence; positions grow with the row.
-  const int32_t c_end = min(c0 + key_chunk, r_last.pos + 1);
+  const int32_t c_end = min(c0 + key_chunk, visible_keys(r_last.pos, stride));
   if (c0 >= c_end) return;
   // Scores of keys my_end and beyond (and every score of an inactive wave)
-  // fall outside the store resource and are dropped.
-  const int32_t my_end = active ? min(c0 + key_chunk, ri.pos + 1) : c0;
+  // fall outside the store resource and are dropped (candidate mode: fail
+  // the admission test).
+  const int32_t my_end = active ? min(c0 + key_chunk, nv) : c0;
   const uint16_t* kseq = k_idx + r_first.key_base * D;
   const __amdgpu_buffer_rsrc_t keys = raw_buffer(kseq, (r_last.pos + 1) * D * 2);
-  const __amdgpu_buffer_rsrc_t outs = raw_buffer(out_row, my_end * 4);
+  const __amdgpu_buffer_rsrc_t outs = raw_buffer(out_row, CAND ? 0 : my_end * 4);
 
   // Stage fill by buffer->LDS DMA: DMA instruction i of a wave writes 64
   // consecutive 16-byte LDS chunks; LDS chunk (key, s) receives global chunk
@@ -202,33 +203,63 @@ __global__ __launch_bounds__(kBlockRows * kWave, 2) void index_scores_block(
   constexpr int KPI = kBlockRows * kWave / CHUNKS;  // keys per DMA instruction of the workgroup
   static_assert(KPI % CHUNKS == 0, "the swizzle must repeat across DMA instructions");
   const int key0 = (wave * kWave + lane) / CHUNKS, s0 = lane % CHUNKS;
-  const int dma_off = key0 * D * 2 + (s0 ^ (key0 & (CHUNKS - 1))) * 16;
+  const int key_bytes = stride * D * 2;  // distance between consecutive keys of this launch
+  const int dma_off = key0 * key_bytes + (s0 ^ (key0 & (CHUNKS - 1))) * 16;
   auto fill_stage = [&](int b, int32_t t) {
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           keys, (__attribute__((address_space(3))) void*)(&tile[b][(i * kBlockRows + wave) * kWave * 8]),
-          16, dma_off, (t + i * KPI) * D * 2, 0, 0);
+          16, dma_off, (t + i * KPI) * key_bytes, 0, 0);
     }
   };
-  // One score per lane of the lower half-wave (the upper half holds copies).
-  auto store = [&](float v, int32_t pos) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), outs, half == 0 ? pos * 4 : 0x7FFFFFF0, 0, 0);
+  // Candidate staging of this wave: a ring of SK entries (candidate mode
+  // launches one key chunk, so the wave owns its row's list).  `fill`
+  // survivors have been appended and `written` of them copied to the list;
+  // the tile loop drains the ring twice per stage (after tiles 1 and 5,
+  // when at most 128 entries wait and at most 128 more can arrive before
+  // the next drain), each drain two range-checked 8-byte stores per lane.
+  CandStage<CAND ? SK : 1, 1>& cs = cstage[CAND ? wave : 0];
+  uint32_t fill = 0, written = 0;
+  const __amdgpu_buffer_rsrc_t lrs = raw_buffer(list, CAND ? o.cap * 8 : 0);
+  auto drain = [&]() {
+    if constexpr (CAND) {
+      const uint32_t n = fill - written;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const uint32_t i = static_cast<uint32_t>(lane + kWave * r);
+        const uint2 e = cs.e[0][(written + i) & (SK - 1)];
+        const u32x2 ev = {e.x, e.y};
+        __builtin_amdgcn_raw_buffer_store_b64(ev, lrs, i < n ? (written + i) * 8 : 0x7FFFFFF0u, 0, 0);
+      }
+      written = fill;
+    }
   };
-
+  // The scores of 64 consecutive keys, key pos at this lane.
+  auto emit = [&](float v, int32_t pos) {
+    if constexpr (CAND) {
+      cand_append<true>(cs, 0, fill, v, pos, my_end, tau, lane);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), outs, pos * 4, 0, 0);
+    }
+  };
   fill_stage(0, c0);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   lds_barrier();
   // Tile j's MFMAs run while tile j-1's epilogue executes on the VALU; each
   // B fragment register is refilled from LDS for tile j+1 as soon as tile
-  // j's MFMAs have consumed it.
+  // j's MFMAs have consumed it.  Tiles pair up (0, 1), (2, 3), ...: the
+  // partial head sums of a pair's first tile are held until its second
+  // tile's are ready, and one swap finishes both tiles' 64 scores.
   f32x16 acc_even[MT], acc_odd[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc_odd[mt] = f32x16{};
-  int32_t prev_pos = 1 << 28;  // the first epilogue has nothing to store
+  int32_t prev_pos = 1 << 28;  // key 0 of the previous tile (the first has none)
+  int32_t pair_pos = 1 << 28;  // key 0 of the pending pair (the first emit is dropped)
+  float held = 0.0f;           // partials of the pending pair's first tile
   int buf = 0;
-  for (int32_t t0 = c0; t0 < c_end; t0 += kStageKeys) {
-    if (t0 + kStageKeys < c_end) fill_stage(buf ^ 1, t0 + kStageKeys);
+  for (int32_t t0 = c0; t0 < c_end; t0 += SK) {
+    if (t0 + SK < c_end) fill_stage(buf ^ 1, t0 + SK);
     const uint16_t* tb = tile[buf];
     bf16x8 b[KS];
 #pragma unroll
@@ -253,8 +284,15 @@ __global__ __launch_bounds__(kBlockRows * kWave, 2) void index_scores_block(
           b[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&tb[((tj + 1) * 32 + col) * D + slot * 8]));
         }
       }
-      store(tile_epilogue<D, MT>(st, prev), prev_pos);
-      prev_pos = t0 + tj * 32 + col;
+      const float part = tile_partial<D, MT>(st, prev);
+      if (tj & 1) {  // tile tj - 1 opens a pair
+        held = part;
+        pair_pos = prev_pos;
+      } else {       // tile tj - 1 closes one
+        emit(pair_scores(held, part), pair_pos + lane);
+      }
+      if (tj == 1 || tj == 5) drain();
+      prev_pos = t0 + tj * 32;
       // Interleave this tile's MFMAs with the previous tile's epilogue (4 VALU
       // after each MFMA) and refill each B fragment right after the MFMA pair
       // that frees it, a full tile before its next use.  Left alone, the
@@ -268,13 +306,25 @@ __global__ __launch_bounds__(kBlockRows * kWave, 2) void index_scores_block(
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
       }
     }
-    // Wait for the next stage's DMA only: the TILES score stores issued after
-    // it may stay in flight.
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(TILES));
+    // Wait for the next stage's DMA only: the stage's TILES / 2 score
+    // stores (candidate mode: its two drains' four stores) issued after it
+    // may stay in flight.
+    static_assert(TILES == 8, "two drains of two stores per stage match TILES / 2 stores");
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(TILES / 2));
     lds_barrier();
     buf ^= 1;
   }
-  store(tile_epilogue<D, MT>(st, acc_odd), prev_pos);
+  // The last stage's last tile (odd) closes the last pair.
+  emit(pair_scores(held, tile_partial<D, MT>(st, acc_odd)), pair_pos + lane);
+  if constexpr (CAND) {
+    // What is left in the ring: at most 192 entries.
+    for (uint32_t i = lane; written + i < fill; i += kWave) {
+      const uint2 e = cs.e[0][(written + i) & (SK - 1)];
+      const u32x2 ev = {e.x, e.y};
+      __builtin_amdgcn_raw_buffer_store_b64(ev, lrs, (written + i) * 8, 0, 0);
+    }
+    if (active && lane == 0) *counter = fill;  // above cap: entries were dropped
+  }
 }
 
 // ---------------------------------------------------------------- decode kernel
@@ -289,17 +339,21 @@ __global__ __launch_bounds__(kBlockRows * kWave, 2) void index_scores_block(
 // ring is private to the wave, so no workgroup barrier is needed.
 constexpr int kRing = 4;
 
-template <int D, int MT>
+template <int D, int MT, bool CAND>
 __global__ __launch_bounds__(kStreamRows * kWave) void index_scores_stream(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
     const float* __restrict__ w, int n_heads, int64_t row_begin, int64_t row_count,
-    float* __restrict__ scores, int64_t ld, int key_chunk, int chunks_per_row) {
+    IndexOut o, int key_chunk, int chunks_per_row) {
   constexpr int KS = D / 16;
   constexpr int CHUNKS = D / 8;
   constexpr int DMA_PER_TILE = 32 * CHUNKS / kWave;   // 16-byte DMA instructions per tile
+  constexpr int GROUP_KEYS = kStreamGroup * 32;       // keys per candidate reservation
   static_assert(DMA_PER_TILE * kWave == 32 * CHUNKS, "tile shape");
   __shared__ __attribute__((aligned(16))) uint16_t ring[kStreamRows][kRing][32 * D];
+  __shared__ CandStage<CAND ? GROUP_KEYS : 1, 2> cstage[CAND ? kStreamRows : 1];
+  static_assert(kStreamGroup % 2 == 0, "groups of whole tile pairs");
+  static_assert(!CAND || kStreamGroup * 32 <= GROUP_KEYS, "a group's survivors fit one half");
 
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
@@ -309,17 +363,22 @@ __global__ __launch_bounds__(kStreamRows * kWave) void index_scores_stream(
   const int64_t local = item / chunks_per_row;
   if (local >= row_count) return;
   const int64_t row = row_begin + local;
+  const int stride = o.key_stride;
   const RowInfo ri = row_info(cu_q, cu_k, batch, row);
   const int32_t c0 = static_cast<int32_t>(item % chunks_per_row) * key_chunk;
-  const int32_t c1 = min(c0 + key_chunk, ri.pos + 1);
+  const int32_t c1 = min(c0 + key_chunk, visible_keys(ri.pos, stride));
   if (c0 >= c1) return;
+  const float tau = CAND ? o.tau[local] : 0.0f;
   RowState<D, MT> st;
   load_row_state<D, MT>(st, q_idx, w, row, n_heads, col, half);
 
   // Keys [c0, c1) only (DMA past c1 reads zeros without touching memory);
-  // scores past c1 are dropped.
-  const __amdgpu_buffer_rsrc_t keys = raw_buffer(k_idx + (ri.key_base + c0) * D, (c1 - c0) * D * 2);
-  const __amdgpu_buffer_rsrc_t outs = raw_buffer(scores + local * ld, c1 * 4);
+  // scores past c1 are dropped.  Key j of this launch is position j * stride.
+  const int key_bytes = stride * D * 2;
+  const __amdgpu_buffer_rsrc_t keys =
+      raw_buffer(k_idx + (ri.key_base + static_cast<int64_t>(c0) * stride) * D,
+                 ((c1 - c0 - 1) * stride + 1) * D * 2);
+  const __amdgpu_buffer_rsrc_t outs = raw_buffer(CAND ? nullptr : o.scores + local * o.ld, CAND ? 0 : c1 * 4);
   auto fill = [&](int slot, int32_t t) {  // tile of keys c0 + t .. c0 + t + 31
 #pragma unroll
     for (int i = 0; i < DMA_PER_TILE; ++i) {
@@ -327,31 +386,61 @@ __global__ __launch_bounds__(kStreamRows * kWave) void index_scores_stream(
       const int key = e / CHUNKS, s = e % CHUNKS;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           keys, (__attribute__((address_space(3))) void*)(&ring[wave][slot][i * kWave * 8]), 16,
-          (key * D + (s ^ (key & (CHUNKS - 1))) * 8) * 2, t * D * 2, 0, 0);
+          key * key_bytes + (s ^ (key & (CHUNKS - 1))) * 16, t * key_bytes, 0, 0);
     }
   };
-  auto store = [&](float v, int32_t pos) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), outs, half == 0 ? pos * 4 : 0x7FFFFFF0, 0, 0);
+  // Candidate staging (see the prefill kernel): groups of kStreamGroup tiles.
+  CandStage<CAND ? GROUP_KEYS : 1, 2>& cs = cstage[CAND ? wave : 0];
+  uint2* list = CAND ? o.cand + local * o.cap : nullptr;
+  uint32_t* counter = CAND ? o.count + local : nullptr;
+  int cur = 0;
+  uint32_t cfill = 0, pend = 0, pend_base = 0;
+  // The scores of 64 consecutive keys, key pos at this lane.
+  auto emit = [&](float v, int32_t pos) {
+    if constexpr (CAND) {
+      cand_append(cs, cur, cfill, v, pos, c1, tau, lane);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), outs, pos * 4, 0, 0);
+    }
   };
+  auto group_end = [&]() {
+    if constexpr (CAND) {
+      if (pend != 0u)
+        cand_copy(cs, cur ^ 1, pend, __builtin_amdgcn_readfirstlane(pend_base), list, o.cap, lane);
+      pend_base = cand_reserve(counter, cfill, lane);
+      pend = cfill;
+      cfill = 0;
+      cur ^= 1;
+    }
+  };
+  // Vector-memory operations that trail each tile's DMA: one store (score
+  // mode: the closing tile of a pair stores the pair's 64 scores, the
+  // opening tile a dropped store) or none (candidate mode; its reservations
+  // and copies only add operations, which makes the waits below stricter,
+  // never weaker).
+  constexpr int TRAIL = CAND ? 0 : 1;
 
-  // Prologue: tiles 0 .. kRing-2, each followed by a dropped store so that
-  // every tile's DMA is trailed by the same count of memory operations as in
-  // the loop (one store, then the next tile's DMA).
+  // Prologue: tiles 0 .. kRing-2, each followed by a dropped store (score
+  // mode) so that every tile's DMA is trailed by the same count of memory
+  // operations as in the loop.
 #pragma unroll
   for (int p = 0; p < kRing - 1; ++p) {
     fill(p, p * 32);
-    store(0.0f, 1 << 28);
+    if constexpr (!CAND) __builtin_amdgcn_raw_buffer_store_b32(0, outs, 0x7FFFFFF0, 0, 0);
   }
   f32x16 acc[MT], prev[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) prev[mt] = f32x16{};
-  int32_t prev_pos = 1 << 28;
+  // Tiles pair up (0, 1), (2, 3), ... as in the prefill kernel.
+  int32_t prev_pos = 1 << 28;  // key 0 of the previous tile (the first has none)
+  int32_t pair_pos = 1 << 28;  // key 0 of the pending pair (the first emit is dropped)
+  float held = 0.0f;
   const int ntiles = (c1 - c0 + 31) / 32;
   for (int j = 0; j < ntiles; ++j) {
     fill((j + kRing - 1) % kRing, (j + kRing - 1) * 32);
     // Tile j has landed once at most the kRing - 1 younger tiles' DMAs and
     // their trailing stores are outstanding.
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kRing - 1) * (DMA_PER_TILE + 1)));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kRing - 1) * (DMA_PER_TILE + TRAIL)));
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const uint16_t* tb = ring[wave][j % kRing];
     bf16x8 b[KS];
@@ -361,74 +450,118 @@ __global__ __launch_bounds__(kStreamRows * kWave) void index_scores_stream(
       b[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&tb[col * D + slot * 8]));
     }
     tile_mfma<D, MT>(st, b, acc);
-    store(tile_epilogue<D, MT>(st, prev), prev_pos);
-    prev_pos = c0 + j * 32 + col;
+    const float part = tile_partial<D, MT>(st, prev);
+    if (j & 1) {  // tile j - 1 opens a pair
+      held = part;
+      pair_pos = prev_pos;
+      if constexpr (!CAND) __builtin_amdgcn_raw_buffer_store_b32(0, outs, 0x7FFFFFF0, 0, 0);
+    } else {      // tile j - 1 closes one
+      emit(pair_scores(held, part), pair_pos + lane);
+      // A group's worth of tiles emitted (the epilogue lags one tile).
+      if (CAND && j % kStreamGroup == 0 && j > 0) group_end();
+    }
+    prev_pos = c0 + j * 32;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) prev[mt] = acc[mt];
     // The slot refilled next iteration was read above: those reads must be
     // done before its DMA is issued.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   }
-  store(tile_epilogue<D, MT>(st, prev), prev_pos);
+  // The last tile closes a pair (ntiles even) or opens one (ntiles odd,
+  // closed by an empty tile past c1).
+  {
+    const float part = tile_partial<D, MT>(st, prev);
+    if (ntiles & 1) {
+      emit(pair_scores(part, 0.0f), prev_pos + lane);
+    } else {
+      emit(pair_scores(held, part), pair_pos + lane);
+    }
+  }
+  if constexpr (CAND) {
+    group_end();
+    if (pend != 0u)
+      cand_copy(cs, cur ^ 1, pend, __builtin_amdgcn_readfirstlane(pend_base), list, o.cap, lane);
+  }
   // No DMA may still be writing this wave's ring when the wave ends.
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
-template <int D, int MT>
+template <int D, int MT, bool CAND>
 hipError_t launch_dm(const dsa_varlen& vl, const uint16_t* q_idx, const uint16_t* k_idx,
                      const float* w, int n_heads, int64_t row_begin, int64_t row_count,
-                     float* scores, int64_t ld, hipStream_t stream) {
+                     const IndexOut& o, hipStream_t stream) {
+  // Keys of the longest row in this launch's units.
+  const int64_t max_keys = (vl.max_seqlen_k - 1) / o.key_stride + 1;
   if (vl.max_seqlen_q >= kBlockRows) {
     // Prefill-like: whole rows per workgroup unless there are too few
     // workgroups to fill the chip, then split the keys.
+    constexpr int SK = kStageKeys;
     const int64_t blocks = (row_count + kBlockRows - 1) / kBlockRows;
-    int64_t chunk = vl.max_seqlen_k;
-    if (blocks < 1024) {
+    int64_t chunk = max_keys;
+    // Candidate mode runs one chunk (a wave owns its row); so does a sampled
+    // pass (key_stride > 1), whose rows are short.
+    if (blocks < 1024 && !CAND && o.key_stride == 1) {
       const int64_t parts = (1024 + blocks - 1) / blocks;
-      chunk = (vl.max_seqlen_k + parts - 1) / parts;
+      chunk = (max_keys + parts - 1) / parts;
     }
-    chunk = ((chunk + kStageKeys - 1) / kStageKeys) * kStageKeys;
-    if (chunk < 512) chunk = 512;
-    const int64_t chunks = (vl.max_seqlen_k + chunk - 1) / chunk;
-    hipLaunchKernelGGL((index_scores_block<D, MT>), dim3(static_cast<unsigned>(blocks),
+    chunk = ((chunk + SK - 1) / SK) * SK;
+    if (chunk < 2 * SK) chunk = 2 * SK;
+    const int64_t chunks = (max_keys + chunk - 1) / chunk;
+    hipLaunchKernelGGL((index_scores_block<D, MT, SK, CAND>), dim3(static_cast<unsigned>(blocks),
                        static_cast<unsigned>(chunks)), dim3(kBlockRows * kWave), 0, stream,
                        vl.cu_seqlens_q, vl.cu_seqlens_k, vl.batch, q_idx, k_idx, w, n_heads,
-                       row_begin, row_count, scores, ld, static_cast<int>(chunk));
+                       row_begin, row_count, o, static_cast<int>(chunk));
   } else {
     // Decode-like: one wave per (row, key chunk), about 2048 work items (two
     // rounds of one 4-wave workgroup per CU; measured best among 2048-8192).
     const int64_t per_row = (2048 + row_count - 1) / row_count;
-    int64_t chunk = (vl.max_seqlen_k + per_row - 1) / per_row;
+    int64_t chunk = (max_keys + per_row - 1) / per_row;
     chunk = ((chunk + 31) / 32) * 32;
     if (chunk < 512) chunk = 512;
-    const int64_t chunks_per_row = (vl.max_seqlen_k + chunk - 1) / chunk;
+    const int64_t chunks_per_row = (max_keys + chunk - 1) / chunk;
     const int64_t items = row_count * chunks_per_row;
-    hipLaunchKernelGGL((index_scores_stream<D, MT>),
+    hipLaunchKernelGGL((index_scores_stream<D, MT, CAND>),
                        dim3(static_cast<unsigned>((items + kStreamRows - 1) / kStreamRows)),
                        dim3(kStreamRows * kWave), 0, stream, vl.cu_seqlens_q, vl.cu_seqlens_k,
-                       vl.batch, q_idx, k_idx, w, n_heads, row_begin, row_count, scores, ld,
+                       vl.batch, q_idx, k_idx, w, n_heads, row_begin, row_count, o,
                        static_cast<int>(chunk), static_cast<int>(chunks_per_row));
   }
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool CAND>
 hipError_t launch_d(const dsa_varlen& vl, const uint16_t* q_idx, const uint16_t* k_idx,
                     const float* w, int n_heads, int64_t row_begin, int64_t row_count,
-                    float* scores, int64_t ld, hipStream_t stream) {
+                    const IndexOut& o, hipStream_t stream) {
   if (n_heads > 32)
-    return launch_dm<D, 2>(vl, q_idx, k_idx, w, n_heads, row_begin, row_count, scores, ld, stream);
-  return launch_dm<D, 1>(vl, q_idx, k_idx, w, n_heads, row_begin, row_count, scores, ld, stream);
+    return launch_dm<D, 2, CAND>(vl, q_idx, k_idx, w, n_heads, row_begin, row_count, o, stream);
+  return launch_dm<D, 1, CAND>(vl, q_idx, k_idx, w, n_heads, row_begin, row_count, o, stream);
 }
 
 }  // namespace
 
+hipError_t launch_index_scores_to(const dsa_varlen& vl, const uint16_t* q_idx,
+                                  const uint16_t* k_idx, const float* w, int n_heads, int d,
+                                  int64_t row_begin, int64_t row_count, const IndexOut& out,
+                                  bool candidates, hipStream_t stream) {
+  if (candidates) {
+    if (d == 128)
+      return launch_d<128, true>(vl, q_idx, k_idx, w, n_heads, row_begin, row_count, out, stream);
+    return launch_d<64, true>(vl, q_idx, k_idx, w, n_heads, row_begin, row_count, out, stream);
+  }
+  if (d == 128)
+    return launch_d<128, false>(vl, q_idx, k_idx, w, n_heads, row_begin, row_count, out, stream);
+  return launch_d<64, false>(vl, q_idx, k_idx, w, n_heads, row_begin, row_count, out, stream);
+}
+
 hipError_t launch_index_scores(const dsa_varlen& vl, const uint16_t* q_idx, const uint16_t* k_idx,
                                const float* w, int n_heads, int d, int64_t row_begin,
                                int64_t row_count, float* scores, int64_t ld, hipStream_t stream) {
-  if (d == 128)
-    return launch_d<128>(vl, q_idx, k_idx, w, n_heads, row_begin, row_count, scores, ld, stream);
-  return launch_d<64>(vl, q_idx, k_idx, w, n_heads, row_begin, row_count, scores, ld, stream);
+  IndexOut o;
+  o.scores = scores;
+  o.ld = ld;
+  return launch_index_scores_to(vl, q_idx, k_idx, w, n_heads, d, row_begin, row_count, o, false,
+                                stream);
 }
 
 }  // namespace dsa

@@ -12,7 +12,8 @@ from __future__ import annotations
 
 from dataclasses import dataclass
 
-from . import (Varlen, dsa_index_scores, dsa_index_scores_fp8, dsa_quantize_fp8,
+from . import (Varlen, dsa_index_scores, dsa_index_scores_fp8, dsa_index_topk,
+               dsa_index_topk_workspace_size, dsa_quantize_fp8,
                dsa_sparse_attn_decode, dsa_sparse_attn_decode_workspace_size,
                dsa_sparse_attn_prefill, dsa_sparse_attn_prefill_grouped,
                dsa_sparse_attn_prefill_grouped_workspace_size, dsa_topk,
@@ -31,6 +32,7 @@ class PrefillConfig:
     times by default; the full-size parity tests run the same object."""
     window: int = 2048      # query rows per score window (fp32 scores of one window in HBM)
     attn_rows: int = 1024   # rows per attention launch inside a window
+    fused: bool = False     # dsa_index_topk instead of dsa_index_scores -> dsa_topk
 
 
 BENCH_PREFILL = PrefillConfig()
@@ -80,18 +82,21 @@ def _scores(vl, q_idx, k_idx, w, scores, fp8, row_begin, row_count, stream):
 
 @dataclass
 class PrefillBuffers:
-    scores: object       # fp32 [window, ld]
+    scores: object       # fp32 [window, ld] (None when fused)
     indices: object      # int32 [window, topk]
     spare: object = None  # a second int32 [window, topk] for the two-stream schedule
     grouped: object = None  # uint8 workspace of the grouped attention (one per index buffer)
     grouped_spare: object = None
+    fused: object = None  # uint8 workspace of dsa_index_topk (fused indexer -> top-k)
+    window: int = 0
 
 
 def alloc_prefill(vl: Varlen, topk: int, window: int, device="cuda", overlap: bool = False,
-                  grouped: bool = False) -> PrefillBuffers:
+                  grouped: bool = False, fused: bool = False) -> PrefillBuffers:
     """Buffers of a windowed prefill; `overlap` adds the second index buffer the
     two-stream schedule alternates with; `grouped` selects the grouped attention
-    (16 adjacent rows per union of index sets) and adds its workspace."""
+    (16 adjacent rows per union of index sets) and adds its workspace; `fused`
+    selects dsa_index_topk (no score rows; its workspace instead)."""
     torch = _torch()
     window = max(1, min(window, vl.total_q))
     ld = score_ld(vl.max_seqlen_k)
@@ -99,9 +104,11 @@ def alloc_prefill(vl: Varlen, topk: int, window: int, device="cuda", overlap: bo
     gws = lambda: torch.empty(  # noqa: E731
         max(256, dsa_sparse_attn_prefill_grouped_workspace_size(vl, window, topk)),
         dtype=torch.uint8, device=device)
-    return PrefillBuffers(torch.empty((window, ld), dtype=torch.float32, device=device), idx(),
-                          idx() if overlap else None, gws() if grouped else None,
-                          gws() if grouped and overlap else None)
+    scores = None if fused else torch.empty((window, ld), dtype=torch.float32, device=device)
+    fws = (torch.empty(dsa_index_topk_workspace_size(vl, window, topk), dtype=torch.uint8,
+                       device=device) if fused else None)
+    return PrefillBuffers(scores, idx(), idx() if overlap else None, gws() if grouped else None,
+                          gws() if grouped and overlap else None, fws, window)
 
 
 def prefill(vl: Varlen, q_idx, k_idx, w, q, k, v, out, bufs: PrefillBuffers, lse=None,
@@ -133,7 +140,9 @@ def prefill(vl: Varlen, q_idx, k_idx, w, q, k, v, out, bufs: PrefillBuffers, lse
     ibufs = [bufs.indices, bufs.spare] if two else [bufs.indices]
     gbufs = [bufs.grouped, bufs.grouped_spare] if two else [bufs.grouped]
     released = [None, None]  # per index buffer: attention done reading it
-    window = bufs.scores.shape[0]
+    window = bufs.window
+    if fp8 is not None and bufs.fused is not None:
+        raise ValueError("the fused indexer -> top-k takes bf16 indexer inputs")
     if fp8 is not None:
         quantize_queries(q_idx, fp8, stream=main)
         quantize_keys(k_idx, fp8, stream=main)
@@ -148,14 +157,25 @@ def prefill(vl: Varlen, q_idx, k_idx, w, q, k, v, out, bufs: PrefillBuffers, lse
     for i, r0 in enumerate(range(0, vl.total_q, window)):
         n = min(window, vl.total_q - r0)
         ib = ibufs[i % len(ibufs)]
-        e0 = mark(main)
-        _scores(vl, q_idx, k_idx, w, bufs.scores, fp8, r0, n, main)
-        e1 = mark(main)
-        if two and released[i % 2] is not None:
-            main.wait_event(released[i % 2])
-        t0 = mark(main)
-        dsa_topk(vl, bufs.scores, ib, row_begin=r0, row_count=n, stream=main)
-        t1 = mark(main)
+        if bufs.fused is not None:
+            # Fused: one call selects the window's indices (no score rows); its
+            # time is reported as the indexer's and the top-k pair is empty.
+            if two and released[i % 2] is not None:
+                main.wait_event(released[i % 2])
+            e0 = mark(main)
+            dsa_index_topk(vl, q_idx, k_idx, w, ib[:n], bufs.fused, row_begin=r0, row_count=n,
+                           stream=main)
+            e1 = mark(main)
+            t0 = t1 = e1
+        else:
+            e0 = mark(main)
+            _scores(vl, q_idx, k_idx, w, bufs.scores, fp8, r0, n, main)
+            e1 = mark(main)
+            if two and released[i % 2] is not None:
+                main.wait_event(released[i % 2])
+            t0 = mark(main)
+            dsa_topk(vl, bufs.scores, ib, row_begin=r0, row_count=n, stream=main)
+            t1 = mark(main)
         if two:
             ready = torch.cuda.Event()
             ready.record(main)
@@ -190,16 +210,18 @@ def prefill(vl: Varlen, q_idx, k_idx, w, q, k, v, out, bufs: PrefillBuffers, lse
 
 @dataclass
 class DecodeBuffers:
-    scores: object          # fp32 [batch, ld]
+    scores: object          # fp32 [batch, ld] (None when fused)
     indices: object         # int32 [batch, topk]
     groups: list            # (row_begin, row_count) of each row group
     workspaces: list        # per group: uint8 [bytes], decode attention partials
     topk_workspace: object  # uint8 [bytes] or None (the top-k needs none today)
+    fused: list = None      # per group: uint8 workspace of dsa_index_topk
 
 
 def alloc_decode(vl: Varlen, n_heads_q: int, head_dim: int, topk: int, groups: int = 1,
-                 device="cuda") -> DecodeBuffers:
-    """Buffers of a decode step whose batch runs as `groups` contiguous row groups."""
+                 device="cuda", fused: bool = False) -> DecodeBuffers:
+    """Buffers of a decode step whose batch runs as `groups` contiguous row
+    groups; `fused` selects dsa_index_topk for the indexer and top-k."""
     torch = _torch()
     ld = score_ld(vl.max_seqlen_k)
     groups = max(1, min(groups, vl.batch))
@@ -210,10 +232,13 @@ def alloc_decode(vl: Varlen, n_heads_q: int, head_dim: int, topk: int, groups: i
         ws = dsa_sparse_attn_decode_workspace_size(vl, n_heads_q, head_dim, topk, row_count=n)
         wss.append(torch.empty(max(ws, 256), dtype=torch.uint8, device=device))
     tws = dsa_topk_workspace_size(vl, vl.batch, topk)
-    return DecodeBuffers(torch.empty((vl.batch, ld), dtype=torch.float32, device=device),
+    fws = ([torch.empty(dsa_index_topk_workspace_size(vl, n, topk), dtype=torch.uint8,
+                        device=device) for _, n in spans] if fused else None)
+    return DecodeBuffers(None if fused else torch.empty((vl.batch, ld), dtype=torch.float32,
+                                                        device=device),
                          torch.empty((vl.batch, topk), dtype=torch.int32, device=device),
                          spans, wss,
-                         torch.empty(tws, dtype=torch.uint8, device=device) if tws else None)
+                         torch.empty(tws, dtype=torch.uint8, device=device) if tws else None, fws)
 
 
 def decode(vl: Varlen, q_idx, k_idx_cache, w, q, k_cache, v_cache, out, bufs: DecodeBuffers,
@@ -239,16 +264,23 @@ def decode(vl: Varlen, q_idx, k_idx_cache, w, q, k_cache, v_cache, out, bufs: De
     if len(streams) > 1:
         side_stream.wait_stream(main)  # inputs written on the main stream
     prev_idx = None
+    if fp8 is not None and bufs.fused is not None:
+        raise ValueError("the fused indexer -> top-k takes bf16 indexer inputs")
     for i, (r0, n) in enumerate(bufs.groups):
         st = streams[i % len(streams)]
         if prev_idx is not None and len(streams) > 1:
             st.wait_event(prev_idx)
-        _scores(vl, q_idx, k_idx_cache, w, bufs.scores[r0:r0 + n], fp8, r0, n, st)
+        if bufs.fused is not None:
+            dsa_index_topk(vl, q_idx, k_idx_cache, w, bufs.indices[r0:r0 + n], bufs.fused[i],
+                           row_begin=r0, row_count=n, stream=st)
+        else:
+            _scores(vl, q_idx, k_idx_cache, w, bufs.scores[r0:r0 + n], fp8, r0, n, st)
         if len(streams) > 1:
             prev_idx = torch.cuda.Event()
             prev_idx.record(st)
-        dsa_topk(vl, bufs.scores[r0:r0 + n], bufs.indices[r0:r0 + n], row_begin=r0, row_count=n,
-                 workspace=bufs.topk_workspace, stream=st)
+        if bufs.fused is None:
+            dsa_topk(vl, bufs.scores[r0:r0 + n], bufs.indices[r0:r0 + n], row_begin=r0,
+                     row_count=n, workspace=bufs.topk_workspace, stream=st)
         dsa_sparse_attn_decode(vl, q, k_cache, v_cache, bufs.indices[r0:r0 + n], out,
                                bufs.workspaces[i], lse=lse, softmax_scale=softmax_scale,
                                row_begin=r0, row_count=n, stream=st)
