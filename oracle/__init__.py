@@ -61,9 +61,11 @@ def _load():
                                             ctypes.c_int, i64, p, p, i64]
     lib.oracle_indexer_kl.argtypes = [ctypes.c_int, p, p, p, p, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_double, i64, p, p, i64, p, p]
+    lib.oracle_index_scores_backward.argtypes = [ctypes.c_int, p, p, p, p, p, ctypes.c_int,
+                                                 ctypes.c_int, i64, p, p, i64, p, p, p]
     for f in (lib.oracle_visible_counts, lib.oracle_index_scores, lib.oracle_topk,
               lib.oracle_sparse_attn, lib.oracle_quantize_fp8, lib.oracle_index_scores_f64,
-              lib.oracle_indexer_kl):
+              lib.oracle_indexer_kl, lib.oracle_index_scores_backward):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -257,6 +259,62 @@ def indexer_kl(cu_q, cu_k, q, k, scores, rows, scale: float, want_grad: bool = T
                              _ptr(grad) if want_grad else None):
         raise ValueError("invalid row or score rows shorter than the causal prefix")
     return loss, grad
+
+
+def _f64(x) -> np.ndarray:
+    """bf16 bit patterns (uint16) widened exactly, or real values as float64."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def index_scores_f64(cu_q, cu_k, q_rows, k_idx, w, rows, ld=None) -> np.ndarray:
+    """The indexer score of index_scores() on real-valued inputs: q_rows
+    [len(rows), H, d] holds the listed rows' queries, k_idx [total_k, d] the
+    keys (float64, or bf16 bits widened exactly)."""
+    lib = _load()
+    cu_q, cu_k = _c(cu_q, np.int32), _c(cu_k, np.int32)
+    rows = _c(rows, np.int64)
+    q_rows, k_all = _f64(q_rows), _f64(k_idx)
+    w = _c(w, np.float32)
+    n_heads, d = q_rows.shape[1], q_rows.shape[2]
+    if ld is None:
+        ld = int(np.max(np.diff(cu_k)))
+    out = np.empty((rows.shape[0], ld), np.float64)
+    if lib.oracle_index_scores_f64(len(cu_q) - 1, _ptr(cu_q), _ptr(cu_k), _ptr(q_rows),
+                                   _ptr(k_all), _ptr(w), n_heads, d, rows.shape[0], _ptr(rows),
+                                   _ptr(out), ld):
+        raise ValueError("invalid row for the varlen layout")
+    return out
+
+
+def index_scores_backward(cu_q, cu_k, q_rows, k_idx, w, grad, rows):
+    """Backward of the indexer score (page 5 section 1: the dense warm-up
+    trains only the indexer, so its loss's gradient reaches the indexer's
+    queries, keys and head weights).  grad [len(rows), ld] holds d L / d I
+    for the listed rows (columns beyond a row's position are not read);
+    q_rows [len(rows), H, d] the listed rows' queries, k_idx [total_k, d] the
+    keys (float64, or bf16 bits widened exactly).  The ReLU's derivative is
+    1 for x > 0 and 0 otherwise.  Returns (dq float64 [n, H, d], dw float64
+    [n, H], dk float64 [total_k, d]); dk sums over the listed rows."""
+    lib = _load()
+    cu_q, cu_k = _c(cu_q, np.int32), _c(cu_k, np.int32)
+    rows = _c(rows, np.int64)
+    q_rows, k_all = _f64(q_rows), _f64(k_idx)
+    w = _c(w, np.float32)
+    grad = _c(grad, np.float64)
+    n, n_heads, d = q_rows.shape
+    if grad.shape[0] != n or rows.shape[0] != n or k_all.shape[1] != d:
+        raise ValueError("backward shapes disagree")
+    dq = np.empty((n, n_heads, d), np.float64)
+    dw = np.empty((n, n_heads), np.float64)
+    dk = np.zeros((k_all.shape[0], d), np.float64)
+    if lib.oracle_index_scores_backward(len(cu_q) - 1, _ptr(cu_q), _ptr(cu_k), _ptr(q_rows),
+                                        _ptr(k_all), _ptr(w), n_heads, d, n, _ptr(rows),
+                                        _ptr(grad), grad.shape[1], _ptr(dq), _ptr(dw), _ptr(dk)):
+        raise ValueError("invalid row or gradient rows shorter than the causal prefix")
+    return dq, dw, dk
 
 
 def dsa_rows(cu_q, cu_k, q_idx, k_idx, w, q, k, v, rows, topk_k: int, scale: float,

@@ -430,3 +430,86 @@ int oracle_indexer_kl(int batch, const int32_t* cu_q, const int32_t* cu_k,
   }
   return bad;
 }
+
+/* ------------------------------------------------------------------------
+ * Backward of the indexer score (page 5 section 1, the two training stages:
+ * the dense warm-up trains only the indexer, so the warm-up loss's gradient
+ * must reach the indexer's own inputs).  With G[i, s] = d L / d I[t, s] for
+ * listed row i (packed row t at position p; columns 0..p), x = qI[t,h] . kI[s]
+ * and the ReLU's derivative read as 1 for x > 0 and 0 otherwise:
+ *   dq[i, h, :] = sum_{s <= p} G[i,s] w[t,h] [x > 0] kI[s, :]
+ *   dw[i, h]    = sum_{s <= p} G[i,s] max(0, x)
+ *   dk[c, :]   += sum_i sum_h G[i, s] w[t,h] [x > 0] qI[t,h,:]  (c = packed key of
+ *                                                               position s of t's sequence)
+ * Inputs as in oracle_index_scores_f64 (double queries of the listed rows,
+ * double keys); dk [total_k, d] is accumulated (the caller clears it).
+ * Columns of G beyond a row's position are never read.
+ * Returns 0, or 1 if a row is outside every sequence or p >= ld.
+ * ------------------------------------------------------------------------ */
+int oracle_index_scores_backward(int batch, const int32_t* cu_q, const int32_t* cu_k,
+                                 const double* q_rows, const double* kI, const float* w,
+                                 int n_heads, int d, int64_t n_rows, const int64_t* rows,
+                                 const double* G, int64_t ld, double* dq, double* dw,
+                                 double* dk) {
+  int bad = 0;
+  int* seq = (int*)malloc(sizeof(int) * (size_t)(n_rows > 0 ? n_rows : 1));
+  int64_t* pos = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_rows > 0 ? n_rows : 1));
+  for (int64_t i = 0; i < n_rows; ++i) {
+    seq[i] = find_seq(batch, cu_q, rows[i]);
+    pos[i] = seq[i] < 0 ? -1 : row_position(cu_q, cu_k, seq[i], rows[i]);
+    if (seq[i] < 0 || pos[i] < 0 || pos[i] >= ld) bad = 1;
+  }
+  if (bad) {
+    free(seq);
+    free(pos);
+    return 1;
+  }
+  /* dq and dw: one listed row at a time. */
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < n_rows; ++i) {
+    const int64_t t = rows[i];
+    const double* q = q_rows + i * (int64_t)n_heads * d;
+    double* dqi = dq + i * (int64_t)n_heads * d;
+    for (int64_t e = 0; e < (int64_t)n_heads * d; ++e) dqi[e] = 0.0;
+    for (int h = 0; h < n_heads; ++h) dw[i * n_heads + h] = 0.0;
+    for (int64_t s = 0; s <= pos[i]; ++s) {
+      const double g = G[i * ld + s];
+      const double* key = kI + (cu_k[seq[i]] + s) * d;
+      for (int h = 0; h < n_heads; ++h) {
+        double x = 0.0;
+        for (int j = 0; j < d; ++j) x += q[h * d + j] * key[j];
+        if (x > 0.0) {
+          const double coef = g * (double)w[t * n_heads + h];
+          for (int j = 0; j < d; ++j) dqi[h * d + j] += coef * key[j];
+          dw[i * n_heads + h] += g * x;
+        }
+      }
+    }
+  }
+  /* dk: one packed key at a time, over the listed rows that see it. */
+  const int64_t total_k = cu_k[batch];
+#pragma omp parallel for schedule(dynamic, 64)
+  for (int64_t c = 0; c < total_k; ++c) {
+    int b = 0;
+    while (b + 1 < batch && cu_k[b + 1] <= c) ++b;
+    const int64_t s = c - cu_k[b];
+    const double* key = kI + c * d;
+    for (int64_t i = 0; i < n_rows; ++i) {
+      if (seq[i] != b || s > pos[i]) continue;
+      const int64_t t = rows[i];
+      const double g = G[i * ld + s];
+      const double* q = q_rows + i * (int64_t)n_heads * d;
+      for (int h = 0; h < n_heads; ++h) {
+        double x = 0.0;
+        for (int j = 0; j < d; ++j) x += q[h * d + j] * key[j];
+        if (x > 0.0) {
+          const double coef = g * (double)w[t * n_heads + h];
+          for (int j = 0; j < d; ++j) dk[c * d + j] += coef * q[h * d + j];
+        }
+      }
+    }
+  }
+  free(seq);
+  free(pos);
+  return 0;
+}
