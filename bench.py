@@ -73,7 +73,10 @@ def parse():
                     help="decode row groups; more than one alternate between two streams "
                          "(measured slower here: the attention gathers compete with the next "
                          "group's indexer for HBM)")
-    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-rows", type=int, default=1024,
+                    help="stratified prefill rows the CPU oracle baseline runs (about 20 s)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the 32K and varlen-512K prefill lines")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -177,30 +180,68 @@ def counter_traffic(kernel_source, record, window_rows):
     return int(rec["fetch_bytes_per_dispatch"] + rec["write_bytes_per_dispatch"])
 
 
-def cpu_baseline(wl, host, n_rows):
-    """The oracle, untuned, on query rows evenly spaced over the prefill."""
+def cpu_model():
+    """The host CPU's model name (the lscpu "Model name" field, read from
+    /proc/cpuinfo so no tool needs to be installed)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def stratified_rows(L, k, n, seed=0):
+    """n rows, one seeded row from each of n equal strata of [0, L), plus rows
+    0, k - 1, k and L - 1."""
+    rng = np.random.default_rng(seed)
+    edges = np.linspace(0, L, n + 1).astype(np.int64)
+    rows = {int(rng.integers(a, max(a + 1, b))) for a, b in zip(edges[:-1], edges[1:])}
+    rows |= {0, k - 1, k, L - 1}
+    return np.array(sorted(r for r in rows if 0 <= r < L), dtype=np.int64)
+
+
+def cpu_baseline(wl, host, n_rows, wd=None, wd_host=None):
+    """The oracle, untuned, on the GPU host's cores: the whole path (scores,
+    top-k, attention in fp64) on a stratified sample of the prefill's rows
+    (about n_rows, one per equal stratum of positions, plus rows 0, k-1, k and
+    L-1), and on every query of the decode batch.  Stratified rows carry the
+    prefill's mean causal length, so the sample's rows/s is its tokens/s."""
     import oracle
 
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     L = wl.seqlens_q[0]
-    rows = np.unique(np.linspace(0, L - 1, n_rows).round().astype(np.int64))
+    rows = stratified_rows(L, wl.topk, n_rows)
     t0 = time.time()
     oracle.dsa_rows(wl.cu_q, wl.cu_k, host["q_idx"], host["k_idx"], host["w"], host["q"],
                     host["k"], host["v"], rows, wl.topk, wl.softmax_scale)
     dt = time.time() - t0
     work = int((rows + 1).sum())
     full_work = L * (L + 1) // 2
-    return {
+    res = {
         "value": round(len(rows) / dt, 3),
         "unit": "tokens/s",
         "cores": cores,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
-        "sample": (f"{len(rows)} query rows evenly spaced over positions 0..{L - 1} of the "
-                   f"131072-token prefill, whole path (scores, top-k, attention) in fp64, "
-                   f"{dt:.1f} s; the full prefill extrapolates to "
-                   f"{dt * full_work / work / 3600:.1f} h"),
+        "sample": (f"{len(rows)} query rows of the 131072-token prefill, one seeded row per equal "
+                   f"stratum of positions plus rows 0, k-1, k and L-1; whole path (scores, top-k, "
+                   f"attention) in fp64, {dt:.1f} s; the full prefill extrapolates to "
+                   f"{dt * full_work / work / 3600:.1f} h (extrapolated, by causal pairs)"),
         "seconds": round(dt, 2),
     }
+    if wd is not None:
+        t0 = time.time()
+        oracle.dsa_rows(wd.cu_q, wd.cu_k, wd_host["q_idx"], wd_host["k_idx"], wd_host["w"],
+                        wd_host["q"], wd_host["k"], wd_host["v"], np.arange(wd.batch), wd.topk,
+                        wd.softmax_scale)
+        dt = time.time() - t0
+        res["decode"] = {"value": round(wd.batch / dt, 3), "unit": "queries/s",
+                         "sample": f"all {wd.batch} queries of the decode step (in full), {dt:.1f} s",
+                         "seconds": round(dt, 2)}
+    return res
 
 
 # ---------------------------------------------------------------- main
@@ -240,7 +281,8 @@ def main():
     wd = synth.decode_b64_128k()
     if not args.no_decode:
         log(f"generating {wd.name}")
-        D, _ = gen_upload(torch, wd, ("q_idx", "k_idx", "w", "q", "k", "v"))
+        D, D_host = gen_upload(torch, wd, ("q_idx", "k_idx", "w", "q", "k", "v"),
+                               keep_host=not args.no_cpu_baseline)
         vd = dsa.Varlen(wd.cu_q.tolist(), wd.cu_k.tolist())
         dbufs = pipeline.alloc_decode(vd, wd.n_heads_q, wd.head_dim, wd.topk,
                                       groups=args.decode_groups)
@@ -429,6 +471,10 @@ def main():
         result["fp8_indexer"] = fp8_variant(torch, pipeline, args, stream, wl, vl, P, out, lse,
                                             None if args.no_decode else (wd, vd, D, dout, dlse))
 
+    if not args.no_workloads:
+        result["workloads"] = {w.name: workload_line(torch, pipeline, args, stream, w)
+                               for w in (synth.prefill_32k(), synth.varlen_512k())}
+
     if not args.no_fused:
         result["fused_index_topk"] = fused_variant(
             torch, dsa, pipeline, args, stream, wl, vl, P, out, lse, pre_ms / args.steps,
@@ -448,7 +494,9 @@ def main():
 
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_rows} sampled rows")
-        result["cpu_baseline"] = cpu_baseline(wl, P_host, args.cpu_rows)
+        result["cpu_baseline"] = cpu_baseline(wl, P_host, args.cpu_rows,
+                                              None if args.no_decode else wd,
+                                              None if args.no_decode else D_host)
 
     print(json.dumps(result), flush=True)
 
@@ -466,7 +514,7 @@ def fp8_variant(torch, pipeline, args, stream, wl, vl, P, out, lse, dec):
     fp8 = pipeline.alloc_fp8_indexer(wl.total_q, wl.total_k, wl.n_heads_idx, wl.d_idx)
     run = lambda rec: pipeline.prefill(vl, P["q_idx"], P["k_idx"], P["w"], P["q"], P["k"],  # noqa: E731
                                        P["v"], out, bufs, lse=lse, stream=stream, record=rec,
-                                       fp8=fp8)
+                                       fp8=fp8, attn_rows=args.attn_rows)
     log("fp8 indexer: prefill")
     for _ in range(args.warmup):
         run(None)
@@ -524,6 +572,59 @@ def fp8_variant(torch, pipeline, args, stream, wl, vl, P, out, lse, dec):
                                       "frac": round(gbs / PEAK_HBM_GBS, 4),
                                       "bytes_per_query": per_q}}
         del dbufs, fp8d
+    torch.cuda.empty_cache()
+    return res
+
+
+def workload_line(torch, pipeline, args, stream, wl):
+    """The headline's prefill (same windows, attention launches, one stream)
+    on another of the seeded workloads: 32K tokens, or the varlen batch of
+    524288 tokens in log-uniform lengths.  Rooflines from the workload's own
+    causal and selected pairs (for varlen, the drawn lengths)."""
+    import long_context_sparse_score_amd as dsa
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    log(f"workload {wl.name}: generating")
+    P, _ = gen_upload(torch, wl, ("q_idx", "k_idx", "w", "q", "k", "v"))
+    vl = dsa.Varlen(wl.cu_q.tolist(), wl.cu_k.tolist())
+    bufs = pipeline.alloc_prefill(vl, wl.topk, args.window)
+    out = torch.empty((wl.total_q, wl.n_heads_q, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((wl.total_q, wl.n_heads_q), dtype=torch.float32, device="cuda")
+    run = lambda rec: pipeline.prefill(vl, P["q_idx"], P["k_idx"], P["w"], P["q"], P["k"],  # noqa: E731
+                                       P["v"], out, bufs, lse=lse, stream=stream, record=rec,
+                                       attn_rows=args.attn_rows)
+    for _ in range(args.warmup):
+        run(None)
+    torch.cuda.synchronize()
+    rec, tot = [], 0.0
+    for _ in range(args.steps):
+        a, b = ev(), ev()
+        a.record(stream)
+        run(rec)
+        b.record(stream)
+        torch.cuda.synchronize()
+        tot += a.elapsed_time(b)
+    ms = tot / args.steps
+    span = lambda name: sum(e[name][0].elapsed_time(e[name][1]) for _, _, e in rec) / args.steps  # noqa: E731
+    pc = prefill_counts(wl)
+    t_mfma = (pc["f_idx"] + pc["f_attn"]) / (PEAK_BF16_TFLOPS * 1e12) * 1e3
+    t_comb = (pc["f_idx"] / (PEAK_BF16_TFLOPS * 1e12) + pc["b_scores"] / (PEAK_HBM_GBS * 1e9)
+              + max(pc["f_attn"] / (PEAK_BF16_TFLOPS * 1e12), pc["b_gather"] / (PEAK_HBM_GBS * 1e9))) * 1e3
+    idx_ms = span("index_scores")
+    tflops = pc["f_idx"] / (idx_ms / 1e3) / 1e12
+    res = {"sequences": len(wl.seqlens_q), "tokens": wl.total_q, "max_seqlen": wl.max_seqlen_k,
+           "ms": round(ms, 3), "tokens_per_s": round(wl.total_q / (ms / 1e3), 1),
+           "index_scores_ms": round(idx_ms, 3), "topk_ms": round(span("topk"), 3),
+           "sparse_attn_ms": round(span("sparse_attn"), 3),
+           "mfma_roofline_ms": round(t_mfma, 3), "mfma_roofline_frac": round(t_mfma / ms, 4),
+           "combined_roofline_ms": round(t_comb, 3), "combined_roofline_frac": round(t_comb / ms, 4),
+           "index_scores_roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4)},
+           "algorithmic": {k: int(v) for k, v in pc.items()}}
+    if len(wl.seqlens_q) > 1:
+        res["seqlens"] = list(wl.seqlens_q)
+    del P, bufs, out, lse
     torch.cuda.empty_cache()
     return res
 
@@ -670,7 +771,8 @@ def grouped_variant(torch, dsa, pipeline, args, stream, wl, vl, P, out, lse, iid
     for name, grouped in (("per_row", False), ("grouped", True)):
         bufs = pipeline.alloc_prefill(vl, wl.topk, args.window, grouped=grouped)
         run = lambda rec: pipeline.prefill(vl, qc, P["k_idx"], P["w"], P["q"], P["k"], P["v"],  # noqa: E731
-                                           out, bufs, lse=lse, stream=stream, record=rec)
+                                           out, bufs, lse=lse, stream=stream, record=rec,
+                                           attn_rows=None if grouped else args.attn_rows)
         for _ in range(args.warmup):
             run(None)
         torch.cuda.synchronize()
@@ -760,9 +862,15 @@ def dense_comparator(torch, P, wl, args, sparse_ms):
             torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / args.steps
         flops = wl.total_q * (wl.total_q + 1) / 2 * 4 * wl.n_heads_q * wl.head_dim
+        roof_ms = flops / (PEAK_BF16_TFLOPS * 1e12) * 1e3
         return {"kind": "torch SDPA flash backend, causal, GQA", "ms": round(ms, 3),
                 "tflops": round(flops / (ms / 1e3) / 1e12, 1),
-                "sparse_over_dense_time": round(sparse_ms / ms, 3)}
+                "sparse_over_dense_time": round(sparse_ms / ms, 3),
+                "dense_mfma_roofline_ms": round(roof_ms, 3),
+                "sparse_over_dense_mfma_roofline": round(sparse_ms / roof_ms, 3),
+                "note": "sparse_over_dense_time uses the SDPA run as measured; "
+                        "sparse_over_dense_mfma_roofline divides by the time dense causal "
+                        "attention of this shape would take at the bf16 dense MFMA peak"}
     except Exception as exc:  # the comparator is context, not the product
         return {"kind": "torch SDPA flash backend", "error": repr(exc)[:300]}
 

@@ -450,3 +450,32 @@ def test_noalloc_decode_validation_and_limit():
     assert call(rc=65) == I
     assert call(hq=30, hkv=4) == I
     assert call(rc=0) == dsa.DSA_OK  # empty window: nothing enqueued, no device touched
+
+
+def test_index_topk_validation():
+    """dsa_index_topk rejects bad arguments, a missing or small workspace,
+    and unsupported k on the host; its workspace size grows with the rows."""
+    lib = dsa.load_library()
+    I, U, W = dsa.DSA_ERR_INVALID_ARGUMENT, dsa.DSA_ERR_UNSUPPORTED, dsa.DSA_ERR_WORKSPACE
+    v = vl(total_q=100, total_k=100, max_q=100, max_k=100)
+    n = ctypes.c_size_t(0)
+    assert lib.dsa_index_topk_workspace_size(ctypes.byref(v), 10, 64, ctypes.byref(n)) == 0
+    small = n.value
+    assert lib.dsa_index_topk_workspace_size(ctypes.byref(v), 20, 64, ctypes.byref(n)) == 0
+    assert n.value > small > 0
+    assert lib.dsa_index_topk_workspace_size(ctypes.byref(v), 10, 4096, ctypes.byref(n)) == U
+    assert lib.dsa_index_topk_workspace_size(ctypes.byref(v), 101, 64, ctypes.byref(n)) == I
+
+    def call(q=FAKE, k=64, rc=10, ws=FAKE, wsb=1 << 40, heads=64, d=128, idx=FAKE):
+        return lib.dsa_index_topk(ctypes.byref(v), q, FAKE, FAKE, heads, d, 0, rc, k, idx, ws, wsb,
+                                  None)
+
+    assert call(rc=0) == dsa.DSA_OK
+    assert call(q=None) == I
+    assert call(q=FAKE + 2) == I
+    assert call(idx=None) == I
+    assert call(k=0) == U and call(k=2049) == U
+    assert call(d=96) == U and call(heads=65) == U
+    assert call(ws=None) == W
+    assert call(wsb=small - 1) == W
+    assert call(ws=FAKE + 16) == W  # not 256-byte aligned

@@ -246,3 +246,60 @@ def test_varlen_512k_sampled():
         rows |= {int(rng.integers(x, max(x + 1, y))) for x, y in zip(edges[:-1], edges[1:])}
     rows = np.array(sorted(rows), dtype=np.int64)
     check_rows(wl, host, rows, out, lse, idx)
+
+
+def _fused_equals_unfused(wl, dev, window):
+    """Every window of a prefill: dsa_index_topk's selection is bitwise that of
+    dsa_index_scores -> dsa_topk.  Returns the rows that fell back."""
+    vl = dsa.Varlen(wl.cu_q.tolist(), wl.cu_k.tolist())
+    bufs = pipeline.alloc_prefill(vl, wl.topk, window)
+    fbufs = pipeline.alloc_prefill(vl, wl.topk, window, fused=True)
+    fallbacks = 0
+    for r0 in range(0, wl.total_q, window):
+        n = min(window, wl.total_q - r0)
+        dsa.dsa_index_scores(vl, dev["q_idx"], dev["k_idx"], dev["w"], bufs.scores, row_begin=r0,
+                             row_count=n)
+        dsa.dsa_topk(vl, bufs.scores, bufs.indices, row_begin=r0, row_count=n)
+        dsa.dsa_index_topk(vl, dev["q_idx"], dev["k_idx"], dev["w"], fbufs.indices[:n], fbufs.fused,
+                           row_begin=r0, row_count=n)
+        assert torch.equal(bufs.indices[:n], fbufs.indices[:n]), f"window at row {r0}"
+        off = (n * 4 + 255) // 256 * 256
+        fallbacks += int(fbufs.fused[off:off + 4 * n].view(torch.int32).sum())
+    torch.cuda.synchronize()
+    return fallbacks
+
+
+def test_fused_index_topk_128k_all_rows():
+    """The fused indexer -> top-k over every row of the 128K prefill in the
+    bench's windows: bitwise the unfused selection (which the sampled and
+    all-rows tests above hold to the oracle)."""
+    wl = synth.prefill_128k()
+    _, dev = device_workload(wl, ("q_idx", "k_idx", "w"))
+    fb = _fused_equals_unfused(wl, dev, CFG.window)
+    log(f"  prefill_128k fused: {fb} rows took the fallback")
+
+
+def test_fused_index_topk_varlen_512k_all_rows():
+    wl = synth.varlen_512k()
+    _, dev = device_workload(wl, ("q_idx", "k_idx", "w"))
+    fb = _fused_equals_unfused(wl, dev, CFG.window)
+    log(f"  varlen_512k fused: {fb} rows took the fallback")
+
+
+def test_fused_decode_b64_128k():
+    """The fused decode step against the unfused one: same indices, same
+    attention output bits."""
+    wl = synth.decode_b64_128k()
+    _, dev = device_workload(wl)
+    vl = dsa.Varlen(wl.cu_q.tolist(), wl.cu_k.tolist())
+    res = []
+    for fused in (False, True):
+        bufs = pipeline.alloc_decode(vl, wl.n_heads_q, wl.head_dim, wl.topk, fused=fused)
+        out = torch.zeros((wl.batch, wl.n_heads_q, wl.head_dim), dtype=torch.bfloat16,
+                          device="cuda")
+        pipeline.decode(vl, dev["q_idx"], dev["k_idx"], dev["w"], dev["q"], dev["k"], dev["v"],
+                        out, bufs)
+        res.append((bufs.indices.clone(), out))
+    torch.cuda.synchronize()
+    assert torch.equal(res[0][0], res[1][0])
+    assert torch.equal(res[0][1].view(torch.int16), res[1][1].view(torch.int16))
