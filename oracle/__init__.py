@@ -63,9 +63,12 @@ def _load():
                                       ctypes.c_int, ctypes.c_double, i64, p, p, i64, p, p]
     lib.oracle_index_scores_backward.argtypes = [ctypes.c_int, p, p, p, p, p, ctypes.c_int,
                                                  ctypes.c_int, i64, p, p, i64, p, p, p]
+    lib.oracle_index_scores_backward_keys.argtypes = [ctypes.c_int, p, p, p, p, p, ctypes.c_int,
+                                                      ctypes.c_int, i64, p, p, i64, p, p]
     for f in (lib.oracle_visible_counts, lib.oracle_index_scores, lib.oracle_topk,
               lib.oracle_sparse_attn, lib.oracle_quantize_fp8, lib.oracle_index_scores_f64,
-              lib.oracle_indexer_kl, lib.oracle_index_scores_backward):
+              lib.oracle_indexer_kl, lib.oracle_index_scores_backward,
+              lib.oracle_index_scores_backward_keys):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -315,6 +318,27 @@ def index_scores_backward(cu_q, cu_k, q_rows, k_idx, w, grad, rows):
                                         _ptr(grad), grad.shape[1], _ptr(dq), _ptr(dw), _ptr(dk)):
         raise ValueError("invalid row or gradient rows shorter than the causal prefix")
     return dq, dw, dk
+
+
+def index_scores_backward_keys(cu_q, cu_k, q_rows, k_idx, w, grad_at, rows, keys):
+    """The key gradient of index_scores_backward() at the listed packed keys
+    only: grad_at [len(rows), len(keys)] holds d L / d I at (row, key); the
+    result dk [len(keys), d] sums over the listed rows that see each key."""
+    lib = _load()
+    cu_q, cu_k = _c(cu_q, np.int32), _c(cu_k, np.int32)
+    rows, keys = _c(rows, np.int64), _c(keys, np.int64)
+    q_rows, k_all = _f64(q_rows), _f64(k_idx)
+    w = _c(w, np.float32)
+    grad_at = _c(grad_at, np.float64)
+    n, n_heads, d = q_rows.shape
+    if grad_at.shape != (n, keys.shape[0]) or rows.shape[0] != n or k_all.shape[1] != d:
+        raise ValueError("backward shapes disagree")
+    dk = np.empty((keys.shape[0], d), np.float64)
+    if lib.oracle_index_scores_backward_keys(len(cu_q) - 1, _ptr(cu_q), _ptr(cu_k), _ptr(q_rows),
+                                             _ptr(k_all), _ptr(w), n_heads, d, n, _ptr(rows),
+                                             _ptr(grad_at), keys.shape[0], _ptr(keys), _ptr(dk)):
+        raise ValueError("invalid row or key")
+    return dk
 
 
 def dsa_rows(cu_q, cu_k, q_idx, k_idx, w, q, k, v, rows, topk_k: int, scale: float,

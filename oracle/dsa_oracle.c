@@ -513,3 +513,57 @@ int oracle_index_scores_backward(int batch, const int32_t* cu_q, const int32_t* 
   free(pos);
   return 0;
 }
+
+/* dk of the indexer backward for listed packed keys only: dk[c] = sum over
+ * the listed rows i that see key keys[c] (same sequence, local position at
+ * most the row's) and every head h with x = qI[i,h] . kI[key] > 0 of
+ * Gk[i, c] * w[row_i, h] * qI[i, h, :].  Gk [n_rows, n_keys] holds dL/dI at
+ * (row i, key c).  The sum is the key's column of the dense backward above,
+ * without touching the keys nobody asked for.  Returns 1 on an invalid row
+ * or key. */
+int oracle_index_scores_backward_keys(int batch, const int32_t* cu_q, const int32_t* cu_k,
+                                      const double* q_rows, const double* kI, const float* w,
+                                      int n_heads, int d, int64_t n_rows, const int64_t* rows,
+                                      const double* Gk, int64_t n_keys, const int64_t* keys,
+                                      double* dk) {
+  int bad = 0;
+  int* seq = (int*)malloc(sizeof(int) * (size_t)(n_rows > 0 ? n_rows : 1));
+  int64_t* pos = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_rows > 0 ? n_rows : 1));
+  for (int64_t i = 0; i < n_rows; ++i) {
+    seq[i] = find_seq(batch, cu_q, rows[i]);
+    pos[i] = seq[i] < 0 ? -1 : row_position(cu_q, cu_k, seq[i], rows[i]);
+    if (seq[i] < 0 || pos[i] < 0) bad = 1;
+  }
+  for (int64_t c = 0; c < n_keys; ++c)
+    if (keys[c] < 0 || keys[c] >= cu_k[batch]) bad = 1;
+  if (bad) {
+    free(seq);
+    free(pos);
+    return 1;
+  }
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t c = 0; c < n_keys; ++c) {
+    int b = 0;
+    while (b + 1 < batch && cu_k[b + 1] <= keys[c]) ++b;
+    const int64_t s = keys[c] - cu_k[b];
+    const double* key = kI + keys[c] * d;
+    double* out = dk + c * d;
+    for (int j = 0; j < d; ++j) out[j] = 0.0;
+    for (int64_t i = 0; i < n_rows; ++i) {
+      if (seq[i] != b || s > pos[i]) continue;
+      const double g = Gk[i * n_keys + c];
+      const double* q = q_rows + i * (int64_t)n_heads * d;
+      for (int h = 0; h < n_heads; ++h) {
+        double x = 0.0;
+        for (int j = 0; j < d; ++j) x += q[h * d + j] * key[j];
+        if (x > 0.0) {
+          const double coef = g * (double)w[rows[i] * n_heads + h];
+          for (int j = 0; j < d; ++j) out[j] += coef * q[h * d + j];
+        }
+      }
+    }
+  }
+  free(seq);
+  free(pos);
+  return 0;
+}

@@ -168,3 +168,36 @@ def test_a_planted_sign_error_is_caught():
     km[idx] -= eps
     fd = (_loss(q, kp, w, g) - _loss(q, km, w, g)) / (2 * eps)
     assert abs(fd - (-dk[idx])) > 1e-3
+
+
+def test_key_restricted_dk_by_central_differences():
+    """index_scores_backward_keys at listed keys, for listed rows only (a
+    window that starts mid-sequence): central differences of the score sum
+    over those rows with respect to each listed key."""
+    q, k, w, g = _case(10)
+    rows = np.arange(4, 15, dtype=np.int64)           # rows 4..14: both sequences, partial
+    keys = np.array([0, 3, 8, 9, 12, 19], np.int64)   # key 19 is seen by no listed row
+    pos = np.array([t - (0 if t < 9 else 9) for t in rows])
+    seq_k0 = np.array([0 if t < 9 else 9 for t in rows])
+    g_rows = g[: len(rows)]   # dL/dI of listed row i (column = local key)
+    grad_at = np.array([[g_rows[i, c - seq_k0[i]] if 0 <= c - seq_k0[i] <= pos[i] and
+                         (c < 9) == (rows[i] < 9) else 0.0 for c in keys]
+                        for i in range(len(rows))])
+    dk = oracle.index_scores_backward_keys(CU, CU, q[rows], k, w, grad_at, rows, keys)
+
+    def loss(kk):
+        s = oracle.index_scores_f64(CU, CU, q[rows], kk, w, rows, ld=LD)
+        return float(np.sum(np.where(np.isnan(s), 0.0, g_rows * np.nan_to_num(s))))
+
+    eps = 1e-6
+    for ci, c in enumerate(keys):
+        for j in range(D):
+            kp, km = k.copy(), k.copy()
+            kp[c, j] += eps
+            km[c, j] -= eps
+            fd = (loss(kp) - loss(km)) / (2 * eps)
+            assert abs(fd - dk[ci, j]) <= 1e-6 * max(1.0, abs(dk[ci, j])), (c, j)
+    assert not dk[-1].any()
+    # the dense backward's key gradient agrees at the listed keys
+    _, _, dk_dense = oracle.index_scores_backward(CU, CU, q[rows], k, w, g_rows, rows)
+    np.testing.assert_allclose(dk, dk_dense[keys], rtol=1e-12, atol=1e-12)
