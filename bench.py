@@ -61,7 +61,7 @@ def parse():
     ap.add_argument("--no-grouped", action="store_true",
                     help="skip the grouped-attention comparison on the correlated-query workload")
     ap.add_argument("--no-kl", action="store_true",
-                    help="skip the indexer warm-up KL loss measurement (a training-side kernel)")
+                    help="skip the indexer warm-up step (scores, KL loss and backward; training side)")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the optional fp8-indexer variant (reported beside the headline)")
     ap.add_argument("--no-fused", action="store_true",
@@ -483,7 +483,7 @@ def main():
                                          (d_idx_ms + d_topk_ms) / args.steps))
 
     if not args.no_kl:
-        result["indexer_kl"] = kl_variant(torch, dsa, args, stream, wl, vl, P, bufs)
+        result["indexer_warmup"] = kl_variant(torch, dsa, pipeline, args, stream, wl, vl, P)
 
     if not args.no_grouped:
         result["grouped_attention"] = grouped_variant(torch, dsa, pipeline, args, stream, wl, vl, P,
@@ -713,43 +713,86 @@ def fused_variant(torch, dsa, pipeline, args, stream, wl, vl, P, out, lse, unfus
     return res
 
 
-def kl_variant(torch, dsa, args, stream, wl, vl, P, bufs):
-    """The indexer's warm-up loss (dsa_indexer_kl) over the whole prefill: per
-    window the indexer scores (untimed), then the KL loss with the gradient
-    written over the scores (timed by HIP events on the launch stream).  Its
-    work is two dense logit passes over every causal pair: 2 x 2 Hq d flops
-    per pair, an MFMA-bound kernel.  Windows of 8192 rows: one workgroup
-    serves 16 rows, so a 2048-row window would fill only 128 of the 256 CUs."""
+def kl_variant(torch, dsa, pipeline, args, stream, wl, vl, P):
+    """The indexer's dense warm-up step over the whole prefill
+    (pipeline.warmup): per 8192-row window the indexer scores, the KL loss
+    with its gradient written over the scores (dsa_indexer_kl), and the
+    gradient into the indexer's queries, weights and keys
+    (dsa_index_scores_backward), each timed by HIP events on the launch
+    stream.  The KL computes two dense logit passes per causal pair
+    (4 Hq d flops); the backward recomputes the head products twice and runs
+    two GEMMs of the same size (8 H_I d_I flops per pair).  A second pass
+    times the backward's two kernels apart (dq/dw alone, dk alone)."""
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     pc = prefill_counts(wl)
-    flops = pc["pairs"] * 4 * wl.n_heads_q * wl.head_dim
-    window = min(8192, wl.total_q)
-    ld = bufs.scores.shape[1]
-    scores = torch.empty((window, ld), dtype=torch.float32, device="cuda")
+    H, D = wl.n_heads_idx, wl.d_idx
+    kl_flops = pc["pairs"] * 4 * wl.n_heads_q * wl.head_dim
+    half_flops = pc["pairs"] * 4 * H * D  # one backward kernel: x again plus one GEMM
+    wb = pipeline.alloc_warmup(vl, H, D)
     loss = torch.empty(wl.total_q, dtype=torch.float32, device="cuda")
-    log("indexer KL: one pass over the prefill")
-    tot, n_launch = 0.0, 0
-    for r0 in range(0, wl.total_q, window):
-        n = min(window, wl.total_q - r0)
-        dsa.dsa_index_scores(vl, P["q_idx"], P["k_idx"], P["w"], scores, row_begin=r0,
-                             row_count=n)
-        a, b = ev(), ev()
-        a.record(stream)
-        dsa.dsa_indexer_kl(vl, P["q"], P["k"], scores, loss[r0:r0 + n], grad=scores,
-                           row_begin=r0, row_count=n)
-        b.record(stream)
-        torch.cuda.synchronize()
-        tot += a.elapsed_time(b)
-        n_launch += 1
-    tflops = flops / (tot / 1e3) / 1e12
-    del scores
+    dq = torch.empty((wl.total_q, H, D), dtype=torch.float32, device="cuda")
+    dw = torch.empty((wl.total_q, H), dtype=torch.float32, device="cuda")
+    dk = torch.empty((wl.total_k, D), dtype=torch.float32, device="cuda")
+    log("indexer warm-up step: one pass over the prefill")
+    rec = []
+    a, b = ev(), ev()
+    a.record(stream)
+    pipeline.warmup(vl, P["q_idx"], P["k_idx"], P["w"], P["q"], P["k"], loss, dq, dw, dk, wb,
+                    stream=stream, record=rec)
+    b.record(stream)
+    torch.cuda.synchronize()
+    total = a.elapsed_time(b)
+    span = {kind: sum(e[kind][0].elapsed_time(e[kind][1]) for _, _, e in rec)
+            for kind in ("index_scores", "indexer_kl", "backward")}
+    log("indexer warm-up step: backward kernels timed apart")
+    parts = {"dq_dw": 0.0, "dk": 0.0}
+    for r0 in range(0, wl.total_q, wb.window):
+        n = min(wb.window, wl.total_q - r0)
+        sc = wb.scores[:n]
+        dsa.dsa_index_scores(vl, P["q_idx"], P["k_idx"], P["w"], sc, row_begin=r0, row_count=n)
+        dsa.dsa_indexer_kl(vl, P["q"], P["k"], sc, loss[r0:r0 + n], grad=sc, row_begin=r0,
+                           row_count=n)
+        for part in ("dq_dw", "dk"):
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            dsa.dsa_index_scores_backward(
+                vl, P["q_idx"], P["k_idx"], P["w"], sc, wb.workspace,
+                dq_idx=dq[r0:r0 + n] if part == "dq_dw" else None,
+                dw=dw[r0:r0 + n] if part == "dq_dw" else None,
+                dk_idx=dk if part == "dk" else None, row_begin=r0, row_count=n)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            parts[part] += e0.elapsed_time(e1)
+    del wb, dq, dw, dk
     torch.cuda.empty_cache()
-    return {"ms": round(tot, 3), "launches": n_launch, "window_rows": window,
-            "mean_loss_per_row": round(float(loss.mean()), 5),
-            "roofline": {"bound": "mfma", "kernel": "indexer_kl", "achieved": round(tflops, 2),
-                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                         "flops_per_causal_pair": 4 * wl.n_heads_q * wl.head_dim}}
+
+    def roof(kernel, flops, ms):
+        tf = flops / (ms / 1e3) / 1e12
+        return {"bound": "mfma", "kernel": kernel, "achieved": round(tf, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    return {
+        "window_rows": pipeline.WARMUP_WINDOW, "launches": len(rec),
+        "step_ms": round(total, 3),
+        "tokens_per_s": round(wl.total_q / (total / 1e3), 1),
+        "index_scores_ms": round(span["index_scores"], 3),
+        "indexer_kl_ms": round(span["indexer_kl"], 3),
+        "backward_ms": round(span["backward"], 3),
+        "mean_loss_per_row": round(float(loss.mean()), 5),
+        "roofline": dict(roof("indexer_kl", kl_flops, span["indexer_kl"]),
+                         flops_per_causal_pair=4 * wl.n_heads_q * wl.head_dim),
+        "backward": {
+            "ms": round(span["backward"], 3),
+            "roofline": dict(roof("index backward (dq/dw + dk)", 2 * half_flops,
+                                  span["backward"]),
+                             flops_per_causal_pair=8 * H * D),
+            "dq_dw_ms": round(parts["dq_dw"], 3),
+            "dq_dw_roofline": roof("index_bwd_dq_kernel (+ key transpose)", half_flops,
+                                   parts["dq_dw"]),
+            "dk_ms": round(parts["dk"], 3),
+            "dk_roofline": roof("index_bwd_dk_kernel (+ query transpose)", half_flops,
+                                parts["dk"]),
+        },
+    }
 
 
 def grouped_variant(torch, dsa, pipeline, args, stream, wl, vl, P, out, lse, iid_attn_ms):

@@ -287,6 +287,50 @@ int dsa_indexer_kl(const dsa_varlen* vl, const void* q, const void* k, const flo
                    int32_t n_heads_kv, int32_t head_dim, float softmax_scale, float* loss,
                    float* grad, int64_t ld_grad, hipStream_t stream);
 
+/*
+ * dsa_index_scores_backward -- gradient of the indexer score with respect to
+ * the indexer's own inputs (page 5 section 1, the two training stages: in
+ * the dense warm-up only the indexer is trained, so the warm-up loss's
+ * gradient has to reach its queries, keys and head weights).  For window
+ * row t at position p, keys s = 0..p, x[t,h,s] = q_idx[t,h,:] . k_idx[s,:]
+ * and G = grad = d loss / d I (as dsa_indexer_kl writes it, or any other
+ * upstream gradient), taking the ReLU's derivative as 1 for x > 0 and 0
+ * otherwise:
+ *   dw[t,h]       = sum_s G[t,s] max(0, x[t,h,s])                   written
+ *   dq_idx[t,h,:] = w[t,h] sum_{s: x > 0} G[t,s] k_idx[s,:]          written
+ *   dk_idx[s,:]  += sum_t sum_{h: x > 0} G[t,s] w[t,h] q_idx[t,h,:]   added
+ *
+ *   q_idx, k_idx, w, n_heads_idx, d_idx, window: as dsa_index_scores
+ *   grad    fp32 [row_count, ld_grad]; columns 0..p of each row read
+ *   dq_idx  fp32 [row_count, n_heads_idx, d_idx], or NULL together with dw
+ *   dw      fp32 [row_count, n_heads_idx], or NULL together with dq_idx
+ *   dk_idx  fp32 [total_k, d_idx] or NULL: the window's contribution is
+ *           added, so the windows of one pass sum into it (the caller zeroes
+ *           it first; calls adding to one dk_idx must run in stream order)
+ *   workspace  device memory of dsa_index_scores_backward_workspace_size
+ *           bytes (for the outputs requested), 256-byte aligned; it holds the
+ *           transposed keys (dq) and the window's weighted, transposed
+ *           queries (dk) and is free again when the call's work is done.
+ * Arithmetic: x recomputed as dsa_index_scores computes it (bf16 MFMA, fp32
+ * accumulation); dw summed in fp32; the dq and dk products take G [x > 0]
+ * and, for dk, w q_idx rounded to bf16 (nearest even) as MFMA operands with
+ * fp32 accumulation.
+ * Supported: as dsa_index_scores, and one sequence's dk_idx rows within
+ * 2 GiB (max_seqlen_k * d_idx * 4 < 2^31).
+ * Invalid: null inputs, misaligned pointers (bf16 inputs 16-byte, fp32
+ * 4-byte), ld_grad < max_seqlen_k, dq_idx without dw or the reverse, no
+ * output at all, a window outside [0, total_q); a missing, short or
+ * misaligned workspace gives DSA_ERR_WORKSPACE.  row_count == 0 is a no-op.
+ */
+int dsa_index_scores_backward_workspace_size(const dsa_varlen* vl, int32_t n_heads_idx,
+                                             int32_t d_idx, int64_t row_count, int want_dq,
+                                             int want_dk, size_t* bytes);
+int dsa_index_scores_backward(const dsa_varlen* vl, const void* q_idx, const void* k_idx,
+                              const float* w, int32_t n_heads_idx, int32_t d_idx,
+                              int64_t row_begin, int64_t row_count, const float* grad,
+                              int64_t ld_grad, float* dq_idx, float* dw, float* dk_idx,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes dsa_sparse_attn_prefill_grouped needs for a window of
    row_count rows (the unions of up to ceil(row_count / 16) groups). */
 int dsa_sparse_attn_prefill_grouped_workspace_size(const dsa_varlen* vl, int64_t row_count,

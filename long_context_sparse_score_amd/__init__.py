@@ -37,6 +37,7 @@ EXPORTED = (
     "dsa_quantize_fp8", "dsa_index_scores_fp8", "dsa_sparse_attn_prefill_grouped_workspace_size",
     "dsa_sparse_attn_prefill_grouped", "dsa_indexer_kl", "dsa_sparse_attn_decode_noalloc",
     "dsa_index_topk_workspace_size", "dsa_index_topk",
+    "dsa_index_scores_backward_workspace_size", "dsa_index_scores_backward",
 )
 
 DSA_OK = 0
@@ -103,6 +104,9 @@ def load_library(path: str = LIB_PATH):
                                                     i32, f32, vp, vp, vp, ctypes.c_size_t, vp]
     lib.dsa_indexer_kl.argtypes = [vl, vp, vp, vp, i64, i64, i64, i32, i32, i32, f32, vp, vp,
                                    i64, vp]
+    lib.dsa_index_scores_backward_workspace_size.argtypes = [vl, i32, i32, i64, i32, i32, sz]
+    lib.dsa_index_scores_backward.argtypes = [vl, vp, vp, vp, i32, i32, i64, i64, vp, i64, vp, vp,
+                                              vp, vp, ctypes.c_size_t, vp]
     lib.dsa_check_varlen.argtypes = [vl, vp]
     lib.dsa_check_indices.argtypes = [vl, vp, i32, i64, i64, vp]
     lib.dsa_check_scores.argtypes = [vl, vp, i64, i64, i64, vp]
@@ -442,6 +446,56 @@ def dsa_indexer_kl(vl: Varlen, q, k, scores, loss, grad=None, softmax_scale=None
         vl.struct, _ptr(q), _ptr(k), _ptr(scores), scores.stride(0), row_begin, row_count,
         q.shape[1], k.shape[1], d, _scale(softmax_scale), _ptr(loss), _ptr(grad),
         0 if grad is None else grad.stride(0), _stream(stream)))
+
+
+def dsa_index_scores_backward_workspace_size(vl: Varlen, n_heads_idx: int, d_idx: int,
+                                             row_count: int, want_dq: bool = True,
+                                             want_dk: bool = True) -> int:
+    """Workspace bytes of a backward call over row_count rows."""
+    n = ctypes.c_size_t(0)
+    _check(load_library().dsa_index_scores_backward_workspace_size(
+        vl.struct, n_heads_idx, d_idx, row_count, int(want_dq), int(want_dk), ctypes.byref(n)))
+    return n.value
+
+
+def dsa_index_scores_backward(vl: Varlen, q_idx, k_idx, w, grad, workspace, dq_idx=None, dw=None,
+                              dk_idx=None, row_begin: int = 0, row_count: int | None = None,
+                              stream=None):
+    """Gradient of the indexer score for rows [row_begin, row_begin +
+    row_count) given grad = d loss / d scores (fp32 [row_count, ld]): writes
+    dq_idx (fp32 [row_count, H, d]) and dw (fp32 [row_count, H]) and adds the
+    window's share of dk_idx (fp32 [total_k, d]); either group may be None."""
+    torch = _torch()
+    _need(q_idx, "q_idx", torch.bfloat16, 3)
+    _need(k_idx, "k_idx", torch.bfloat16, 2)
+    _need(w, "w", torch.float32, 2)
+    _need(grad, "grad", torch.float32, 2)
+    _need(workspace, "workspace", torch.uint8, 1)
+    for t, name, nd in ((dq_idx, "dq_idx", 3), (dw, "dw", 2), (dk_idx, "dk_idx", 2)):
+        if t is not None:
+            _need(t, name, torch.float32, nd)
+    row_count = grad.shape[0] if row_count is None else row_count
+    _window(vl, row_begin, row_count)
+    h, d = q_idx.shape[1], q_idx.shape[2]
+    _shape(q_idx, "q_idx", (vl.total_q, h, d))
+    _shape(k_idx, "k_idx", (vl.total_k, d))
+    _shape(w, "w", (vl.total_q, h))
+    _rows(grad, "grad", row_count)
+    _score_cols(grad, "grad", vl)
+    if dq_idx is not None:
+        _extent(dq_idx.shape[0] >= row_count and tuple(dq_idx.shape[1:]) == (h, d),
+                f"dq_idx has shape {tuple(dq_idx.shape)}, expected ({row_count}, {h}, {d})")
+    if dw is not None:
+        _extent(dw.shape[0] >= row_count and dw.shape[1] == h,
+                f"dw has shape {tuple(dw.shape)}, expected ({row_count}, {h})")
+    if dk_idx is not None:
+        _shape(dk_idx, "dk_idx", (vl.total_k, d))
+    _on_device(q_idx=q_idx, k_idx=k_idx, w=w, grad=grad, workspace=workspace, dq_idx=dq_idx,
+               dw=dw, dk_idx=dk_idx)
+    _check(load_library().dsa_index_scores_backward(
+        vl.struct, _ptr(q_idx), _ptr(k_idx), _ptr(w), h, d, row_begin, row_count, _ptr(grad),
+        grad.stride(0), _ptr(dq_idx), _ptr(dw), _ptr(dk_idx), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
 
 
 def dsa_sparse_attn_decode_workspace_size(vl: Varlen, n_heads_q: int, head_dim: int,

@@ -34,6 +34,7 @@ COMMON_FLAGS = [
 FILE_FLAGS = {
     "index_scores.hip": ["-fno-honor-nans"],
     "index_scores_fp8.hip": ["-fno-honor-nans"],
+    "index_backward.hip": ["-fno-honor-nans"],
 }
 
 

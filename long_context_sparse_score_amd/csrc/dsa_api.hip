@@ -455,6 +455,61 @@ int dsa_indexer_kl(const dsa_varlen* vl, const void* q, const void* k, const flo
       "indexer_kl launch");
 }
 
+int dsa_index_scores_backward_workspace_size(const dsa_varlen* vl, int32_t n_heads_idx,
+                                             int32_t d_idx, int64_t row_count, int want_dq,
+                                             int want_dk, size_t* bytes) {
+  int st;
+  if ((st = check_varlen(vl))) return st;
+  if (bytes == nullptr) return fail(DSA_ERR_INVALID_ARGUMENT, "bytes pointer is NULL");
+  if (row_count < 0 || row_count > vl->total_q)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "row_count %lld outside [0, total_q]",
+                static_cast<long long>(row_count));
+  if ((st = check_index_shape(n_heads_idx, d_idx))) return st;
+  *bytes = dsa::index_backward_workspace_bytes(*vl, n_heads_idx, d_idx, row_count, want_dq != 0,
+                                               want_dk != 0);
+  return ok();
+}
+
+int dsa_index_scores_backward(const dsa_varlen* vl, const void* q_idx, const void* k_idx,
+                              const float* w, int32_t n_heads_idx, int32_t d_idx,
+                              int64_t row_begin, int64_t row_count, const float* grad,
+                              int64_t ld_grad, float* dq_idx, float* dw, float* dk_idx,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st;
+  if ((st = check_varlen(vl))) return st;
+  if ((st = check_window(vl, row_begin, row_count))) return st;
+  if ((st = check_bf16(q_idx, "q_idx"))) return st;
+  if ((st = check_bf16(k_idx, "k_idx"))) return st;
+  if (w == nullptr || !aligned(w, 4)) return fail(DSA_ERR_INVALID_ARGUMENT, "w is NULL or misaligned");
+  if (grad == nullptr || !aligned(grad, 4))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "grad is NULL or misaligned");
+  if (ld_grad < vl->max_seqlen_k)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "ld_grad (%lld) < max_seqlen_k (%d)",
+                static_cast<long long>(ld_grad), vl->max_seqlen_k);
+  if ((dq_idx == nullptr) != (dw == nullptr))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dq_idx and dw are given together or not at all");
+  if (dq_idx == nullptr && dk_idx == nullptr)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "no output requested (dq_idx, dw and dk_idx all NULL)");
+  if ((dq_idx != nullptr && !aligned(dq_idx, 4)) || (dw != nullptr && !aligned(dw, 4)) ||
+      (dk_idx != nullptr && !aligned(dk_idx, 4)))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dq_idx, dw or dk_idx misaligned");
+  if ((st = check_index_shape(n_heads_idx, d_idx))) return st;
+  if ((st = check_index_extent(vl, d_idx, 4))) return st;  // dk rows of one sequence in fp32
+  if (checks_enabled() && (st = device_offsets(vl, stream))) return st;
+  if (row_count == 0) return ok();
+  const size_t need = dsa::index_backward_workspace_bytes(*vl, n_heads_idx, d_idx, row_count,
+                                                          dq_idx != nullptr, dk_idx != nullptr);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
+    return fail(DSA_ERR_WORKSPACE,
+                "index backward workspace needs %zu bytes (256-byte aligned), got %zu", need,
+                workspace_bytes);
+  return hip_status(dsa::launch_index_backward(*vl, static_cast<const uint16_t*>(q_idx),
+                                               static_cast<const uint16_t*>(k_idx), w, n_heads_idx,
+                                               d_idx, row_begin, row_count, grad, ld_grad, dq_idx,
+                                               dw, dk_idx, workspace, stream),
+                    "index backward launch");
+}
+
 int dsa_sparse_attn_decode_workspace_size(const dsa_varlen* vl, int64_t row_count,
                                           int32_t n_heads_q, int32_t head_dim, int32_t topk,
                                           size_t* bytes) {

@@ -94,6 +94,19 @@ hipError_t launch_indexer_kl(const dsa_varlen& vl, const uint16_t* q, const uint
                              float scale, float* loss, float* grad, int64_t ld_grad,
                              hipStream_t stream);
 
+// Backward of the indexer score: dq and dw of the window's rows (written)
+// and their contribution to dk (added); any of the two outputs may be
+// skipped (dq and dw go together).  The workspace holds the transposed keys
+// (for dq) and the window's transposed, weighted queries (for dk).
+size_t index_backward_tiles_bytes(int64_t tiles, int d);
+size_t index_backward_workspace_bytes(const dsa_varlen& vl, int n_heads, int d, int64_t row_count,
+                                      bool want_dq, bool want_dk);
+hipError_t launch_index_backward(const dsa_varlen& vl, const uint16_t* q_idx,
+                                 const uint16_t* k_idx, const float* w, int n_heads, int d,
+                                 int64_t row_begin, int64_t row_count, const float* grad,
+                                 int64_t ld, float* dq, float* dw, float* dk, void* workspace,
+                                 hipStream_t stream);
+
 // Device-side precondition checks.  Each clears a report word, runs one
 // kernel on `stream`, waits for the stream and stores the first finding as
 // (item << 8) | code, or all ones when there is none.  The first call on a

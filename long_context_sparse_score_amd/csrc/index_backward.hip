@@ -1,0 +1,575 @@
+// index_backward.hip -- gradient of the indexer score with respect to the
+// indexer's queries, keys and head weights (gfx950).
+//
+// Keye-VL-2.0 report summary, page 5 section 1: in the dense warm-up only
+// the indexer is trained (its distribution pulled towards the full
+// attention's), so the loss's gradient must reach the indexer's own inputs.
+// With the score I[t, s] = sum_h w[t, h] relu(x[t, h, s]),
+// x = qI[t, h, :] . kI[s, :], and an upstream gradient G[t, s] = dL / dI
+// over s = 0..p(t), and taking the ReLU's derivative as 1 for x > 0 and 0
+// otherwise:
+//   dw[t, h]    = sum_s G[t, s] relu(x[t, h, s])
+//   dq[t, h, :] = w[t, h] sum_{s : x > 0} G[t, s] kI[s, :]
+//   dk[s, :]   += sum_t sum_{h : x > 0} G[t, s] w[t, h] qI[t, h, :]
+// Both gradients are small GEMMs around the recomputed head products x,
+// which are recomputed exactly as the forward kernels compute them (bf16
+// operands, fp32 MFMA accumulation, the same contraction order).
+//
+// The MQA shape makes dq 64 times larger than dk per position, so the two
+// are computed by two kernels, each keeping its own output in registers:
+//
+//  * dq / dw, one query row per wave, 4 rows per workgroup.  The row's
+//    queries are the stationary MFMA operand; stages of 128 keys stream
+//    through LDS by buffer->LDS DMA.  x is computed as a keys x heads tile,
+//    so each lane holds one head and 16 of the tile's keys: after the mask
+//    (x > 0) and the gradient are applied those registers already are the
+//    A operand of the dq GEMM (heads x keys), whose B operand, keys x d, is
+//    a pre-transposed copy of the keys.  dw is accumulated in fp32 on the
+//    VALU, dq in fp32 by MFMA and multiplied by w at the end.
+//  * dk, 64 keys per wave, 256 per workgroup.  The keys are the stationary
+//    operand; pairs of rows stream through LDS.  x is computed as a heads x
+//    keys tile (lane = key, registers = heads), which after the mask is the
+//    A operand of the dk GEMM (keys x heads); its B operand is a per-row
+//    transposed copy of the queries with w folded in (heads x d).  Every
+//    key block is owned by one workgroup, which adds its result to dk.
+//
+// A prep kernel writes the two transposed copies into the caller's
+// workspace, with the LDS bank swizzle part of the layout so that the DMA
+// is a straight copy.  The GEMM operands G (and G w q) are rounded to bf16.
+#include "dsa_common.h"
+#include "dsa_internal.h"
+#include "index_core.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kBwdWaves = 4;          // waves per workgroup (one per SIMD)
+constexpr int kBwdThreads = kBwdWaves * kWave;
+constexpr int kDqStageKeys = 128;     // keys per LDS stage of the dq kernel
+constexpr int kDkWaveKeys = 64;       // keys per wave of the dk kernel
+constexpr int kDkBlockKeys = kBwdWaves * kDkWaveKeys;
+constexpr int kDkStageRows = 2;       // rows per LDS stage of the dk kernel
+
+// Transposed key tiles.  Tile j of sequence b (its keys 32 j .. 32 j + 31)
+// is tile number cu_k[b] / 32 + b + j of the workspace: sequences never
+// share a tile, and the count stays below total_k / 32 + batch + 1.  A tile
+// is d_idx rows of 32 bf16 (4 chunks of 16 bytes); logical chunk c = 2 kk + h
+// of row d holds, as element e, key 16 kk + 8 (e / 4) + 4 h + e % 4 -- the
+// keys that lane half h feeds to k-step kk of the dq GEMM -- and is stored
+// at chunk c ^ ((d / 2) % 4), which spreads the 8 lanes of one LDS read
+// phase over distinct banks.
+__host__ __device__ __forceinline__ int64_t kt_tile(int32_t key_start, int b) {
+  return static_cast<int64_t>(key_start / 32) + b;
+}
+__host__ __device__ __forceinline__ int kt_phys(int c, int d) { return c ^ ((d >> 1) & 3); }
+
+// Transposed queries with the head weight folded in, one block per row:
+// d_idx rows of HP = 32 MT bf16 (heads padded with zeros); logical chunk
+// c = 2 kk + h of row d holds, as element e, head 16 kk + 8 (e / 4) + 4 h +
+// e % 4 times its weight, and is stored at chunk c ^ (d % 8) (HP = 64) or
+// c ^ ((d / 2) % 4) (HP = 32).
+template <int HP>
+__host__ __device__ __forceinline__ int qw_phys(int c, int d) {
+  return HP == 64 ? (c ^ (d & 7)) : (c ^ ((d >> 1) & 3));
+}
+
+__device__ __forceinline__ int slot_key(int c, int e) {  // element e of logical chunk c
+  return 16 * (c >> 1) + 8 * (e >> 2) + 4 * (c & 1) + (e & 3);
+}
+
+// Sequence b whose blocks cover index i, where sequence b's blocks start at
+// cu_k[b] / unit + b (strictly increasing in b).
+__device__ __forceinline__ int block_sequence(const int32_t* __restrict__ cu_k, int batch,
+                                             int64_t i, int unit) {
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (static_cast<int64_t>(cu_k[mid] / unit) + mid <= i) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------- prep
+
+// One workgroup per transposed key tile.
+template <int D>
+__global__ __launch_bounds__(256) void prep_key_tiles(const int32_t* __restrict__ cu_k, int batch,
+                                                      const uint16_t* __restrict__ k_idx,
+                                                      uint16_t* __restrict__ kt) {
+  __shared__ uint16_t tile[32 * D];
+  const int64_t i = blockIdx.x;
+  const int b = block_sequence(cu_k, batch, i, 32);
+  const int32_t k0 = cu_k[b], len = cu_k[b + 1] - k0;
+  const int32_t j = static_cast<int32_t>(i - kt_tile(k0, b));
+  if (j < 0 || 32 * j >= len) return;  // a gap between sequences: never read
+  const int32_t n = min(32, len - 32 * j);
+  constexpr int CH = D / 8;
+  for (int f = threadIdx.x; f < 32 * CH; f += blockDim.x) {
+    const int key = f / CH, s = f % CH;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (key < n) v = *reinterpret_cast<const uint4*>(k_idx + (k0 + 32 * j + key) * static_cast<int64_t>(D) + s * 8);
+    *reinterpret_cast<uint4*>(&tile[key * D + s * 8]) = v;
+  }
+  __syncthreads();
+  uint16_t* out = kt + i * (32 * D);
+  for (int f = threadIdx.x; f < D * 4; f += blockDim.x) {
+    const int d = f / 4, c = f % 4;
+    uint16_t e[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) e[x] = tile[slot_key(c, x) * D + d];
+    uint4 v;
+    v.x = e[0] | (static_cast<uint32_t>(e[1]) << 16);
+    v.y = e[2] | (static_cast<uint32_t>(e[3]) << 16);
+    v.z = e[4] | (static_cast<uint32_t>(e[5]) << 16);
+    v.w = e[6] | (static_cast<uint32_t>(e[7]) << 16);
+    *reinterpret_cast<uint4*>(out + d * 32 + kt_phys(c, d) * 8) = v;
+  }
+}
+
+// One workgroup per window row: bf16(w[t, h] * qI[t, h, d]), transposed.
+template <int D, int HP>
+__global__ __launch_bounds__(256) void prep_query_rows(const uint16_t* __restrict__ q_idx,
+                                                       const float* __restrict__ w, int n_heads,
+                                                       int64_t row_begin,
+                                                       uint16_t* __restrict__ qw) {
+  __shared__ float wq[HP];
+  __shared__ uint16_t q[HP * D];
+  const int64_t local = blockIdx.x, row = row_begin + local;
+  constexpr int CH = D / 8;
+  for (int f = threadIdx.x; f < HP * CH; f += blockDim.x) {
+    const int h = f / CH, s = f % CH;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (h < n_heads) v = *reinterpret_cast<const uint4*>(q_idx + (row * n_heads + h) * D + s * 8);
+    *reinterpret_cast<uint4*>(&q[h * D + s * 8]) = v;
+  }
+  for (int h = threadIdx.x; h < HP; h += blockDim.x) wq[h] = h < n_heads ? w[row * n_heads + h] : 0.0f;
+  __syncthreads();
+  constexpr int CPR = HP / 8;  // chunks per transposed row
+  uint16_t* out = qw + local * (static_cast<int64_t>(D) * HP);
+  for (int f = threadIdx.x; f < D * CPR; f += blockDim.x) {
+    const int d = f / CPR, c = f % CPR;
+    uint32_t e[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const int h = slot_key(c, x);
+      const float qv = __uint_as_float(static_cast<uint32_t>(q[h * D + d]) << 16);
+      e[x] = f32_to_bf16_bits(wq[h] * qv);
+    }
+    uint4 v;
+    v.x = e[0] | (e[1] << 16);
+    v.y = e[2] | (e[3] << 16);
+    v.z = e[4] | (e[5] << 16);
+    v.w = e[6] | (e[7] << 16);
+    *reinterpret_cast<uint4*>(out + d * HP + qw_phys<HP>(c, d) * 8) = v;
+  }
+}
+
+// Eight fp32 values as a bf16 MFMA operand (round to nearest even).
+__device__ __forceinline__ bf16x8 to_bf16x8(const float (&m)[8]) {
+  typedef float f32x8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 bf16v8 __attribute__((ext_vector_type(8)));
+  const f32x8 f = {m[0], m[1], m[2], m[3], m[4], m[5], m[6], m[7]};
+  return __builtin_bit_cast(bf16x8, __builtin_convertvector(f, bf16v8));
+}
+
+__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+// ---------------------------------------------------------------- dq / dw
+
+template <int D, int MT>
+__global__ __launch_bounds__(kBwdThreads, 1) void index_bwd_dq_kernel(
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
+    const uint16_t* __restrict__ q_idx, const uint16_t* k_idx, const uint16_t* kt,
+    const float* __restrict__ w, int n_heads, int64_t row_begin, int64_t row_count,
+    const float* grad, int64_t ld, float* __restrict__ dq, float* __restrict__ dw) {
+  constexpr int SK = kDqStageKeys, KS = D / 16, CH = D / 8, ND = D / 32, TILES = SK / 32;
+  constexpr int KPI = kBwdThreads / CH;  // keys per DMA instruction of the workgroup
+  constexpr int DMA_K = SK * CH / kBwdThreads;
+  static_assert(KPI % CH == 0 && DMA_K * kBwdThreads == SK * CH, "stage shape");
+  __shared__ __attribute__((aligned(16))) uint16_t ks_lds[2][SK * D];  // keys, swizzled rows
+  __shared__ __attribute__((aligned(16))) uint16_t kt_lds[2][SK * D];  // transposed tiles
+  __shared__ __attribute__((aligned(16))) float g_lds[2][kBwdWaves * SK];
+
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  const int col = lane & 31, half = lane >> 5;
+  const int64_t blk = static_cast<int64_t>(gridDim.x) - 1 - blockIdx.x;  // long rows first
+  const int64_t first = blk * kBwdWaves;
+  const int64_t last = min(first + kBwdWaves, row_count) - 1;
+  const int64_t local = first + wave;
+  const bool active = local < row_count;
+  const int64_t row = row_begin + (active ? local : last);
+  const int b_me = find_sequence(cu_q, batch, row);
+  const int b_lo = find_sequence(cu_q, batch, row_begin + first);
+  const int b_hi = find_sequence(cu_q, batch, row_begin + last);
+  const RowInfo ri = row_info(cu_q, cu_k, batch, row);
+
+  core::RowState<D, MT> st;
+  core::load_row_state<D, MT>(st, q_idx, w, row, n_heads, col, half);
+
+  f32x16 dqacc[MT][ND];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd) dqacc[mt][nd] = f32x16{};
+  float dwacc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) dwacc[mt] = 0.0f;
+
+  const int f = wave * kWave + lane;
+  const int key0 = f / CH, s0 = f % CH;
+  int buf = 0;
+  for (int b = b_lo; b <= b_hi; ++b) {
+    // Keys 0..pmax of sequence b, pmax the position of the block's last row in b.
+    const int32_t q0 = cu_q[b], q1 = cu_q[b + 1], kb = cu_k[b], lk = cu_k[b + 1] - kb;
+    if (q1 == q0) continue;  // no query rows (uniform: every wave skips it)
+    const int64_t last_in_b = min(row_begin + last, static_cast<int64_t>(q1) - 1);
+    const int32_t nkeys = lk - (q1 - q0) + static_cast<int32_t>(last_in_b - q0) + 1;
+    const bool mine = active && b_me == b;
+    const __amdgpu_buffer_rsrc_t rk = raw_buffer(k_idx + static_cast<int64_t>(kb) * D, nkeys * D * 2);
+    const __amdgpu_buffer_rsrc_t rt =
+        raw_buffer(kt + kt_tile(kb, b) * (32 * D), ((nkeys + 31) / 32) * D * 64);
+    const __amdgpu_buffer_rsrc_t rg = raw_buffer(grad + local * ld, mine ? (ri.pos + 1) * 4 : 0);
+    auto fill = [&](int bb, int32_t c) {
+#pragma unroll
+      for (int i = 0; i < DMA_K; ++i) {
+        const int key = c + i * KPI + key0;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rk, (__attribute__((address_space(3))) void*)(&ks_lds[bb][(i * kBwdWaves + wave) * kWave * 8]),
+            16, key * (D * 2) + ((s0 ^ (key0 & (CH - 1))) * 16), 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < DMA_K; ++i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rt, (__attribute__((address_space(3))) void*)(&kt_lds[bb][(i * kBwdWaves + wave) * kWave * 8]),
+            16, c * (D * 2) + (i * kBwdThreads + f) * 16, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < SK / kWave; ++i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rg, (__attribute__((address_space(3))) void*)(&g_lds[bb][wave * SK + i * kWave]), 4,
+            (c + i * kWave + lane) * 4, 0, 0, 0);
+      }
+    };
+    fill(buf, 0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    lds_barrier();
+    for (int32_t c = 0; c < nkeys; c += SK) {
+      if (c + SK < nkeys) fill(buf ^ 1, c + SK);
+      const uint16_t* kst = ks_lds[buf];
+      const uint16_t* ktt = kt_lds[buf];
+      const float* gst = g_lds[buf] + wave * SK;
+#pragma unroll
+      for (int tj = 0; tj < TILES; ++tj) {
+        // x as keys x heads: lane = head 32 mt + col, register v = key
+        // 8 (v / 4) + 4 half + v % 4 of the tile.
+        f32x16 x[MT];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int slot = (half * KS + ks) ^ (col & (CH - 1));
+          const bf16x8 a = lds_frag(&kst[(tj * 32 + col) * D + slot * 8]);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            x[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.a[mt][ks], ks == 0 ? f32x16{} : x[mt], 0, 0, 0);
+        }
+        float g[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 v = *reinterpret_cast<const float4*>(&gst[tj * 32 + 8 * i + 4 * half]);
+          g[4 * i] = v.x;
+          g[4 * i + 1] = v.y;
+          g[4 * i + 2] = v.z;
+          g[4 * i + 3] = v.w;
+        }
+        bf16x8 m[MT][2];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          float mv[16];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            dwacc[mt] += g[v] * fmaxf(x[mt][v], 0.0f);
+            mv[v] = x[mt][v] > 0.0f ? g[v] : 0.0f;
+          }
+          float lo[8], hi[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            lo[e] = mv[e];
+            hi[e] = mv[8 + e];
+          }
+          m[mt][0] = to_bf16x8(lo);
+          m[mt][1] = to_bf16x8(hi);
+        }
+#pragma unroll
+        for (int nd = 0; nd < ND; ++nd) {
+          const int d = nd * 32 + col;
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            const bf16x8 bfr = lds_frag(&ktt[tj * (32 * D) + d * 32 + kt_phys(2 * kk + half, d) * 8]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              dqacc[mt][nd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(m[mt][kk], bfr, dqacc[mt][nd], 0, 0, 0);
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      lds_barrier();
+      buf ^= 1;
+    }
+  }
+  if (!active) return;
+  // dq[t, h, d] = w[t, h] * acc: register v of tile (mt, nd) is head
+  // 32 mt + 8 (v / 4) + 4 half + v % 4, column d = 32 nd + col.
+  const __amdgpu_buffer_rsrc_t rq = raw_buffer(dq + local * n_heads * D, n_heads * D * 4);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int h = mt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(st.wv[mt][v] * dqacc[mt][nd][v]), rq,
+                                              (h * D + nd * 32 + col) * 4, 0, 0);
+      }
+  // dw: the two lane halves hold the same head's sums over different keys.
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const float other = __shfl_xor(dwacc[mt], 32);
+    const int h = mt * 32 + col;
+    if (half == 0 && h < n_heads) dw[local * n_heads + h] = dwacc[mt] + other;
+  }
+}
+
+// ---------------------------------------------------------------- dk
+
+template <int D, int MT>
+__global__ __launch_bounds__(kBwdThreads, 1) void index_bwd_dk_kernel(
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
+    const uint16_t* q_idx, const uint16_t* __restrict__ k_idx, const uint16_t* qw, int n_heads,
+    int64_t row_begin, int64_t row_count, const float* grad, int64_t ld, float* dk) {
+  constexpr int HP = 32 * MT, KS = D / 16, CH = D / 8, ND = D / 32, KT = kDkWaveKeys / 32;
+  constexpr int RS = kDkStageRows, KB = kDkBlockKeys, HALF = D / 2;
+  constexpr int QCH = RS * HP * CH;                  // 16-byte chunks of a stage's queries
+  constexpr int DMA_Q = QCH / kBwdThreads;
+  constexpr int DMA_W = RS * D * HP / 8 / kBwdThreads;  // chunks of a stage's transposed rows
+  static_assert(DMA_Q * kBwdThreads == QCH && DMA_W * kBwdThreads * 8 == RS * D * HP, "stage shape");
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[2][RS * HP * D];   // [row][head][chunk ^ head]
+  __shared__ __attribute__((aligned(16))) uint16_t w_lds[2][RS * D * HP];   // [row][d][phys chunk]
+  __shared__ __attribute__((aligned(16))) float g_lds[2][RS * KB];
+
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  const int col = lane & 31, half = lane >> 5;
+  const int64_t bi = blockIdx.x;
+  const int b = block_sequence(cu_k, batch, bi, KB);
+  const int32_t q0 = cu_q[b], q1 = cu_q[b + 1], kb = cu_k[b], lk = cu_k[b + 1] - kb;
+  const int32_t j = static_cast<int32_t>(bi - (kb / KB + b));
+  const int32_t key_lo = j * KB;
+  if (j < 0 || key_lo >= lk) return;
+  // Window rows of sequence b whose position reaches key_lo.
+  const int32_t shift = lk - (q1 - q0);  // position of local query i is shift + i
+  const int64_t r_lo = max(max(row_begin, static_cast<int64_t>(q0)),
+                           static_cast<int64_t>(q0) + key_lo - shift);
+  const int64_t r_hi = min(row_begin + row_count, static_cast<int64_t>(q1));
+  if (r_lo >= r_hi) return;
+
+  // This wave's keys as the stationary B operand of x (lane = key).
+  const int32_t wkey = key_lo + wave * kDkWaveKeys;
+  const __amdgpu_buffer_rsrc_t rk = raw_buffer(k_idx + static_cast<int64_t>(kb) * D, lk * D * 2);
+  bf16x8 kop[KT][KS];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int key = wkey + kt * 32 + col;
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rk, key * (D * 2) + (half * HALF + ks * 8) * 2, 0, 0);
+      kop[kt][ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  f32x16 acc[KT][ND];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd) acc[kt][nd] = f32x16{};
+
+  const int f = wave * kWave + lane;
+  // Stage resources start at the stage's first row, so offsets stay small
+  // whatever the window size; rows past the window read as zeros.
+  auto fill = [&](int bb, int64_t r0) {
+    const int64_t l0 = r0 - row_begin;  // window-local first row of the stage
+    const int nrows = static_cast<int>(min(static_cast<int64_t>(RS), row_count - l0));
+    const __amdgpu_buffer_rsrc_t rq = raw_buffer(q_idx + r0 * n_heads * D, nrows * n_heads * D * 2);
+    const __amdgpu_buffer_rsrc_t rw = raw_buffer(qw + l0 * D * HP, nrows * D * HP * 2);
+#pragma unroll
+    for (int i = 0; i < DMA_Q; ++i) {
+      const int c = i * kBwdThreads + f;          // chunk of the stage
+      const int r = c / (HP * CH), h = (c / CH) % HP, s = c % CH;
+      const int src = (r * n_heads + h) * D * 2 + ((s ^ (h & (CH - 1))) * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rq, (__attribute__((address_space(3))) void*)(&q_lds[bb][(i * kBwdWaves + wave) * kWave * 8]),
+          16, src, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < DMA_W; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rw, (__attribute__((address_space(3))) void*)(&w_lds[bb][(i * kBwdWaves + wave) * kWave * 8]),
+          16, (i * kBwdThreads + f) * 16, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < RS; ++r) {
+      const int64_t row = r0 + r;
+      const int32_t p = shift + static_cast<int32_t>(row - q0);
+      const __amdgpu_buffer_rsrc_t rg =
+          raw_buffer(grad + (row - row_begin) * ld, row < r_hi ? (p + 1) * 4 : 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rg, (__attribute__((address_space(3))) void*)(&g_lds[bb][r * KB + wave * kWave]), 4,
+          (key_lo + f) * 4, 0, 0, 0);
+    }
+  };
+
+  int buf = 0;
+  fill(buf, r_lo);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  lds_barrier();
+  for (int64_t r0 = r_lo; r0 < r_hi; r0 += RS) {
+    if (r0 + RS < r_hi) fill(buf ^ 1, r0 + RS);
+#pragma unroll
+    for (int r = 0; r < RS; ++r) {
+      const uint16_t* qs = q_lds[buf] + r * HP * D;
+      const uint16_t* ws = w_lds[buf] + r * D * HP;
+      // x as heads x keys: lane = key (tile kt), register v = head
+      // 32 mt + 8 (v / 4) + 4 half + v % 4.
+      f32x16 x[KT][MT];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int h = mt * 32 + col;
+          const bf16x8 a = lds_frag(&qs[h * D + (((half * KS + ks) ^ (h & (CH - 1))) * 8)]);
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+            x[kt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kop[kt][ks], ks == 0 ? f32x16{} : x[kt][mt], 0, 0, 0);
+        }
+      // The mask times the gradient, as the A operand (keys x heads): k-step
+      // kk = 2 mt + v / 8 holds heads 16 kk + 8 (e / 4) + 4 half + e % 4.
+      bf16x8 m[KT][2 * MT];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const float g = g_lds[buf][r * KB + wave * kDkWaveKeys + kt * 32 + col];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          float lo[8], hi[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            lo[e] = x[kt][mt][e] > 0.0f ? g : 0.0f;
+            hi[e] = x[kt][mt][8 + e] > 0.0f ? g : 0.0f;
+          }
+          m[kt][2 * mt] = to_bf16x8(lo);
+          m[kt][2 * mt + 1] = to_bf16x8(hi);
+        }
+      }
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) {
+        const int d = nd * 32 + col;
+#pragma unroll
+        for (int kk = 0; kk < 2 * MT; ++kk) {
+          const bf16x8 bfr = lds_frag(&ws[d * HP + qw_phys<HP>(2 * kk + half, d) * 8]);
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+            acc[kt][nd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(m[kt][kk], bfr, acc[kt][nd], 0, 0, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    lds_barrier();
+    buf ^= 1;
+  }
+  // dk[key, d] += acc: register v of tile (kt, nd) is key
+  // kt * 32 + 8 (v / 4) + 4 half + v % 4 of this wave, column d = 32 nd + col.
+  const __amdgpu_buffer_rsrc_t ro = raw_buffer(dk + static_cast<int64_t>(kb) * D, lk * D * 4);
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd) {
+      float old[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = wkey + kt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+        old[v] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, (key * D + nd * 32 + col) * 4, 0, 0));
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = wkey + kt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(old[v] + acc[kt][nd][v]), ro,
+                                              (key * D + nd * 32 + col) * 4, 0, 0);
+      }
+    }
+}
+
+template <int D, int MT>
+hipError_t launch_backward(const dsa_varlen& vl, const uint16_t* q_idx, const uint16_t* k_idx,
+                           const float* w, int n_heads, int64_t row_begin, int64_t row_count,
+                           const float* grad, int64_t ld, float* dq, float* dw, float* dk,
+                           uint8_t* ws, hipStream_t stream) {
+  constexpr int HP = 32 * MT;
+  uint8_t* p = ws;
+  if (dq != nullptr) {
+    const int64_t tiles = vl.total_k / 32 + vl.batch + 1;
+    uint16_t* kt = reinterpret_cast<uint16_t*>(p);
+    p += index_backward_tiles_bytes(tiles, D);
+    hipLaunchKernelGGL((prep_key_tiles<D>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0,
+                       stream, vl.cu_seqlens_k, vl.batch, k_idx, kt);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    const unsigned blocks = static_cast<unsigned>((row_count + kBwdWaves - 1) / kBwdWaves);
+    hipLaunchKernelGGL((index_bwd_dq_kernel<D, MT>), dim3(blocks), dim3(kBwdThreads), 0, stream,
+                       vl.cu_seqlens_q, vl.cu_seqlens_k, vl.batch, q_idx, k_idx, kt, w, n_heads,
+                       row_begin, row_count, grad, ld, dq, dw);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
+  if (dk != nullptr) {
+    uint16_t* qw = reinterpret_cast<uint16_t*>(p);
+    hipLaunchKernelGGL((prep_query_rows<D, HP>), dim3(static_cast<unsigned>(row_count)), dim3(256),
+                       0, stream, q_idx, w, n_heads, row_begin, qw);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    const int64_t blocks = vl.total_k / kDkBlockKeys + vl.batch + 1;
+    hipLaunchKernelGGL((index_bwd_dk_kernel<D, MT>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kBwdThreads), 0, stream, vl.cu_seqlens_q, vl.cu_seqlens_k, vl.batch,
+                       q_idx, k_idx, qw, n_heads, row_begin, row_count, grad, ld, dk);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+size_t index_backward_tiles_bytes(int64_t tiles, int d) {
+  return (static_cast<size_t>(tiles) * 32 * d * 2 + 255) / 256 * 256;
+}
+
+size_t index_backward_workspace_bytes(const dsa_varlen& vl, int n_heads, int d, int64_t row_count,
+                                      bool want_dq, bool want_dk) {
+  size_t bytes = 0;
+  if (want_dq) bytes += index_backward_tiles_bytes(vl.total_k / 32 + vl.batch + 1, d);
+  if (want_dk) {
+    const int hp = n_heads <= 32 ? 32 : 64;
+    bytes += static_cast<size_t>(row_count) * d * hp * 2;
+  }
+  return bytes;
+}
+
+hipError_t launch_index_backward(const dsa_varlen& vl, const uint16_t* q_idx,
+                                 const uint16_t* k_idx, const float* w, int n_heads, int d,
+                                 int64_t row_begin, int64_t row_count, const float* grad,
+                                 int64_t ld, float* dq, float* dw, float* dk, void* workspace,
+                                 hipStream_t stream) {
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const bool wide = n_heads > 32;
+  if (d == 128)
+    return wide ? launch_backward<128, 2>(vl, q_idx, k_idx, w, n_heads, row_begin, row_count, grad, ld, dq, dw, dk, ws, stream)
+                : launch_backward<128, 1>(vl, q_idx, k_idx, w, n_heads, row_begin, row_count, grad, ld, dq, dw, dk, ws, stream);
+  return wide ? launch_backward<64, 2>(vl, q_idx, k_idx, w, n_heads, row_begin, row_count, grad, ld, dq, dw, dk, ws, stream)
+              : launch_backward<64, 1>(vl, q_idx, k_idx, w, n_heads, row_begin, row_count, grad, ld, dq, dw, dk, ws, stream);
+}
+
+}  // namespace dsa

@@ -12,8 +12,9 @@ from __future__ import annotations
 
 from dataclasses import dataclass
 
-from . import (Varlen, dsa_index_scores, dsa_index_scores_fp8, dsa_index_topk,
-               dsa_index_topk_workspace_size, dsa_quantize_fp8,
+from . import (Varlen, dsa_index_scores, dsa_index_scores_backward,
+               dsa_index_scores_backward_workspace_size, dsa_index_scores_fp8, dsa_index_topk,
+               dsa_index_topk_workspace_size, dsa_indexer_kl, dsa_quantize_fp8,
                dsa_sparse_attn_decode, dsa_sparse_attn_decode_workspace_size,
                dsa_sparse_attn_prefill, dsa_sparse_attn_prefill_grouped,
                dsa_sparse_attn_prefill_grouped_workspace_size, dsa_topk,
@@ -286,3 +287,70 @@ def decode(vl: Varlen, q_idx, k_idx_cache, w, q, k_cache, v_cache, out, bufs: De
                                row_begin=r0, row_count=n, stream=st)
     if len(streams) > 1:
         main.wait_stream(side_stream)
+
+
+# ---------------------------------------------------------------- warm-up
+
+# Query rows per window of the warm-up step: the KL kernel serves 16 rows per
+# workgroup, so 8192 rows fill 512 workgroups (two per CU).
+WARMUP_WINDOW = 8192
+
+
+@dataclass
+class WarmupBuffers:
+    scores: object     # fp32 [window, ld]: a window's scores, then d loss / d scores over them
+    workspace: object  # uint8: dsa_index_scores_backward's workspace for a full window
+    window: int
+
+
+def alloc_warmup(vl: Varlen, n_heads_idx: int, d_idx: int, window: int = WARMUP_WINDOW,
+                 device="cuda") -> WarmupBuffers:
+    torch = _torch()
+    window = max(1, min(window, vl.total_q))
+    scores = torch.empty((window, score_ld(vl.max_seqlen_k)), dtype=torch.float32, device=device)
+    ws = torch.empty(max(1, dsa_index_scores_backward_workspace_size(vl, n_heads_idx, d_idx,
+                                                                     window)),
+                     dtype=torch.uint8, device=device)
+    return WarmupBuffers(scores, ws, window)
+
+
+def warmup(vl: Varlen, q_idx, k_idx, w, q, k, loss, dq_idx, dw, dk_idx, bufs: WarmupBuffers,
+           softmax_scale=None, stream=None, record=None):
+    """The indexer's step of the dense warm-up (page 5 section 1: the rest of
+    the model frozen, the indexer trained so that its distribution over
+    positions approaches the full attention's, measured by KL divergence).
+    Per window of query rows: the indexer scores, the KL loss per row with
+    its gradient written over the scores, then that gradient carried into
+    the indexer's inputs.  loss (fp32 [total_q]), dq_idx (fp32 [total_q, H,
+    d]) and dw (fp32 [total_q, H]) are written; dk_idx (fp32 [total_k, d]) is
+    zeroed and then summed over the windows.  `record`, a list, receives
+    (row_begin, rows, events) per window with (start, end) event pairs
+    "index_scores", "indexer_kl" and "backward"."""
+    torch = _torch()
+    main = torch.cuda.current_stream() if stream is None else stream
+
+    def mark():
+        if record is None:
+            return None
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(main)
+        return e
+
+    with torch.cuda.stream(main):
+        dk_idx.zero_()
+    for r0 in range(0, vl.total_q, bufs.window):
+        n = min(bufs.window, vl.total_q - r0)
+        sc = bufs.scores[:n]
+        e0 = mark()
+        dsa_index_scores(vl, q_idx, k_idx, w, sc, row_begin=r0, row_count=n, stream=main)
+        e1 = mark()
+        dsa_indexer_kl(vl, q, k, sc, loss[r0:r0 + n], grad=sc, softmax_scale=softmax_scale,
+                       row_begin=r0, row_count=n, stream=main)
+        e2 = mark()
+        dsa_index_scores_backward(vl, q_idx, k_idx, w, sc, bufs.workspace,
+                                  dq_idx=dq_idx[r0:r0 + n], dw=dw[r0:r0 + n], dk_idx=dk_idx,
+                                  row_begin=r0, row_count=n, stream=main)
+        e3 = mark()
+        if record is not None:
+            record.append((r0, n, {"index_scores": (e0, e1), "indexer_kl": (e1, e2),
+                                   "backward": (e2, e3)}))

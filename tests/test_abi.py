@@ -479,3 +479,66 @@ def test_index_topk_validation():
     assert call(ws=None) == W
     assert call(wsb=small - 1) == W
     assert call(ws=FAKE + 16) == W  # not 256-byte aligned
+
+
+def test_index_backward_validation():
+    """dsa_index_scores_backward rejects bad arguments, a missing or small
+    workspace and unsupported shapes on the host; the workspace covers only
+    the outputs asked for."""
+    lib = dsa.load_library()
+    I, U, W = dsa.DSA_ERR_INVALID_ARGUMENT, dsa.DSA_ERR_UNSUPPORTED, dsa.DSA_ERR_WORKSPACE
+    v = vl(total_q=100, total_k=100, max_q=100, max_k=100)
+    n = ctypes.c_size_t(0)
+
+    def size(rows=10, dq=1, dk=1, heads=64, d=128):
+        assert lib.dsa_index_scores_backward_workspace_size(ctypes.byref(v), heads, d, rows, dq,
+                                                            dk, ctypes.byref(n)) == 0
+        return n.value
+    both, only_dq, only_dk = size(), size(dk=0), size(dq=0)
+    assert both == only_dq + only_dk and only_dq > 0 and only_dk > 0
+    assert size(rows=20, dq=0) == 2 * only_dk
+    assert lib.dsa_index_scores_backward_workspace_size(ctypes.byref(v), 65, 128, 10, 1, 1,
+                                                        ctypes.byref(n)) == U
+    assert lib.dsa_index_scores_backward_workspace_size(ctypes.byref(v), 64, 128, 101, 1, 1,
+                                                        ctypes.byref(n)) == I
+
+    def call(q=FAKE, grad=FAKE, ld=128, dq=FAKE, dw=FAKE, dk=FAKE, rc=10, ws=FAKE, wsb=1 << 40,
+             heads=64, d=128):
+        return lib.dsa_index_scores_backward(ctypes.byref(v), q, FAKE, FAKE, heads, d, 0, rc, grad,
+                                             ld, dq, dw, dk, ws, wsb, None)
+
+    assert call(rc=0) == dsa.DSA_OK
+    assert call(q=None) == I and call(q=FAKE + 2) == I
+    assert call(grad=None) == I and call(grad=FAKE + 2) == I
+    assert call(ld=99) == I                                      # < max_seqlen_k
+    assert call(dw=None) == I and call(dq=None) == I             # one without the other
+    assert call(dq=None, dw=None, dk=None) == I                  # nothing to compute
+    assert call(dk=FAKE + 2) == I
+    assert call(d=96) == U and call(heads=65) == U and call(heads=0) == U
+    assert call(ws=None) == W
+    assert call(wsb=both - 1) == W
+    assert call(dk=None, wsb=only_dq) != W                       # only what is asked for
+    assert call(ws=FAKE + 16) == W                               # not 256-byte aligned
+
+
+def test_binding_backward_extents():
+    v = _cpu_varlen()
+    q, k, w, g = _bf(100, 64, 128), _bf(100, 128), _f32(100, 64), _f32(100, 100)
+    ws = torch_u8(64)
+    _expect(lambda: dsa.dsa_index_scores_backward(v, q, k, w, _f32(100, 59), ws, dk_idx=_f32(100, 128)))
+    _expect(lambda: dsa.dsa_index_scores_backward(v, q, k, w, g, ws, dk_idx=_f32(99, 128)))
+    _expect(lambda: dsa.dsa_index_scores_backward(v, q, k, w, g, ws, dq_idx=_f32(100, 64, 64),
+                                                  dw=_f32(100, 64)))
+    _expect(lambda: dsa.dsa_index_scores_backward(v, q, k, w, g, ws, dq_idx=_f32(100, 64, 128),
+                                                  dw=_f32(100, 32)))
+    _expect(lambda: dsa.dsa_index_scores_backward(v, q, k, w, g[:50], ws, dk_idx=_f32(100, 128),
+                                                  row_count=100))
+    # shapes right: only the device check is left
+    _expect(lambda: dsa.dsa_index_scores_backward(v, q, k, w, g, ws, dk_idx=_f32(100, 128)),
+            TypeError)
+
+
+def torch_u8(n):
+    import torch
+
+    return torch.zeros(n, dtype=torch.uint8)

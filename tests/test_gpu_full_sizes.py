@@ -303,3 +303,82 @@ def test_fused_decode_b64_128k():
     torch.cuda.synchronize()
     assert torch.equal(res[0][0], res[1][0])
     assert torch.equal(res[0][1].view(torch.int16), res[1][1].view(torch.int16))
+
+
+def test_backward_128k_last_warmup_window():
+    """The indexer backward on the 128K prefill's last warm-up window (the
+    longest rows, 8192 of them, in the launch shape the warm-up step uses),
+    with a rank-one upstream gradient G[t, s] = a[t] b[s] of bf16-exact
+    factors (every product exact in fp32, so host and device hold the same
+    G).  dq and dw on sampled rows, dk on sampled keys (summed over the
+    window's rows), each within the derived bound of the module
+    test_gpu_backward (bf16 GEMM operands, fp32 accumulation, ReLU-mask
+    decisions near x = 0)."""
+    wl = synth.prefill_128k()
+    host, dev = device_workload(wl, ("q_idx", "k_idx", "w"))
+    vl = dsa.Varlen(wl.cu_q.tolist(), wl.cu_k.tolist())
+    L, H, D = wl.total_q, wl.n_heads_idx, wl.d_idx
+    W = pipeline.WARMUP_WINDOW
+    r0 = L - W
+    ld = pipeline.score_ld(vl.max_seqlen_k)
+    rng = np.random.default_rng(12)
+    bf = lambda x: synth.bf16_to_float(synth.bf16_bits_from_float(x)).astype(np.float32)  # noqa: E731
+    a = bf(rng.normal(0, 1, W))
+    b = bf(rng.normal(0, 2.0 ** -8, ld))
+    g_dev = torch.outer(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda())
+    ws = torch.empty(dsa.dsa_index_scores_backward_workspace_size(vl, H, D, W), dtype=torch.uint8,
+                     device="cuda")
+    dq = torch.empty((W, H, D), dtype=torch.float32, device="cuda")
+    dw = torch.empty((W, H), dtype=torch.float32, device="cuda")
+    dk = torch.zeros((L, D), dtype=torch.float32, device="cuda")
+    dsa.dsa_index_scores_backward(vl, dev["q_idx"], dev["k_idx"], dev["w"], g_dev, ws, dq_idx=dq,
+                                  dw=dw, dk_idx=dk, row_begin=r0, row_count=W)
+    torch.cuda.synchronize()
+    del g_dev
+    qf = synth.bf16_to_float(host["q_idx"][r0:]).astype(np.float64)   # [W, H, D]
+    kf = synth.bf16_to_float(host["k_idx"]).astype(np.float64)        # [L, D]
+    wv = host["w"][r0:].astype(np.float64)
+    pos = r0 + np.arange(W)
+
+    # dq, dw on sampled rows
+    loc = np.unique(np.concatenate([[0, 1, 2, 3, W // 2, W - 4, W - 3, W - 2, W - 1],
+                                    rng.integers(0, W, 7)]))
+    g_rows = (a[loc][:, None] * b[None, :]).astype(np.float64)
+    rq, rw, _ = oracle.index_scores_backward(wl.cu_q, wl.cu_k, host["q_idx"][r0 + loc],
+                                             host["k_idx"], host["w"], g_rows, r0 + loc)
+    got_q, got_w = dq[torch.from_numpy(loc).cuda()].cpu().numpy(), dw.cpu().numpy()[loc]
+    for i, t in enumerate(loc):
+        p = pos[t]
+        keys = kf[:p + 1]
+        gt = np.abs(g_rows[i, :p + 1])
+        x = qf[t] @ keys.T
+        xabs = np.abs(qf[t]) @ np.abs(keys).T
+        near = np.abs(x) <= 2.0 ** -17 * xabs
+        tq = np.abs(wv[t])[:, None] * (2.0 ** -8 * (gt @ np.abs(keys))[None, :]
+                                       + (near * gt[None, :]) @ np.abs(keys))
+        tw = 2.0 ** -12 * (np.abs(x) @ gt) + 2.0 ** -17 * (xabs @ gt)
+        eq = np.abs(got_q[i] - rq[i])
+        ew = np.abs(got_w[i] - rw[i])
+        assert (eq <= tq + 1e-30).all(), f"dq row {r0 + t}: max err/bound {np.max(eq / (tq + 1e-30))}"
+        assert (ew <= tw + 1e-30).all(), f"dw row {r0 + t}: max err/bound {np.max(ew / (tw + 1e-30))}"
+    log(f"  dq/dw: {len(loc)} rows within the bound")
+
+    # dk on sampled keys, over every row of the window
+    keys = np.unique(np.array([0, 1, 31, 32, 255, 256, 65535, r0 - 1, r0, r0 + 1, L - 2, L - 1]))
+    seen = pos[:, None] >= keys[None, :]                                   # [W, n_keys]
+    grad_at = np.where(seen, a[:, None].astype(np.float64) * b[keys][None, :], 0.0)
+    rk = oracle.index_scores_backward_keys(wl.cu_q, wl.cu_k, host["q_idx"][r0:], host["k_idx"],
+                                           host["w"], grad_at, r0 + np.arange(W), keys)
+    got_k = dk[torch.from_numpy(keys).cuda()].cpu().numpy()
+    wq = np.abs(wv)[:, :, None] * np.abs(qf)                               # [W, H, D]
+    wq_sum = wq.sum(1)
+    for c, s in enumerate(keys):
+        x = qf @ kf[s]                                                     # [W, H]
+        xabs = np.abs(qf) @ np.abs(kf[s])
+        near = np.abs(x) <= 2.0 ** -17 * xabs
+        gabs = np.abs(grad_at[:, c])[:, None]                              # [W, 1]
+        tk = 2.0 ** -7 * np.einsum("t,tj->j", gabs[:, 0], wq_sum) \
+            + np.einsum("th,thj->j", near * gabs, wq)
+        ek = np.abs(got_k[c] - rk[c])
+        assert (ek <= tk + 1e-30).all(), f"dk key {s}: max err/bound {np.max(ek / (tk + 1e-30))}"
+    log(f"  dk: {len(keys)} keys within the bound")
