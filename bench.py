@@ -456,6 +456,15 @@ def main():
                                        / (d_idx_ms / 1e3) / 1e9, 1),
         }
 
+    att = attainable_peaks(torch, stream)
+    result["attainable"] = att
+    result["roofline"]["attainable_peak"] = att["mfma_bf16_tflops"]
+    result["roofline"]["frac_of_attainable"] = round(idx_tflops / att["mfma_bf16_tflops"], 4)
+    if "decode" in result:
+        r = result["decode"]["roofline"]
+        r["attainable_peak"] = att["read_GBps"]
+        r["frac_of_attainable"] = round(r["achieved"] / att["read_GBps"], 4)
+
     if args.calib_copy:
         # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counter readings
         # calibrate the same counters taken on the DSA kernels.
@@ -871,6 +880,72 @@ def grouped_variant(torch, dsa, pipeline, args, stream, wl, vl, P, out, lse, iid
     del qc
     torch.cuda.empty_cache()
     return res
+
+
+def attainable_peaks(torch, stream):
+    """Measured ceilings beside the published peaks: a loop of back-to-back
+    bf16 MFMAs on every SIMD (libdsa_calib.so, outside the C ABI; no loads)
+    and a plain device-to-device copy.  Under full matrix-core load the chip
+    holds an engine clock below the boost clock the published MFMA peak
+    assumes, so a kernel's fraction of the attainable figure says how much
+    of the achievable throughput it gets."""
+    import ctypes
+
+    from long_context_sparse_score_amd import build_lib
+    lib = ctypes.CDLL(build_lib.CALIB_PATH)
+    lib.dsa_calib_mfma_bf16.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    lib.dsa_calib_mfma_bf16.restype = ctypes.c_int
+    lib.dsa_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    lib.dsa_calib_read.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = cus * 4, 40000            # four 256-thread workgroups per CU
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    assert lib.dsa_calib_mfma_bf16(iters // 4, blocks, out.data_ptr(), stream.cuda_stream) == 0
+    a, b = ev(), ev()
+    a.record(stream)
+    assert lib.dsa_calib_mfma_bf16(iters, blocks, out.data_ptr(), stream.cuda_stream) == 0
+    b.record(stream)
+    torch.cuda.synchronize()
+    mfma_tflops = blocks * 4 * iters * 16 * 32768 / (a.elapsed_time(b) / 1e3) / 1e12
+    src = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    a.record(stream)
+    for _ in range(3):
+        dst.copy_(src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 3 * 2 * src.numel() / (a.elapsed_time(b) / 1e3) / 1e9
+    del dst
+    read = {}
+    sink = torch.empty(cus * 16 * 256, dtype=torch.int32, device="cuda")  # one word per thread
+    for per_cu in (4, 8, 16):
+        nb = cus * per_cu
+        assert nb * 256 <= sink.numel()
+        assert lib.dsa_calib_read(src.data_ptr(), src.numel(), nb, sink.data_ptr(),
+                                  stream.cuda_stream) == 0
+        a.record(stream)
+        for _ in range(3):
+            lib.dsa_calib_read(src.data_ptr(), src.numel(), nb, sink.data_ptr(), stream.cuda_stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        read[per_cu] = 3 * src.numel() / (a.elapsed_time(b) / 1e3) / 1e9
+    read_gbs = max(read.values())
+    del src, sink
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_tflops": round(mfma_tflops, 1),
+            "mfma_frac_of_published": round(mfma_tflops / PEAK_BF16_TFLOPS, 4),
+            "copy_GBps": round(copy_gbs, 1),
+            "copy_frac_of_published": round(copy_gbs / PEAK_HBM_GBS, 4),
+            "read_GBps": round(read_gbs, 1),
+            "read_frac_of_published": round(read_gbs / PEAK_HBM_GBS, 4),
+            "how": "bf16 MFMA: back-to-back v_mfma_f32_32x32x16_bf16, 4 waves per SIMD, "
+                   "4 independent accumulators; copy: 4 GiB device-to-device, bytes read + written; "
+                   "read: 4 GiB streamed by 16-byte loads (best of 4, 8, 16 workgroups per CU)"}
 
 
 def device_info(torch):

@@ -312,9 +312,10 @@ int dsa_indexer_kl(const dsa_varlen* vl, const void* q, const void* k, const flo
  *           transposed keys (dq) and the window's weighted, transposed
  *           queries (dk) and is free again when the call's work is done.
  * Arithmetic: x recomputed as dsa_index_scores computes it (bf16 MFMA, fp32
- * accumulation); dw summed in fp32; the dq and dk products take G [x > 0]
- * and, for dk, w q_idx rounded to bf16 (nearest even) as MFMA operands with
- * fp32 accumulation.
+ * accumulation); the dq and dk products take G [x > 0] and, for dk,
+ * w q_idx rounded to bf16 (nearest even) as MFMA operands with fp32
+ * accumulation; dw is q_idx[t,h,:] dotted (fp32) with the dq sum before the
+ * weight, which equals sum_s G relu(x) since relu(x) = [x > 0] x.
  * Supported: as dsa_index_scores, and one sequence's dk_idx rows within
  * 2 GiB (max_seqlen_k * d_idx * 4 < 2^31).
  * Invalid: null inputs, misaligned pointers (bf16 inputs 16-byte, fp32

@@ -18,6 +18,8 @@ ROOT = os.path.dirname(_HERE)
 CSRC = os.path.join(_HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(_HERE, "libdsa.so")
+CALIB_DIR = os.path.join(_HERE, "calib")
+CALIB_PATH = os.path.join(_HERE, "libdsa_calib.so")  # bench-only calibration kernels
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -70,6 +72,16 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB_PATH)
+    # The bench's calibration kernels: their own library, outside the C ABI.
+    calib = sorted(glob.glob(os.path.join(CALIB_DIR, "*.hip")))
+    tmp = CALIB_PATH + ".tmp"
+    cmd = [HIPCC, *COMMON_FLAGS, "-shared", "-o", tmp, *calib]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on the calibration kernels:\n{r.stderr}")
+    os.replace(tmp, CALIB_PATH)
     return LIB_PATH
 
 

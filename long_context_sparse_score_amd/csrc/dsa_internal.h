@@ -99,6 +99,7 @@ hipError_t launch_indexer_kl(const dsa_varlen& vl, const uint16_t* q, const uint
 // skipped (dq and dw go together).  The workspace holds the transposed keys
 // (for dq) and the window's transposed, weighted queries (for dk).
 size_t index_backward_tiles_bytes(int64_t tiles, int d);
+size_t index_backward_rows_bytes(int64_t row_count, int d, int hp);
 size_t index_backward_workspace_bytes(const dsa_varlen& vl, int n_heads, int d, int64_t row_count,
                                       bool want_dq, bool want_dk);
 hipError_t launch_index_backward(const dsa_varlen& vl, const uint16_t* q_idx,

@@ -34,11 +34,12 @@ struct RowState {
   float wv[MT][16];
 };
 
+// The row's queries as the MFMA operand: heads on the rows (lane = head),
+// eight consecutive d_idx values per lane half and k-step.
 template <int D, int MT>
-__device__ __forceinline__ void load_row_state(RowState<D, MT>& st,
-                                               const uint16_t* __restrict__ q_idx,
-                                               const float* __restrict__ w, int64_t row,
-                                               int n_heads, int col, int half) {
+__device__ __forceinline__ void load_row_queries(bf16x8 (&a)[MT][D / 16],
+                                                 const uint16_t* __restrict__ q_idx, int64_t row,
+                                                 int n_heads, int col, int half) {
   constexpr int KS = D / 16, HALF = D / 2;
   // Loads are issued for clamped heads and zeroed afterwards: a load under
   // a lane-dependent branch becomes its own basic block, and the loads would
@@ -50,16 +51,33 @@ __device__ __forceinline__ void load_row_state(RowState<D, MT>& st,
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 x = load_bf16x8(q_idx + (row * n_heads + hl) * D + half * HALF + ks * 8);
-      st.a[mt][ks] = h < n_heads ? x : zero_bf16x8();
+      a[mt][ks] = h < n_heads ? x : zero_bf16x8();
     }
-    // Accumulator element v of this lane is MFMA row 8*(v/4) + 4*half + v%4.
+  }
+}
+
+// The row's head weights laid out like the accumulator rows: element v of
+// this lane is head 32 mt + 8 (v / 4) + 4 half + v % 4 (0 past n_heads).
+template <int MT>
+__device__ __forceinline__ void load_row_weights(float (&wv)[MT][16], const float* __restrict__ w,
+                                                 int64_t row, int n_heads, int half) {
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int hr = mt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
       const float x = w[row * n_heads + min(hr, n_heads - 1)];
-      st.wv[mt][v] = hr < n_heads ? x : 0.0f;
+      wv[mt][v] = hr < n_heads ? x : 0.0f;
     }
-  }
+}
+
+template <int D, int MT>
+__device__ __forceinline__ void load_row_state(RowState<D, MT>& st,
+                                               const uint16_t* __restrict__ q_idx,
+                                               const float* __restrict__ w, int64_t row,
+                                               int n_heads, int col, int half) {
+  load_row_queries<D, MT>(st.a, q_idx, row, n_heads, col, half);
+  load_row_weights<MT>(st.wv, w, row, n_heads, half);
 }
 
 // Head products of one 32-key tile.

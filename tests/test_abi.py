@@ -496,7 +496,7 @@ def test_index_backward_validation():
         return n.value
     both, only_dq, only_dk = size(), size(dk=0), size(dq=0)
     assert both == only_dq + only_dk and only_dq > 0 and only_dk > 0
-    assert size(rows=20, dq=0) == 2 * only_dk
+    assert size(rows=20, dq=0) > only_dk
     assert lib.dsa_index_scores_backward_workspace_size(ctypes.byref(v), 65, 128, 10, 1, 1,
                                                         ctypes.byref(n)) == U
     assert lib.dsa_index_scores_backward_workspace_size(ctypes.byref(v), 64, 128, 101, 1, 1,
