@@ -71,13 +71,30 @@ __device__ __forceinline__ void load_row_weights(float (&wv)[MT][16], const floa
     }
 }
 
+// Both, interleaved per head tile (the order the forward kernels' schedules
+// were tuned with).
 template <int D, int MT>
 __device__ __forceinline__ void load_row_state(RowState<D, MT>& st,
                                                const uint16_t* __restrict__ q_idx,
                                                const float* __restrict__ w, int64_t row,
                                                int n_heads, int col, int half) {
-  load_row_queries<D, MT>(st.a, q_idx, row, n_heads, col, half);
-  load_row_weights<MT>(st.wv, w, row, n_heads, half);
+  constexpr int KS = D / 16, HALF = D / 2;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int h = mt * 32 + col;
+    const int hl = min(h, n_heads - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 x = load_bf16x8(q_idx + (row * n_heads + hl) * D + half * HALF + ks * 8);
+      st.a[mt][ks] = h < n_heads ? x : zero_bf16x8();
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int hr = mt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+      const float x = w[row * n_heads + min(hr, n_heads - 1)];
+      st.wv[mt][v] = hr < n_heads ? x : 0.0f;
+    }
+  }
 }
 
 // Head products of one 32-key tile.
