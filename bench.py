@@ -47,7 +47,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=5)
     from long_context_sparse_score_amd.pipeline import BENCH_PREFILL
 
     ap.add_argument("--window", type=int, default=BENCH_PREFILL.window,
