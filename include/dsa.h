@@ -346,14 +346,14 @@ int dsa_sparse_attn_prefill_grouped_workspace_size(const dsa_varlen* vl, int64_t
  * per-(row, position) mask keeps every query to its own set, so the result
  * is that of dsa_sparse_attn_prefill on the same indices (same arithmetic per
  * query; the group may span sequences).  Pays off when the sets overlap: the
- * K/V rows gathered per group are the union's, the matrix work is 16 rows
- * times the union.
+ * K/V rows gathered per group are the union's, and the union is ordered so
+ * that each 32-entry tile is computed only for the query heads of the rows
+ * that own one of its entries.
  *
  *   q, k, v, out, lse, softmax_scale, window: as dsa_sparse_attn_prefill.
- *   indices int32 [row_count, topk]: every row ascending, with its valid
- *           positions (0..p) first and -1 after them, as dsa_topk writes
- *           them.  (Other orders are not detected; they drop positions from
- *           the union.)
+ *   indices int32 [row_count, topk]: every row's selected positions in any
+ *           order, no position twice in a row; entries outside 0..p (-1
+ *           padding included) are skipped, as in dsa_sparse_attn_prefill.
  *   workspace  device buffer of at least
  *              dsa_sparse_attn_prefill_grouped_workspace_size bytes for this
  *              row_count and topk, 256-byte aligned, contents clobbered; calls

@@ -378,20 +378,33 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(const float* __restrict__
 // mask restricts every query to its own set, so each query's result is the
 // one of its own set.
 //
-// Pass 1 (union_kernel, one workgroup per group): the union as packed key
-// rows (sequence key base + position, ascending) with a 16-bit row mask per
-// entry, in the caller's workspace.  The index rows must be ascending with
-// -1 padding after the valid entries (as dsa_topk writes them): a cursor per
-// row then walks its list once while the packed-key range is swept in spans
-// of kUnionSpan, each marked in an LDS bitmap and compacted in order.
+// Pass 1 (union_kernel, one workgroup per group, wave r holding row r's
+// index list in registers): the union as packed key rows (sequence key base
+// + position) with a 16-bit row mask per entry, in the caller's workspace,
+// in the order described below.
 // Pass 2 (grouped_attn_kernel, one workgroup per (group, KV head), one wave
 // per 16 of the group's 16 * G queries): every union tile of 32 entries is
-// gathered into LDS by the whole workgroup and used by every wave with the
-// tile update of the per-row kernel, the validity bits taken from the masks.
+// gathered into LDS by the whole workgroup and used by the waves whose rows
+// own one of its entries, with the tile update of the per-row kernel and the
+// validity bits taken from the masks.
+//
+// The order.  Wave w of pass 2 serves rows w 16/G .. (w + 1) 16/G - 1, so an
+// entry's wave byte (bit w set when one of those rows owns it) says which
+// waves compute a tile holding it.  Most entries belong to few rows (on a
+// workload whose 16 adjacent queries draw about 10000 distinct positions,
+// 41% of them belong to one row only), so in key order nearly every tile
+// holds an entry of every wave, and each wave computes every tile.  Sorted
+// by the Gray-code rank of the wave byte, neighbouring entries share their
+// byte or differ in one wave, and a tile is computed by the 2 to 4 waves
+// that need it (measured on such groups: 950 wave-tiles instead of 2400 per
+// group and KV head, against 1024 for 16 rows of 64 tiles each).  Ties keep
+// key order, so the order is a function of the index sets alone.
 
 constexpr int kGroupRows = 16;
-constexpr int kUnionSpan = 8192;
-constexpr int kUnionThreads = 256;
+constexpr int kUnionThreads = kGroupRows * kWave;  // wave r: row r of the group
+constexpr int kUnionSpan = 16384;                  // packed keys per sweep
+constexpr int kUnionHeld = 2048;                   // index entries a wave holds in registers
+constexpr int kUnionBuckets = 256;                 // sort keys: up to 8 waves in pass 2
 
 // Workspace of the grouped path for `groups` groups: union keys (int32), row
 // masks (uint16), one count per group.
@@ -405,126 +418,256 @@ __host__ __device__ inline size_t grouped_ws_entries(int topk) {
   return static_cast<size_t>(kGroupRows) * topk;
 }
 
+inline size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
 inline GroupedWorkspace grouped_ws_layout(void* base, int64_t groups, int topk) {
   char* p = static_cast<char*>(base);
   GroupedWorkspace w;
   const size_t n = static_cast<size_t>(groups) * grouped_ws_entries(topk);
   w.keys = reinterpret_cast<int32_t*>(p);
-  p += (n * sizeof(int32_t) + 255) / 256 * 256;
+  p += round256(n * sizeof(int32_t));
   w.masks = reinterpret_cast<uint16_t*>(p);
-  p += (n * sizeof(uint16_t) + 255) / 256 * 256;
+  p += round256(n * sizeof(uint16_t));
   w.counts = reinterpret_cast<int32_t*>(p);
   return w;
 }
 
+// Sort key of a union entry: the Gray-code rank (prefix XOR) of its wave
+// byte, for `waves` waves of 16 / waves rows each.
+__device__ __forceinline__ int union_bucket(uint32_t mask, int waves) {
+  const int rpw = kGroupRows / waves;
+  const uint32_t rows_of_wave = (1u << rpw) - 1u;
+  uint32_t b = 0u;
+  for (int w = 0; w < waves; ++w) b |= (((mask >> (w * rpw)) & rows_of_wave) != 0u ? 1u : 0u) << w;
+  b ^= b >> 1;
+  b ^= b >> 2;
+  b ^= b >> 4;
+  return static_cast<int>(b);
+}
+
+// Lanes of this wave holding the same 8-bit key (among the lanes with `in`).
+__device__ __forceinline__ unsigned long long same_key_lanes(int key, bool in) {
+  unsigned long long peers = __ballot(in);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const bool bit = (key >> b) & 1;
+    const unsigned long long set = __ballot(in && bit);
+    peers &= bit ? set : ~set;
+  }
+  return peers;
+}
+
+// Exclusive prefix sum over the first `n` threads' values (n a multiple of
+// kWave, at most kUnionThreads); every thread gets the total.  Two barriers;
+// `wsum` holds kUnionThreads / kWave ints.
+__device__ __forceinline__ int union_scan(int x, int n, int* wsum, int& total) {
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  int incl = tid < n ? x : 0;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == kWave - 1 && tid < n) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+  for (int w = 0; w < n / kWave; ++w) {
+    before += w < wave ? wsum[w] : 0;
+    total += wsum[w];
+  }
+  __syncthreads();  // wsum is free again
+  return before + incl - (tid < n ? x : 0);
+}
+
+// Pass 1.  The packed-key range of the group's rows is swept in spans of
+// kUnionSpan keys, twice.  Per span: every wave marks its row's keys in a
+// presence bitmap; a prefix count over the bitmap gives each key its rank
+// within the span; every wave then ORs its row bit into the 16-bit mask at
+// its keys' ranks.  The first sweep counts the entries of every sort key;
+// their prefix sum is where each sort key's entries start in the output.
+// The second sweep rebuilds each span and scatters its entries, in key
+// order, to their sort key's next places (wave w of the scatter takes a
+// consecutive share of the span's entries: its own counts, then the offsets
+// over all waves, then the writes).  Only integers are summed, so the
+// result does not depend on timing, and the index lists need no order.
 __global__ __launch_bounds__(kUnionThreads) void union_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
     const int32_t* __restrict__ indices, int topk, int64_t row_begin, int64_t row_count,
-    int32_t* __restrict__ ukeys, uint16_t* __restrict__ umasks, int32_t* __restrict__ ucount) {
-  constexpr int kWavesU = kUnionThreads / kWave;
-  constexpr int kPer = kUnionSpan / kUnionThreads;  // bitmap entries per thread
-  static_assert(kPer % 4 == 0, "bitmap entries are read 4 at a time");
-  __shared__ __attribute__((aligned(16))) uint32_t bits[kUnionSpan / 2];  // 16-bit masks, paired
-  __shared__ int64_t rbase[kGroupRows];
-  __shared__ int32_t rlim[kGroupRows];
-  __shared__ int32_t rcur[kGroupRows];
-  __shared__ int32_t wsum[kWavesU];
-  __shared__ int64_t span[2];
+    int waves, int32_t* __restrict__ ukeys, uint16_t* __restrict__ umasks,
+    int32_t* __restrict__ ucount) {
+  constexpr int W = kUnionThreads / kWave;
+  constexpr int PW = kUnionSpan / 32;  // presence words
+  constexpr int NJ = kUnionHeld / kWave;
+  static_assert(PW % kWave == 0 && PW <= kUnionThreads && kUnionBuckets <= kUnionThreads,
+                "one thread per presence word and per sort key");
+  __shared__ uint32_t present[PW];
+  __shared__ int32_t rank0[PW];                   // entries before each presence word
+  __shared__ uint32_t mask2[kUnionSpan / 2];      // the span's masks, two per word
+  __shared__ uint16_t soff[kUnionSpan];           // the span's keys (offset from the span start)
+  __shared__ int32_t whist[W][kUnionBuckets];     // per-wave counts, then places
+  __shared__ int32_t next[kUnionBuckets];         // next place of each sort key
+  __shared__ int32_t wsum[W];
+  __shared__ int64_t range[2];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int64_t g = blockIdx.x;
   const int64_t first = g * kGroupRows;
   const int nrows = static_cast<int>(min<int64_t>(kGroupRows, row_count - first));
-  if (tid < kGroupRows) {
-    if (tid < nrows) {
-      const RowInfo ri = row_info(cu_q, cu_k, batch, row_begin + first + tid);
-      rbase[tid] = ri.key_base;
-      rlim[tid] = ri.pos;
-    }
-    rcur[tid] = 0;
+  const unsigned long long below = (1ull << lane) - 1ull;
+
+  // This wave's row: packed keys of its valid entries (-1 otherwise), up to
+  // kUnionHeld of them in registers; a longer list is walked in parts of
+  // kUnionHeld, reloaded at every walk.
+  int32_t key[NJ];
+  int64_t kbase = 0;
+  int32_t lim = -1;
+  if (wave < nrows) {
+    const RowInfo ri = row_info(cu_q, cu_k, batch, row_begin + first + wave);
+    kbase = ri.key_base;
+    lim = ri.pos;
   }
+  const int32_t* irow = indices + (first + min(wave, nrows - 1)) * topk;
+  const int parts = (topk + kUnionHeld - 1) / kUnionHeld;
+  auto load_keys = [&](int part) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int c = part * kUnionHeld + j * kWave + lane;
+      const int32_t e = wave < nrows && c < topk ? irow[c] : -1;
+      key[j] = e >= 0 && e <= lim ? static_cast<int32_t>(kbase + e) : -1;
+    }
+  };
+  // fn(key) for every valid key of this wave's row.
+  auto each_key = [&](auto fn) __attribute__((always_inline)) {
+    for (int part = 0; part < parts; ++part) {
+      if (parts > 1) load_keys(part);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        if (key[j] >= 0) fn(key[j]);
+    }
+  };
+  load_keys(0);
+  // Key range of the group: [lo, hi].
+  int32_t klo = INT32_MAX, khi = -1;
+  each_key([&](int32_t x) __attribute__((always_inline)) {
+    klo = min(klo, x);
+    khi = max(khi, x);
+  });
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    klo = min(klo, __shfl_xor(klo, o));
+    khi = max(khi, __shfl_xor(khi, o));
+  }
+  if (lane == 0) {
+    whist[wave][0] = klo;
+    whist[wave][1] = khi;
+  }
+  if (tid < kUnionBuckets) next[tid] = 0;
   __syncthreads();
   if (tid == 0) {
-    int64_t lo = rbase[0], hi = rbase[0] + rlim[0];
-    for (int r = 1; r < nrows; ++r) {
-      lo = min(lo, rbase[r]);
-      hi = max(hi, rbase[r] + rlim[r]);
+    int32_t lo = INT32_MAX, hi = -1;
+    for (int w = 0; w < W; ++w) {
+      lo = min(lo, whist[w][0]);
+      hi = max(hi, whist[w][1]);
     }
-    span[0] = lo;
-    span[1] = hi;
+    range[0] = hi < 0 ? 0 : lo;
+    range[1] = hi;
   }
   __syncthreads();
-  const int64_t lo = span[0], hi = span[1];
-  int32_t* keys = ukeys + g * grouped_ws_entries(topk);
-  uint16_t* masks = umasks + g * grouped_ws_entries(topk);
-  int32_t out = 0;
-  for (int64_t x0 = lo; x0 <= hi; x0 += kUnionSpan) {
-    for (int i = tid; i < kUnionSpan / 2; i += kUnionThreads) bits[i] = 0u;
+  const int32_t lo = static_cast<int32_t>(range[0]), hi = static_cast<int32_t>(range[1]);
+  int32_t* okeys = ukeys + g * grouped_ws_entries(topk);
+  uint16_t* omasks = umasks + g * grouped_ws_entries(topk);
+
+  // Builds the span at x0: presence, ranks, masks and keys; returns its entry count.
+  auto build_span = [&](int32_t x0) __attribute__((always_inline)) {
+    for (int i = tid; i < PW; i += kUnionThreads) present[i] = 0u;
     __syncthreads();
-    // Mark: wave w walks rows w, w + kWavesU, ... from their cursors while
-    // the packed keys stay below x0 + kUnionSpan.
-    for (int r = wave; r < nrows; r += kWavesU) {
-      const int32_t* irow = indices + (first + r) * topk;
-      const int64_t base = rbase[r];
-      const int32_t lim = rlim[r];
-      int32_t c = rcur[r];
-      while (c < topk) {
-        const int32_t e = c + lane < topk ? irow[c + lane] : -1;
-        const bool valid = e >= 0 && e <= lim;
-        const int64_t key = base + e;
-        const bool in = valid && key < x0 + kUnionSpan;
-        if (in && key >= x0) {
-          const int off = static_cast<int>(key - x0);
-          atomicOr(&bits[off >> 1], (1u << r) << (16 * (off & 1)));
-        }
-        const int n_in = __popcll(__ballot(in));
-        c += n_in;
-        if (n_in < kWave) break;
+    each_key([&](int32_t x) __attribute__((always_inline)) {
+      const uint32_t off = static_cast<uint32_t>(x - x0);
+      if (off < kUnionSpan) atomicOr(&present[off >> 5], 1u << (off & 31));
+    });
+    __syncthreads();
+    const uint32_t word = tid < PW ? present[tid] : 0u;
+    int n = 0;
+    const int before = union_scan(__popc(word), PW, wsum, n);
+    if (tid < PW) {
+      rank0[tid] = before;
+      uint32_t m = word;
+      for (int at = before; m != 0u; ++at, m &= m - 1u)
+        soff[at] = static_cast<uint16_t>(tid * 32 + __builtin_ctz(m));
+    }
+    for (int i = tid; i < (n + 1) / 2; i += kUnionThreads) mask2[i] = 0u;
+    __syncthreads();
+    each_key([&](int32_t x) __attribute__((always_inline)) {
+      const uint32_t off = static_cast<uint32_t>(x - x0);
+      if (off < kUnionSpan) {
+        const int w = static_cast<int>(off >> 5);
+        const int r = rank0[w] + __popc(present[w] & ((1u << (off & 31)) - 1u));
+        atomicOr(&mask2[r >> 1], (1u << wave) << (16 * (r & 1)));
       }
-      if (lane == 0) rcur[r] = c;
-    }
+    });
     __syncthreads();
-    // Compact the marked entries in key order: thread t owns entries
-    // [t kPer, (t + 1) kPer).
-    uint32_t m[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer / 2; i += 2) {
-      const uint2 w2 = *reinterpret_cast<const uint2*>(&bits[tid * (kPer / 2) + i]);
-      m[2 * i] = w2.x & 0xFFFFu;
-      m[2 * i + 1] = w2.x >> 16;
-      m[2 * i + 2] = w2.y & 0xFFFFu;
-      m[2 * i + 3] = w2.y >> 16;
-    }
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) cnt += m[i] != 0u;
-    // Exclusive prefix over the workgroup.
-    int incl = cnt;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    if (lane == kWave - 1) wsum[wave] = incl;
-    __syncthreads();
-    int before = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < kWavesU; ++w) {
-      before += w < wave ? wsum[w] : 0;
-      total += wsum[w];
-    }
-    int at = out + before + incl - cnt;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      if (m[i] != 0u) {
-        keys[at] = static_cast<int32_t>(x0 + tid * kPer + i);
-        masks[at] = static_cast<uint16_t>(m[i]);
-        ++at;
-      }
-    }
-    out += total;
+    return n;
+  };
+  auto mask_at = [&](int i) __attribute__((always_inline)) {
+    return (mask2[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+  };
+
+  // Sweep 1: entries per sort key.
+  for (int32_t x0 = lo; x0 <= hi; x0 += kUnionSpan) {
+    const int n = build_span(x0);
+    for (int i = tid; i < n; i += kUnionThreads) atomicAdd(&next[union_bucket(mask_at(i), waves)], 1);
     __syncthreads();
   }
-  if (tid == 0) ucount[g] = out;
+  {
+    const int cnt = tid < kUnionBuckets ? next[tid] : 0;
+    int total = 0;
+    const int start = union_scan(cnt, kUnionBuckets, wsum, total);
+    if (tid < kUnionBuckets) next[tid] = start;
+    if (tid == 0) ucount[g] = total;
+    __syncthreads();
+  }
+  // Sweep 2: the scatter.
+  for (int32_t x0 = lo; x0 <= hi; x0 += kUnionSpan) {
+    for (int i = tid; i < W * kUnionBuckets; i += kUnionThreads) (&whist[0][0])[i] = 0;
+    const int n = build_span(x0);  // its first barrier also orders the clear above
+    const int per = ((n + W - 1) / W + kWave - 1) / kWave * kWave;
+    const int e0 = wave * per, e1 = min(n, e0 + per);
+    for (int c = e0; c < e1; c += kWave) {
+      const int i = c + lane;
+      const bool in = i < e1;
+      const int b = in ? union_bucket(mask_at(i), waves) : 0;
+      const unsigned long long peers = same_key_lanes(b, in);
+      // One lane per sort key (the lowest) adds its count: distinct addresses.
+      if (in && (peers & below) == 0ull) whist[wave][b] += __popcll(peers);
+    }
+    __syncthreads();
+    if (tid < kUnionBuckets) {
+      int at = next[tid];
+      for (int w = 0; w < W; ++w) {
+        const int c = whist[w][tid];
+        whist[w][tid] = at;
+        at += c;
+      }
+      next[tid] = at;
+    }
+    __syncthreads();
+    for (int c = e0; c < e1; c += kWave) {
+      const int i = c + lane;
+      const bool in = i < e1;
+      const uint32_t m = in ? mask_at(i) : 0u;
+      const int b = in ? union_bucket(m, waves) : 0;
+      const unsigned long long peers = same_key_lanes(b, in);
+      // Every lane reads its sort key's place before the lowest lane moves
+      // it on (one wave's LDS operations are performed in order).
+      const int dst = (in ? whist[wave][b] : 0) + __popcll(peers & below);
+      if (in) {
+        okeys[dst] = x0 + soff[i];
+        omasks[dst] = static_cast<uint16_t>(m);
+      }
+      if (in && (peers & below) == 0ull) whist[wave][b] = dst + __popcll(peers);
+    }
+    __syncthreads();
+  }
 }
 
 // One workgroup per (group, KV head); wave w serves the group's queries
@@ -579,6 +722,31 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// Workgroup i -> (group, KV head), so that the 16 groups of one block of
+// 256 rows with one KV head run on one XCD.  Workgroups are dealt to the 8
+// XCDs round-robin by id, and each XCD has its own L2: adjacent groups share
+// most of their positions, so the union rows one group gathers are then
+// mostly in the L2 that its neighbours filled.  Units u = 16 c + k stand for
+// group 16 (c / n_heads_kv) + k with KV head c mod n_heads_kv; ids come in
+// runs of 128, whose id i % 8 (the XCD) picks the unit run c and i / 8 its
+// group k.  The grid is padded to whole runs; a unit past the last group
+// has nothing to do.
+constexpr int kXcds = 8;
+__device__ __forceinline__ bool grouped_unit(int64_t i, int64_t groups, int n_heads_kv,
+                                             int64_t& g, int& h) {
+  const int64_t run = i / (kXcds * kGroupRows);
+  const int within = static_cast<int>(i % (kXcds * kGroupRows));
+  const int64_t c = run * kXcds + within % kXcds;
+  h = static_cast<int>(c % n_heads_kv);
+  g = (c / n_heads_kv) * kGroupRows + within / kXcds;
+  return g < groups;
+}
+__host__ inline int64_t grouped_grid(int64_t groups, int n_heads_kv) {
+  const int64_t units = (groups + kGroupRows - 1) / kGroupRows * kGroupRows * n_heads_kv;
+  const int64_t run = kXcds * kGroupRows;
+  return (units + run - 1) / run * run;
+}
+
 template <int D, int COPIES>
 __global__ __launch_bounds__(8 * D / COPIES) void grouped_attn_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
@@ -586,7 +754,7 @@ __global__ __launch_bounds__(8 * D / COPIES) void grouped_attn_kernel(
     const uint16_t* __restrict__ v, int64_t total_k, int topk, int64_t row_begin,
     int64_t row_count, int n_heads_q, int n_heads_kv, float scale_log2,
     uint16_t* __restrict__ out, float* __restrict__ lse, const int32_t* __restrict__ ukeys,
-    const uint16_t* __restrict__ umasks, const int32_t* __restrict__ ucount) {
+    const uint16_t* __restrict__ umasks, const int32_t* __restrict__ ucount, int64_t groups) {
   using C = AttnCfg<D>;
   constexpr int CH = 32 * C::PIECES;      // 16-byte chunks of one K (or V) tile
   constexpr int RPI = kWave / C::PIECES;  // tile rows per copy instruction
@@ -596,8 +764,9 @@ __global__ __launch_bounds__(8 * D / COPIES) void grouped_attn_kernel(
   constexpr int NTHREADS = 8 * D / COPIES;  // the launch's block size, 64 G
   const int G = n_heads_q / n_heads_kv;
   const int col = lane & 15, qd = lane >> 4;
-  const int64_t g = blockIdx.x;
-  const int h = blockIdx.y;
+  int64_t g;
+  int h;
+  if (!grouped_unit(blockIdx.x, groups, n_heads_kv, g, h)) return;  // uniform: past the last group
   const int64_t first = g * kGroupRows;
   // This lane's query column.
   const int cq = 16 * wave + col;
@@ -749,9 +918,11 @@ void launch_grouped_attn_d(dim3 grid, dim3 block, hipStream_t stream, const dsa_
                            int64_t row_begin, int64_t row_count, int n_heads_q, int n_heads_kv,
                            float scale_log2, uint16_t* out, float* lse,
                            const GroupedWorkspace& ws) {
+  const int64_t groups = (row_count + kGroupRows - 1) / kGroupRows;
   hipLaunchKernelGGL((grouped_attn_kernel<D, COPIES>), grid, block, 0, stream, vl.cu_seqlens_q,
                      vl.cu_seqlens_k, vl.batch, q, k, v, vl.total_k, topk, row_begin, row_count,
-                     n_heads_q, n_heads_kv, scale_log2, out, lse, ws.keys, ws.masks, ws.counts);
+                     n_heads_q, n_heads_kv, scale_log2, out, lse, ws.keys, ws.masks, ws.counts,
+                     groups);
 }
 
 }  // namespace
@@ -759,7 +930,7 @@ void launch_grouped_attn_d(dim3 grid, dim3 block, hipStream_t stream, const dsa_
 size_t grouped_attn_workspace_bytes(int64_t row_count, int topk) {
   const int64_t groups = (row_count + kGroupRows - 1) / kGroupRows;
   const size_t n = static_cast<size_t>(groups) * grouped_ws_entries(topk);
-  return (n * sizeof(int32_t) + 255) / 256 * 256 + (n * sizeof(uint16_t) + 255) / 256 * 256 +
+  return round256(n * sizeof(int32_t)) + round256(n * sizeof(uint16_t)) +
          static_cast<size_t>(groups) * sizeof(int32_t);
 }
 
@@ -770,13 +941,13 @@ hipError_t launch_grouped_attn(const dsa_varlen& vl, const uint16_t* q, const ui
                                float* lse, void* workspace, hipStream_t stream) {
   const int64_t groups = (row_count + kGroupRows - 1) / kGroupRows;
   const GroupedWorkspace ws = grouped_ws_layout(workspace, groups, topk);
+  const int G = n_heads_q / n_heads_kv;
   hipLaunchKernelGGL(union_kernel, dim3(static_cast<unsigned>(groups)), dim3(kUnionThreads), 0,
                      stream, vl.cu_seqlens_q, vl.cu_seqlens_k, vl.batch, indices, topk, row_begin,
-                     row_count, ws.keys, ws.masks, ws.counts);
+                     row_count, G, ws.keys, ws.masks, ws.counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int G = n_heads_q / n_heads_kv;
-  const dim3 grid(static_cast<unsigned>(groups), static_cast<unsigned>(n_heads_kv));
+  const dim3 grid(static_cast<unsigned>(grouped_grid(groups, n_heads_kv)));
   const dim3 block(kWave * G);  // 16 G queries per KV head, 16 per wave
   const float scale_log2 = scale * kLog2e;
   // Copies per lane and tile: 2 x 32 rows x head_dim / 8 chunks over 64 G

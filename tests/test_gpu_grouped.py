@@ -52,6 +52,50 @@ def workspace_counts(ws, row_count, topk):
     return raw.view(np.int32)
 
 
+def gray_rank(b):
+    """Inverse Gray code of b (prefix XOR of its bits)."""
+    r = 0
+    while b:
+        r ^= b
+        b >>= 1
+    return r
+
+
+def check_union_order(ws, row_count, topk, groups_keys, waves):
+    """Every group's union in the workspace: exactly the distinct packed keys
+    of its rows with the right 16-bit row masks, ordered by the Gray rank of
+    the wave byte (bit w: one of rows w 16/waves .. (w + 1) 16/waves - 1 owns
+    the key), ties in ascending key order.  groups_keys[g][r] is the array of
+    packed keys of row r of group g."""
+    groups = (row_count + GROUP - 1) // GROUP
+    n = groups * GROUP * topk
+    keys_all = ws[:n * 4].cpu().numpy().view(np.int32)
+    moff = -(-n * 4 // 256) * 256
+    masks_all = ws[moff:moff + n * 2].cpu().numpy().view(np.uint16)
+    counts = workspace_counts(ws, row_count, topk)
+    rpw = GROUP // waves
+    for g in range(groups):
+        own = {}
+        for r, ks in enumerate(groups_keys[g]):
+            for x in ks.tolist():
+                own[x] = own.get(x, 0) | (1 << r)
+        c = int(counts[g])
+        assert c == len(own), f"group {g}: {c} != {len(own)}"
+        got_k = keys_all[g * GROUP * topk:g * GROUP * topk + c]
+        got_m = masks_all[g * GROUP * topk:g * GROUP * topk + c]
+
+        def bucket(m):
+            b = 0
+            for w in range(waves):
+                if (m >> (w * rpw)) & ((1 << rpw) - 1):
+                    b |= 1 << w
+            return gray_rank(b)
+
+        want = sorted(own, key=lambda x: (bucket(own[x]), x))
+        np.testing.assert_array_equal(got_k, np.array(want, np.int32), err_msg=f"group {g}")
+        np.testing.assert_array_equal(got_m, np.array([own[x] for x in want], np.uint16))
+
+
 @pytest.mark.parametrize("hq,hkv,d", [(32, 4, 128), (8, 1, 128), (8, 2, 64), (8, 8, 64),
                                       (8, 4, 128), (16, 2, 64), (32, 8, 64), (4, 4, 128)])
 def test_grouped_matches_oracle_varlen(hq, hkv, d):
@@ -67,17 +111,13 @@ def test_grouped_matches_oracle_varlen(hq, hkv, d):
     mx, mean = check_attn(from_dev_bf16(out), ref["out"])
     log(f"  max abs {mx:.2e} mean abs {mean:.2e}")
     assert np.allclose(lse.cpu().numpy(), ref["lse"], atol=2e-3)
-    # The union sizes: distinct packed keys over each group's rows.
-    counts = workspace_counts(ws, wl.total_q, wl.topk)
+    # The unions: distinct packed keys over each group's rows, their masks
+    # and their order.
     cu_k = wl.cu_k
     seq = np.searchsorted(wl.cu_q, rows, side="right") - 1
-    for g in range(len(counts)):
-        rr = rows[g * GROUP:(g + 1) * GROUP]
-        keys = set()
-        for r in rr:
-            sel = ref["idx"][r]
-            keys |= set((cu_k[seq[r]] + sel[sel >= 0]).tolist())
-        assert counts[g] == len(keys), f"group {g}: {counts[g]} != {len(keys)}"
+    packed = [cu_k[seq[r]] + ref["idx"][r][ref["idx"][r] >= 0] for r in rows]
+    check_union_order(ws, wl.total_q, wl.topk,
+                      [packed[g:g + GROUP] for g in range(0, len(rows), GROUP)], hq // hkv)
 
 
 def test_grouped_row_window_and_long_rows():
@@ -95,10 +135,29 @@ def test_grouped_row_window_and_long_rows():
     assert np.allclose(lse.cpu().numpy()[8700:9000], ref["lse"], atol=2e-3)
     untouched = from_dev_bf16(out)[:8700]
     assert (untouched == 0x40E0).all()  # 7.0 in bf16: rows outside the window stay
-    counts = workspace_counts(ws, 300, wl.topk)
-    for g in range(len(counts)):
-        sel = ref["idx"][g * GROUP:(g + 1) * GROUP]
-        assert counts[g] == np.unique(sel[sel >= 0]).size
+    packed = [ref["idx"][i][ref["idx"][i] >= 0] for i in range(300)]
+    check_union_order(ws, 300, wl.topk, [packed[g:g + GROUP] for g in range(0, 300, GROUP)], 8)
+
+
+def test_grouped_any_row_order_and_long_lists():
+    """Index rows in any order give the same union and bitwise the same
+    output (the union's order depends on the sets only), also for k = 3000,
+    more entries per row than the union pass holds at once."""
+    wl = small_wl([5000], [5000], 32, 4, 128, topk=3000, qstd=4.0, seed=21, hi=16, di=64)
+    host, dev = device_workload(wl)
+    rows = np.arange(4000, 4100)
+    ref = oracle_rows(wl, host, rows)
+    log("grouped attention, k = 3000, rows 4000..4099, ascending then shuffled index rows")
+    out_a, lse_a, ws = run_grouped(wl, dev, ref["idx"], row_begin=4000, row_count=100)
+    mx, mean = check_attn(from_dev_bf16(out_a)[4000:4100], ref["out"])
+    log(f"  max abs {mx:.2e} mean abs {mean:.2e}")
+    packed = [ref["idx"][i][ref["idx"][i] >= 0] for i in range(100)]
+    check_union_order(ws, 100, wl.topk, [packed[g:g + GROUP] for g in range(0, 100, GROUP)], 8)
+    rng = np.random.default_rng(0)
+    shuffled = np.stack([rng.permutation(r) for r in ref["idx"]])
+    out_b, lse_b, ws_b = run_grouped(wl, dev, shuffled, row_begin=4000, row_count=100)
+    assert torch.equal(out_a, out_b) and torch.equal(lse_a, lse_b)
+    check_union_order(ws_b, 100, wl.topk, [packed[g:g + GROUP] for g in range(0, 100, GROUP)], 8)
 
 
 def test_grouped_equals_per_row_pipeline_end_to_end():
