@@ -402,8 +402,9 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(const float* __restrict__
 
 constexpr int kGroupRows = 16;
 constexpr int kUnionThreads = kGroupRows * kWave;  // wave r: row r of the group
-constexpr int kUnionSpan = 16384;                  // packed keys per sweep
 constexpr int kUnionHeld = 2048;                   // index entries a wave holds in registers
+constexpr int kUnionEntries = kGroupRows * kUnionHeld;  // masks one span can hold
+constexpr int kUnionSpan = 131072;                 // packed keys per span (presence bits)
 constexpr int kUnionBuckets = 256;                 // sort keys: up to 8 waves in pass 2
 
 // Workspace of the grouped path for `groups` groups: union keys (int32), row
@@ -480,16 +481,19 @@ __device__ __forceinline__ int union_scan(int x, int n, int* wsum, int& total) {
   return before + incl - (tid < n ? x : 0);
 }
 
-// Pass 1.  The packed-key range of the group's rows is swept in spans of
-// kUnionSpan keys, twice.  Per span: every wave marks its row's keys in a
-// presence bitmap; a prefix count over the bitmap gives each key its rank
-// within the span; every wave then ORs its row bit into the 16-bit mask at
-// its keys' ranks.  The first sweep counts the entries of every sort key;
-// their prefix sum is where each sort key's entries start in the output.
-// The second sweep rebuilds each span and scatters its entries, in key
-// order, to their sort key's next places (wave w of the scatter takes a
-// consecutive share of the span's entries: its own counts, then the offsets
-// over all waves, then the writes).  Only integers are summed, so the
+// Pass 1.  The packed-key range of the group's rows is covered by spans of
+// kUnionSpan keys when every row holds at most kUnionHeld entries (so a
+// span's union fits the kUnionEntries masks), else of kUnionEntries keys.
+// Per span: every wave marks its row's keys in a presence bitmap; a prefix
+// count over the bitmap gives each key its rank within the span; every wave
+// then ORs its row bit into the 16-bit mask at its keys' ranks.  Counting
+// the entries of every sort key over all spans and a prefix sum over the
+// sort keys give where each sort key's entries start in the output; then
+// each span (rebuilt when there is more than one) is scattered in key order
+// to its sort keys' next places: wave w takes a consecutive share of the
+// span's entries (its counts per sort key, then the offsets over all waves,
+// then the writes; an entry's key is found from its rank by a binary search
+// over the ranks of the presence words).  Only integers are summed, so the
 // result does not depend on timing, and the index lists need no order.
 __global__ __launch_bounds__(kUnionThreads) void union_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
@@ -497,23 +501,24 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(
     int waves, int32_t* __restrict__ ukeys, uint16_t* __restrict__ umasks,
     int32_t* __restrict__ ucount) {
   constexpr int W = kUnionThreads / kWave;
-  constexpr int PW = kUnionSpan / 32;  // presence words
+  constexpr int PW = kUnionSpan / 32;      // presence words
+  constexpr int WPT = PW / kUnionThreads;  // presence words per thread
   constexpr int NJ = kUnionHeld / kWave;
-  static_assert(PW % kWave == 0 && PW <= kUnionThreads && kUnionBuckets <= kUnionThreads,
-                "one thread per presence word and per sort key");
+  static_assert(WPT * kUnionThreads == PW && kUnionBuckets <= kUnionThreads, "shapes");
   __shared__ uint32_t present[PW];
   __shared__ int32_t rank0[PW];                   // entries before each presence word
-  __shared__ uint32_t mask2[kUnionSpan / 2];      // the span's masks, two per word
-  __shared__ uint16_t soff[kUnionSpan];           // the span's keys (offset from the span start)
+  __shared__ uint32_t mask2[kUnionEntries / 2];   // the span's masks, two per word
   __shared__ int32_t whist[W][kUnionBuckets];     // per-wave counts, then places
   __shared__ int32_t next[kUnionBuckets];         // next place of each sort key
   __shared__ int32_t wsum[W];
-  __shared__ int64_t range[2];
+  __shared__ int32_t range[2];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int64_t g = blockIdx.x;
   const int64_t first = g * kGroupRows;
   const int nrows = static_cast<int>(min<int64_t>(kGroupRows, row_count - first));
   const unsigned long long below = (1ull << lane) - 1ull;
+  const int span = topk <= kUnionHeld ? kUnionSpan : kUnionEntries;
+  const int nwords = span / 32;
 
   // This wave's row: packed keys of its valid entries (-1 otherwise), up to
   // kUnionHeld of them in registers; a longer list is walked in parts of
@@ -573,33 +578,40 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(
     range[1] = hi;
   }
   __syncthreads();
-  const int32_t lo = static_cast<int32_t>(range[0]), hi = static_cast<int32_t>(range[1]);
+  const int32_t lo = range[0], hi = range[1];
+  const int spans = hi < lo ? 0 : (hi - lo) / span + 1;
   int32_t* okeys = ukeys + g * grouped_ws_entries(topk);
   uint16_t* omasks = umasks + g * grouped_ws_entries(topk);
 
-  // Builds the span at x0: presence, ranks, masks and keys; returns its entry count.
+  // The span at x0: presence bits, word ranks and masks; returns its entry count.
   auto build_span = [&](int32_t x0) __attribute__((always_inline)) {
-    for (int i = tid; i < PW; i += kUnionThreads) present[i] = 0u;
+#pragma unroll
+    for (int k = 0; k < WPT; ++k) present[tid * WPT + k] = 0u;
     __syncthreads();
     each_key([&](int32_t x) __attribute__((always_inline)) {
       const uint32_t off = static_cast<uint32_t>(x - x0);
-      if (off < kUnionSpan) atomicOr(&present[off >> 5], 1u << (off & 31));
+      if (off < static_cast<uint32_t>(span)) atomicOr(&present[off >> 5], 1u << (off & 31));
     });
     __syncthreads();
-    const uint32_t word = tid < PW ? present[tid] : 0u;
+    int cnt[WPT];
+    int mine = 0;
+#pragma unroll
+    for (int k = 0; k < WPT; ++k) {
+      cnt[k] = __popc(present[tid * WPT + k]);
+      mine += cnt[k];
+    }
     int n = 0;
-    const int before = union_scan(__popc(word), PW, wsum, n);
-    if (tid < PW) {
-      rank0[tid] = before;
-      uint32_t m = word;
-      for (int at = before; m != 0u; ++at, m &= m - 1u)
-        soff[at] = static_cast<uint16_t>(tid * 32 + __builtin_ctz(m));
+    int at = union_scan(mine, kUnionThreads, wsum, n);
+#pragma unroll
+    for (int k = 0; k < WPT; ++k) {
+      rank0[tid * WPT + k] = at;
+      at += cnt[k];
     }
     for (int i = tid; i < (n + 1) / 2; i += kUnionThreads) mask2[i] = 0u;
     __syncthreads();
     each_key([&](int32_t x) __attribute__((always_inline)) {
       const uint32_t off = static_cast<uint32_t>(x - x0);
-      if (off < kUnionSpan) {
+      if (off < static_cast<uint32_t>(span)) {
         const int w = static_cast<int>(off >> 5);
         const int r = rank0[w] + __popc(present[w] & ((1u << (off & 31)) - 1u));
         atomicOr(&mask2[r >> 1], (1u << wave) << (16 * (r & 1)));
@@ -611,25 +623,26 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(
   auto mask_at = [&](int i) __attribute__((always_inline)) {
     return (mask2[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
   };
-
-  // Sweep 1: entries per sort key.
-  for (int32_t x0 = lo; x0 <= hi; x0 += kUnionSpan) {
-    const int n = build_span(x0);
+  // Offset from the span start of the span's entry of rank i: the last
+  // presence word whose rank is at most i holds it.
+  auto offset_of = [&](int i) __attribute__((always_inline)) {
+    int a = 0, b = nwords;
+    while (b - a > 1) {
+      const int mid = (a + b) >> 1;
+      if (rank0[mid] <= i) a = mid;
+      else b = mid;
+    }
+    uint32_t m = present[a];
+    for (int k = i - rank0[a]; k > 0; --k) m &= m - 1u;
+    return a * 32 + __builtin_ctz(m);
+  };
+  auto count_span = [&](int n) __attribute__((always_inline)) {
     for (int i = tid; i < n; i += kUnionThreads) atomicAdd(&next[union_bucket(mask_at(i), waves)], 1);
     __syncthreads();
-  }
-  {
-    const int cnt = tid < kUnionBuckets ? next[tid] : 0;
-    int total = 0;
-    const int start = union_scan(cnt, kUnionBuckets, wsum, total);
-    if (tid < kUnionBuckets) next[tid] = start;
-    if (tid == 0) ucount[g] = total;
-    __syncthreads();
-  }
-  // Sweep 2: the scatter.
-  for (int32_t x0 = lo; x0 <= hi; x0 += kUnionSpan) {
+  };
+  auto scatter_span = [&](int32_t x0, int n) __attribute__((always_inline)) {
     for (int i = tid; i < W * kUnionBuckets; i += kUnionThreads) (&whist[0][0])[i] = 0;
-    const int n = build_span(x0);  // its first barrier also orders the clear above
+    __syncthreads();
     const int per = ((n + W - 1) / W + kWave - 1) / kWave * kWave;
     const int e0 = wave * per, e1 = min(n, e0 + per);
     for (int c = e0; c < e1; c += kWave) {
@@ -661,13 +674,34 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(
       // it on (one wave's LDS operations are performed in order).
       const int dst = (in ? whist[wave][b] : 0) + __popcll(peers & below);
       if (in) {
-        okeys[dst] = x0 + soff[i];
+        okeys[dst] = x0 + offset_of(i);
         omasks[dst] = static_cast<uint16_t>(m);
       }
       if (in && (peers & below) == 0ull) whist[wave][b] = dst + __popcll(peers);
     }
     __syncthreads();
+  };
+
+  int n_last = 0;
+  for (int sp = 0; sp < spans; ++sp) {
+    n_last = build_span(lo + sp * span);
+    count_span(n_last);
   }
+  {
+    const int cnt = tid < kUnionBuckets ? next[tid] : 0;
+    int total = 0;
+    const int start = union_scan(cnt, kUnionBuckets, wsum, total);
+    if (tid < kUnionBuckets) next[tid] = start;
+    if (tid == 0) ucount[g] = total;
+    __syncthreads();
+  }
+  // One span is still built; more are rebuilt one by one.
+  if (spans == 1) scatter_span(lo, n_last);
+  else
+    for (int sp = 0; sp < spans; ++sp) {
+      const int32_t x0 = lo + sp * span;
+      scatter_span(x0, build_span(x0));
+    }
 }
 
 // One workgroup per (group, KV head); wave w serves the group's queries
