@@ -38,6 +38,10 @@ constexpr int kKlRows = 16;  // query rows per workgroup (MFMA columns)
 constexpr int kKlKeys = 32;  // positions per tile
 constexpr float kKlLog2e = 1.4426950408889634f;
 constexpr float kKlLn2 = 0.6931471805599453f;
+// Growth of a (row, head) maximum (log2 units) that pass 1's running
+// reference absorbs before it is moved: terms of the running sum stay below
+// 2^8, and most half tiles skip the rescale's exponential.
+constexpr float kKlRescaleLog2 = 8.0f;
 
 template <int D>
 struct KlCfg {
@@ -268,21 +272,29 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
       load_scores(min(t + 1, ntiles - 1), sv_next);
       load_tile(min(t + 1, ntiles - 1));
       if (t < full_tiles) {
-        // Each half tile of 16 keys updates the running statistics.
+        // Each half tile of 16 keys updates the running statistics.  The
+        // reference hm moves only when a lane's maximum passes it by more
+        // than kKlRescaleLog2 (lazy rescaling; the first tile always moves
+        // it from -inf), so the sum's terms are taken against a reference
+        // up to 2^8 below the maximum, and the final reduction, which
+        // rescales every lane's sum from its own reference, is unchanged.
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
           f32x4 st[HPW];
           dots_sub(sub, one_g, st);
 #pragma unroll
           for (int j = 0; j < HPW; ++j) {
-            const float mx = fmaxf(fmaxf(st[j][0], st[j][1]), fmaxf(st[j][2], st[j][3]));
-            const float mn = fmaxf(hm[j], mx * scale_log2);
-            float sum = 0.0f;
+            const float mx =
+                fmaxf(fmaxf(st[j][0], st[j][1]), fmaxf(st[j][2], st[j][3])) * scale_log2;
+            const bool move = mx > hm[j] + kKlRescaleLog2;
+            if (__any(move)) {
+              const float mn = move ? mx : hm[j];
+              hl[j] *= __builtin_amdgcn_exp2f(hm[j] - mn);
+              hm[j] = mn;
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              sum += __builtin_amdgcn_exp2f(__builtin_fmaf(st[j][r], scale_log2, -mn));
-            hl[j] = hl[j] * __builtin_amdgcn_exp2f(hm[j] - mn) + sum;
-            hm[j] = mn;
+              hl[j] += __builtin_amdgcn_exp2f(__builtin_fmaf(st[j][r], scale_log2, -hm[j]));
           }
         }
       } else {
@@ -312,7 +324,7 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
         if (sv[i] != -INFINITY) {
           const float x = sv[i] * kKlLog2e;
           const float mn = fmaxf(im[i], x);
-          il[i] = il[i] * exp2f(im[i] - mn) + exp2f(x - mn);
+          il[i] = il[i] * __builtin_amdgcn_exp2f(im[i] - mn) + __builtin_amdgcn_exp2f(x - mn);
           im[i] = mn;
         }
       }
@@ -397,8 +409,8 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
           for (int w = 0; w < W; ++w) psum += ppart[(w * kKlRows + r) * kPStride + e_key[i]];
           const float P = psum * inv_hq;
           const float lpi = sv[i] - lnorm[i];
-          const float pi = __expf(lpi);
-          if (P > 0.0f) kl[i] += P * (__logf(P) - lpi);
+          const float pi = __builtin_amdgcn_exp2f(lpi * kKlLog2e);
+          if (P > 0.0f) kl[i] += P * (__builtin_amdgcn_logf(P) * kKlLn2 - lpi);
           if (grad != nullptr) grad[(first + r) * ld_grad + s] = pi - P;
         }
       }
