@@ -187,6 +187,101 @@ __device__ __forceinline__ void compute_tile(const bf16x8 (&qb)[AttnCfg<D>::KS],
   }
 }
 
+// Online-softmax update of two tiles at once (64 slots: tile 0 from
+// ks0/vs0 with validity vm0, tile 1 from ks1/vs1 with vm1), the same
+// arithmetic as two compute_tile calls except that one reference update
+// covers both: the four S sub-products are independent, and so are the two
+// P V products, which gives the wave more work in flight per step.
+template <int D>
+__device__ __forceinline__ void compute_tile_pair(const bf16x8 (&qb)[AttnCfg<D>::KS],
+                                                  const uint16_t* ks0, const uint16_t* vs0,
+                                                  uint32_t vm0, const uint16_t* ks1,
+                                                  const uint16_t* vs1, uint32_t vm1,
+                                                  float scale_log2, int lane, float& m_run,
+                                                  float& l_run, f32x4 (&acc)[AttnCfg<D>::DT]) {
+  using C = AttnCfg<D>;
+  const int col = lane & 15, qd = lane >> 4;
+  const uint16_t* ks[2] = {ks0, ks1};
+  const uint16_t* vs[2] = {vs0, vs1};
+  const uint32_t vm[2] = {vm0, vm1};
+  f32x4 st[2][2];
+#pragma unroll
+  for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      st[tl][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < C::KS; ++k) {
+        const bf16x8 ka = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(ks[tl] + tile_at<D>(16 * sub + col, 4 * k + qd)));
+        st[tl][sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[k], st[tl][sub], 0, 0, 0);
+      }
+    }
+  float z[2][2][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = (vm[tl] >> (16 * sub + 4 * qd + r)) & 1u;
+        z[tl][sub][r] = ok ? st[tl][sub][r] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, z[tl][sub][r]);
+      }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  if (__any(mx > m_run + kRescaleLog2)) {
+    const float m_new = fmaxf(m_run, mx);
+    const float corr = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= corr;
+    m_run = m_new;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float cr = __shfl(corr, 4 * qd + r);
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) acc[dt][r] *= cr;
+    }
+  }
+  const float m_use = m_run == -INFINITY ? 0.0f : m_run;
+  typedef float f32x8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 bf16x8n __attribute__((ext_vector_type(8)));
+  bf16x8 pa[2];
+  float psum = 0.0f;
+#pragma unroll
+  for (int tl = 0; tl < 2; ++tl) {
+    float pr[2][4];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pr[sub][r] = __builtin_amdgcn_exp2f(z[tl][sub][r] - m_use);
+        psum += pr[sub][r];
+      }
+    const f32x8 pf = {pr[0][0], pr[0][1], pr[0][2], pr[0][3], pr[1][0], pr[1][1], pr[1][2], pr[1][3]};
+    pa[tl] = __builtin_bit_cast(bf16x8, __builtin_convertvector(pf, bf16x8n));
+  }
+  l_run += psum;
+  // B operands as in compute_tile (transposing reads), for each tile.
+  const int tr_row = 4 * qd + (col >> 2);
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) {
+    const int d0 = dt * 16 + 4 * (col & 3);
+    const int piece = d0 / 8, e = d0 % 8;
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int tl = 0; tl < 2; ++tl) {
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16*)(vs[tl] + tile_at<D>(tr_row, piece) + e));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16*)(vs[tl] + tile_at<D>(16 + tr_row, piece) + e));
+      const bf16x8 vb = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo),
+                                                __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3, 4, 5, 6, 7);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[tl], vb, acc[dt], 0, 0, 0);
+    }
+  }
+}
+
 // A wave's own tile: its K and V rows to its private LDS tiles, then the
 // update.  LDS operations of one wave are performed in order, so the reads
 // see these writes and the next tile's writes come after them.
@@ -706,40 +801,37 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(
 
 // One workgroup per (group, KV head); wave w serves the group's queries
 // 16 w .. 16 w + 15 of this KV head (query c = row c / G, head c mod G).
-// Union tiles of 32 entries stream through an LDS ring of R slots by
-// buffer->LDS DMA, so R - 1 tiles are in flight while one is used: the
-// K and V rows of the tile's entries (2 x 32 x D / 8 16-byte chunks, COPIES
-// per lane: G is a power of two, so every wave issues the same copies),
-// while each wave loads the tile's 32 row masks into a register.  The union
-// keys that address a tile's copies are loaded into registers R - 1 tiles
-// earlier, so they have landed by the ring's counted wait that precedes the
-// copies (a key read at copy time would stall every wave on a miss each
-// tile).  Every step issues the same loads (past the union's end they read
-// zeros, copied into a slot nobody reads), which keeps the counts fixed.
+// Union tiles of 32 entries stream through an LDS ring of kRingG slots by
+// buffer->LDS DMA, two tiles (a pair) a step: step s uses pair s while the
+// copies of pairs s + 1 and s + 2 are in flight, so four tiles are on their
+// way while two are used.  A pair's K and V rows (2 x 32 x D / 8 16-byte
+// chunks a tile, COPIES per lane and tile: G is a power of two, so every
+// wave issues the same copies) and its 64 row masks are copied by every
+// wave, addressed by the pair's union keys, which come into a key slot one
+// step before (a key read at copy time would stall every wave on a miss).
+// Every step issues the same loads (past the union's end they read zeros),
+// so one counted wait per step is exact, and one barrier per step (two
+// tiles) makes every wave's copies visible and frees the slots of the pair
+// before.  Six ring slots and two key slots are all the LDS the copies
+// write: the compiler tells a few such targets apart (with more, or with
+// the keys in registers, it waited for every copy in flight).
 //
-// R = grouped_ring: as many slots as leave room in LDS (at most
-// kMaxRingG), bounded so that the counted wait ((R - 2) (COPIES + 2) loads)
-// fits its 6-bit field.  Four slots measured as fast as eight, at fewer
-// registers.
-constexpr int kMaxRingG = 4;
-template <int D, int COPIES>
-constexpr int grouped_ring() {
-  constexpr int by_wait = 2 + 63 / (COPIES + 2);
-  constexpr int by_lds = (128 * 1024) / (2 * AttnCfg<D>::TILE * 2 + 512);
-  constexpr int r = by_wait < by_lds ? by_wait : by_lds;
-  return r < kMaxRingG ? r : kMaxRingG;
-}
+// A wave computes a pair when its rows own an entry of either tile, both
+// tiles in one update (compute_tile_pair: four independent S products and
+// one softmax reference update); a wave whose rows own nothing in the pair
+// skips it.
+constexpr int kRingG = 6;  // slots: three pairs
 
-// Ring slot B: K tile, V tile, then 128 union masks from the tile's first
-// (only its 32 are read); and key slot B: 64 union keys from a tile's first.
-// One LDS variable each: the compiler then sees that a slot being read is
-// not the one a copy in flight writes, and places no wait for those copies
-// before the reads.
+// Ring slot B: K tile, V tile, then 128 union masks (slot 2 p mod kRingG
+// holds its pair's 64, from the pair's first entry).  One LDS variable each:
+// the compiler then sees that a slot being read is not the one a copy in
+// flight writes, and places no wait for those copies before the reads.
 template <int D, int B>
 __device__ __forceinline__ uint16_t* grouped_slot() {
   __shared__ __attribute__((aligned(16))) uint16_t buf[2 * AttnCfg<D>::TILE + 2 * kWave];
   return buf;
 }
+// Key slot B: the 64 union keys of a pair (one variable each, as above).
 template <int B>
 __device__ __forceinline__ int32_t* grouped_keyslot() {
   __shared__ __attribute__((aligned(16))) int32_t buf[kWave];
@@ -791,8 +883,6 @@ __global__ __launch_bounds__(8 * D / COPIES) void grouped_attn_kernel(
     const uint16_t* __restrict__ umasks, const int32_t* __restrict__ ucount, int64_t groups) {
   using C = AttnCfg<D>;
   constexpr int CH = 32 * C::PIECES;      // 16-byte chunks of one K (or V) tile
-  constexpr int RPI = kWave / C::PIECES;  // tile rows per copy instruction
-  constexpr int R = grouped_ring<D, COPIES>();
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   constexpr int NTHREADS = 8 * D / COPIES;  // the launch's block size, 64 G
@@ -826,101 +916,112 @@ __global__ __launch_bounds__(8 * D / COPIES) void grouped_attn_kernel(
   // Whole words up to the union's end (a word read partly past the range
   // would come back as zero); the group's mask region always holds them.
   const __amdgpu_buffer_rsrc_t mr = raw_buffer(masks, (count * 2 + 3) & ~3);
-  // Copies of tile t into a ring slot.  Copy j of this wave covers chunks
-  // cbase .. cbase + 63 (cbase uniform); chunk c is piece c mod PIECES of
-  // tile row c / PIECES in LDS, filled from global piece
-  // (c mod PIECES) ^ (row mod PIECES) (the tile_at swizzle).  The tile's 32
-  // row masks come with them into a register: lane l gets the word holding
-  // the masks of slots 2 (l mod 32) / 2 and the one after (zero past the
-  // union's end).
   const __amdgpu_buffer_rsrc_t kyr = raw_buffer(keys, count * 4);
-  // Union keys u*32 .. u*32 + 63 into a key slot (4 bytes a lane; zero past
-  // the union's end).  Every wave copies the same words, so every wave
-  // issues the same loads.
-  auto copy_keys = [&](int u, int32_t* ks) __attribute__((always_inline)) {
+  // Union keys of pair p into a key slot (4 bytes a lane; zero past the
+  // union's end).  Every wave copies the same words.
+  auto copy_keys = [&](int p, int32_t* ks) __attribute__((always_inline)) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        kyr, (__attribute__((address_space(3))) void*)ks, 4, lane * 4, u * 128, 0, 0);
+        kyr, (__attribute__((address_space(3))) void*)ks, 4, lane * 4, p * 256, 0, 0);
   };
-  // Copies of tile u into ring slot rs, addressed by the keys in key slot ks;
-  // then its masks (4 bytes a lane, from entry u*32) behind the V tile.
-  auto issue = [&](int u, uint16_t* rs, const int32_t* ks) __attribute__((always_inline)) {
+  // Copies of pair p: tile 2 p into ring slot r0, tile 2 p + 1 into r1,
+  // addressed by the keys in key slot ks; then the pair's masks (4 bytes a
+  // lane, from entry 64 p) behind r0's V tile.  Copy j of this wave covers
+  // chunks cbase .. cbase + 63 of a tile (cbase uniform); chunk c is piece
+  // c mod PIECES of tile row c / PIECES in LDS, filled from global piece
+  // (c mod PIECES) ^ (row mod PIECES) (the tile_at swizzle).
+  auto issue_pair = [&](int p, uint16_t* r0, uint16_t* r1, const int32_t* ks)
+                        __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < COPIES; ++j) {
-      // Chunks 0 .. CH - 1 are the K tile's, CH .. 2 CH - 1 the V tile's
-      // (CH is a multiple of 64, so a copy is all K or all V).
-      const int cc = j * NTHREADS + kWave * wave;
-      const bool is_v = cc >= CH;
-      const int cbase = is_v ? cc - CH : cc;
-      const int c = cbase + lane;
-      const int r = c / C::PIECES;
-      const int piece = (c % C::PIECES) ^ (r % C::PIECES);
-      const int off = ((ks[r] * n_heads_kv + h) * D + piece * 8) * 2;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          raw_buffer(is_v ? v : k, kv_bytes),
-          (__attribute__((address_space(3))) void*)(&rs[(is_v ? C::TILE : 0) + cbase * 8]), 16,
-          off, 0, 0, 0);
+    for (int half = 0; half < 2; ++half) {
+      uint16_t* rs = half == 0 ? r0 : r1;
+#pragma unroll
+      for (int j = 0; j < COPIES; ++j) {
+        // Chunks 0 .. CH - 1 are the K tile's, CH .. 2 CH - 1 the V tile's
+        // (CH is a multiple of 64, so a copy is all K or all V).
+        const int cc = j * NTHREADS + kWave * wave;
+        const bool is_v = cc >= CH;
+        const int cbase = is_v ? cc - CH : cc;
+        const int c = cbase + lane;
+        const int r = c / C::PIECES;
+        const int piece = (c % C::PIECES) ^ (r % C::PIECES);
+        const int off = ((ks[32 * half + r] * n_heads_kv + h) * D + piece * 8) * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            raw_buffer(is_v ? v : k, kv_bytes),
+            (__attribute__((address_space(3))) void*)(&rs[(is_v ? C::TILE : 0) + cbase * 8]), 16,
+            off, 0, 0, 0);
+      }
     }
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        mr, (__attribute__((address_space(3))) void*)(&rs[2 * C::TILE]), 4, lane * 4, u * 64, 0, 0);
+        mr, (__attribute__((address_space(3))) void*)(&r0[2 * C::TILE]), 4, lane * 4, p * 128, 0, 0);
   };
+  // Loads per step: the keys of one pair, 2 COPIES copies, the masks.
+  constexpr int L = 2 * COPIES + 2;
+  static_assert(L <= 63 && kRingG == 6, "counted wait; three pairs in the ring");
 
   f32x4 acc[C::DT];
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;
   const int ntiles = (count + 31) / 32;
-  // Every step issues, in order, the keys of tile u + R - 1, the copies of
-  // tile u and its masks (COPIES + 2 loads); the loop's step t is such a step
-  // with u = t + R - 1.  The prologue runs it for u = 0 .. R - 2 once the
-  // first tiles' keys are in.
-  static_for<R - 1>([&](auto b) __attribute__((always_inline)) {
-    copy_keys(decltype(b)::value, grouped_keyslot<decltype(b)::value>());
-  });
+  const int npairs = (ntiles + 1) / 2;
+  // Prologue, as steps -2 and -1 without their barriers' first purpose: the
+  // keys of pair s + 3 (key slot (s + 3) mod 2) and the copies of pair s + 2
+  // (keys from slot (s + 2) mod 2), after the keys of pair 0, waited for.
+  // The loads in flight at step 0 are then exactly those the steps count on.
+  copy_keys(0, grouped_keyslot<0>());
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   lds_barrier();
-  static_for<R - 1>([&](auto b) __attribute__((always_inline)) {
-    constexpr int U = decltype(b)::value;
-    // Key slot (U + R - 1) mod R held tile U - 1's keys: every wave has
-    // read them once past this barrier.
-    if constexpr (U > 0) lds_barrier();
-    copy_keys(U + R - 1, grouped_keyslot<(U + R - 1) % R>());
-    issue(U, grouped_slot<D, U>(), grouped_keyslot<U>());
-  });
-  // Tile t from ring slot B = t mod R; the copies of tile t + R - 1 go to
-  // slot (B + R - 1) mod R, the one tile t - 1 used.
-  auto step = [&](auto tag, int t) __attribute__((always_inline)) {
-    constexpr int B = decltype(tag)::value;
-    constexpr int BN = (B + R - 1) % R;
-    // Tile t has landed once only the R - 2 younger steps' loads are
-    // outstanding, and so have the keys of tile t + R - 1, copied before
-    // tile t; the barrier makes every wave's copies visible and frees slot
-    // BN and key slot (B + R - 2) mod R (all waves are done with tile t - 1).
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((R - 2) * (COPIES + 2)));
+  copy_keys(1, grouped_keyslot<1>());
+  issue_pair(0, grouped_slot<D, 0>(), grouped_slot<D, 1>(), grouped_keyslot<0>());
+  lds_barrier();  // every wave has read key slot 0 before it is refilled
+  copy_keys(2, grouped_keyslot<0>());
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(L));  // the keys of pair 1
+  issue_pair(1, grouped_slot<D, 2>(), grouped_slot<D, 3>(), grouped_keyslot<1>());
+  // Step s (pair s in slots 2 P, 2 P + 1 with P = s mod 3): once pair s and
+  // the keys of pair s + 2 have landed (only step s - 1's loads after its
+  // first are younger) and every wave is past the previous step, the keys of
+  // pair s + 3 (into the key slot that held pair s + 1's, read a step ago)
+  // and the copies of pair s + 2 (into the slots of pair s - 1); then pair s.
+  // (Issuing the copies after the pair's compute measured slower: 32.0 ms
+  // against 29.9 ms on the correlated 128K prefill.)
+  auto step = [&](auto tag, int s) __attribute__((always_inline)) {
+    constexpr int B = decltype(tag)::value;  // s mod 6
+    constexpr int P = B % 3, PI = (B + 2) % 3;
+    constexpr int KR = B % 2, KW = (B + 1) % 2;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(L - 1));
     lds_barrier();
-    const uint16_t* rs = grouped_slot<D, B>();
-    const uint32_t mw = reinterpret_cast<const uint32_t*>(rs + 2 * C::TILE)[(lane & 31) >> 1];
-    copy_keys(t + 2 * R - 2, grouped_keyslot<(B + 2 * R - 2) % R>());
-    issue(t + R - 1, grouped_slot<D, BN>(), grouped_keyslot<BN>());
-    const uint32_t m16 = t * 32 + (lane & 31) >= count ? 0u
-                         : (lane & 1)                   ? (mw >> 16)
-                                                        : (mw & 0xFFFFu);
-    // Validity of the 32 slots for this lane's row.
-    uint32_t vm = 0u;
+    const uint16_t* rs0 = grouped_slot<D, 2 * P>();
+    const uint16_t* rs1 = grouped_slot<D, 2 * P + 1>();
+    const uint32_t* mw = reinterpret_cast<const uint32_t*>(rs0 + 2 * C::TILE);
+    const uint32_t mw0 = mw[(lane & 31) >> 1], mw1 = mw[16 + ((lane & 31) >> 1)];
+    copy_keys(s + 3, grouped_keyslot<KW>());
+    issue_pair(s + 2, grouped_slot<D, 2 * PI>(), grouped_slot<D, 2 * PI + 1>(),
+               grouped_keyslot<KR>());
+    // This lane's entry of each tile: the masks of its rows.
+    const int e0 = 2 * s * 32 + (lane & 31);
+    const uint32_t m0 = e0 >= count ? 0u : (lane & 1) ? (mw0 >> 16) : (mw0 & 0xFFFFu);
+    const uint32_t m1 = e0 + 32 >= count ? 0u : (lane & 1) ? (mw1 >> 16) : (mw1 & 0xFFFFu);
+    // Validity of the 64 slots for this lane's row.
+    uint32_t vm0 = 0u, vm1 = 0u;
     for (int i = 0; i < nrw; ++i) {
-      const uint32_t w = static_cast<uint32_t>(__ballot((m16 >> (rl_first + i)) & 1u));
-      if (rl == rl_first + i) vm = w;
+      const uint32_t w0 = static_cast<uint32_t>(__ballot((m0 >> (rl_first + i)) & 1u));
+      const uint32_t w1 = static_cast<uint32_t>(__ballot((m1 >> (rl_first + i)) & 1u));
+      if (rl == rl_first + i) {
+        vm0 = w0;
+        vm1 = w1;
+      }
     }
-    // The index sets come in runs of nearby positions, so a tile often holds
-    // none of this wave's rows: the wave then skips it (a fully masked tile
-    // changes nothing).
-    if (__any(vm != 0u))
-      compute_tile<D>(qb, rs, rs + C::TILE, vm, scale_log2, lane, m_run, l_run, acc);
+    // A pair holding none of this wave's rows is skipped (a fully masked
+    // tile changes nothing).
+    if (__any((vm0 | vm1) != 0u))
+      compute_tile_pair<D>(qb, rs0, rs0 + C::TILE, vm0, rs1, rs1 + C::TILE, vm1, scale_log2, lane,
+                           m_run, l_run, acc);
   };
-  // Whole rounds of R tiles: a tile past the union's end has all masks zero
-  // and changes nothing, and straight-line rounds let the compiler see which
-  // loads each register waits for.
-  for (int t = 0; t < ntiles; t += R)
-    static_for<R>([&](auto b) __attribute__((always_inline)) { step(b, t + decltype(b)::value); });
+  // Whole rounds of six pairs: a pair past the union's end has all masks
+  // zero and changes nothing, and straight-line rounds keep the slots and
+  // key slots static.
+  for (int s = 0; s < npairs; s += 6)
+    static_for<6>([&](auto b) __attribute__((always_inline)) { step(b, s + decltype(b)::value); });
   // No copy may still be writing LDS when the wave ends.
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
