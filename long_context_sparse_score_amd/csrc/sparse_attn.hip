@@ -503,11 +503,13 @@ constexpr int kUnionSpan = 131072;                 // packed keys per span (pres
 constexpr int kUnionBuckets = 256;                 // sort keys: up to 8 waves in pass 2
 
 // Workspace of the grouped path for `groups` groups: union keys (int32), row
-// masks (uint16), one count per group.
+// masks (uint16), one count per group, then each group's keys in key order
+// (staging for the union pass's scatter).
 struct GroupedWorkspace {
   int32_t* keys;
   uint16_t* masks;
   int32_t* counts;
+  int32_t* stage;
 };
 
 __host__ __device__ inline size_t grouped_ws_entries(int topk) {
@@ -525,6 +527,8 @@ inline GroupedWorkspace grouped_ws_layout(void* base, int64_t groups, int topk) 
   w.masks = reinterpret_cast<uint16_t*>(p);
   p += round256(n * sizeof(uint16_t));
   w.counts = reinterpret_cast<int32_t*>(p);
+  p += round256(static_cast<size_t>(groups) * sizeof(int32_t));
+  w.stage = reinterpret_cast<int32_t*>(p);
   return w;
 }
 
@@ -587,14 +591,14 @@ __device__ __forceinline__ int union_scan(int x, int n, int* wsum, int& total) {
 // each span (rebuilt when there is more than one) is scattered in key order
 // to its sort keys' next places: wave w takes a consecutive share of the
 // span's entries (its counts per sort key, then the offsets over all waves,
-// then the writes; an entry's key is found from its rank by a binary search
-// over the ranks of the presence words).  Only integers are summed, so the
+// then the writes; an entry's key is read back by rank from a staging copy
+// that the mask step writes).  Only integers are summed, so the
 // result does not depend on timing, and the index lists need no order.
 __global__ __launch_bounds__(kUnionThreads) void union_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
     const int32_t* __restrict__ indices, int topk, int64_t row_begin, int64_t row_count,
     int waves, int32_t* __restrict__ ukeys, uint16_t* __restrict__ umasks,
-    int32_t* __restrict__ ucount) {
+    int32_t* __restrict__ ucount, int32_t* __restrict__ ustage) {
   constexpr int W = kUnionThreads / kWave;
   constexpr int PW = kUnionSpan / 32;      // presence words
   constexpr int WPT = PW / kUnionThreads;  // presence words per thread
@@ -613,7 +617,6 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(
   const int nrows = static_cast<int>(min<int64_t>(kGroupRows, row_count - first));
   const unsigned long long below = (1ull << lane) - 1ull;
   const int span = topk <= kUnionHeld ? kUnionSpan : kUnionEntries;
-  const int nwords = span / 32;
 
   // This wave's row: packed keys of its valid entries (-1 otherwise), up to
   // kUnionHeld of them in registers; a longer list is walked in parts of
@@ -677,6 +680,7 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(
   const int spans = hi < lo ? 0 : (hi - lo) / span + 1;
   int32_t* okeys = ukeys + g * grouped_ws_entries(topk);
   uint16_t* omasks = umasks + g * grouped_ws_entries(topk);
+  int32_t* stage = ustage + g * grouped_ws_entries(topk);  // the span's keys by rank
 
   // The span at x0: presence bits, word ranks and masks; returns its entry count.
   auto build_span = [&](int32_t x0) __attribute__((always_inline)) {
@@ -710,32 +714,23 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(
         const int w = static_cast<int>(off >> 5);
         const int r = rank0[w] + __popc(present[w] & ((1u << (off & 31)) - 1u));
         atomicOr(&mask2[r >> 1], (1u << wave) << (16 * (r & 1)));
+        // Every row holding the key writes the same value.
+        stage[r] = x;
       }
     });
+    // The staged keys are complete in L2 before any wave reads them.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
     return n;
   };
   auto mask_at = [&](int i) __attribute__((always_inline)) {
     return (mask2[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
   };
-  // Offset from the span start of the span's entry of rank i: the last
-  // presence word whose rank is at most i holds it.
-  auto offset_of = [&](int i) __attribute__((always_inline)) {
-    int a = 0, b = nwords;
-    while (b - a > 1) {
-      const int mid = (a + b) >> 1;
-      if (rank0[mid] <= i) a = mid;
-      else b = mid;
-    }
-    uint32_t m = present[a];
-    for (int k = i - rank0[a]; k > 0; --k) m &= m - 1u;
-    return a * 32 + __builtin_ctz(m);
-  };
   auto count_span = [&](int n) __attribute__((always_inline)) {
     for (int i = tid; i < n; i += kUnionThreads) atomicAdd(&next[union_bucket(mask_at(i), waves)], 1);
     __syncthreads();
   };
-  auto scatter_span = [&](int32_t x0, int n) __attribute__((always_inline)) {
+  auto scatter_span = [&](int n) __attribute__((always_inline)) {
     for (int i = tid; i < W * kUnionBuckets; i += kUnionThreads) (&whist[0][0])[i] = 0;
     __syncthreads();
     const int per = ((n + W - 1) / W + kWave - 1) / kWave * kWave;
@@ -769,7 +764,7 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(
       // it on (one wave's LDS operations are performed in order).
       const int dst = (in ? whist[wave][b] : 0) + __popcll(peers & below);
       if (in) {
-        okeys[dst] = x0 + offset_of(i);
+        okeys[dst] = stage[i];
         omasks[dst] = static_cast<uint16_t>(m);
       }
       if (in && (peers & below) == 0ull) whist[wave][b] = dst + __popcll(peers);
@@ -791,12 +786,9 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(
     __syncthreads();
   }
   // One span is still built; more are rebuilt one by one.
-  if (spans == 1) scatter_span(lo, n_last);
+  if (spans == 1) scatter_span(n_last);
   else
-    for (int sp = 0; sp < spans; ++sp) {
-      const int32_t x0 = lo + sp * span;
-      scatter_span(x0, build_span(x0));
-    }
+    for (int sp = 0; sp < spans; ++sp) scatter_span(build_span(lo + sp * span));
 }
 
 // One workgroup per (group, KV head); wave w serves the group's queries
@@ -1065,8 +1057,8 @@ void launch_grouped_attn_d(dim3 grid, dim3 block, hipStream_t stream, const dsa_
 size_t grouped_attn_workspace_bytes(int64_t row_count, int topk) {
   const int64_t groups = (row_count + kGroupRows - 1) / kGroupRows;
   const size_t n = static_cast<size_t>(groups) * grouped_ws_entries(topk);
-  return round256(n * sizeof(int32_t)) + round256(n * sizeof(uint16_t)) +
-         static_cast<size_t>(groups) * sizeof(int32_t);
+  return 2 * round256(n * sizeof(int32_t)) + round256(n * sizeof(uint16_t)) +
+         round256(static_cast<size_t>(groups) * sizeof(int32_t));
 }
 
 hipError_t launch_grouped_attn(const dsa_varlen& vl, const uint16_t* q, const uint16_t* k,
@@ -1079,7 +1071,7 @@ hipError_t launch_grouped_attn(const dsa_varlen& vl, const uint16_t* q, const ui
   const int G = n_heads_q / n_heads_kv;
   hipLaunchKernelGGL(union_kernel, dim3(static_cast<unsigned>(groups)), dim3(kUnionThreads), 0,
                      stream, vl.cu_seqlens_q, vl.cu_seqlens_k, vl.batch, indices, topk, row_begin,
-                     row_count, G, ws.keys, ws.masks, ws.counts);
+                     row_count, G, ws.keys, ws.masks, ws.counts, ws.stage);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const dim3 grid(static_cast<unsigned>(grouped_grid(groups, n_heads_kv)));
