@@ -142,20 +142,22 @@ def test_grouped_row_window_and_long_rows():
 def test_grouped_any_row_order_and_long_lists():
     """Index rows in any order give the same union and bitwise the same
     output (the union's order depends on the sets only), also for k = 3000,
-    more entries per row than the union pass holds at once."""
-    wl = small_wl([5000], [5000], 32, 4, 128, topk=3000, qstd=4.0, seed=21, hi=16, di=64)
+    more entries per row than the union pass holds at once, whose rows here
+    see about 40000 keys: more than one 32768-key span of the union pass."""
+    wl = small_wl([40000], [40000], 32, 4, 128, topk=3000, qstd=4.0, seed=21, hi=16, di=64)
     host, dev = device_workload(wl)
-    rows = np.arange(4000, 4100)
+    r0 = 39900
+    rows = np.arange(r0, r0 + 100)
     ref = oracle_rows(wl, host, rows)
-    log("grouped attention, k = 3000, rows 4000..4099, ascending then shuffled index rows")
-    out_a, lse_a, ws = run_grouped(wl, dev, ref["idx"], row_begin=4000, row_count=100)
-    mx, mean = check_attn(from_dev_bf16(out_a)[4000:4100], ref["out"])
+    log("grouped attention, k = 3000, rows 39900..39999, ascending then shuffled index rows")
+    out_a, lse_a, ws = run_grouped(wl, dev, ref["idx"], row_begin=r0, row_count=100)
+    mx, mean = check_attn(from_dev_bf16(out_a)[r0:r0 + 100], ref["out"])
     log(f"  max abs {mx:.2e} mean abs {mean:.2e}")
     packed = [ref["idx"][i][ref["idx"][i] >= 0] for i in range(100)]
     check_union_order(ws, 100, wl.topk, [packed[g:g + GROUP] for g in range(0, 100, GROUP)], 8)
     rng = np.random.default_rng(0)
     shuffled = np.stack([rng.permutation(r) for r in ref["idx"]])
-    out_b, lse_b, ws_b = run_grouped(wl, dev, shuffled, row_begin=4000, row_count=100)
+    out_b, lse_b, ws_b = run_grouped(wl, dev, shuffled, row_begin=r0, row_count=100)
     assert torch.equal(out_a, out_b) and torch.equal(lse_a, lse_b)
     check_union_order(ws_b, 100, wl.topk, [packed[g:g + GROUP] for g in range(0, 100, GROUP)], 8)
 
