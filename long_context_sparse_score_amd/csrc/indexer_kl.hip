@@ -16,7 +16,8 @@
 // no MFMA column is wasted whatever Hq / Hkv is.  W waves split the Hq
 // heads (HPW = Hq / W each).  Key tiles of 32 positions with all KV heads
 // are staged in LDS (XOR-swizzled like the attention tiles) and shared by
-// all waves; the next tile is loaded into registers while one is used.
+// all waves: two LDS buffers, the next tile copied into one by
+// buffer->LDS DMA while the other is used.
 //   Pass 1: the dense logits of every head, for the running max and sum of
 //           each (row, head) softmax, and the rows' indexer scores, for the
 //           max and sum of theirs.
@@ -27,6 +28,8 @@
 //           gradient.
 // Rows of several sequences in one workgroup are served one sequence at a
 // time, the other rows' columns masked.
+#include <type_traits>
+
 #include "dsa_common.h"
 #include "dsa_internal.h"
 
@@ -55,13 +58,18 @@ __device__ __forceinline__ int kl_at(int key, int g, int n_heads_kv, int piece) 
   return (key * n_heads_kv + g) * D + ((piece ^ (key % KlCfg<D>::PIECES)) * 8);
 }
 
-// LDS layout (dynamic): the K tile (32 keys x Hkv x D bf16), a 1 KB dump
-// for the stores of lanes without a chunk, the waves' partial sums
-// [W][16 rows][kPStride] fp32 (32 keys, padded), then per-row words.
+// LDS: two K tile buffers of ELEMS bf16 (the copies of one tile, at least
+// 32 keys x Hkv x D; one static variable apiece, so that the compiler sees
+// which buffer a copy in flight writes and places no wait for it before
+// reads of the other), the waves' partial sums [W][16 rows][kPStride] fp32
+// (32 keys, padded) and the per-row words.
 constexpr int kPStride = kKlKeys + 1;
-__host__ __device__ constexpr size_t kl_lds_bytes(int d, int n_heads_kv, int waves) {
-  return static_cast<size_t>(kKlKeys) * n_heads_kv * d * 2 + kWave * 16 +
-         static_cast<size_t>(waves) * kKlRows * kPStride * 4 + 4 * kKlRows * 4;
+// s_waitcnt immediate: lgkmcnt(0), vmcnt and expcnt left unconstrained.
+constexpr int kLgkmcnt0 = 0xF | (3 << 14) | 0x70;
+template <int ELEMS, int B>
+__device__ __forceinline__ uint16_t* kl_kbuf() {
+  __shared__ __attribute__((aligned(16))) uint16_t buf[ELEMS];
+  return buf;
 }
 
 template <int D, int HPW, int W, int CPT>
@@ -75,12 +83,9 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
   constexpr int NT = W * kWave;
   constexpr int RI = kKlRows * kKlKeys / NT;  // (row, key) entries per thread
   static_assert(RI * NT == kKlRows * kKlKeys, "entries split evenly");
-  extern __shared__ __attribute__((aligned(16))) uint16_t kl_lds[];
-  uint16_t* ktile = kl_lds;
-  uint16_t* dump = kl_lds + kKlKeys * n_heads_kv * D;
-  float* ppart = reinterpret_cast<float*>(dump + kWave * 8);
-  int32_t* rowkb = reinterpret_cast<int32_t*>(ppart + W * kKlRows * kPStride);  // key base per row
-  int32_t* rowpos = rowkb + kKlRows;                                           // position per row
+  __shared__ float ppart[W * kKlRows * kPStride];
+  __shared__ int32_t rowkb[kKlRows];   // key base per row
+  __shared__ int32_t rowpos[kKlRows];  // position per row
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -120,13 +125,14 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
   }
 
   // 16-byte chunks of one K tile, CPT per thread (the launcher picks CPT =
-  // ceil(chunks / NT)).  Load indices past the
-  // tile are clamped to its last chunk, so the loads carry no branch and
-  // stay in flight during the tile's products (a wave's lanes then share
-  // one address, one request); their stores go to a per-lane dump slot
-  // (a branch there would again make the compiler drain the loads).
+  // ceil(chunks / NT)), copied from global memory to LDS by buffer->LDS
+  // DMA: copy i of a wave fills LDS chunks cbase .. cbase + 63 (cbase
+  // uniform), chunk cb being physical piece cb mod PIECES of LDS row
+  // cb / PIECES (key * Hkv + g), filled from global piece
+  // (cb mod PIECES) ^ (key mod PIECES) (kl_at's swizzle).  Chunks past the
+  // tile read a clamped valid chunk into the buffer's unused part.
+  constexpr int KB = CPT * NT * 8;  // bf16 per buffer
   const int chunks = kKlKeys * n_heads_kv * C::PIECES;
-  constexpr int kMaxCpt = CPT;
 
   // Serve the rows one sequence at a time (key bases ascend with the row).
   int32_t seg_kb = rowkb[0];
@@ -138,30 +144,29 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
     const int ntiles = (pmax + kKlKeys) / kKlKeys;
     const uint16_t* kseq = k + static_cast<int64_t>(seg_kb) * n_heads_kv * D;
 
-    u32x4 pre[kMaxCpt];
-    auto load_tile = [&](int t) {
+    // Starts the copy of tile t into kt.  The tile's visible K rows (keys
+    // t * 32 .. min(t * 32 + 31, pmax)) form one range-checked buffer; a
+    // key past pmax is clamped to the last of them.
+    auto issue_tile = [&](int t, uint16_t* kt) __attribute__((always_inline)) {
+      const int rows = min(kKlKeys, pmax + 1 - t * kKlKeys);
+      const __amdgpu_buffer_rsrc_t krs =
+          raw_buffer(kseq + static_cast<int64_t>(t) * kKlKeys * n_heads_kv * D,
+                     rows * n_heads_kv * D * 2);
 #pragma unroll
-      for (int i = 0; i < kMaxCpt; ++i) {
-        const int c = min(tid + NT * i, chunks - 1);
-        const int key = c / (n_heads_kv * C::PIECES);
-        const int s = min(t * kKlKeys + key, pmax);  // past the prefix: any visible row
-        const int rest = c % (n_heads_kv * C::PIECES);
-        pre[i] = *reinterpret_cast<const u32x4*>(kseq + static_cast<int64_t>(s) * n_heads_kv * D +
-                                                 rest * 8);
+      for (int i = 0; i < CPT; ++i) {
+        const int cbase = i * NT + kWave * wave;
+        const int cc = min(cbase + lane, chunks - 1);
+        const int rowg = cc / C::PIECES;
+        const int key = rowg / n_heads_kv, g = rowg % n_heads_kv;
+        const int piece = (cc % C::PIECES) ^ (key % C::PIECES);
+        const int off = ((min(key, rows - 1) * n_heads_kv + g) * D + piece * 8) * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            krs, (__attribute__((address_space(3))) void*)(kt + cbase * 8), 16, off, 0, 0, 0);
       }
     };
-    auto store_tile = [&]() {
-#pragma unroll
-      for (int i = 0; i < kMaxCpt; ++i) {
-        const int c = tid + NT * i;
-        const int cc = min(c, chunks - 1);
-        const int key = cc / (n_heads_kv * C::PIECES);
-        const int rest = cc % (n_heads_kv * C::PIECES);
-        const int at = c < chunks ? kl_at<D>(key, rest / C::PIECES, n_heads_kv, rest % C::PIECES)
-                                  : kKlKeys * n_heads_kv * D + lane * 8;
-        *reinterpret_cast<u32x4*>(kl_lds + at) = pre[i];
-      }
-    };
+    // The two buffers; tile t is staged in buffer t mod 2.
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
     // Scores of this thread's entries of the tile at t (-inf when not
     // visible); the address is clamped into the row, so the load carries no
     // branch.
@@ -179,7 +184,7 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
     // 16 sub + 4 qd + r of this lane's row, -inf when not visible.
     // Raw dot products of head j for the tile: st[sub][r] is key
     // 16 sub + 4 qd + r of this lane's row.
-    auto dots = [&](int j, f32x4 (&st)[2]) {
+    auto dots = [&](const uint16_t* kt, int j, f32x4 (&st)[2]) {
       const int g = (wave * HPW + j) / G;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
@@ -188,7 +193,7 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
         for (int ks = 0; ks < C::KS; ++ks) {
           const bf16x8 ka = __builtin_bit_cast(
               bf16x8, *reinterpret_cast<const u32x4*>(
-                          ktile + kl_at<D>(16 * sub + col, g, n_heads_kv, 4 * ks + qd)));
+                          kt + kl_at<D>(16 * sub + col, g, n_heads_kv, 4 * ks + qd)));
           st[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[j][ks], st[sub], 0, 0, 0);
         }
       }
@@ -196,7 +201,7 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
     // Raw dot products of all HPW heads for half sub of the tile (keys
     // 16 sub + 4 qd + r): when the heads share one KV head (G a multiple of
     // HPW) each K fragment is read from LDS once for all of them.
-    auto dots_sub = [&](int sub, bool one_g, f32x4 (&st)[HPW]) {
+    auto dots_sub = [&](const uint16_t* kt, int sub, bool one_g, f32x4 (&st)[HPW]) {
 #pragma unroll
       for (int j = 0; j < HPW; ++j) st[j] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (one_g) {
@@ -205,7 +210,7 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
         for (int ks = 0; ks < C::KS; ++ks) {
           const bf16x8 ka = __builtin_bit_cast(
               bf16x8, *reinterpret_cast<const u32x4*>(
-                          ktile + kl_at<D>(16 * sub + col, g, n_heads_kv, 4 * ks + qd)));
+                          kt + kl_at<D>(16 * sub + col, g, n_heads_kv, 4 * ks + qd)));
 #pragma unroll
           for (int j = 0; j < HPW; ++j)
             st[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[j][ks], st[j], 0, 0, 0);
@@ -218,7 +223,7 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
           for (int ks = 0; ks < C::KS; ++ks) {
             const bf16x8 ka = __builtin_bit_cast(
                 bf16x8, *reinterpret_cast<const u32x4*>(
-                            ktile + kl_at<D>(16 * sub + col, g, n_heads_kv, 4 * ks + qd)));
+                            kt + kl_at<D>(16 * sub + col, g, n_heads_kv, 4 * ks + qd)));
             st[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[j][ks], st[j], 0, 0, 0);
           }
         }
@@ -227,9 +232,9 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
     const bool one_g = G % HPW == 0;
     // Logits (log2 domain) of head j for the tile at t, -inf when not
     // visible.
-    auto logits = [&](int t, int j, float (&z)[2][4]) {
+    auto logits = [&](const uint16_t* kt, int t, int j, float (&z)[2][4]) {
       f32x4 st[2];
-      dots(j, st);
+      dots(kt, j, st);
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -256,21 +261,25 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
     float im[RI], il[RI];
 #pragma unroll
     for (int i = 0; i < RI; ++i) { im[i] = -INFINITY; il[i] = 0.0f; }
-    // The scores and the K rows of tile t + 1 are loaded while tile t is
-    // used, unconditionally (the last tile reloads itself): a branch would
-    // make the compiler drain the loads at the first use of any of them.
-    float sv_next[RI];
-    load_scores(0, sv_next);
-    load_tile(0);
-    for (int t = 0; t < ntiles; ++t) {
-      __syncthreads();  // every wave is done with the previous tile
-      store_tile();
-      __syncthreads();
-      float sv[RI];
+    // Step t: once tile t has landed for every wave (and every wave is done
+    // with tile t - 1, whose buffer is refilled next), the copy of tile t + 1
+    // and the load of its scores are started, unconditionally (the last
+    // tile copies itself again), and tile t is used while they are in
+    // flight.  One drain and one barrier per tile.
+    auto begin_step = [&](auto b, int t, float (&sv)[RI], float (&sv_next)[RI])
+        __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      lds_barrier();
 #pragma unroll
       for (int i = 0; i < RI; ++i) sv[i] = sv_next[i];
+      issue_tile(min(t + 1, ntiles - 1), kl_kbuf<KB, 1 - decltype(b)::value>());
       load_scores(min(t + 1, ntiles - 1), sv_next);
-      load_tile(min(t + 1, ntiles - 1));
+    };
+    float sv_next[RI];
+    auto step1 = [&](auto b, int t) __attribute__((always_inline)) {
+      const uint16_t* kt = kl_kbuf<KB, decltype(b)::value>();
+      float sv[RI];
+      begin_step(b, t, sv, sv_next);
       if (t < full_tiles) {
         // Each half tile of 16 keys updates the running statistics.  The
         // reference hm moves only when a lane's maximum passes it by more
@@ -281,7 +290,7 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
           f32x4 st[HPW];
-          dots_sub(sub, one_g, st);
+          dots_sub(kt, sub, one_g, st);
 #pragma unroll
           for (int j = 0; j < HPW; ++j) {
             const float mx =
@@ -301,7 +310,7 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
 #pragma unroll
         for (int j = 0; j < HPW; ++j) {
           float z[2][4];
-          logits(t, j, z);
+          logits(kt, t, j, z);
           float mx = -INFINITY;
 #pragma unroll
           for (int sub = 0; sub < 2; ++sub)
@@ -328,6 +337,12 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
           im[i] = mn;
         }
       }
+    };
+    load_scores(0, sv_next);
+    issue_tile(0, kl_kbuf<KB, 0>());
+    for (int t = 0; t < ntiles; t += 2) {
+      step1(B0{}, t);
+      if (t + 1 < ntiles) step1(B1{}, t + 1);
     }
     // Whole-row statistics: the four lane quarters hold one row's keys.
     // hb[j] = log2 of the normaliser of head j: A = exp2(z - hb[j]).
@@ -359,23 +374,29 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
 #pragma unroll
     for (int i = 0; i < RI; ++i) kl[i] = 0.0f;
     const float inv_hq = 1.0f / static_cast<float>(n_heads_q);
-    load_scores(0, sv_next);
-    load_tile(0);
-    for (int t = 0; t < ntiles; ++t) {
-      __syncthreads();  // tile t-1's reads of K and of the partial sums are done
-      store_tile();
-      __syncthreads();
-      float sv[RI];
+    // Tile t's gradient is stored in step t + 1, after that step's loads
+    // are issued, so the drain that opens step t + 2 finds the stores long
+    // done instead of waiting for them right after they were issued.
+    float gval[RI];
+    bool gok[RI];
 #pragma unroll
-      for (int i = 0; i < RI; ++i) sv[i] = sv_next[i];
-      load_scores(min(t + 1, ntiles - 1), sv_next);
-      load_tile(min(t + 1, ntiles - 1));
+    for (int i = 0; i < RI; ++i) { gval[i] = 0.0f; gok[i] = false; }
+    auto store_grads = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < RI; ++i)
+        if (gok[i]) grad[(first + e_row[i]) * ld_grad + t * kKlKeys + e_key[i]] = gval[i];
+    };
+    auto step2 = [&](auto b, int t) __attribute__((always_inline)) {
+      const uint16_t* kt = kl_kbuf<KB, decltype(b)::value>();
+      float sv[RI];
+      begin_step(b, t, sv, sv_next);  // also: every wave is done with the partial sums
+      store_grads(t - 1);
       float acc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
       if (t < full_tiles) {
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
           f32x4 st[HPW];
-          dots_sub(sub, one_g, st);
+          dots_sub(kt, sub, one_g, st);
 #pragma unroll
           for (int j = 0; j < HPW; ++j)
 #pragma unroll
@@ -386,7 +407,7 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
 #pragma unroll
         for (int j = 0; j < HPW; ++j) {
           float z[2][4];
-          logits(t, j, z);
+          logits(kt, t, j, z);
 #pragma unroll
           for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -398,11 +419,14 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           ppart[(wave * kKlRows + col) * kPStride + 16 * sub + 4 * qd + r] = acc[sub][r];
-      __syncthreads();
+      // LDS writes done, nothing else: a workgroup fence here would also
+      // wait for the next tile's copy.
+      __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
+      lds_barrier();
 #pragma unroll
       for (int i = 0; i < RI; ++i) {
         const int r = e_row[i];
-        const int s = t * kKlKeys + e_key[i];
+        gok[i] = grad != nullptr && sv[i] != -INFINITY;
         if (sv[i] != -INFINITY) {
           float psum = 0.0f;
 #pragma unroll
@@ -411,10 +435,21 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
           const float lpi = sv[i] - lnorm[i];
           const float pi = __builtin_amdgcn_exp2f(lpi * kKlLog2e);
           if (P > 0.0f) kl[i] += P * (__builtin_amdgcn_logf(P) * kKlLn2 - lpi);
-          if (grad != nullptr) grad[(first + r) * ld_grad + s] = pi - P;
+          gval[i] = pi - P;
         }
       }
+    };
+    // Every wave is done with pass 1's last tile before tile 0 is copied
+    // again.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    lds_barrier();
+    load_scores(0, sv_next);
+    issue_tile(0, kl_kbuf<KB, 0>());
+    for (int t = 0; t < ntiles; t += 2) {
+      step2(B0{}, t);
+      if (t + 1 < ntiles) step2(B1{}, t + 1);
     }
+    store_grads(ntiles - 1);
     // Per-row loss: the row's 32 lanes.
 #pragma unroll
     for (int i = 0; i < RI; ++i) {
@@ -431,6 +466,7 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
       if (rowkb[r] > seg_kb) { next = rowkb[r]; break; }
     if (next < 0) break;
     seg_kb = next;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the last step's copy has landed
     __syncthreads();
   }
 }
@@ -440,16 +476,8 @@ hipError_t launch_kl_d(const dsa_varlen& vl, const uint16_t* q, const uint16_t* 
                        const float* scores, int64_t ld, int64_t row_begin, int64_t row_count,
                        int n_heads_q, int n_heads_kv, float scale, float* loss, float* grad,
                        int64_t ld_grad, hipStream_t stream) {
-  const size_t lds = kl_lds_bytes(D, n_heads_kv, W);
-  // Up to 64 KB of K tile (8 KV heads at d = 128) plus the partial sums:
-  // above the default dynamic LDS limit, within the 160 KB of a CU.  Set
-  // once per instantiation (thread-safe static initialisation).
-  static const hipError_t lds_ok = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&indexer_kl_kernel<D, HPW, W, CPT>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kl_lds_bytes(D, 8, W)));
-  if (lds_ok != hipSuccess) return lds_ok;
   const unsigned blocks = static_cast<unsigned>((row_count + kKlRows - 1) / kKlRows);
-  hipLaunchKernelGGL((indexer_kl_kernel<D, HPW, W, CPT>), dim3(blocks), dim3(W * kWave), lds, stream,
+  hipLaunchKernelGGL((indexer_kl_kernel<D, HPW, W, CPT>), dim3(blocks), dim3(W * kWave), 0, stream,
                      vl.cu_seqlens_q, vl.cu_seqlens_k, vl.batch, q, k, scores, ld, row_begin,
                      row_count, n_heads_q, n_heads_kv, scale * kKlLog2e, loss, grad, ld_grad);
   return hipGetLastError();
