@@ -66,6 +66,20 @@ __device__ __forceinline__ int kl_at(int key, int g, int n_heads_kv, int piece) 
 constexpr int kPStride = kKlKeys + 1;
 // s_waitcnt immediate: lgkmcnt(0), vmcnt and expcnt left unconstrained.
 constexpr int kLgkmcnt0 = 0xF | (3 << 14) | 0x70;
+// Scheduling of a block that issues one tile's MFMAs beside independent
+// VALU work: the K-fragment reads first, then NVALU VALU instructions
+// after each of the NMFMA MFMAs, so the wave's exponentials issue while its
+// matrix products run instead of after the last of them.
+template <int NMFMA, int NVALU>
+__device__ __forceinline__ void interleave_mfma_valu() {
+  __builtin_amdgcn_sched_group_barrier(0x100, NMFMA / 4, 0);  // LDS reads
+#pragma unroll
+  for (int i = 0; i < NMFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, NVALU, 0);  // VALU
+  }
+}
+
 template <int ELEMS, int B>
 __device__ __forceinline__ uint16_t* kl_kbuf() {
   __shared__ __attribute__((aligned(16))) uint16_t buf[ELEMS];
@@ -180,67 +194,39 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
         sv[i] = vis ? x : -INFINITY;
       }
     };
-    // Logits (log2 domain) of head j for the tile at t: z[sub][r] is key
-    // 16 sub + 4 qd + r of this lane's row, -inf when not visible.
-    // Raw dot products of head j for the tile: st[sub][r] is key
-    // 16 sub + 4 qd + r of this lane's row.
-    auto dots = [&](const uint16_t* kt, int j, f32x4 (&st)[2]) {
-      const int g = (wave * HPW + j) / G;
+    // Raw dot products of the tile in kt for all HPW heads: st[sub][j][r]
+    // is head j's product with key 16 sub + 4 qd + r of this lane's row.
+    // The wave's heads share one KV head (Hq = 2^n <= 64 split over
+    // W = min(8, Hq) waves, Hkv in {1, 2, 4, 8} dividing Hq: G = Hq / Hkv
+    // is a multiple of HPW), so each K fragment is read from LDS once for
+    // all of them.
+    const int g_w = wave * HPW / G;
+    auto tile_dots = [&](const uint16_t* kt, f32x4 (&st)[2][HPW]) __attribute__((always_inline)) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
-        st[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) st[sub][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
           const bf16x8 ka = __builtin_bit_cast(
               bf16x8, *reinterpret_cast<const u32x4*>(
-                          kt + kl_at<D>(16 * sub + col, g, n_heads_kv, 4 * ks + qd)));
-          st[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[j][ks], st[sub], 0, 0, 0);
-        }
-      }
-    };
-    // Raw dot products of all HPW heads for half sub of the tile (keys
-    // 16 sub + 4 qd + r): when the heads share one KV head (G a multiple of
-    // HPW) each K fragment is read from LDS once for all of them.
-    auto dots_sub = [&](const uint16_t* kt, int sub, bool one_g, f32x4 (&st)[HPW]) {
-#pragma unroll
-      for (int j = 0; j < HPW; ++j) st[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (one_g) {
-        const int g = (wave * HPW) / G;
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          const bf16x8 ka = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(
-                          kt + kl_at<D>(16 * sub + col, g, n_heads_kv, 4 * ks + qd)));
+                          kt + kl_at<D>(16 * sub + col, g_w, n_heads_kv, 4 * ks + qd)));
 #pragma unroll
           for (int j = 0; j < HPW; ++j)
-            st[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[j][ks], st[j], 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < HPW; ++j) {
-          const int g = (wave * HPW + j) / G;
-#pragma unroll
-          for (int ks = 0; ks < C::KS; ++ks) {
-            const bf16x8 ka = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4*>(
-                            kt + kl_at<D>(16 * sub + col, g, n_heads_kv, 4 * ks + qd)));
-            st[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[j][ks], st[j], 0, 0, 0);
-          }
+            st[sub][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[j][ks], st[sub][j], 0, 0, 0);
         }
       }
     };
-    const bool one_g = G % HPW == 0;
-    // Logits (log2 domain) of head j for the tile at t, -inf when not
-    // visible.
-    auto logits = [&](const uint16_t* kt, int t, int j, float (&z)[2][4]) {
-      f32x4 st[2];
-      dots(kt, j, st);
+    // Logits (log2 domain) of head j for tile t from its products, -inf
+    // where not visible.
+    auto logits = [&](const f32x4 (&st)[2][HPW], int t, int j, float (&z)[2][4])
+        __attribute__((always_inline)) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int s = t * kKlKeys + 16 * sub + 4 * qd + r;
-          z[sub][r] = col_in && s <= my_pos ? st[sub][r] * scale_log2 : -INFINITY;
+          z[sub][r] = col_in && s <= my_pos ? st[sub][j][r] * scale_log2 : -INFINITY;
         }
     };
     // A tile is full when all 16 rows belong to this sequence and see all
@@ -254,13 +240,18 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
     }
     const int full_tiles = all_in ? (min_pos + 1) / kKlKeys : 0;
 
-    // ---- pass 1: per-(row, head) softmax statistics, per-row indexer ones.
-    float hm[HPW], hl[HPW];
+    // Both passes are software-pipelined by one tile: step t issues tile
+    // t's MFMAs and then does the exponential work of tile t - 1, whose
+    // products the step before left in registers.  In the steps whose
+    // previous tile is full, that work and the MFMAs form one basic block,
+    // scheduled so that each wave's VALU work runs beside its own matrix
+    // products.  Tile t sits in K buffer t % 2 and its products in stA (t
+    // even) or stB (t odd).
+    f32x4 stA[2][HPW], stB[2][HPW];
 #pragma unroll
-    for (int j = 0; j < HPW; ++j) { hm[j] = -INFINITY; hl[j] = 0.0f; }
-    float im[RI], il[RI];
+    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-    for (int i = 0; i < RI; ++i) { im[i] = -INFINITY; il[i] = 0.0f; }
+      for (int j = 0; j < HPW; ++j) stA[sub][j] = stB[sub][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     // Step t: once tile t has landed for every wave (and every wave is done
     // with tile t - 1, whose buffer is refilled next), the copy of tile t + 1
     // and the load of its scores are started, unconditionally (the last
@@ -275,59 +266,117 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
       issue_tile(min(t + 1, ntiles - 1), kl_kbuf<KB, 1 - decltype(b)::value>());
       load_scores(min(t + 1, ntiles - 1), sv_next);
     };
-    float sv_next[RI];
-    auto step1 = [&](auto b, int t) __attribute__((always_inline)) {
-      const uint16_t* kt = kl_kbuf<KB, decltype(b)::value>();
-      float sv[RI];
-      begin_step(b, t, sv, sv_next);
-      if (t < full_tiles) {
-        // Each half tile of 16 keys updates the running statistics.  The
-        // reference hm moves only when a lane's maximum passes it by more
-        // than kKlRescaleLog2 (lazy rescaling; the first tile always moves
-        // it from -inf), so the sum's terms are taken against a reference
-        // up to 2^8 below the maximum, and the final reduction, which
-        // rescales every lane's sum from its own reference, is unchanged.
+    // A pass's steps: step(b, t, cur, next) with cur the products of tile
+    // t - 1 and next the set for tile t's.  Steps 0 and 1 and the steps
+    // after the full tiles take the generic step, the pairs of steps in
+    // between the fast one; the last tile's values follow the loop.
+    auto run_pass = [&](auto fast_step, auto generic_step, auto last_values)
+        __attribute__((always_inline)) {
+      generic_step(B0{}, 0, stB, stA);
+      int t = 1;
+      if (ntiles > 1) {
+        generic_step(B1{}, 1, stA, stB);
+        t = 2;
+      }
+      const int tf = min(full_tiles, ntiles - 1);  // last step whose previous tile is full
+      for (; t + 1 <= tf; t += 2) {
+        fast_step(B0{}, t, stB, stA);
+        fast_step(B1{}, t + 1, stA, stB);
+      }
+      for (; t < ntiles; t += 2) {
+        generic_step(B0{}, t, stB, stA);
+        if (t + 1 < ntiles) generic_step(B1{}, t + 1, stA, stB);
+      }
+      if ((ntiles - 1) & 1) last_values(stB, ntiles - 1);
+      else last_values(stA, ntiles - 1);
+    };
+
+    // ---- pass 1: per-(row, head) softmax statistics, per-row indexer ones.
+    float hm[HPW], hl[HPW];
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-          f32x4 st[HPW];
-          dots_sub(kt, sub, one_g, st);
+    for (int j = 0; j < HPW; ++j) { hm[j] = -INFINITY; hl[j] = 0.0f; }
+    float im[RI], il[RI];
 #pragma unroll
-          for (int j = 0; j < HPW; ++j) {
-            const float mx =
-                fmaxf(fmaxf(st[j][0], st[j][1]), fmaxf(st[j][2], st[j][3])) * scale_log2;
-            const bool move = mx > hm[j] + kKlRescaleLog2;
-            if (__any(move)) {
-              const float mn = move ? mx : hm[j];
-              hl[j] *= __builtin_amdgcn_exp2f(hm[j] - mn);
-              hm[j] = mn;
-            }
+    for (int i = 0; i < RI; ++i) { im[i] = -INFINITY; il[i] = 0.0f; }
+    // Full tiles: the reference hm moves only when a lane's term would pass
+    // 2^kKlRescaleLog2 (lazy rescaling; the first tile always moves it from
+    // -inf), so the sum's terms are taken against a reference up to 2^8
+    // below the maximum, and the final reduction, which rescales every
+    // lane's sum from its own reference, is unchanged.  The sums h are
+    // taken against the current reference first; where a lane's tile sum
+    // passes 2^8 (the only way one of its terms can), the tile is redone
+    // with the lane maxima (redo1), which moves exactly the lanes whose
+    // maximum passed the reference by more than 2^8.
+    auto sums1 = [&](const f32x4 (&st)[2][HPW], float (&h)[HPW], bool& redo)
+        __attribute__((always_inline)) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              hl[j] += __builtin_amdgcn_exp2f(__builtin_fmaf(st[j][r], scale_log2, -hm[j]));
-          }
-        }
-      } else {
+      for (int j = 0; j < HPW; ++j) {
+        h[j] = hl[j];
 #pragma unroll
-        for (int j = 0; j < HPW; ++j) {
-          float z[2][4];
-          logits(kt, t, j, z);
-          float mx = -INFINITY;
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            h[j] += __builtin_amdgcn_exp2f(__builtin_fmaf(st[sub][j][r], scale_log2, -hm[j]));
+        redo = redo | !(h[j] <= hl[j] + 256.0f);
+      }
+    };
+    auto redo1 = [&](const f32x4 (&st)[2][HPW], float (&h)[HPW]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < HPW; ++j) {
+        const float mx = fmaxf(fmaxf(fmaxf(st[0][j][0], st[0][j][1]), fmaxf(st[0][j][2], st[0][j][3])),
+                               fmaxf(fmaxf(st[1][j][0], st[1][j][1]), fmaxf(st[1][j][2], st[1][j][3]))) *
+                         scale_log2;
+        const bool move = mx > hm[j] + kKlRescaleLog2;
+        const float mn = move ? mx : hm[j];
+        h[j] = hl[j] * __builtin_amdgcn_exp2f(hm[j] - mn);
+        hm[j] = mn;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            h[j] += __builtin_amdgcn_exp2f(__builtin_fmaf(st[sub][j][r], scale_log2, -hm[j]));
+      }
+    };
+    // Tiles with masked entries: the exact running max and sum.
+    auto masked1 = [&](const f32x4 (&st)[2][HPW], int t) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < HPW; ++j) {
+        float z[2][4];
+        logits(st, t, j, z);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, z[sub][r]);
+        const float mn = fmaxf(hm[j], mx);
+        if (mn != -INFINITY) {
+          float sum = 0.0f;
 #pragma unroll
           for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, z[sub][r]);
-          const float mn = fmaxf(hm[j], mx);
-          if (mn != -INFINITY) {
-            float sum = 0.0f;
-#pragma unroll
-            for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) sum += __builtin_amdgcn_exp2f(z[sub][r] - mn);
-            hl[j] = hl[j] * __builtin_amdgcn_exp2f(hm[j] - mn) + sum;
-            hm[j] = mn;
-          }
+            for (int r = 0; r < 4; ++r) sum += __builtin_amdgcn_exp2f(z[sub][r] - mn);
+          hl[j] = hl[j] * __builtin_amdgcn_exp2f(hm[j] - mn) + sum;
+          hm[j] = mn;
         }
       }
+    };
+    // Statistics of tile t (nothing for t < 0).
+    auto values1 = [&](const f32x4 (&st)[2][HPW], int t) __attribute__((always_inline)) {
+      float h[HPW];
+      bool redo = false;
+      if (static_cast<unsigned>(t) < static_cast<unsigned>(full_tiles)) {
+        sums1(st, h, redo);
+      } else {
+        if (t >= 0) masked1(st, t);
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) h[j] = hl[j];
+      }
+      if (__any(redo)) redo1(st, h);
+#pragma unroll
+      for (int j = 0; j < HPW; ++j) hl[j] = h[j];
+    };
+    // The indexer's own running statistics over the tile's scores.
+    auto score_stats = [&](const float (&sv)[RI]) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < RI; ++i) {
         if (sv[i] != -INFINITY) {
@@ -338,12 +387,32 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
         }
       }
     };
+    float sv_next[RI];
+    auto step1 = [&](auto b, int t, f32x4 (&cur)[2][HPW], f32x4 (&next)[2][HPW])
+        __attribute__((always_inline)) {
+      float sv[RI];
+      begin_step(b, t, sv, sv_next);
+      tile_dots(kl_kbuf<KB, decltype(b)::value>(), next);
+      values1(cur, t - 1);
+      score_stats(sv);
+    };
+    auto fast1 = [&](auto b, int t, f32x4 (&cur)[2][HPW], f32x4 (&next)[2][HPW])
+        __attribute__((always_inline)) {
+      float sv[RI];
+      begin_step(b, t, sv, sv_next);
+      float h[HPW];
+      bool redo = false;
+      tile_dots(kl_kbuf<KB, decltype(b)::value>(), next);
+      sums1(cur, h, redo);
+      interleave_mfma_valu<2 * HPW * C::KS, 3>();
+      if (__any(redo)) redo1(cur, h);
+#pragma unroll
+      for (int j = 0; j < HPW; ++j) hl[j] = h[j];
+      score_stats(sv);
+    };
     load_scores(0, sv_next);
     issue_tile(0, kl_kbuf<KB, 0>());
-    for (int t = 0; t < ntiles; t += 2) {
-      step1(B0{}, t);
-      if (t + 1 < ntiles) step1(B1{}, t + 1);
-    }
+    run_pass(fast1, step1, values1);
     // Whole-row statistics: the four lane quarters hold one row's keys.
     // hb[j] = log2 of the normaliser of head j: A = exp2(z - hb[j]).
     float hb[HPW];
@@ -374,46 +443,45 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
 #pragma unroll
     for (int i = 0; i < RI; ++i) kl[i] = 0.0f;
     const float inv_hq = 1.0f / static_cast<float>(n_heads_q);
-    // Tile t's gradient is stored in step t + 1, after that step's loads
-    // are issued, so the drain that opens step t + 2 finds the stores long
-    // done instead of waiting for them right after they were issued.
-    float gval[RI];
+    // Tile t's gradient is stored in step t + 2, after that step's loads
+    // are issued, so the drain that opens the next step finds the stores
+    // long done instead of waiting for them right after they were issued.
+    float gval[RI], sv_prev[RI];
     bool gok[RI];
 #pragma unroll
-    for (int i = 0; i < RI; ++i) { gval[i] = 0.0f; gok[i] = false; }
+    for (int i = 0; i < RI; ++i) { gval[i] = 0.0f; gok[i] = false; sv_prev[i] = -INFINITY; }
     auto store_grads = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < RI; ++i)
         if (gok[i]) grad[(first + e_row[i]) * ld_grad + t * kKlKeys + e_key[i]] = gval[i];
     };
-    auto step2 = [&](auto b, int t) __attribute__((always_inline)) {
-      const uint16_t* kt = kl_kbuf<KB, decltype(b)::value>();
-      float sv[RI];
-      begin_step(b, t, sv, sv_next);  // also: every wave is done with the partial sums
-      store_grads(t - 1);
-      float acc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-      if (t < full_tiles) {
+    // Each wave sums A = exp2(z - hb) over its heads for every (key, row)
+    // of the tile.
+    auto sums2 = [&](const f32x4 (&st)[2][HPW], float (&acc)[2][4]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-          f32x4 st[HPW];
-          dots_sub(kt, sub, one_g, st);
+      for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-          for (int j = 0; j < HPW; ++j)
+        for (int j = 0; j < HPW; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              acc[sub][r] += __builtin_amdgcn_exp2f(__builtin_fmaf(st[j][r], scale_log2, -hb[j]));
-        }
-      } else {
+          for (int r = 0; r < 4; ++r)
+            acc[sub][r] += __builtin_amdgcn_exp2f(__builtin_fmaf(st[sub][j][r], scale_log2, -hb[j]));
+    };
+    auto masked2 = [&](const f32x4 (&st)[2][HPW], int t, float (&acc)[2][4])
+        __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < HPW; ++j) {
-          float z[2][4];
-          logits(kt, t, j, z);
+      for (int j = 0; j < HPW; ++j) {
+        float z[2][4];
+        logits(st, t, j, z);
 #pragma unroll
-          for (int sub = 0; sub < 2; ++sub)
+        for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[sub][r] += __builtin_amdgcn_exp2f(z[sub][r] - hb[j]);
-        }
+          for (int r = 0; r < 4; ++r) acc[sub][r] += __builtin_amdgcn_exp2f(z[sub][r] - hb[j]);
       }
+    };
+    // The waves' sums go through LDS; after a barrier one thread per (row,
+    // key) adds them (/ Hq = P), forms ln Pi from the score and the row's
+    // normaliser, accumulates the KL term and keeps Pi - P for the store.
+    auto finish2 = [&](const float (&acc)[2][4], const float (&sv_t)[RI]) __attribute__((always_inline)) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -426,18 +494,59 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
 #pragma unroll
       for (int i = 0; i < RI; ++i) {
         const int r = e_row[i];
-        gok[i] = grad != nullptr && sv[i] != -INFINITY;
-        if (sv[i] != -INFINITY) {
+        gok[i] = grad != nullptr && sv_t[i] != -INFINITY;
+        if (sv_t[i] != -INFINITY) {
           float psum = 0.0f;
 #pragma unroll
           for (int w = 0; w < W; ++w) psum += ppart[(w * kKlRows + r) * kPStride + e_key[i]];
           const float P = psum * inv_hq;
-          const float lpi = sv[i] - lnorm[i];
+          const float lpi = sv_t[i] - lnorm[i];
           const float pi = __builtin_amdgcn_exp2f(lpi * kKlLog2e);
           if (P > 0.0f) kl[i] += P * (__builtin_amdgcn_logf(P) * kKlLn2 - lpi);
           gval[i] = pi - P;
         }
       }
+    };
+    // Tile t (nothing for t < 0), its scores in sv_prev.
+    auto values2 = [&](const f32x4 (&st)[2][HPW], int t) __attribute__((always_inline)) {
+      if (t < 0) return;
+      float acc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      if (t < full_tiles) sums2(st, acc);
+      else masked2(st, t, acc);
+      finish2(acc, sv_prev);
+    };
+    // Every step starts with: every wave is done reading the partial sums.
+    auto step2 = [&](auto b, int t, f32x4 (&cur)[2][HPW], f32x4 (&next)[2][HPW])
+        __attribute__((always_inline)) {
+      float sv[RI];
+      begin_step(b, t, sv, sv_next);
+      store_grads(t - 2);
+      tile_dots(kl_kbuf<KB, decltype(b)::value>(), next);
+      values2(cur, t - 1);
+#pragma unroll
+      for (int i = 0; i < RI; ++i) sv_prev[i] = sv[i];
+    };
+    auto fast2 = [&](auto b, int t, f32x4 (&cur)[2][HPW], f32x4 (&next)[2][HPW])
+        __attribute__((always_inline)) {
+      float sv[RI];
+      begin_step(b, t, sv, sv_next);
+      store_grads(t - 2);
+      float acc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      tile_dots(kl_kbuf<KB, decltype(b)::value>(), next);
+      sums2(cur, acc);
+      interleave_mfma_valu<2 * HPW * C::KS, 3>();
+      finish2(acc, sv_prev);
+#pragma unroll
+      for (int i = 0; i < RI; ++i) sv_prev[i] = sv[i];
+    };
+    // The last tile: once every wave is done with tile ntiles - 2's partial
+    // sums.
+    auto last2 = [&](const f32x4 (&st)[2][HPW], int t) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
+      lds_barrier();
+      store_grads(t - 1);
+      values2(st, t);
+      store_grads(t);
     };
     // Every wave is done with pass 1's last tile before tile 0 is copied
     // again.
@@ -445,11 +554,7 @@ __global__ __launch_bounds__(W * kWave) void indexer_kl_kernel(
     lds_barrier();
     load_scores(0, sv_next);
     issue_tile(0, kl_kbuf<KB, 0>());
-    for (int t = 0; t < ntiles; t += 2) {
-      step2(B0{}, t);
-      if (t + 1 < ntiles) step2(B1{}, t + 1);
-    }
-    store_grads(ntiles - 1);
+    run_pass(fast2, step2, last2);
     // Per-row loss: the row's 32 lanes.
 #pragma unroll
     for (int i = 0; i < RI; ++i) {
