@@ -28,13 +28,13 @@
 // Both kernels have a candidate mode for the fused indexer -> top-k: instead
 // of writing every score, the epilogue keeps the scores at or above the
 // row's threshold.  The two tiles of a pair finish their head sums together
-// (index_core.h), so each 64-key step ranks its survivors with one ballot and
-// writes them to the wave's LDS staging area with one LDS write per lane and
-// no branch.  The prefill kernel runs its rows whole (one key chunk), so a
-// wave owns its row's list: its staging ring is drained twice per stage from
-// inside the tile schedule, two range-checked stores per lane, the same
-// store count per stage as score mode, and no atomics.  The decode kernel
-// splits rows into chunks: each group of 8 tiles reserves room in the row's
+// (index_core.h), so each 64-key step ranks its survivors with one ballot.
+// The prefill kernel runs its rows whole (one key chunk), so a wave owns its
+// row's list and writes each step's survivors straight to it: one
+// range-checked 8-byte store per lane and step, the same store count as
+// score mode, no branch and no atomics.  The decode kernel splits rows into
+// chunks: survivors go to the wave's LDS staging area (one LDS write per
+// lane, no branch), and each group of 8 tiles reserves room in the row's
 // list with one atomic whose result is used a group later.  In score mode
 // both kernels can also score only every key_stride-th key (the fused path's
 // sample).
@@ -104,11 +104,12 @@ __device__ __forceinline__ uint32_t cand_reserve(uint32_t* count, uint32_t n, in
 
 // ---------------------------------------------------------------- prefill kernel
 
-// SK keys per LDS stage; CAND selects the candidate mode (no score rows):
-// the 8 waves' staging areas (SK entries plus 64 dump slots each, 20 KB at
-// SK = 256) sit beside the key stages (148 KB at d_idx = 128).  Candidate mode runs with
-// one key chunk (gridDim.y == 1): each wave then owns its row's list and
-// counter, so no atomics are needed.
+// SK keys per LDS stage; CAND selects the candidate mode (no score rows).
+// Candidate mode runs with one key chunk (gridDim.y == 1): each wave then
+// owns its row's list and counter, so no atomics are needed.  The 8 waves'
+// staging areas (SK entries plus 64 dump slots each, 20 KB at SK = 256, beside
+// the 128 KB of key stages at d_idx = 128) serve only workgroups whose rows
+// span several sequences.
 template <int D, int MT, int SK, bool CAND>
 __global__ __launch_bounds__(kBlockRows * kWave, 2) void index_scores_block(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
@@ -213,32 +214,25 @@ __global__ __launch_bounds__(kBlockRows * kWave, 2) void index_scores_block(
           16, dma_off, (t + i * KPI) * key_bytes, 0, 0);
     }
   };
-  // Candidate staging of this wave: a ring of SK entries (candidate mode
-  // launches one key chunk, so the wave owns its row's list).  `fill`
-  // survivors have been appended and `written` of them copied to the list;
-  // the tile loop drains the ring twice per stage (after tiles 1 and 5,
-  // when at most 128 entries wait and at most 128 more can arrive before
-  // the next drain), each drain two range-checked 8-byte stores per lane.
-  CandStage<CAND ? SK : 1, 1>& cs = cstage[CAND ? wave : 0];
-  uint32_t fill = 0, written = 0;
+  // Candidate mode launches one key chunk, so the wave owns its row's list
+  // and its count: each 64-key step stores its survivors straight to the
+  // list, ranked by ballot, with one range-checked 8-byte store per lane
+  // (lanes without a survivor, and entries past the list's capacity, get
+  // an offset outside the buffer and store nothing).  That is one store per
+  // 64 keys, as in score mode.
+  uint32_t fill = 0;
   const __amdgpu_buffer_rsrc_t lrs = raw_buffer(list, CAND ? o.cap * 8 : 0);
-  auto drain = [&]() {
-    if constexpr (CAND) {
-      const uint32_t n = fill - written;
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const uint32_t i = static_cast<uint32_t>(lane + kWave * r);
-        const uint2 e = cs.e[0][(written + i) & (SK - 1)];
-        const u32x2 ev = {e.x, e.y};
-        __builtin_amdgcn_raw_buffer_store_b64(ev, lrs, i < n ? (written + i) * 8 : 0x7FFFFFF0u, 0, 0);
-      }
-      written = fill;
-    }
-  };
   // The scores of 64 consecutive keys, key pos at this lane.
   auto emit = [&](float v, int32_t pos) {
     if constexpr (CAND) {
-      cand_append<true>(cs, 0, fill, v, pos, my_end, tau, lane);
+      const unsigned long long m =
+          __builtin_amdgcn_ballot_w64(pos < my_end) & __builtin_amdgcn_ballot_w64(v >= tau);
+      const uint32_t at = __builtin_amdgcn_mbcnt_hi(
+          static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), fill));
+      const u32x2 ev = {__float_as_uint(v), static_cast<uint32_t>(pos)};
+      __builtin_amdgcn_raw_buffer_store_b64(
+          ev, lrs, __builtin_amdgcn_inverse_ballot_w64(m) ? at * 8u : 0x7FFFFFF0u, 0, 0);
+      fill += static_cast<uint32_t>(__popcll(m));
     } else {
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), outs, pos * 4, 0, 0);
     }
@@ -291,7 +285,6 @@ __global__ __launch_bounds__(kBlockRows * kWave, 2) void index_scores_block(
       } else {       // tile tj - 1 closes one
         emit(pair_scores(held, part), pair_pos + lane);
       }
-      if (tj == 1 || tj == 5) drain();
       prev_pos = t0 + tj * 32;
       // Interleave this tile's MFMAs with the previous tile's epilogue (4 VALU
       // after each MFMA) and refill each B fragment right after the MFMA pair
@@ -306,10 +299,8 @@ __global__ __launch_bounds__(kBlockRows * kWave, 2) void index_scores_block(
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
       }
     }
-    // Wait for the next stage's DMA only: the stage's TILES / 2 score
-    // stores (candidate mode: its two drains' four stores) issued after it
-    // may stay in flight.
-    static_assert(TILES == 8, "two drains of two stores per stage match TILES / 2 stores");
+    // Wait for the next stage's DMA only: the stage's TILES / 2 score (or
+    // candidate) stores issued after it may stay in flight.
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(TILES / 2));
     lds_barrier();
     buf ^= 1;
@@ -317,12 +308,6 @@ __global__ __launch_bounds__(kBlockRows * kWave, 2) void index_scores_block(
   // The last stage's last tile (odd) closes the last pair.
   emit(pair_scores(held, tile_partial<D, MT>(st, acc_odd)), pair_pos + lane);
   if constexpr (CAND) {
-    // What is left in the ring: at most 192 entries.
-    for (uint32_t i = lane; written + i < fill; i += kWave) {
-      const uint2 e = cs.e[0][(written + i) & (SK - 1)];
-      const u32x2 ev = {e.x, e.y};
-      __builtin_amdgcn_raw_buffer_store_b64(ev, lrs, (written + i) * 8, 0, 0);
-    }
     if (active && lane == 0) *counter = fill;  // above cap: entries were dropped
   }
 }
@@ -389,7 +374,7 @@ __global__ __launch_bounds__(kStreamRows * kWave) void index_scores_stream(
           key * key_bytes + (s ^ (key & (CHUNKS - 1))) * 16, t * key_bytes, 0, 0);
     }
   };
-  // Candidate staging (see the prefill kernel): groups of kStreamGroup tiles.
+  // Candidate staging (cand_append): groups of kStreamGroup tiles.
   CandStage<CAND ? GROUP_KEYS : 1, 2>& cs = cstage[CAND ? wave : 0];
   uint2* list = CAND ? o.cand + local * o.cap : nullptr;
   uint32_t* counter = CAND ? o.count + local : nullptr;
