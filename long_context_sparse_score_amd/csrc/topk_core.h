@@ -462,12 +462,12 @@ struct TopkImpl {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    uint32_t thr0 = 0u;  // accept key > thr; 0 admits every finite score
-    if (n > kSampleMinRow) {
-      // Start threshold: the m-th largest of a spread sample (piece i of
-      // thread t: 4 elements at (t kSampleVec + i) / (kThreads kSampleVec) of
-      // the stream), m chosen so that about TARGET2 k / 2 elements of the
-      // stream are expected above it.
+    // Start threshold: the m-th largest of a spread sample (piece i of
+    // thread t: 4 elements at (t kSampleVec + i) / (kThreads kSampleVec) of
+    // the stream), m chosen so that about mult TARGET2 k / 2 elements of the
+    // stream are expected above it (0, admitting every finite score, when
+    // that rank is past the sample).  Block-wide.
+    auto sampled_thr = [&](int mult) __attribute__((always_inline)) -> uint32_t {
       uint32_t sk[4 * kSampleVec];
 #pragma unroll
       for (int i = 0; i < kSampleVec; ++i) {
@@ -480,17 +480,21 @@ struct TopkImpl {
         for (int e = 0; e < 4; ++e) sk[4 * i + e] = order_key_bits(b4[e]);
       }
       const int64_t want =
-          (static_cast<int64_t>(TARGET2 * k) * kSamples + 2 * static_cast<int64_t>(n) - 1) /
+          (static_cast<int64_t>(mult) * TARGET2 * k * kSamples + 2 * static_cast<int64_t>(n) - 1) /
           (2 * static_cast<int64_t>(n));
+      if (mult > 1 && want > kSamples) return 0u;
       const uint32_t m = static_cast<uint32_t>(want < 1 ? 1 : (want > kSamples ? kSamples : want));
       uint32_t tau, above, equal;
       select_kth(
           sh, m, [&](int j) { return sk[j % (4 * kSampleVec)]; },
           [](int j) { return j < 4 * kSampleVec; }, tau, above, equal);
       // Keys equal to tau are not admitted; lower it by one so they are.
-      thr0 = tau > 0u ? tau - 1u : 0u;
-    }
+      return tau > 0u ? tau - 1u : 0u;
+    };
+    // accept key > thr; 0 admits every finite score
+    const uint32_t thr0 = n > kSampleMinRow ? sampled_thr(1) : 0u;
     uint32_t thr = thr0;
+    int restarts = 0;
     uint32_t mine = 0u;  // this wave's segment fill (uniform within the wave)
     int parity = 0;
 #pragma unroll
@@ -631,8 +635,13 @@ struct TopkImpl {
       // fewer; the row then gets fewer positions, padded, and never loops).
       if (fl.total() >= static_cast<uint32_t>(k) || thr == 0u) break;
       // The sampled threshold was too high (fewer than k elements beat it and
-      // no cut happened): stream again from zero.
-      thr = 0u;
+      // no cut happened): stream again, first from the same sample's rank
+      // for four times as many survivors, then from zero.  (A restart from
+      // zero admits every score until the first cut and then cuts about
+      // k ln(n / k) / (CAP - k) more times.)
+      const uint32_t lower = restarts == 0 && n > kSampleMinRow ? sampled_thr(4) : 0u;
+      thr = lower < thr ? lower : 0u;
+      ++restarts;
       lim = admit_limit(thr);
       next = 0;
       mine = 0u;

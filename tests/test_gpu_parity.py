@@ -208,6 +208,47 @@ def test_topk_sample_threshold_too_high_restarts(pieces):
         _topk_case(s2, cu_q, cu_k, k, ld)
 
 
+@pytest.mark.parametrize("pieces,band", [(1024, (120, 300)), (512, (60, 150))])
+def test_topk_restart_from_a_deeper_sample_rank(pieces, band):
+    """Rows where the sampled start threshold admits fewer than k scores but
+    a threshold four times deeper in the same sample admits enough: the
+    sampled elements carry distinct large values (so the sample's order is
+    known), and 3000 other positions carry values between the sample's
+    band[0]-th and band[1]-th largest -- below the first threshold (rank
+    about 49 of 2048 samples in the many-rows configuration, 97 of 4096 in
+    the few-rows one, at n = 131072) and above the restart's (four times
+    that rank).  The row is then streamed a second time from the deeper
+    threshold rather than from zero; the result must equal the oracle
+    exactly.  (Should the sampling rule change, the test still checks
+    exactness; only this path may go unexercised.)"""
+    rng = np.random.default_rng(300 + pieces)
+    k = 2048
+    lk = [131072, 120000]
+    ld = 131072
+    s = (rng.standard_normal((len(lk), ld)) * 0.1).astype(np.float32)
+    for b, n in enumerate(lk):
+        hot = _sampled_positions(n, pieces)
+        h = len(hot)
+        s[b, hot] = 100.0 + rng.permutation(h).astype(np.float32)  # rank r: 100 + h - r
+        cold = np.setdiff1d(np.arange(n), hot)
+        warm = rng.choice(cold, 3000, replace=False)
+        lo, hi = 100.0 + h - band[1], 100.0 + h - band[0]
+        s[b, warm] = (lo + 0.5 + (hi - lo - 1.0) * rng.random(3000)).astype(np.float32)
+    log(f"topk restart from a deeper sample rank, {pieces} sample pieces")
+    if pieces == 1024:
+        cu_q = list(range(len(lk) + 1))
+        cu_k = np.concatenate([[0], np.cumsum(lk)]).tolist()
+        _topk_case(s, cu_q, cu_k, k, ld)
+    else:
+        pad = 600
+        lk2 = [1] * pad + lk
+        s2 = np.zeros((pad + len(lk), ld), np.float32)
+        s2[pad:] = s
+        cu_q = list(range(len(lk2) + 1))
+        cu_k = np.concatenate([[0], np.cumsum(lk2)]).tolist()
+        _topk_case(s2, cu_q, cu_k, k, ld)
+
+
 def test_topk_row_window():
     """A window of rows inside the packed batch writes only its own rows."""
     rng = np.random.default_rng(9)
