@@ -51,10 +51,12 @@ def parse():
     from long_context_sparse_score_amd.pipeline import BENCH_PREFILL
 
     ap.add_argument("--window", type=int, default=BENCH_PREFILL.window,
-                    help="prefill query rows per score window (2048 measured fastest of 512..8192)")
+                    help="prefill query rows per score window (with 1024-row attention "
+                         "launches, 8192 rows: 156.7-157.1 ms per 128K prefill against "
+                         "161.8-163.0 ms with 2048)")
     ap.add_argument("--attn-rows", type=int, default=BENCH_PREFILL.attn_rows,
                     help="split each window's attention into launches of this many rows "
-                         "(1024: 51.0 ms against 52.9 ms in one launch per 2048-row window)")
+                         "(1024: 50.6 ms against 50.9 ms with 512 and 51.9 ms with 2048)")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")

@@ -31,7 +31,7 @@ def _torch():
 class PrefillConfig:
     """Launch shape of a windowed prefill.  BENCH_PREFILL is the one bench.py
     times by default; the full-size parity tests run the same object."""
-    window: int = 2048      # query rows per score window (fp32 scores of one window in HBM)
+    window: int = 8192      # query rows per score window (fp32 scores of one window in HBM)
     attn_rows: int = 1024   # rows per attention launch inside a window
     fused: bool = False     # dsa_index_topk instead of dsa_index_scores -> dsa_topk
 
