@@ -130,6 +130,29 @@ def test_prefill_128k_repeatable():
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
 
 
+def test_prefill_128k_two_streams_bitwise_one_stream():
+    """The bench's two-stream prefill (each window's attention on a second
+    stream, overlapping the next window's indexer and top-k) in the bench's
+    launch configuration: outputs, lse and selections bitwise those of the
+    one-stream run, which the sampled test checks against the oracle."""
+    wl = synth.prefill_128k()
+    log("prefill_128k two streams: generate")
+    host, dev = device_workload(wl)
+    out1, lse1, idx1 = run_prefill(wl, dev)
+    vl = dsa.Varlen(wl.cu_q.tolist(), wl.cu_k.tolist())
+    bufs = pipeline.alloc_prefill(vl, wl.topk, CFG.window, overlap=True)
+    out2 = torch.zeros_like(out1)
+    lse2 = torch.zeros_like(lse1)
+    idx2 = torch.full_like(idx1, -7)
+    side = torch.cuda.Stream()
+    pipeline.prefill(vl, dev["q_idx"], dev["k_idx"], dev["w"], dev["q"], dev["k"], dev["v"], out2,
+                     bufs, lse=lse2, keep_indices=idx2, side_stream=side, attn_rows=CFG.attn_rows)
+    torch.cuda.synchronize()
+    assert torch.equal(idx1, idx2)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse1, lse2)
+
+
 def test_prefill_128k_topk_property_all_rows():
     """Every row of the 128K prefill, in the bench's score windows: the
     selection is causal, ascending, unique, min(k, p + 1) long, and exact for
