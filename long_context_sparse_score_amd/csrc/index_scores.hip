@@ -38,6 +38,8 @@
 // list with one atomic whose result is used a group later.  In score mode
 // both kernels can also score only every key_stride-th key (the fused path's
 // sample).
+#include <type_traits>
+
 #include "dsa_common.h"
 #include "dsa_internal.h"
 #include "index_core.h"
@@ -104,6 +106,16 @@ __device__ __forceinline__ uint32_t cand_reserve(uint32_t* count, uint32_t n, in
 
 // ---------------------------------------------------------------- prefill kernel
 
+// LDS key stage B of a prefill workgroup (ELEMS bf16).  Each stage buffer is
+// a variable of its own, so the compiler can tell the buffer a DMA is
+// filling from the one being read, and places no wait for the copy in
+// flight before reads of the other.
+template <int ELEMS, int B>
+__device__ __forceinline__ uint16_t* stage_buf() {
+  __shared__ __attribute__((aligned(16))) uint16_t buf[ELEMS];
+  return buf;
+}
+
 // SK keys per LDS stage; CAND selects the candidate mode (no score rows).
 // Candidate mode runs with one key chunk (gridDim.y == 1): each wave then
 // owns its row's list and counter, so no atomics are needed.  The 8 waves'
@@ -121,7 +133,6 @@ __global__ __launch_bounds__(kBlockRows * kWave, 2) void index_scores_block(
   constexpr int DMA_PER_WAVE = SK * CHUNKS / (kBlockRows * kWave);
   constexpr int TILES = SK / 32;                                    // 32-key MFMA tiles per stage
   static_assert(TILES % 2 == 0 && DMA_PER_WAVE * kBlockRows * kWave == SK * CHUNKS, "stage shape");
-  __shared__ __attribute__((aligned(16))) uint16_t tile[2][SK * D];
   __shared__ CandStage<CAND ? SK : 1, 1> cstage[CAND ? kBlockRows : 1];
   static_assert(!CAND || TILES * 32 <= SK, "a stage's survivors fit one half");
 
@@ -206,11 +217,11 @@ __global__ __launch_bounds__(kBlockRows * kWave, 2) void index_scores_block(
   const int key0 = (wave * kWave + lane) / CHUNKS, s0 = lane % CHUNKS;
   const int key_bytes = stride * D * 2;  // distance between consecutive keys of this launch
   const int dma_off = key0 * key_bytes + (s0 ^ (key0 & (CHUNKS - 1))) * 16;
-  auto fill_stage = [&](int b, int32_t t) {
+  auto fill_stage = [&](uint16_t* dst, int32_t t) {
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          keys, (__attribute__((address_space(3))) void*)(&tile[b][(i * kBlockRows + wave) * kWave * 8]),
+          keys, (__attribute__((address_space(3))) void*)(&dst[(i * kBlockRows + wave) * kWave * 8]),
           16, dma_off, (t + i * KPI) * key_bytes, 0, 0);
     }
   };
@@ -237,7 +248,9 @@ __global__ __launch_bounds__(kBlockRows * kWave, 2) void index_scores_block(
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), outs, pos * 4, 0, 0);
     }
   };
-  fill_stage(0, c0);
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  fill_stage(stage_buf<SK * D, 0>(), c0);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   lds_barrier();
   // Tile j's MFMAs run while tile j-1's epilogue executes on the VALU; each
@@ -251,10 +264,17 @@ __global__ __launch_bounds__(kBlockRows * kWave, 2) void index_scores_block(
   int32_t prev_pos = 1 << 28;  // key 0 of the previous tile (the first has none)
   int32_t pair_pos = 1 << 28;  // key 0 of the pending pair (the first emit is dropped)
   float held = 0.0f;           // partials of the pending pair's first tile
-  int buf = 0;
-  for (int32_t t0 = c0; t0 < c_end; t0 += SK) {
-    if (t0 + SK < c_end) fill_stage(buf ^ 1, t0 + SK);
-    const uint16_t* tb = tile[buf];
+  // One stage: keys [t0, t0 + SK) from stage buffer B, the next stage's DMA
+  // into the other buffer.
+  auto stage = [&](auto bsel, int32_t t0) __attribute__((always_inline)) {
+    constexpr int B = decltype(bsel)::value;
+    if (t0 + SK < c_end) fill_stage(stage_buf<SK * D, 1 - B>(), t0 + SK);
+    // The buffer's address is rebuilt every stage (a zero the compiler cannot
+    // see through): held across the loop, both buffers' per-lane read
+    // addresses would cost eight more registers.
+    int32_t zero = 0;
+    asm volatile("" : "+s"(zero));
+    const uint16_t* tb = stage_buf<SK * D, B>() + zero;
     bf16x8 b[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -303,7 +323,10 @@ __global__ __launch_bounds__(kBlockRows * kWave, 2) void index_scores_block(
     // candidate) stores issued after it may stay in flight.
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(TILES / 2));
     lds_barrier();
-    buf ^= 1;
+  };
+  for (int32_t t0 = c0; t0 < c_end; t0 += 2 * SK) {
+    stage(B0{}, t0);
+    if (t0 + SK < c_end) stage(B1{}, t0 + SK);
   }
   // The last stage's last tile (odd) closes the last pair.
   emit(pair_scores(held, tile_partial<D, MT>(st, acc_odd)), pair_pos + lane);
