@@ -43,6 +43,14 @@
 // transposed copies into the caller's workspace, with the LDS bank swizzle
 // part of the layout so that the DMA is a straight copy.  The GEMM operands
 // G [x > 0] and w qI are rounded to bf16.
+//
+// Stage buffers are separate LDS variables and the stage loops are unrolled
+// by two, and every LDS read's address stays a short chain of offsets from
+// its variable: only then does the compiler know which buffer an in-flight
+// DMA copy writes, and it places no wait for the next stage's copy before
+// reads of the current one (otherwise every stage began with a drain).
+#include <type_traits>
+
 #include "dsa_common.h"
 #include "dsa_internal.h"
 #include "index_core.h"
@@ -234,6 +242,26 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float (&m)[8]) {
   return __builtin_bit_cast(bf16x8, __builtin_convertvector(f, bf16v8));
 }
 
+// LDS stage buffers, one variable per (array, buffer) pair: with each stage's
+// buffer known at compile time the compiler can tell the buffer a DMA is
+// filling from the one being read and places no wait for the copy in flight
+// before reads of the other (one array indexed by the stage parity made it
+// drain every copy in flight at the start of each stage).
+template <typename T, int ELEMS, int ID, int B>
+__device__ __forceinline__ T* stage_lds() {
+  __shared__ __attribute__((aligned(16))) T buf[ELEMS];
+  return buf;
+}
+
+// A zero the compiler cannot see through: added to a stage buffer's address
+// at every stage, it keeps both buffers' per-lane addresses from being held
+// in registers across the stage loop.
+__device__ __forceinline__ int32_t opaque_zero() {
+  int32_t z = 0;
+  asm volatile("" : "+s"(z));
+  return z;
+}
+
 __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
@@ -255,9 +283,12 @@ __global__ __launch_bounds__(kDqRows * MT * kWave, 1) void index_bwd_dq_kernel(
   constexpr int KPI = NT / CH;  // keys per DMA instruction of the workgroup
   constexpr int DMA_K = SK * CH / NT;
   static_assert(KPI % CH == 0 && DMA_K * NT == SK * CH, "stage shape");
-  __shared__ __attribute__((aligned(16))) uint16_t ks_lds[2][SK * D];  // keys, swizzled rows
-  __shared__ __attribute__((aligned(16))) uint16_t kt_lds[2][SK * D];  // transposed tiles
-  __shared__ __attribute__((aligned(16))) float g_lds[2][kDqRows * SK];
+  // Stage buffers: keys (swizzled rows), transposed tiles, gradient rows.
+  auto ks_lds = [](auto bb) { return stage_lds<uint16_t, SK * D, 0, decltype(bb)::value>(); };
+  auto kt_lds = [](auto bb) { return stage_lds<uint16_t, SK * D, 1, decltype(bb)::value>(); };
+  auto g_lds = [](auto bb) { return stage_lds<float, kDqRows * SK, 2, decltype(bb)::value>(); };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
 
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
@@ -292,7 +323,6 @@ __global__ __launch_bounds__(kDqRows * MT * kWave, 1) void index_bwd_dq_kernel(
 
   const int f = wave * kWave + lane;
   const int key0 = f / CH, s0 = f % CH;
-  int buf = 0;
   for (int b = b_lo; b <= b_hi; ++b) {
     // Keys 0..pmax of sequence b, pmax the position of the block's last row in b.
     const int32_t q0 = cu_q[b], q1 = cu_q[b + 1], kb = cu_k[b], lk = cu_k[b + 1] - kb;
@@ -304,37 +334,44 @@ __global__ __launch_bounds__(kDqRows * MT * kWave, 1) void index_bwd_dq_kernel(
     const __amdgpu_buffer_rsrc_t rt =
         raw_buffer(kt + kt_tile(kb, b) * (32 * D), ((nkeys + 31) / 32) * D * 64);
     const __amdgpu_buffer_rsrc_t rg = raw_buffer(grad + local * ld, mine ? (ri.pos + 1) * 4 : 0);
-    auto fill = [&](int bb, int32_t c) {
+    auto fill = [&](auto bb, int32_t c) __attribute__((always_inline)) {
+      uint16_t* ksd = ks_lds(bb);
+      uint16_t* ktd = kt_lds(bb);
+      float* gd = g_lds(bb);
 #pragma unroll
       for (int i = 0; i < DMA_K; ++i) {
         const int key = c + i * KPI + key0;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rk, (__attribute__((address_space(3))) void*)(&ks_lds[bb][(i * NT + wave * kWave) * 8]),
+            rk, (__attribute__((address_space(3))) void*)(&ksd[(i * NT + wave * kWave) * 8]),
             16, key * (D * 2) + ((s0 ^ (key0 & (CH - 1))) * 16), 0, 0, 0);
       }
 #pragma unroll
       for (int i = 0; i < DMA_K; ++i) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rt, (__attribute__((address_space(3))) void*)(&kt_lds[bb][(i * NT + wave * kWave) * 8]),
+            rt, (__attribute__((address_space(3))) void*)(&ktd[(i * NT + wave * kWave) * 8]),
             16, c * (D * 2) + (i * NT + f) * 16, 0, 0, 0);
       }
-      if (mt == 0) {  // the row's first head wave fetches its gradient row
+      // The row's gradient: each of its head waves copies half of it.
 #pragma unroll
-        for (int i = 0; i < SK / kWave; ++i) {
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rg, (__attribute__((address_space(3))) void*)(&g_lds[bb][slot * SK + i * kWave]), 4,
-              (c + i * kWave + lane) * 4, 0, 0, 0);
-        }
+      for (int i = 0; i < SK / kWave / MT; ++i) {
+        const int o = (i * MT + mt) * kWave;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rg, (__attribute__((address_space(3))) void*)(&gd[slot * SK + o]), 4,
+            (c + o + lane) * 4, 0, 0, 0);
       }
     };
-    fill(buf, 0);
+    fill(B0{}, 0);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     lds_barrier();
-    for (int32_t c = 0; c < nkeys; c += SK) {
-      if (c + SK < nkeys) fill(buf ^ 1, c + SK);
-      const uint16_t* kst = ks_lds[buf];
-      const uint16_t* ktt = kt_lds[buf];
-      const float* gst = g_lds[buf] + slot * SK;
+    // One stage: keys [c, c + SK) from buffer bsel, the next stage's copy into
+    // the other buffer.
+    auto stage = [&](auto bsel, int32_t c) __attribute__((always_inline)) {
+      constexpr int B = decltype(bsel)::value;
+      if (c + SK < nkeys) fill(std::integral_constant<int, 1 - B>{}, c + SK);
+      const int32_t z = opaque_zero();
+      const uint16_t* kst = ks_lds(bsel) + z;
+      const uint16_t* ktt = kt_lds(bsel) + z;
+      const float* gst = g_lds(bsel);
       // A tile takes NF fragments from LDS: KS key fragments for x (A
       // operand, lane = key), then 2 ND transposed-key fragments for dq
       // (B operand, lane = d).  Each is read PF fragments ahead of its MFMA,
@@ -356,11 +393,11 @@ __global__ __launch_bounds__(kDqRows * MT * kWave, 1) void index_bwd_dq_kernel(
         float g[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float4 v = *reinterpret_cast<const float4*>(&gst[tj * 32 + 8 * i + 4 * half]);
-          g[4 * i] = v.x;
-          g[4 * i + 1] = v.y;
-          g[4 * i + 2] = v.z;
-          g[4 * i + 3] = v.w;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(&gst[slot * SK + tj * 32 + 8 * i + 4 * half]);
+          g[4 * i] = v[0];
+          g[4 * i + 1] = v[1];
+          g[4 * i + 2] = v[2];
+          g[4 * i + 3] = v[3];
         }
         // The schedule is pinned: the first PF fragment reads and the four
         // gradient reads go first, then every MFMA is followed by the read
@@ -396,7 +433,10 @@ __global__ __launch_bounds__(kDqRows * MT * kWave, 1) void index_bwd_dq_kernel(
       }
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       lds_barrier();
-      buf ^= 1;
+    };
+    for (int32_t c = 0; c < nkeys; c += 2 * SK) {
+      stage(B0{}, c);
+      if (c + SK < nkeys) stage(B1{}, c + SK);
     }
   }
   if (!active) return;
@@ -456,9 +496,13 @@ __global__ __launch_bounds__(kDkWaves * kWave, 1) void index_bwd_dk_kernel(
   constexpr int DMA_W = RS * D * HP / 8 / NT;           // chunks of a stage's transposed rows
   static_assert(DMA_Q * NT == QCH && DMA_W * NT * 8 == RS * D * HP, "stage shape");
   static_assert(RS * KB == NT, "one gradient word per thread and stage");
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[2][RS * HP * D];   // [row][head][chunk ^ head]
-  __shared__ __attribute__((aligned(16))) uint16_t w_lds[2][RS * D * HP];   // [row][d][phys chunk]
-  __shared__ __attribute__((aligned(16))) float g_lds[2][RS * KB];
+  // Stage buffers: queries [row][head][chunk ^ head], weighted transposed
+  // queries [row][d][phys chunk], gradient rows.
+  auto q_lds = [](auto bb) { return stage_lds<uint16_t, RS * HP * D, 3, decltype(bb)::value>(); };
+  auto w_lds = [](auto bb) { return stage_lds<uint16_t, RS * D * HP, 4, decltype(bb)::value>(); };
+  auto g_lds = [](auto bb) { return stage_lds<float, RS * KB, 5, decltype(bb)::value>(); };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
 
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
@@ -515,7 +559,10 @@ __global__ __launch_bounds__(kDkWaves * kWave, 1) void index_bwd_dk_kernel(
   const int f = wave * kWave + lane;
   // Stage resources start at the stage's first row, so offsets stay small
   // whatever the window size; rows past the window read as zeros.
-  auto fill = [&](int bb, int64_t r0) {
+  auto fill = [&](auto bb, int64_t r0) __attribute__((always_inline)) {
+    uint16_t* qd = q_lds(bb);
+    uint16_t* wd = w_lds(bb);
+    float* gd = g_lds(bb);
     const int64_t l0 = r0 - row_begin;  // window-local first row of the stage
     const int nrows = static_cast<int>(min(static_cast<int64_t>(RS), row_count - l0));
     const __amdgpu_buffer_rsrc_t rq = raw_buffer(q_idx + r0 * n_heads * D, nrows * n_heads * D * 2);
@@ -526,13 +573,13 @@ __global__ __launch_bounds__(kDkWaves * kWave, 1) void index_bwd_dk_kernel(
       const int r = c / (HP * CH), h = (c / CH) % HP, s = c % CH;
       const int src = (r * n_heads + h) * D * 2 + ((s ^ (h & (CH - 1))) * 16);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rq, (__attribute__((address_space(3))) void*)(&q_lds[bb][(i * NT + wave * kWave) * 8]),
+          rq, (__attribute__((address_space(3))) void*)(&qd[(i * NT + wave * kWave) * 8]),
           16, src, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < DMA_W; ++i) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rw, (__attribute__((address_space(3))) void*)(&w_lds[bb][(i * NT + wave * kWave) * 8]),
+          rw, (__attribute__((address_space(3))) void*)(&wd[(i * NT + wave * kWave) * 8]),
           16, (i * NT + f) * 16, 0, 0, 0);
     }
     // The gradient of the stage's rows at the block's keys: wave w fetches
@@ -543,7 +590,7 @@ __global__ __launch_bounds__(kDkWaves * kWave, 1) void index_bwd_dk_kernel(
     const __amdgpu_buffer_rsrc_t rg =
         raw_buffer(grad + (row - row_begin) * ld, row < r_hi ? (p + 1) * 4 : 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rg, (__attribute__((address_space(3))) void*)(&g_lds[bb][wave * kWave]), 4,
+        rg, (__attribute__((address_space(3))) void*)(&gd[wave * kWave]), 4,
         (key_lo + (wave % (KB / kWave)) * kWave + lane) * 4, 0, 0, 0);
   };
 
@@ -551,16 +598,19 @@ __global__ __launch_bounds__(kDkWaves * kWave, 1) void index_bwd_dk_kernel(
   // operand, lane = head), then 2 MT ND weighted-query fragments for dk
   // (B operand, lane = d); each is read PF fragments ahead of its MFMA.
   constexpr int NX = MT * KS, NF = NX + 2 * MT * ND, PF = 3;
-  int buf = 0;
-  fill(buf, r_lo);
+  fill(B0{}, r_lo);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   lds_barrier();
-  for (int64_t r0 = r_lo; r0 < r_hi; r0 += RS) {
-    if (r0 + RS < r_hi) fill(buf ^ 1, r0 + RS);
+  // One stage: rows [r0, r0 + RS) from buffer bsel, the next stage's copy
+  // into the other buffer.
+  auto stage = [&](auto bsel, int64_t r0) __attribute__((always_inline)) {
+    constexpr int B = decltype(bsel)::value;
+    if (r0 + RS < r_hi) fill(std::integral_constant<int, 1 - B>{}, r0 + RS);
+    const float* gs = g_lds(bsel);
 #pragma unroll
     for (int r = 0; r < RS; ++r) {
-      const uint16_t* qs = q_lds[buf] + r * HP * D;
-      const uint16_t* ws = w_lds[buf] + r * D * HP;
+      const uint16_t* qs = q_lds(bsel) + r * HP * D;
+      const uint16_t* ws = w_lds(bsel) + r * D * HP;
       auto frag = [&](int i) -> bf16x8 {
         if (i < NX) {  // x fragment (ks, mt) = (i / MT, i % MT)
           const int h = (i % MT) * 32 + col;
@@ -572,7 +622,7 @@ __global__ __launch_bounds__(kDkWaves * kWave, 1) void index_bwd_dk_kernel(
       bf16x8 fr[NF];
 #pragma unroll
       for (int i = 0; i < PF; ++i) fr[i] = frag(i);
-      const float g = g_lds[buf][r * KB + wave * 32 + col];
+      const float g = gs[r * KB + wave * 32 + col];
       __builtin_amdgcn_sched_group_barrier(0x100, PF + 1, 0);
       // x as heads x keys: lane = key, register v = head 32 mt + 8 (v / 4) +
       // 4 half + v % 4.
@@ -610,7 +660,10 @@ __global__ __launch_bounds__(kDkWaves * kWave, 1) void index_bwd_dk_kernel(
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     lds_barrier();
-    buf ^= 1;
+  };
+  for (int64_t r0 = r_lo; r0 < r_hi; r0 += 2 * RS) {
+    stage(B0{}, r0);
+    if (r0 + RS < r_hi) stage(B1{}, r0 + RS);
   }
   // dk[key, d] += acc: register v of tile nd is key 8 (v / 4) + 4 half +
   // v % 4 of this wave's 32, column d = 32 nd + col.
