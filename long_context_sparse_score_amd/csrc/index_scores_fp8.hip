@@ -19,6 +19,8 @@
 // with the same XOR swizzle of 16-byte chunks; the key scales travel with
 // them, and each tile's scale is read with its B fragments.  The LDS swizzle
 // differs from the bf16 kernels' because a key row is half as long.
+#include <type_traits>
+
 #include "dsa_common.h"
 #include "dsa_internal.h"
 
@@ -155,6 +157,25 @@ __device__ void row_direct8(const RowState8<D, MT>& st, const uint8_t* __restric
 
 // ---------------------------------------------------------------- prefill kernel
 
+// LDS stage buffers of the prefill kernel, one variable per (array, buffer):
+// with each stage's buffer known at compile time, the compiler can tell the
+// buffer an in-flight DMA copy fills from the one being read and places no
+// wait for the copy before reads of the other.
+template <typename T, int ELEMS, int ID, int B>
+__device__ __forceinline__ T* stage_lds8() {
+  __shared__ __attribute__((aligned(16))) T buf[ELEMS];
+  return buf;
+}
+
+// A zero the compiler cannot see through, added to a stage buffer's address
+// at every stage: both buffers' per-lane read addresses are then not held in
+// registers across the stage loop.
+__device__ __forceinline__ int32_t opaque_zero8() {
+  int32_t z = 0;
+  asm volatile("" : "+s"(z));
+  return z;
+}
+
 template <int D, int MT>
 __global__ __launch_bounds__(kBlockRows8 * kWave, 2) void index_scores_fp8_block(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch,
@@ -168,8 +189,11 @@ __global__ __launch_bounds__(kBlockRows8 * kWave, 2) void index_scores_fp8_block
   static_assert(TILES % 2 == 0 && DMA_PER_WAVE * kBlockRows8 * kWave == kStageKeys8 * CHUNKS,
                 "stage shape");
   static_assert(kStageKeys8 == kBlockRows8 * kWave, "every lane carries one key scale");
-  __shared__ __attribute__((aligned(16))) uint8_t tile[2][kStageKeys8 * D];
-  __shared__ float tscale[2][kStageKeys8];
+  // Stage buffers (key codes, key scales), one LDS variable each.
+  auto tile = [](auto bb) { return stage_lds8<uint8_t, kStageKeys8 * D, 0, decltype(bb)::value>(); };
+  auto tscale = [](auto bb) { return stage_lds8<float, kStageKeys8, 1, decltype(bb)::value>(); };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
 
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
@@ -213,15 +237,17 @@ __global__ __launch_bounds__(kBlockRows8 * kWave, 2) void index_scores_fp8_block
                 "the swizzle must repeat across DMA instructions");
   const int key0 = (wave * kWave + lane) / CHUNKS, s0 = lane % CHUNKS;
   const int dma_off = key0 * D + (s0 ^ swz<D>(key0)) * 16;
-  auto fill_stage = [&](int b, int32_t t) {
+  auto fill_stage = [&](auto b, int32_t t) __attribute__((always_inline)) {
+    uint8_t* td = tile(b);
+    float* sd = tscale(b);
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          keys, (__attribute__((address_space(3))) void*)(&tile[b][(i * kBlockRows8 + wave) * kWave * 16]),
+          keys, (__attribute__((address_space(3))) void*)(&td[(i * kBlockRows8 + wave) * kWave * 16]),
           16, dma_off, (t + i * KPI) * D, 0, 0);
     }
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          kscl, (__attribute__((address_space(3))) void*)(&tscale[b][wave * kWave]), 4, lane * 4,
+          kscl, (__attribute__((address_space(3))) void*)(&sd[wave * kWave]), 4, lane * 4,
           (t + wave * kWave) * 4, 0, 0);
   };
   auto store = [&](float v, int32_t pos) {
@@ -237,7 +263,7 @@ __global__ __launch_bounds__(kBlockRows8 * kWave, 2) void index_scores_fp8_block
     return join(lo, hi);
   };
 
-  fill_stage(0, c0);
+  fill_stage(B0{}, c0);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   lds_barrier();
   f32x16 acc_even[MT], acc_odd[MT];
@@ -245,14 +271,17 @@ __global__ __launch_bounds__(kBlockRows8 * kWave, 2) void index_scores_fp8_block
   for (int mt = 0; mt < MT; ++mt) acc_odd[mt] = f32x16{};
   float sk_even = 0.0f, sk_odd = 0.0f;
   int32_t prev_pos = 1 << 28;  // the first epilogue has nothing to store
-  int buf = 0;
-  for (int32_t t0 = c0; t0 < c_end; t0 += kStageKeys8) {
-    if (t0 + kStageKeys8 < c_end) fill_stage(buf ^ 1, t0 + kStageKeys8);
-    const uint8_t* tb = tile[buf];
+  // One stage: keys [t0, t0 + kStageKeys8) from buffer bsel, the next
+  // stage's copy into the other buffer.
+  auto stage = [&](auto bsel, int32_t t0) __attribute__((always_inline)) {
+    constexpr int BS = decltype(bsel)::value;
+    if (t0 + kStageKeys8 < c_end) fill_stage(std::integral_constant<int, 1 - BS>{}, t0 + kStageKeys8);
+    const uint8_t* tb = tile(bsel) + opaque_zero8();
+    const float* ts = tscale(bsel);
     i32x8 b[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) b[ks] = read_b(tb, col, ks);
-    sk_even = tscale[buf][col];
+    sk_even = ts[col];
     // The first tile's fragments stay out of the interleaving pattern below.
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -269,8 +298,8 @@ __global__ __launch_bounds__(kBlockRows8 * kWave, 2) void index_scores_fp8_block
         if (tj + 1 < TILES) b[ks] = read_b(tb, (tj + 1) * 32 + col, ks);
       }
       if (tj + 1 < TILES) {
-        if (tj & 1) sk_even = tscale[buf][(tj + 1) * 32 + col];
-        else sk_odd = tscale[buf][(tj + 1) * 32 + col];
+        if (tj & 1) sk_even = ts[(tj + 1) * 32 + col];
+        else sk_odd = ts[(tj + 1) * 32 + col];
       }
       store(sk_prev * tile_epilogue8<D, MT>(st, prev), prev_pos);
       prev_pos = t0 + tj * 32 + col;
@@ -293,7 +322,10 @@ __global__ __launch_bounds__(kBlockRows8 * kWave, 2) void index_scores_fp8_block
     // it may stay in flight.
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(TILES));
     lds_barrier();
-    buf ^= 1;
+  };
+  for (int32_t t0 = c0; t0 < c_end; t0 += 2 * kStageKeys8) {
+    stage(B0{}, t0);
+    if (t0 + kStageKeys8 < c_end) stage(B1{}, t0 + kStageKeys8);
   }
   store(((TILES - 1) & 1 ? sk_odd : sk_even) * tile_epilogue8<D, MT>(st, acc_odd), prev_pos);
 }
