@@ -358,7 +358,7 @@ __global__ __launch_bounds__(kStreamRows * kWave) void index_scores_stream(
   constexpr int DMA_PER_TILE = 32 * CHUNKS / kWave;   // 16-byte DMA instructions per tile
   constexpr int GROUP_KEYS = kStreamGroup * 32;       // keys per candidate reservation
   static_assert(DMA_PER_TILE * kWave == 32 * CHUNKS, "tile shape");
-  __shared__ __attribute__((aligned(16))) uint16_t ring[kStreamRows][kRing][32 * D];
+  static_assert(kRing == 4, "the tile loop below is unrolled by the ring depth");
   __shared__ CandStage<CAND ? GROUP_KEYS : 1, 2> cstage[CAND ? kStreamRows : 1];
   static_assert(kStreamGroup % 2 == 0, "groups of whole tile pairs");
   static_assert(!CAND || kStreamGroup * 32 <= GROUP_KEYS, "a group's survivors fit one half");
@@ -387,13 +387,20 @@ __global__ __launch_bounds__(kStreamRows * kWave) void index_scores_stream(
       raw_buffer(k_idx + (ri.key_base + static_cast<int64_t>(c0) * stride) * D,
                  ((c1 - c0 - 1) * stride + 1) * D * 2);
   const __amdgpu_buffer_rsrc_t outs = raw_buffer(CAND ? nullptr : o.scores + local * o.ld, CAND ? 0 : c1 * 4);
-  auto fill = [&](int slot, int32_t t) {  // tile of keys c0 + t .. c0 + t + 31
+  // Ring slot B of this wave.  Each slot is an LDS variable of its own and
+  // is picked at compile time, so the compiler sees that reading one slot
+  // does not wait for the DMA into another.
+  auto slot_buf = [&](auto bsel) -> uint16_t* {
+    return stage_buf<kStreamRows * 32 * D, decltype(bsel)::value>() + wave * (32 * D);
+  };
+  auto fill = [&](auto bsel, int32_t t) {  // tile of keys c0 + t .. c0 + t + 31
+    uint16_t* dst = slot_buf(bsel);
 #pragma unroll
     for (int i = 0; i < DMA_PER_TILE; ++i) {
       const int e = i * kWave + lane;
       const int key = e / CHUNKS, s = e % CHUNKS;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          keys, (__attribute__((address_space(3))) void*)(&ring[wave][slot][i * kWave * 8]), 16,
+          keys, (__attribute__((address_space(3))) void*)(dst + i * kWave * 8), 16,
           key * key_bytes + (s ^ (key & (CHUNKS - 1))) * 16, t * key_bytes, 0, 0);
     }
   };
@@ -431,11 +438,17 @@ __global__ __launch_bounds__(kStreamRows * kWave) void index_scores_stream(
   // Prologue: tiles 0 .. kRing-2, each followed by a dropped store (score
   // mode) so that every tile's DMA is trailed by the same count of memory
   // operations as in the loop.
-#pragma unroll
-  for (int p = 0; p < kRing - 1; ++p) {
-    fill(p, p * 32);
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  auto prologue = [&](auto bsel) {
+    fill(bsel, decltype(bsel)::value * 32);
     if constexpr (!CAND) __builtin_amdgcn_raw_buffer_store_b32(0, outs, 0x7FFFFFF0, 0, 0);
-  }
+  };
+  prologue(S0{});
+  prologue(S1{});
+  prologue(S2{});
   f32x16 acc[MT], prev[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) prev[mt] = f32x16{};
@@ -443,14 +456,18 @@ __global__ __launch_bounds__(kStreamRows * kWave) void index_scores_stream(
   int32_t prev_pos = 1 << 28;  // key 0 of the previous tile (the first has none)
   int32_t pair_pos = 1 << 28;  // key 0 of the pending pair (the first emit is dropped)
   float held = 0.0f;
-  const int ntiles = (c1 - c0 + 31) / 32;
-  for (int j = 0; j < ntiles; ++j) {
-    fill((j + kRing - 1) % kRing, (j + kRing - 1) * 32);
+  // Wave-uniform, so the loop exits below are scalar branches.
+  const int ntiles = __builtin_amdgcn_readfirstlane((c1 - c0 + 31) / 32);
+  // Tile j sits in slot j % kRing; the step for tile j refills slot
+  // (j - 1) % kRing, read by the step before, with tile j + kRing - 1.
+  auto step = [&](auto bsel, int j) {
+    constexpr int B = decltype(bsel)::value;
+    fill(std::integral_constant<int, (B + kRing - 1) % kRing>{}, (j + kRing - 1) * 32);
     // Tile j has landed once at most the kRing - 1 younger tiles' DMAs and
     // their trailing stores are outstanding.
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((kRing - 1) * (DMA_PER_TILE + TRAIL)));
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const uint16_t* tb = ring[wave][j % kRing];
+    const uint16_t* tb = slot_buf(bsel);
     bf16x8 b[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -459,11 +476,11 @@ __global__ __launch_bounds__(kStreamRows * kWave) void index_scores_stream(
     }
     tile_mfma<D, MT>(st, b, acc);
     const float part = tile_partial<D, MT>(st, prev);
-    if (j & 1) {  // tile j - 1 opens a pair
+    if constexpr (B & 1) {  // tile j - 1 opens a pair
       held = part;
       pair_pos = prev_pos;
       if constexpr (!CAND) __builtin_amdgcn_raw_buffer_store_b32(0, outs, 0x7FFFFFF0, 0, 0);
-    } else {      // tile j - 1 closes one
+    } else {                // tile j - 1 closes one
       emit(pair_scores(held, part), pair_pos + lane);
       // A group's worth of tiles emitted (the epilogue lags one tile).
       if (CAND && j % kStreamGroup == 0 && j > 0) group_end();
@@ -471,10 +488,23 @@ __global__ __launch_bounds__(kStreamRows * kWave) void index_scores_stream(
     prev_pos = c0 + j * 32;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) prev[mt] = acc[mt];
-    // The slot refilled next iteration was read above: those reads must be
+    // The slot refilled by the next step was read above: those reads must be
     // done before its DMA is issued.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  };
+  // Whole groups of kRing tiles, then the 0 .. kRing - 1 left: the loop has
+  // one exit, so its only way back to slot 0 is through slot 3 (the
+  // compiler's waits follow every control path).
+  int j = 0;
+  for (; j + kRing <= ntiles; j += kRing) {
+    step(S0{}, j);
+    step(S1{}, j + 1);
+    step(S2{}, j + 2);
+    step(S3{}, j + 3);
   }
+  if (j < ntiles) step(S0{}, j);
+  if (j + 1 < ntiles) step(S1{}, j + 1);
+  if (j + 2 < ntiles) step(S2{}, j + 2);
   // The last tile closes a pair (ntiles even) or opens one (ntiles odd,
   // closed by an empty tile past c1).
   {
