@@ -175,6 +175,25 @@ def test_fused_decode_small_varlen_and_groups():
         assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
 
 
+def test_fused_decode_stream_every_tail():
+    """Candidate mode of the per-wave streaming indexer on integer inputs,
+    with cache lengths that end a row or its last key chunk in every tail of
+    0-3 tiles after the groups of four: the fused selection equals the
+    unfused one and the oracle's (ties to the lower position)."""
+    lk = [1, 32, 33, 64, 96, 97, 128, 200, 224, 992, 1000, 1057, 1120, 1568, 1600, 2047]
+    wl = synth.Workload(name="fused_dec_tails", seed=45, seqlens_q=(1,) * len(lk),
+                        seqlens_k=tuple(lk), n_heads_q=8, n_heads_kv=2, head_dim=64,
+                        n_heads_idx=64, d_idx=128, topk=64, integer_indexer=True)
+    host, dev = device_workload(wl, ("q_idx", "k_idx", "w"))
+    vl = dsa.Varlen(wl.cu_q.tolist(), wl.cu_k.tolist())
+    log("fused decode tails")
+    got, counts, flags = fused(vl, dev, wl.topk, wl.batch)
+    ref = unfused(vl, dev, wl.topk, wl.batch)
+    assert torch.equal(got, ref)
+    ora = oracle_select(wl, host, np.arange(wl.batch))
+    check_topk_rows(got.cpu().numpy(), ora["idx"], ora["scores"], ora["counts"], wl.topk)
+
+
 def test_fused_prefill_pipeline_equals_unfused():
     """The whole prefill (windows, attention launches) fused and unfused:
     bitwise equal outputs and indices."""

@@ -313,6 +313,36 @@ def test_index_scores_real_valued_bound(hi, di):
         assert np.isnan(got[r, n:]).all()
 
 
+# Cache lengths for the decode-shaped indexer: it streams each (row, key
+# chunk) in groups of four 32-key tiles and then a tail of 0-3 tiles.  With
+# 512-key chunks these give every tail on rows of 1-7 tiles and on the last
+# chunk of chunked rows (992: 15 tiles, 1057: 2, 1120: 3, 1568: 1).
+DECODE_TAIL_LENGTHS = [1, 32, 33, 64, 96, 97, 128, 200, 224, 992, 1000, 1057, 1120, 1568, 1600,
+                       2047]
+
+
+@pytest.mark.parametrize("hi,di", [(64, 128), (4, 64)])
+def test_index_scores_decode_stream_every_tail(hi, di):
+    """One query per sequence (the per-wave streaming indexer) on integer
+    inputs: every score is an exact integer, so the kernel must reproduce the
+    oracle bit for bit whatever the tile count modulo four."""
+    lk = DECODE_TAIL_LENGTHS
+    wl = small_wl([1] * len(lk), lk, hi=hi, di=di, integer=True, seed=44 + hi)
+    host, dev = device_workload(wl, ("q_idx", "k_idx", "w"))
+    vl = varlen_for(wl)
+    ld = pipeline.score_ld(wl.max_seqlen_k)
+    scores = torch.full((wl.total_q, ld), float("nan"), dtype=torch.float32, device="cuda")
+    log(f"index_scores decode tails H={hi} d={di}")
+    dsa.dsa_index_scores(vl, dev["q_idx"], dev["k_idx"], dev["w"], scores)
+    got = scores.cpu().numpy().astype(np.float64)
+    ref = oracle.index_scores(wl.cu_q, wl.cu_k, host["q_idx"], host["k_idx"], host["w"],
+                              np.arange(wl.total_q), ld=ld)
+    causal = ~np.isnan(ref)
+    assert causal.sum() == sum(lk)
+    assert np.array_equal(got[causal], ref[causal])
+    assert np.isnan(got[~causal]).all()
+
+
 def test_index_scores_row_window_and_empty():
     wl = small_wl([700], [700], hi=64, di=128, seed=3)
     host, dev = device_workload(wl, ("q_idx", "k_idx", "w"))
